@@ -1,0 +1,204 @@
+"""Benchmark of the Muon per-owner update step on one MI355X.
+
+A step is one muon_step over every matrix of the workload (momentum, norm,
+Newton-Schulz, scale / weight decay / apply).  Inputs are synthetic and
+already resident in HBM when timing starts.  Default workload: the 4-layer
+transformer block set (d=1024, ffn=4096; 16 bf16 matrices, fp32 momentum).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--no-cpu-baseline]
+
+Prints one JSON line.  `value` is the NS throughput of the whole step:
+algorithmic (symmetric-aware) NS flops per step / measured step time.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2, help="workload number 1..5")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--tune", default="once", choices=["off", "once", "force"])
+    ap.add_argument("--cache", default=os.path.join(os.path.expanduser("~"), ".cache", "muon_mi355x",
+                                                    "tune.txt"))
+    ap.add_argument("--no-kernel-times", action="store_true")
+    return ap.parse_args()
+
+
+def make_inputs(wl, torch):
+    """Device-resident params / grads (workload's laws, fixed torch generator) and zero momenta."""
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(1234 + wl.cfg)
+    dt = torch.float32 if wl.dtype == "f32" else torch.bfloat16
+    P, G, B = [], [], []
+    for (r, c) in wl.shapes:
+        w = torch.randn(r, c, device="cuda", generator=gen) * wl.w_scale
+        if wl.grad_law == "student_t":
+            # t(3) = N / sqrt(chi2_3 / 3)
+            z = torch.randn(r, c, device="cuda", generator=gen)
+            chi = sum(torch.randn(r, c, device="cuda", generator=gen) ** 2 for _ in range(3))
+            g = z / torch.sqrt(chi / 3.0) * wl.grad_scale
+        else:
+            g = torch.randn(r, c, device="cuda", generator=gen) * wl.grad_scale
+        P.append(w.to(dt).contiguous())
+        G.append(g.to(dt).contiguous())
+        B.append(torch.zeros(r, c, device="cuda", dtype=torch.float32))
+    return P, G, B
+
+
+def cpu_baseline(wl, ns_flops_per_step):
+    """The fp64 oracle on the host cores, on a bounded sample of the same workload."""
+    import numpy as np
+    import workloads as WL
+    from oracle import muon_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
+    except Exception:
+        threads = os.cpu_count()
+    h = wl.hyper
+    # sample: whole steps of the workload (every matrix), repeated for >= 10 s (at most 3)
+    mats = [(WL.draw(wl, i, 0, WL.KIND_W).value, WL.draw(wl, i, 0, WL.KIND_G).value)
+            for i in range(wl.n_matrices)]
+    done, t0 = 0, time.perf_counter()
+    while True:
+        for W, g in mats:
+            O.muon_step_ref(W, g, np.zeros_like(W), lr=h.lr, beta=h.beta, wd=h.wd,
+                            ns_steps=h.ns_steps, coeffs=h.coeffs, eps=h.eps,
+                            param_dtype=wl.dtype)
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= 10.0 or done >= 3:
+            break
+    sec = el / done
+    return {"value": ns_flops_per_step / sec / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle", "ms_per_step": sec * 1e3,
+            "sample": f"{done} full step(s) of workload {wl.cfg} ({wl.n_matrices} matrices), "
+                      f"fp64 numpy, input generation excluded"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU runs are not "
+                                   "supported (matrices would be sharded whole across owners)"}))
+        sys.exit(2)
+    import torch
+    import workloads as WL
+    import matrix_orthogonalizing_optimizer_muon_amd as MU
+
+    wl = WL.workload(args.config)
+    torch.cuda.init()
+    os.makedirs(os.path.dirname(args.cache), exist_ok=True)
+    t0 = time.perf_counter()
+    plan = MU.MuonPlan(wl.shapes, wl.dtype, tune=args.tune, cache_path=args.cache)
+    plan_s = time.perf_counter() - t0
+    info = plan.info()
+    P, G, B = make_inputs(wl, torch)
+    h = wl.hyper
+    stream = torch.cuda.current_stream()
+
+    def step():
+        plan.step(P, G, B, lr=h.lr, beta=h.beta, wd=h.wd, ns_steps=h.ns_steps, coeffs=h.coeffs)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"# warmup done ({args.warmup} steps), timing {args.steps}", file=sys.stderr, flush=True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    per = []
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        s0 = torch.cuda.Event(enable_timing=True)
+        s1 = torch.cuda.Event(enable_timing=True)
+        s0.record(stream)
+        step()
+        s1.record(stream)
+        per.append((s0, s1))
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    total_ms = e0.elapsed_time(e1)
+    ms = total_ms / args.steps
+    step_ms = sorted(a.elapsed_time(b) for a, b in per)
+    p = lambda q: step_ms[min(len(step_ms) - 1, int(q * len(step_ms)))]
+
+    # per-kernel HIP-event times (the library records them on the step's stream)
+    kt = []
+    if not args.no_kernel_times:
+        plan.set_profiling(True)
+        plan.kernel_times(reset=True)
+        for _ in range(args.steps):
+            step()
+        kt = plan.kernel_times(reset=True)
+        plan.set_profiling(False)
+    ns_flops = info["ns_flops_min"]
+    bf16 = wl.dtype == "bf16"
+    peak = PEAK_BF16_TFLOPS if bf16 else PEAK_FP32_TFLOPS
+    ns_kinds = [k for k in kt if k["flops"] > 0]
+    ew_kinds = [k for k in kt if k["bytes"] > 0]
+    ns_ms = sum(k["total_ms"] for k in ns_kinds) / max(args.steps, 1)
+    roofline = None
+    if ns_kinds:
+        dom = max(ns_kinds, key=lambda k: k["total_ms"])
+        avg_ms = dom["total_ms"] / dom["launches"]
+        ach = dom["flops"] / dom["launches"] / (avg_ms * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "kernel": dom["name"], "achieved": round(ach, 2),
+                    "peak": peak, "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": None,
+                    "avg_launch_us": round(avg_ms * 1e3, 2),
+                    "flops_per_launch": dom["flops"] / dom["launches"]}
+    ew = {}
+    for k in ew_kinds:
+        avg_ms = k["total_ms"] / k["launches"]
+        gbs = k["bytes"] / k["launches"] / (avg_ms * 1e-3) / 1e9
+        ew[k["name"]] = {"GB/s": round(gbs, 1), "frac_of_hbm": round(gbs / PEAK_HBM_GBS, 4),
+                         "avg_launch_us": round(avg_ms * 1e3, 2)}
+    value = ns_flops / (ms * 1e-3) / 1e12
+    out = {
+        "metric": "Muon optimizer-step ms + NS TFLOP/s (% of MI355X bf16 MFMA peak)",
+        "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if bf16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "matrices": wl.n_matrices, "elements": wl.n_elements,
+                   "ns_steps": h.ns_steps, "coeffs": list(h.coeffs), "lr": h.lr, "beta": h.beta,
+                   "wd": h.wd, "parallelism": "single GPU"},
+        "step_ms_p10_p50_p90": [round(p(0.1), 4), round(p(0.5), 4), round(p(0.9), 4)],
+        "ns_flops_per_step": ns_flops, "ns_flops_issued_per_step": info["ns_flops_issued"],
+        "ns_ms_per_step": round(ns_ms, 4) if kt else None,
+        "ns_tflops_kernels": round(ns_flops / (ns_ms * 1e-3) / 1e12, 2) if ns_ms else None,
+        "ns_frac_of_peak": round(ns_flops / (ns_ms * 1e-3) / 1e12 / peak, 4) if ns_ms else None,
+        "step_frac_of_peak": round(value / peak, 4),
+        "elementwise": ew, "roofline": roofline,
+        "kernels": [{"name": k["name"], "launches_per_step": k["launches"] / args.steps,
+                     "ms_per_step": round(k["total_ms"] / args.steps, 4)} for k in kt],
+        "plan": {"groups": info["n_groups"], "chunks": info["n_chunks"], "gram": info["n_gram"],
+                 "workspace_gb": round(info["workspace_bytes"] / 1e9, 3),
+                 "create_s": round(plan_s, 3), "hash": info["plan_hash"]},
+        "wall_s_timed": round(wall, 3),
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print("# cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(wl, ns_flops)
+    plan.close()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

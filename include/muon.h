@@ -1,0 +1,216 @@
+/*
+ * muon.h - C ABI of the MI355X (gfx950) Muon per-owner update step.
+ *
+ * One call of muon_step performs, for every weight matrix of a plan, the Muon
+ * update as the pages describe it:
+ *   - "DeepSpeed now supports Muon" (setupai.cc), section "technical deep
+ *     dive": Newton-Schulz (NS) iterations orthogonalize the momentum-based
+ *     update of 2-D weight matrices; weight decay is decoupled; each
+ *     parameter's update is scaled so its RMS matches AdamW's, letting AdamW's
+ *     lr and wd carry over.
+ *   - DMuon announcement (wjxwpt.net), improvement 2 "shape-adaptive execution
+ *     stack": per shape the mathematical form (matrix space or m x m Gram
+ *     space, item 1), the execution mode (alone or batched with other matrices)
+ *     and the kernel change; the step does not change the update rule.
+ *   - DMuon announcement (zaocj.com), second of the "three moves": many kernels
+ *     are tried on a new shape, the fastest is kept and reused for that shape.
+ *
+ * Per matrix W (rows x cols), gradient g and fp32 momentum buf:
+ *   buf <- beta*buf + g;  d <- g + beta*buf           (Nesterov; plain: d <- buf)
+ *   X0  <- d / (||d||_F + eps)
+ *   X   <- NS_T(X0): T times  A = X X^T, B = b A + c A^2, X <- a X + B X
+ *          (on the smaller side: tall matrices are iterated as their transpose)
+ *   W   <- W - lr * (wd * W + s * X),   s = rms_scale * sqrt(max(rows, cols))
+ * Both terms of the last line use the old W.  fp32 matrices take an fp32 NS;
+ * bf16 matrices take bf16 MFMA operands with fp32 accumulation.
+ *
+ * Conventions for every entry point:
+ *   - returns a muon_status; MUON_OK is 0.  No C++ exception crosses the ABI.
+ *     muon_last_error() returns a thread-local message about the last failure.
+ *   - "device pointer" means memory on the HIP device that was current when the
+ *     plan was created; "host pointer" means ordinary process memory.
+ *   - matrices are dense row-major, rows x cols, leading dimension = cols.
+ *   - a stream argument is a hipStream_t passed as void* (NULL = null stream).
+ */
+#ifndef MUON_MI355X_H
+#define MUON_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MUON_ABI_VERSION 1
+
+typedef enum muon_status {
+  MUON_OK = 0,
+  MUON_EINVAL = 1,        /* bad argument (NULL pointer, negative count, non-finite scalar) */
+  MUON_EUNSUPPORTED = 2,  /* unsupported dtype, zero-size matrix, no gfx950 device */
+  MUON_ENOMEM = 3,        /* device or pinned-host allocation failed / over the workspace cap */
+  MUON_EHIP = 4,          /* a HIP runtime call or kernel launch failed */
+  MUON_ESTATE = 5         /* call not valid for this plan (e.g. step on a host-only plan) */
+} muon_status;
+
+typedef enum muon_dtype { MUON_F32 = 0, MUON_BF16 = 1 } muon_dtype;
+
+typedef enum muon_precision {
+  MUON_PRECISION_AUTO = 0,  /* fp32 NS for fp32 params, bf16 MFMA NS for bf16 params */
+  MUON_PRECISION_FP32 = 1,  /* fp32 NS for every matrix */
+  MUON_PRECISION_BF16 = 2   /* bf16 MFMA NS for every matrix */
+} muon_precision;
+
+typedef enum muon_form {
+  MUON_FORM_AUTO = 0,    /* the planner chooses per shape (timed once, or by cost model) */
+  MUON_FORM_DIRECT = 1,  /* NS in the m x n matrix space */
+  MUON_FORM_GRAM = 2     /* NS recursion in the m x m Gram space, X_T = Q_T X0 */
+} muon_form;
+
+typedef enum muon_tune {
+  MUON_TUNE_OFF = 0,   /* never time: analytic cost model only (deterministic) */
+  MUON_TUNE_ONCE = 1,  /* use the cache; time and record shapes it does not hold */
+  MUON_TUNE_FORCE = 2  /* time every shape again and rewrite its cache entries */
+} muon_tune;
+
+/* One weight matrix.  The gradient has the parameter's dtype; the momentum is fp32. */
+typedef struct muon_matrix_desc {
+  int64_t rows;
+  int64_t cols;
+  int32_t dtype;     /* muon_dtype of the parameter and its gradient */
+  int32_t reserved;  /* must be 0 */
+} muon_matrix_desc;
+
+typedef struct muon_plan_opts {
+  uint32_t struct_size;         /* sizeof(muon_plan_opts); set by muon_plan_opts_default */
+  int32_t nesterov;             /* 1 (default): d = g + beta*buf;  0: d = buf */
+  float eps;                    /* added to ||d||_F before dividing; default 1e-7 */
+  float rms_scale;              /* s = rms_scale * sqrt(max(rows, cols)); default 0.2 */
+  int32_t precision;            /* muon_precision, default AUTO */
+  int32_t form;                 /* muon_form, default AUTO */
+  int32_t tune;                 /* muon_tune, default ONCE (OFF when no cache path is known) */
+  int32_t host_only;            /* 1: plan on the host only - no device, no workspace, no
+                                   timing; muon_step refuses such a plan (planner tests) */
+  uint64_t workspace_cap_bytes; /* 0: default (48 GiB).  Matrices are processed in chunks
+                                   whose workspace fits the cap; one matrix over it: ENOMEM */
+  const char* cache_path;       /* tune cache file; NULL: $MUON_TUNE_CACHE, else no cache */
+} muon_plan_opts;
+
+typedef struct muon_plan muon_plan;
+
+/* Summary of a plan (host memory, filled by muon_plan_info). */
+typedef struct muon_plan_info {
+  int32_t n_matrices;
+  int32_t n_groups;           /* distinct (canonical shape, precision, form, tile) keys */
+  int32_t n_chunks;           /* workspace chunks (1 unless the cap forces more) */
+  int32_t n_gram;             /* matrices that run the Gram-space form */
+  uint64_t workspace_bytes;   /* device workspace the plan owns */
+  double ns_flops_min;        /* per step at the default T = 5: symmetric-aware algorithmic flops */
+  double ns_flops_issued;     /* per step at T = 5: flops the chosen tiles actually issue */
+  double ew_bytes;            /* per step: algorithmic HBM bytes of the elementwise kernels */
+  uint64_t plan_hash;         /* FNV-1a of the canonical serialization */
+} muon_plan_info;
+
+/* Per-kernel timing collected while profiling is on (see muon_plan_set_profiling). */
+typedef struct muon_kernel_time {
+  char name[32];        /* kernel kind, e.g. "ns_apply", "ew_momentum" */
+  int64_t launches;     /* launches timed */
+  double total_ms;      /* summed hipEvent time of those launches */
+  double flops;         /* summed algorithmic flops of those launches (0 for elementwise) */
+  double bytes;         /* summed algorithmic HBM bytes of those launches */
+} muon_kernel_time;
+
+/* Fills *opts with the defaults listed above.  NULL: EINVAL. */
+int muon_plan_opts_default(muon_plan_opts* opts);
+
+/*
+ * Builds a plan for n matrices (descs: host array of n).  Groups matrices by
+ * canonical shape (m = min(rows, cols), n = max) and precision; picks per group
+ * the NS form and tile configuration (timed once and cached, or by the cost
+ * model); lays the groups out in chunks under the workspace cap; allocates the
+ * device workspace on the current HIP device (except host_only).  The plan owns
+ * its workspace; release it with muon_plan_destroy.  Given the same descs,
+ * options and cache contents the plan is byte-identical (muon_plan_serialize).
+ * opts NULL: defaults.  Errors: EINVAL (NULL descs/out, n <= 0, reserved != 0),
+ * EUNSUPPORTED (dtype, rows or cols < 1, no gfx950 device), ENOMEM, EHIP.
+ */
+int muon_plan_create(const muon_matrix_desc* descs, int n, const muon_plan_opts* opts,
+                     muon_plan** out);
+
+/* Frees the plan and its workspace (waits for the device first).  NULL: no-op, OK. */
+int muon_plan_destroy(muon_plan* plan);
+
+/*
+ * One Muon step over all matrices of the plan, enqueued on `stream`; returns
+ * without waiting for the device.  params, grads, momenta: host arrays of n
+ * device pointers in the order of the plan's descs (params and grads in the
+ * matrix dtype, momenta fp32).  params and momenta are updated in place; grads
+ * are read only.  coeffs: host pointer to (a, b, c) used at every NS step, or
+ * NULL for (3.4445, -4.7750, 2.0315).  ns_steps = 0 applies the normalized
+ * Nesterov direction.  The plan's workspace is shared by its calls: do not run
+ * two steps of one plan concurrently on different streams.
+ * Errors: EINVAL (NULL array or entry, ns_steps < 0 or > 64, non-finite scalar),
+ * ESTATE (host-only plan), EHIP (launch failure).
+ */
+int muon_step(muon_plan* plan, void* const* params, const void* const* grads,
+              float* const* momenta, float lr, float beta, float wd, int ns_steps,
+              const float* coeffs, void* stream);
+
+/* As muon_step with a per-step coefficient schedule: coeffs holds 3*ns_steps
+ * floats, (a_k, b_k, c_k) for step k.  coeffs may be NULL only if ns_steps = 0. */
+int muon_step_schedule(muon_plan* plan, void* const* params, const void* const* grads,
+                       float* const* momenta, float lr, float beta, float wd, int ns_steps,
+                       const float* coeffs, void* stream);
+
+/*
+ * Test hook: while set, every muon_step also writes the fp32 update
+ * U = -lr * (wd * W + s * X_T) of matrix i, before rounding to the parameter
+ * dtype, to dst[i] (device pointer, rows x cols fp32, row-major).  dst is a host
+ * array of n device pointers (an entry may be NULL); dst = NULL turns it off.
+ */
+int muon_plan_set_update_capture(muon_plan* plan, float* const* dst);
+
+/*
+ * Non-finite detection: bit 0 of *flags is set when some matrix had a
+ * non-finite ||d||_F in a step since the last clear (its X is then NaN and so
+ * is its update).  Synchronizes the device.  clear != 0 resets the flag.
+ */
+int muon_plan_get_flags(muon_plan* plan, uint32_t* flags, int clear);
+
+/*
+ * Canonical plan bytes (groups, forms, tiles, chunks, launch order).  buf NULL:
+ * *len receives the size.  Otherwise *len is the capacity of buf; too small: EINVAL.
+ */
+int muon_plan_serialize(const muon_plan* plan, void* buf, size_t* len);
+
+/* Fills *info.  EINVAL on NULL. */
+int muon_plan_info_get(const muon_plan* plan, muon_plan_info* info);
+
+/*
+ * Per-matrix decision: form (muon_form DIRECT or GRAM), group index and chunk
+ * index of matrix i.  Any out pointer may be NULL.
+ */
+int muon_plan_matrix_choice(const muon_plan* plan, int i, int32_t* form, int32_t* group,
+                            int32_t* chunk);
+
+/*
+ * Profiling: while enabled, muon_step records a hipEvent pair around each
+ * kernel launch on the step's stream.  muon_plan_get_kernel_times synchronizes,
+ * folds the recorded pairs into per-kind totals and writes up to max entries to
+ * out (host array), the count to *n_out.  reset != 0 clears the totals after.
+ */
+int muon_plan_set_profiling(muon_plan* plan, int enable);
+int muon_plan_get_kernel_times(muon_plan* plan, muon_kernel_time* out, int max, int* n_out,
+                               int reset);
+
+/* Thread-local text of the last error on this thread ("" if none).  Never NULL. */
+const char* muon_last_error(void);
+
+/* MUON_ABI_VERSION of the library. */
+int muon_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MUON_MI355X_H */

@@ -1,0 +1,208 @@
+"""MI355X (gfx950) Muon per-owner update step.
+
+Python binding of libmuon_mi355x.so (C ABI in include/muon.h).  This module
+only marshals arguments: it checks that the tensors it is handed match the
+plan (shape, dtype, device, contiguity) so no kernel is launched on mismatched
+memory, and passes raw device pointers to the library.  Every step of the
+update runs in the library's HIP kernels; there is no fallback path.
+
+    plan = MuonPlan([(3072, 1024), (1024, 1024)], "bf16")
+    plan.step(params, grads, momenta, lr=0.02, beta=0.95, wd=0.01)
+"""
+import ctypes
+
+from . import _lib as L
+from ._lib import MuonError  # noqa: F401
+
+__all__ = ["MuonPlan", "MuonError", "library_path"]
+
+
+def library_path():
+    return L.LIB_PATH
+
+
+def _dtype_code(d):
+    if isinstance(d, int):
+        return d
+    s = str(d).replace("torch.", "")
+    if s in ("f32", "float32", "fp32", "float"):
+        return L.MUON_F32
+    if s in ("bf16", "bfloat16"):
+        return L.MUON_BF16
+    raise ValueError(f"unsupported dtype {d!r}")
+
+
+class MuonPlan:
+    """A plan over a fixed list of matrix shapes (see muon_plan_create)."""
+
+    def __init__(self, shapes, dtypes, *, nesterov=True, eps=1e-7, rms_scale=0.2,
+                 precision="auto", form="auto", tune="once", cache_path=None,
+                 workspace_cap=0, host_only=False):
+        lib = L.lib()
+        shapes = [(int(r), int(c)) for r, c in shapes]
+        if isinstance(dtypes, (list, tuple)):
+            codes = [_dtype_code(d) for d in dtypes]
+        else:
+            codes = [_dtype_code(dtypes)] * len(shapes)
+        if len(codes) != len(shapes):
+            raise ValueError("one dtype per shape")
+        self.shapes = shapes
+        self.dtypes = codes
+        n = len(shapes)
+        descs = (L.MatrixDesc * max(n, 1))()
+        for i, ((r, c), d) in enumerate(zip(shapes, codes)):
+            descs[i].rows, descs[i].cols, descs[i].dtype, descs[i].reserved = r, c, d, 0
+        opts = L.PlanOpts()
+        L.check(lib.muon_plan_opts_default(ctypes.byref(opts)))
+        opts.nesterov = 1 if nesterov else 0
+        opts.eps = eps
+        opts.rms_scale = rms_scale
+        opts.precision = L.PRECISION[precision]
+        opts.form = L.FORM[form]
+        opts.tune = L.TUNE[tune]
+        opts.host_only = 1 if host_only else 0
+        opts.workspace_cap_bytes = int(workspace_cap)
+        self._cache = cache_path.encode() if cache_path else None
+        opts.cache_path = self._cache
+        handle = ctypes.c_void_p()
+        L.check(lib.muon_plan_create(descs, n, ctypes.byref(opts), ctypes.byref(handle)))
+        self._h = handle
+        self._capture = None
+
+    # ---------------------------------------------------------------- lifetime
+    def close(self):
+        if getattr(self, "_h", None):
+            L.lib().muon_plan_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    # ------------------------------------------------------------------ checks
+    def _check_tensors(self, name, ts, want_dtype_codes):
+        import torch
+        if len(ts) != len(self.shapes):
+            raise ValueError(f"{name}: expected {len(self.shapes)} tensors, got {len(ts)}")
+        dev = None
+        for i, (t, shp, dc) in enumerate(zip(ts, self.shapes, want_dtype_codes)):
+            if not isinstance(t, torch.Tensor):
+                raise TypeError(f"{name}[{i}] is not a tensor")
+            if not t.is_cuda:
+                raise ValueError(f"{name}[{i}] is not on the GPU")
+            if tuple(t.shape) != shp:
+                raise ValueError(f"{name}[{i}] has shape {tuple(t.shape)}, plan says {shp}")
+            want = torch.float32 if dc == L.MUON_F32 else torch.bfloat16
+            if t.dtype != want:
+                raise ValueError(f"{name}[{i}] has dtype {t.dtype}, plan says {want}")
+            if not t.is_contiguous():
+                raise ValueError(f"{name}[{i}] is not contiguous")
+            if dev is None:
+                dev = t.device
+            elif t.device != dev:
+                raise ValueError(f"{name}[{i}] is on {t.device}, others on {dev}")
+        return dev
+
+    @staticmethod
+    def _ptrs(ts):
+        arr = (ctypes.c_void_p * max(len(ts), 1))()
+        for i, t in enumerate(ts):
+            arr[i] = t.data_ptr() if t is not None else None
+        return arr
+
+    @staticmethod
+    def _stream(stream, device):
+        import torch
+        if stream is None:
+            return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+        if isinstance(stream, torch.cuda.Stream):
+            return ctypes.c_void_p(stream.cuda_stream)
+        return ctypes.c_void_p(int(stream))
+
+    # -------------------------------------------------------------------- step
+    def step(self, params, grads, momenta, lr=0.02, beta=0.95, wd=0.01, ns_steps=5,
+             coeffs=None, stream=None):
+        """One Muon step (muon_step); coeffs is (a, b, c) or a list of ns_steps triples."""
+        dev = self._check_tensors("params", params, self.dtypes)
+        self._check_tensors("grads", grads, self.dtypes)
+        self._check_tensors("momenta", momenta, [L.MUON_F32] * len(self.shapes))
+        for i, (p, g, m) in enumerate(zip(params, grads, momenta)):
+            if p.data_ptr() == g.data_ptr() or p.data_ptr() == m.data_ptr():
+                raise ValueError(f"matrix {i}: params alias grads or momenta")
+        P, G, M = self._ptrs(params), self._ptrs(grads), self._ptrs(momenta)
+        s = self._stream(stream, dev)
+        lib = L.lib()
+        if coeffs is not None and len(coeffs) and isinstance(coeffs[0], (list, tuple)):
+            if len(coeffs) != ns_steps:
+                raise ValueError("schedule needs one (a, b, c) per NS step")
+            flat = [float(x) for row in coeffs for x in row]
+            arr = (ctypes.c_float * max(len(flat), 1))(*flat)
+            L.check(lib.muon_step_schedule(self._h, P, G, M, lr, beta, wd, int(ns_steps), arr, s))
+            return
+        carr = None
+        if coeffs is not None:
+            if len(coeffs) != 3:
+                raise ValueError("coeffs must be (a, b, c)")
+            carr = (ctypes.c_float * 3)(*[float(x) for x in coeffs])
+        L.check(lib.muon_step(self._h, P, G, M, lr, beta, wd, int(ns_steps), carr, s))
+
+    def set_update_capture(self, dst):
+        """dst: list of fp32 tensors (or None entries) shaped like the params, or None."""
+        if dst is None:
+            self._capture = None
+            L.check(L.lib().muon_plan_set_update_capture(self._h, None))
+            return
+        import torch
+        if len(dst) != len(self.shapes):
+            raise ValueError("one capture tensor (or None) per matrix")
+        for i, (t, shp) in enumerate(zip(dst, self.shapes)):
+            if t is None:
+                continue
+            if not (t.is_cuda and t.dtype == torch.float32 and tuple(t.shape) == shp and t.is_contiguous()):
+                raise ValueError(f"capture[{i}] must be a contiguous fp32 GPU tensor of shape {shp}")
+        self._capture = list(dst)
+        L.check(L.lib().muon_plan_set_update_capture(self._h, self._ptrs(self._capture)))
+
+    # ------------------------------------------------------------ inspection
+    def flags(self, clear=False):
+        f = ctypes.c_uint32()
+        L.check(L.lib().muon_plan_get_flags(self._h, ctypes.byref(f), 1 if clear else 0))
+        return f.value
+
+    def serialize(self):
+        n = ctypes.c_size_t()
+        lib = L.lib()
+        L.check(lib.muon_plan_serialize(self._h, None, ctypes.byref(n)))
+        buf = ctypes.create_string_buffer(n.value)
+        L.check(lib.muon_plan_serialize(self._h, buf, ctypes.byref(n)))
+        return buf.raw[: n.value]
+
+    def info(self):
+        i = L.PlanInfo()
+        L.check(L.lib().muon_plan_info_get(self._h, ctypes.byref(i)))
+        return {k: getattr(i, k) for k, _ in L.PlanInfo._fields_}
+
+    def matrix_choice(self, i):
+        f, g, c = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        L.check(L.lib().muon_plan_matrix_choice(self._h, int(i), ctypes.byref(f), ctypes.byref(g),
+                                                ctypes.byref(c)))
+        return {"form": {1: "direct", 2: "gram"}[f.value], "group": g.value, "chunk": c.value}
+
+    def set_profiling(self, enable=True):
+        L.check(L.lib().muon_plan_set_profiling(self._h, 1 if enable else 0))
+
+    def kernel_times(self, reset=True):
+        arr = (L.KernelTime * 32)()
+        n = ctypes.c_int()
+        L.check(L.lib().muon_plan_get_kernel_times(self._h, arr, 32, ctypes.byref(n), 1 if reset else 0))
+        return [{"name": arr[k].name.decode(), "launches": arr[k].launches,
+                 "total_ms": arr[k].total_ms, "flops": arr[k].flops, "bytes": arr[k].bytes}
+                for k in range(n.value)]

@@ -1,0 +1,725 @@
+// C ABI of the Muon step: plan objects, device tables, the per-step launch
+// sequence, one-time per-shape timing with a persisted cache, and profiling.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <string>
+#include <vector>
+
+#include "muon.h"
+#include "kernels.hpp"
+#include "plan.hpp"
+
+using namespace muon;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+#define HIP_TRY(x)                                                                        \
+  do {                                                                                    \
+    hipError_t e_ = (x);                                                                  \
+    if (e_ != hipSuccess) return fail(MUON_EHIP, std::string(#x) + ": " + hipGetErrorString(e_)); \
+  } while (0)
+
+enum Kind { kEwMom = 0, kNorm, kNsSyrk, kNsComb, kNsApply, kGramXxt, kGramSquare, kGramFinal, kEwApply, kKinds };
+const char* kKindNames[kKinds] = {"ew_momentum", "ew_norm", "ns_syrk", "ns_comb", "ns_apply",
+                                  "gram_xxt", "gram_square", "gram_final", "ew_apply"};
+
+struct SetDev {
+  int path = 0, form = kFormDirect, tile = 0;
+  int nmats = 0;
+  NsMat* mats = nullptr;
+  WorkItem* sym = nullptr;
+  int n_sym = 0;
+  WorkItem* full = nullptr;
+  int n_full = 0;
+  double fl_gram = 0, fl_square = 0, fl_apply = 0;   // algorithmic (symmetric-aware) flops
+};
+
+struct ChunkDev {
+  std::vector<int> mats;          // global indices, chunk order
+  EwMat* ew = nullptr;
+  int64_t* prefix = nullptr;
+  EwDyn* dyn = nullptr;
+  EwDyn* dyn_pinned = nullptr;
+  std::vector<EwDyn> dyn_last;
+  bool dyn_valid = false;
+  hipEvent_t upload_ev = nullptr;
+  bool upload_pending = false;
+  float* partials = nullptr;
+  int64_t total_tiles = 0;
+  double bytes_mom = 0, bytes_apply = 0;
+  std::vector<SetDev> sets;
+};
+
+struct ProfRec {
+  int kind;
+  double flops, bytes;
+  hipEvent_t a, b;
+};
+
+struct Totals {
+  int64_t launches = 0;
+  double ms = 0, flops = 0, bytes = 0;
+};
+
+}  // namespace
+
+struct muon_plan {
+  PlanHost host;
+  std::string serialized;
+  uint64_t hash = 0;
+  int device = -1;
+  int grid_cap = 2048;
+  char* ws = nullptr;
+  float* rscale = nullptr;
+  uint32_t* flags = nullptr;
+  std::vector<void*> dev_allocs;
+  std::vector<void*> host_allocs;
+  std::vector<ChunkDev> chunks;
+  std::vector<float*> capture;
+  bool profiling = false;
+  std::vector<ProfRec> recs;
+  std::vector<hipEvent_t> ev_pool;
+  Totals tot[kKinds];
+};
+
+namespace {
+
+template <typename T>
+int dev_alloc(muon_plan* p, T** ptr, size_t bytes) {
+  void* v = nullptr;
+  if (bytes == 0) bytes = 256;
+  hipError_t e = hipMalloc(&v, bytes);
+  if (e != hipSuccess) return fail(MUON_ENOMEM, std::string("hipMalloc: ") + hipGetErrorString(e));
+  p->dev_allocs.push_back(v);
+  *ptr = static_cast<T*>(v);
+  return MUON_OK;
+}
+
+template <typename T>
+int host_alloc(muon_plan* p, T** ptr, size_t bytes) {
+  void* v = nullptr;
+  if (bytes == 0) bytes = 64;
+  hipError_t e = hipHostMalloc(&v, bytes, hipHostMallocDefault);
+  if (e != hipSuccess) return fail(MUON_ENOMEM, std::string("hipHostMalloc: ") + hipGetErrorString(e));
+  p->host_allocs.push_back(v);
+  *ptr = static_cast<T*>(v);
+  return MUON_OK;
+}
+
+void free_plan_memory(muon_plan* p) {
+  if (!p) return;
+  if (!p->host.opts.host_only) (void)hipDeviceSynchronize();
+  for (ChunkDev& c : p->chunks)
+    if (c.upload_ev) (void)hipEventDestroy(c.upload_ev);
+  for (ProfRec& r : p->recs) {
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
+  }
+  for (hipEvent_t e : p->ev_pool) (void)hipEventDestroy(e);
+  for (void* v : p->dev_allocs) (void)hipFree(v);
+  for (void* v : p->host_allocs) (void)hipHostFree(v);
+  p->dev_allocs.clear();
+  p->host_allocs.clear();
+}
+
+std::string device_tag(int dev) {
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return "unknown";
+  std::string arch = prop.gcnArchName;
+  const size_t colon = arch.find(':');
+  if (colon != std::string::npos) arch = arch.substr(0, colon);
+  return arch + "-cu" + std::to_string(prop.multiProcessorCount) + "-abi" + std::to_string(MUON_ABI_VERSION);
+}
+
+// Uploads the static tables of a host plan and wires the workspace.
+int materialize(muon_plan* p) {
+  const PlanHost& H = p->host;
+  const size_t n = H.mats.size();
+  int rc;
+  if ((rc = dev_alloc(p, &p->ws, H.ws_bytes))) return rc;
+  if ((rc = dev_alloc(p, &p->rscale, n * sizeof(float)))) return rc;
+  if ((rc = dev_alloc(p, &p->flags, sizeof(uint32_t)))) return rc;
+  HIP_TRY(hipMemset(p->flags, 0, sizeof(uint32_t)));
+  HIP_TRY(hipMemset(p->rscale, 0, n * sizeof(float)));
+  p->capture.assign(n, nullptr);
+  p->chunks.resize(H.chunks.size());
+  for (size_t c = 0; c < H.chunks.size(); ++c) {
+    const ChunkPlan& CP = H.chunks[c];
+    ChunkDev& C = p->chunks[c];
+    C.mats.assign(CP.mats.begin(), CP.mats.end());
+    const size_t nm = C.mats.size();
+    std::vector<EwMat> ew(nm);
+    std::vector<int64_t> prefix(nm);
+    int64_t tb = 0;
+    for (size_t k = 0; k < nm; ++k) {
+      const MatPlan& M = H.mats[C.mats[k]];
+      EwMat& E = ew[k];
+      std::memset(&E, 0, sizeof E);
+      E.rows = M.rows;
+      E.cols = M.cols;
+      E.m = M.m;
+      E.n = M.n;
+      E.ldd = M.n_pad;
+      E.tile_begin = tb;
+      E.tiles_i = (int32_t)(M.m_pad / kEwTile);
+      E.tiles_j = (int32_t)(M.n_pad / kEwTile);
+      E.trans = M.trans;
+      E.pdtype = M.dtype;
+      E.ddtype = M.path;
+      E.mat = C.mats[k];
+      E.d = p->ws + M.off[kX0];
+      E.xt = reinterpret_cast<float*>(p->ws + M.off[kXT]);
+      E.s = M.s;
+      prefix[k] = tb;
+      tb += M.ew_tiles;
+      const double e = (double)M.rows * M.cols, pes = M.dtype ? 2 : 4, es = M.path ? 2 : 4;
+      C.bytes_mom += e * (pes + 8 + es);
+      C.bytes_apply += e * (4 + 2 * pes);
+    }
+    C.total_tiles = tb;
+    if ((rc = dev_alloc(p, &C.ew, nm * sizeof(EwMat)))) return rc;
+    if ((rc = dev_alloc(p, &C.prefix, nm * sizeof(int64_t)))) return rc;
+    if ((rc = dev_alloc(p, &C.dyn, nm * sizeof(EwDyn)))) return rc;
+    if ((rc = dev_alloc(p, &C.partials, std::max<int64_t>(tb, 1) * sizeof(float)))) return rc;
+    if ((rc = host_alloc(p, &C.dyn_pinned, nm * sizeof(EwDyn)))) return rc;
+    HIP_TRY(hipMemcpy(C.ew, ew.data(), nm * sizeof(EwMat), hipMemcpyHostToDevice));
+    HIP_TRY(hipMemcpy(C.prefix, prefix.data(), nm * sizeof(int64_t), hipMemcpyHostToDevice));
+    HIP_TRY(hipEventCreateWithFlags(&C.upload_ev, hipEventDisableTiming));
+    for (const LaunchSetPlan& S : CP.sets) {
+      SetDev D;
+      D.path = S.path;
+      D.form = S.form;
+      D.tile = S.tile;
+      D.nmats = (int)S.mats.size();
+      std::vector<NsMat> nsm(S.mats.size());
+      for (size_t k = 0; k < S.mats.size(); ++k) {
+        const MatPlan& M = H.mats[S.mats[k]];
+        NsMat& N = nsm[k];
+        std::memset(&N, 0, sizeof N);
+        for (int b = 0; b < kNumBufs; ++b) N.buf[b] = p->ws + M.off[b];
+        N.m = (int32_t)M.m;
+        N.n = (int32_t)M.n;
+        N.m_pad = (int32_t)M.m_pad;
+        N.n_pad = (int32_t)M.n_pad;
+        N.mat = S.mats[k];
+      }
+      auto items = [](const std::vector<ItemHost>& v) {
+        std::vector<WorkItem> w(v.size());
+        for (size_t i = 0; i < v.size(); ++i) w[i] = WorkItem{v[i].slot, v[i].tm, v[i].tn, 0};
+        return w;
+      };
+      const std::vector<WorkItem> sym = items(S.items_sym), full = items(S.items_full);
+      D.n_sym = (int)sym.size();
+      D.n_full = (int)full.size();
+      D.fl_gram = S.flops_gram_min;
+      D.fl_square = S.flops_square_min;
+      D.fl_apply = S.flops_apply_min;
+      if ((rc = dev_alloc(p, &D.mats, nsm.size() * sizeof(NsMat)))) return rc;
+      if ((rc = dev_alloc(p, &D.sym, sym.size() * sizeof(WorkItem)))) return rc;
+      if ((rc = dev_alloc(p, &D.full, full.size() * sizeof(WorkItem)))) return rc;
+      HIP_TRY(hipMemcpy(D.mats, nsm.data(), nsm.size() * sizeof(NsMat), hipMemcpyHostToDevice));
+      HIP_TRY(hipMemcpy(D.sym, sym.data(), sym.size() * sizeof(WorkItem), hipMemcpyHostToDevice));
+      HIP_TRY(hipMemcpy(D.full, full.data(), full.size() * sizeof(WorkItem), hipMemcpyHostToDevice));
+      C.sets.push_back(D);
+    }
+  }
+  return MUON_OK;
+}
+
+hipEvent_t pool_event(muon_plan* p) {
+  if (!p->ev_pool.empty()) {
+    hipEvent_t e = p->ev_pool.back();
+    p->ev_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+template <typename F>
+int run(muon_plan* p, int kind, double flops, double bytes, hipStream_t s, F&& launch) {
+  hipEvent_t a = nullptr, b = nullptr;
+  if (p->profiling) {
+    a = pool_event(p);
+    b = pool_event(p);
+    if (!a || !b) return fail(MUON_EHIP, "hipEventCreate failed");
+    HIP_TRY(hipEventRecord(a, s));
+  }
+  const hipError_t e = launch();
+  if (e != hipSuccess)
+    return fail(MUON_EHIP, std::string(kKindNames[kind]) + " launch: " + hipGetErrorString(e));
+  if (p->profiling) {
+    HIP_TRY(hipEventRecord(b, s));
+    p->recs.push_back({kind, flops, bytes, a, b});
+  }
+  return MUON_OK;
+}
+
+GemmParams gp(const SetDev& S, bool sym, int shape, int pid, int qid, int cid, int oid, int o2id,
+              float alpha, float beta, float gamma, int scale_pow, const float* rscale) {
+  GemmParams g;
+  std::memset(&g, 0, sizeof g);
+  g.items = sym ? S.sym : S.full;
+  g.n_items = sym ? S.n_sym : S.n_full;
+  g.mats = S.mats;
+  g.rscale = rscale;
+  g.shape = shape;
+  g.scale_pow = scale_pow;
+  g.sym = sym ? 1 : 0;
+  g.p_id = pid;
+  g.q_id = qid;
+  g.c_id = cid;
+  g.o_id = oid;
+  g.o2_id = o2id;
+  g.alpha = alpha;
+  g.beta = beta;
+  g.gamma = gamma;
+  return g;
+}
+
+// The NS stages of one launch set (T steps, coefficient schedule sched[3*T]).
+int enqueue_ns(muon_plan* p, const SetDev& S, int T, const float* sched, hipStream_t s) {
+  if (T <= 0) return MUON_OK;
+  const int pdt = S.path ? kBF16 : kF32;
+  int rc;
+  if (S.form == kFormDirect) {
+    for (int k = 0; k < T; ++k) {
+      const float a = sched[3 * k], b = sched[3 * k + 1], c = sched[3 * k + 2];
+      const int src = (k % 2 == 0) ? kX0 : kX1;
+      const int dst = (k == T - 1) ? kXT : (src == kX0 ? kX1 : kX0);
+      GemmParams g1 = gp(S, true, kShapeGram, src, src, -1, kA, -1, 1.f, 0.f, 0.f, k == 0 ? 2 : 0, p->rscale);
+      if ((rc = run(p, kNsSyrk, S.fl_gram, 0, s, [&] { return launch_gemm(S.tile, pdt, pdt, g1, s); }))) return rc;
+      GemmParams g2 = gp(S, true, kShapeSquare, kA, kA, kA, kB, -1, c, b, 0.f, 0, p->rscale);
+      if ((rc = run(p, kNsComb, S.fl_square, 0, s, [&] { return launch_gemm(S.tile, pdt, pdt, g2, s); }))) return rc;
+      GemmParams g3 = gp(S, false, kShapeApply, kB, src, src, dst, -1, 1.f, a, 0.f, k == 0 ? 1 : 0, p->rscale);
+      const int odt = dst == kXT ? kF32 : pdt;
+      if ((rc = run(p, kNsApply, S.fl_apply, 0, s, [&] { return launch_gemm(S.tile, pdt, odt, g3, s); }))) return rc;
+    }
+    return MUON_OK;
+  }
+  // Gram space: G = X0 X0^T (scaled by r^2), m x m iterates in fp32, X_T = r * Q_T D.
+  const bool bf = S.path != 0;
+  GemmParams g0 = gp(S, true, kShapeGram, kX0, kX0, -1, kA, -1, 1.f, 0.f, 0.f, 2, p->rscale);
+  if ((rc = run(p, kGramXxt, S.fl_gram, 0, s, [&] { return launch_gemm(S.tile, pdt, kF32, g0, s); }))) return rc;
+  int cur = kQX;
+  for (int k = 0; k < T; ++k) {
+    const float a = sched[3 * k], b = sched[3 * k + 1], c = sched[3 * k + 2];
+    const bool last = k == T - 1;
+    const int hbuf = (k == 0) ? kQX : kH;
+    // H = a I + b A + c A^2 (at k = 0 this is Q_1 itself)
+    GemmParams gh = gp(S, true, kShapeSquare, kA, kA, kA, hbuf, (k == 0 && last && bf) ? kQH : -1, c, b, a, 0, p->rscale);
+    if ((rc = run(p, kGramSquare, S.fl_square, 0, s, [&] { return launch_gemm(S.tile, kF32, kF32, gh, s); }))) return rc;
+    if (k > 0) {
+      const int nxt = cur == kQX ? kQY : kQX;
+      GemmParams gq = gp(S, true, kShapeSquare, kH, cur, -1, nxt, (last && bf) ? kQH : -1, 1.f, 0.f, 0.f, 0, p->rscale);
+      if ((rc = run(p, kGramSquare, S.fl_square, 0, s, [&] { return launch_gemm(S.tile, kF32, kF32, gq, s); }))) return rc;
+      cur = nxt;
+    }
+    if (!last) {
+      GemmParams gt = gp(S, true, kShapeSquare, hbuf, kA, -1, kT1, -1, 1.f, 0.f, 0.f, 0, p->rscale);
+      if ((rc = run(p, kGramSquare, S.fl_square, 0, s, [&] { return launch_gemm(S.tile, kF32, kF32, gt, s); }))) return rc;
+      GemmParams ga = gp(S, true, kShapeSquare, kT1, hbuf, -1, kA, -1, 1.f, 0.f, 0.f, 0, p->rscale);
+      if ((rc = run(p, kGramSquare, S.fl_square, 0, s, [&] { return launch_gemm(S.tile, kF32, kF32, ga, s); }))) return rc;
+    }
+  }
+  const int qsrc = bf ? kQH : cur;
+  GemmParams gf = gp(S, false, kShapeApply, qsrc, kX0, -1, kXT, -1, 1.f, 0.f, 0.f, 1, p->rscale);
+  if ((rc = run(p, kGramFinal, S.fl_apply, 0, s, [&] { return launch_gemm(S.tile, pdt, kF32, gf, s); }))) return rc;
+  return MUON_OK;
+}
+
+bool aligned16(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; }
+
+int upload_dyn(muon_plan* p, ChunkDev& C, void* const* params, const void* const* grads,
+               float* const* momenta, hipStream_t s) {
+  const size_t nm = C.mats.size();
+  std::vector<EwDyn> d(nm);
+  for (size_t k = 0; k < nm; ++k) {
+    const int i = C.mats[k];
+    const MatPlan& M = p->host.mats[i];
+    EwDyn& e = d[k];
+    std::memset(&e, 0, sizeof e);
+    e.w = params[i];
+    e.g = grads[i];
+    e.buf = momenta[i];
+    e.upd = p->capture[i];
+    e.vec = (M.cols % 8 == 0 && aligned16(e.w) && aligned16(e.g) && aligned16(e.buf) &&
+             (!e.upd || aligned16(e.upd))) ? 1 : 0;
+  }
+  if (C.dyn_valid && std::memcmp(d.data(), C.dyn_last.data(), nm * sizeof(EwDyn)) == 0) return MUON_OK;
+  if (C.upload_pending) HIP_TRY(hipEventSynchronize(C.upload_ev));
+  std::memcpy(C.dyn_pinned, d.data(), nm * sizeof(EwDyn));
+  HIP_TRY(hipMemcpyAsync(C.dyn, C.dyn_pinned, nm * sizeof(EwDyn), hipMemcpyHostToDevice, s));
+  HIP_TRY(hipEventRecord(C.upload_ev, s));
+  C.upload_pending = true;
+  C.dyn_last = d;
+  C.dyn_valid = true;
+  return MUON_OK;
+}
+
+int step_impl(muon_plan* p, void* const* params, const void* const* grads, float* const* momenta,
+              float lr, float beta, float wd, int T, const float* sched, void* stream) {
+  if (!p) return fail(MUON_EINVAL, "plan is NULL");
+  if (p->host.opts.host_only) return fail(MUON_ESTATE, "muon_step on a host-only plan");
+  if (!params || !grads || !momenta) return fail(MUON_EINVAL, "NULL pointer array");
+  if (T < 0 || T > 64) return fail(MUON_EINVAL, "ns_steps must be in [0, 64]");
+  if (!std::isfinite(lr) || !std::isfinite(beta) || !std::isfinite(wd))
+    return fail(MUON_EINVAL, "non-finite lr, beta or wd");
+  for (int k = 0; k < 3 * T; ++k)
+    if (!std::isfinite(sched[k])) return fail(MUON_EINVAL, "non-finite NS coefficient");
+  const size_t n = p->host.mats.size();
+  for (size_t i = 0; i < n; ++i)
+    if (!params[i] || !grads[i] || !momenta[i]) return fail(MUON_EINVAL, "NULL matrix pointer at index " + std::to_string(i));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int rc;
+  for (ChunkDev& C : p->chunks) {
+    if ((rc = upload_dyn(p, C, params, grads, momenta, s))) return rc;
+    const int nm = (int)C.mats.size();
+    if ((rc = run(p, kEwMom, 0, C.bytes_mom, s, [&] {
+           return launch_ew_momentum(C.ew, C.dyn, C.prefix, nm, C.total_tiles, C.partials, beta,
+                                     p->host.opts.nesterov, p->grid_cap, s);
+         }))) return rc;
+    if ((rc = run(p, kNorm, 0, 0, s, [&] {
+           return launch_norm(C.ew, nm, C.partials, p->rscale, p->flags, p->host.opts.eps, s);
+         }))) return rc;
+    for (const SetDev& S : C.sets)
+      if ((rc = enqueue_ns(p, S, T, sched, s))) return rc;
+    if ((rc = run(p, kEwApply, 0, C.bytes_apply, s, [&] {
+           return launch_ew_apply(C.ew, C.dyn, C.prefix, nm, C.total_tiles, p->rscale, lr, wd,
+                                  T == 0 ? 1 : 0, p->grid_cap, s);
+         }))) return rc;
+  }
+  return MUON_OK;
+}
+
+const float kQuintic[3] = {3.4445f, -4.7750f, 2.0315f};
+
+// Times both forms of one shape on a batch of up to 8 matrices (NS stages only, T = 5).
+int time_shape(const ShapeKey& k, const PlanOptions& base, int count, ShapeChoice* out) {
+  const int batch = std::max(1, std::min(count, 8));
+  double us[3] = {0, 0, 0};
+  for (int form : {kFormDirect, kFormGram}) {
+    PlanHost H;
+    std::map<ShapeKey, ShapeChoice> ch;
+    ShapeChoice c;
+    c.form = form;
+    c.tile = 0;
+    ch[k] = c;
+    PlanOptions o = base;
+    o.workspace_cap = 0;
+    std::vector<int64_t> rows(batch, k.m), cols(batch, k.n);
+    std::vector<int32_t> dts(batch, k.path ? MUON_BF16 : MUON_F32);
+    o.precision = k.path ? MUON_PRECISION_BF16 : MUON_PRECISION_FP32;
+    std::string err = build_plan(rows, cols, dts, o, ch, &H);
+    if (!err.empty()) return fail(MUON_ENOMEM, "tuning: " + err);
+    muon_plan tp;
+    tp.host = std::move(H);
+    int rc = materialize(&tp);
+    if (rc) { free_plan_memory(&tp); return rc; }
+    // bounded, finite inputs: every X0 byte 0x3C (bf16 ~0.0115), scaled to unit Frobenius norm
+    const MatPlan& M0 = tp.host.mats[0];
+    const double v = k.path ? 0.011474609375 : 0.011483338475227356;
+    std::vector<float> r(batch, (float)(1.0 / (v * std::sqrt((double)M0.m_pad * M0.n_pad))));
+    hipStream_t s = nullptr;
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    auto cleanup = [&] {
+      if (e0) (void)hipEventDestroy(e0);
+      if (e1) (void)hipEventDestroy(e1);
+      if (s) (void)hipStreamDestroy(s);
+      free_plan_memory(&tp);
+    };
+    if (hipMemset(tp.ws, 0x3C, tp.host.ws_bytes) != hipSuccess ||
+        hipMemcpy(tp.rscale, r.data(), batch * sizeof(float), hipMemcpyHostToDevice) != hipSuccess ||
+        hipStreamCreate(&s) != hipSuccess || hipEventCreate(&e0) != hipSuccess ||
+        hipEventCreate(&e1) != hipSuccess) {
+      cleanup();
+      return fail(MUON_EHIP, "tuning setup failed");
+    }
+    float sched[15];
+    for (int i = 0; i < 5; ++i) std::memcpy(sched + 3 * i, kQuintic, sizeof kQuintic);
+    float best = 1e30f;
+    for (int rep = 0; rep < 4; ++rep) {
+      (void)hipEventRecord(e0, s);
+      for (const SetDev& S : tp.chunks[0].sets)
+        if ((rc = enqueue_ns(&tp, S, 5, sched, s))) { cleanup(); return rc; }
+      (void)hipEventRecord(e1, s);
+      if (hipEventSynchronize(e1) != hipSuccess) { cleanup(); return fail(MUON_EHIP, "tuning sync failed"); }
+      float ms = 0;
+      (void)hipEventElapsedTime(&ms, e0, e1);
+      if (rep > 0) best = std::min(best, ms);
+    }
+    cleanup();
+    us[form] = best * 1000.0 / batch;
+  }
+  out->us_direct = us[kFormDirect];
+  out->us_gram = us[kFormGram];
+  out->form = us[kFormGram] < 0.97 * us[kFormDirect] ? kFormGram : kFormDirect;
+  out->tile = 0;
+  out->timed = true;
+  return MUON_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int muon_abi_version(void) { return MUON_ABI_VERSION; }
+
+const char* muon_last_error(void) { return g_err.c_str(); }
+
+int muon_plan_opts_default(muon_plan_opts* o) {
+  if (!o) return fail(MUON_EINVAL, "opts is NULL");
+  std::memset(o, 0, sizeof *o);
+  o->struct_size = sizeof(muon_plan_opts);
+  o->nesterov = 1;
+  o->eps = 1e-7f;
+  o->rms_scale = 0.2f;
+  o->precision = MUON_PRECISION_AUTO;
+  o->form = MUON_FORM_AUTO;
+  o->tune = MUON_TUNE_ONCE;
+  o->host_only = 0;
+  o->workspace_cap_bytes = 0;
+  o->cache_path = nullptr;
+  return MUON_OK;
+}
+
+int muon_plan_create(const muon_matrix_desc* descs, int n, const muon_plan_opts* opts_in,
+                     muon_plan** out) {
+  g_err.clear();
+  if (!out) return fail(MUON_EINVAL, "out is NULL");
+  *out = nullptr;
+  if (!descs || n <= 0) return fail(MUON_EINVAL, "descs is NULL or n <= 0");
+  muon_plan_opts o;
+  muon_plan_opts_default(&o);
+  if (opts_in) {
+    if (opts_in->struct_size != sizeof(muon_plan_opts)) return fail(MUON_EINVAL, "opts.struct_size mismatch");
+    o = *opts_in;
+  }
+  if (!(o.eps >= 0.f) || !std::isfinite(o.eps) || !(o.rms_scale > 0.f) || !std::isfinite(o.rms_scale))
+    return fail(MUON_EINVAL, "eps must be >= 0 and rms_scale > 0, both finite");
+  if (o.precision < 0 || o.precision > 2 || o.form < 0 || o.form > 2 || o.tune < 0 || o.tune > 2)
+    return fail(MUON_EINVAL, "precision, form or tune out of range");
+  std::vector<int64_t> rows(n), cols(n);
+  std::vector<int32_t> dts(n);
+  for (int i = 0; i < n; ++i) {
+    if (descs[i].reserved != 0) return fail(MUON_EINVAL, "desc.reserved must be 0");
+    if (descs[i].dtype != MUON_F32 && descs[i].dtype != MUON_BF16)
+      return fail(MUON_EUNSUPPORTED, "unsupported dtype at index " + std::to_string(i));
+    if (descs[i].rows < 1 || descs[i].cols < 1)
+      return fail(MUON_EUNSUPPORTED, "zero-size matrix at index " + std::to_string(i));
+    if (std::min(descs[i].rows, descs[i].cols) > 32768 || std::max(descs[i].rows, descs[i].cols) > (1 << 20))
+      return fail(MUON_EUNSUPPORTED, "matrix too large at index " + std::to_string(i));
+    rows[i] = descs[i].rows;
+    cols[i] = descs[i].cols;
+    dts[i] = descs[i].dtype;
+  }
+  PlanOptions po;
+  po.nesterov = o.nesterov ? 1 : 0;
+  po.eps = o.eps;
+  po.rms_scale = o.rms_scale;
+  po.precision = o.precision;
+  po.form = o.form;
+  po.host_only = o.host_only ? 1 : 0;
+  po.workspace_cap = o.workspace_cap_bytes;
+  if (o.cache_path) po.cache_path = o.cache_path;
+  else if (const char* env = std::getenv("MUON_TUNE_CACHE")) po.cache_path = env;
+  po.tune = po.cache_path.empty() ? MUON_TUNE_OFF : o.tune;
+  if (const char* env = std::getenv("MUON_TUNE")) {
+    if (!std::strcmp(env, "off")) po.tune = MUON_TUNE_OFF;
+  }
+  int dev = -1;
+  std::string tag = "host";
+  if (!po.host_only) {
+    if (hipGetDevice(&dev) != hipSuccess) return fail(MUON_EUNSUPPORTED, "no HIP device");
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return fail(MUON_EHIP, "hipGetDeviceProperties failed");
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+      return fail(MUON_EUNSUPPORTED, std::string("device is ") + prop.gcnArchName + ", not gfx950");
+    tag = device_tag(dev);
+  }
+  // per-shape choices: forced form, cache, timing, or cost model
+  std::map<ShapeKey, int> counts;
+  for (int i = 0; i < n; ++i) counts[shape_key(rows[i], cols[i], dts[i], po.precision)]++;
+  // a host-only plan reads the cache (tag "host") but never times
+  std::map<ShapeKey, ShapeChoice> cache;
+  if (po.tune != MUON_TUNE_OFF) cache = read_cache(po.cache_path, tag);
+  std::map<ShapeKey, ShapeChoice> choices;
+  bool cache_dirty = false;
+  for (const auto& kv : counts) {
+    const ShapeKey& k = kv.first;
+    if (po.form == MUON_FORM_DIRECT || po.form == MUON_FORM_GRAM) {
+      choices[k] = model_choice(k, po.form);
+      continue;
+    }
+    auto it = cache.find(k);
+    if (it != cache.end() && (po.tune == MUON_TUNE_ONCE || po.host_only)) {
+      choices[k] = it->second;
+      continue;
+    }
+    if (po.tune == MUON_TUNE_OFF || po.host_only) {
+      choices[k] = model_choice(k, 0);
+      continue;
+    }
+    ShapeChoice c;
+    const int rc = time_shape(k, po, kv.second, &c);
+    if (rc) return rc;
+    choices[k] = c;
+    cache[k] = c;
+    cache_dirty = true;
+  }
+  if (cache_dirty) (void)write_cache(po.cache_path, tag, cache);
+
+  muon_plan* p = new muon_plan;
+  const std::string err = build_plan(rows, cols, dts, po, choices, &p->host);
+  if (!err.empty()) {
+    delete p;
+    return fail(MUON_ENOMEM, err);
+  }
+  p->serialized = serialize_plan(p->host);
+  p->hash = fnv1a(p->serialized);
+  p->device = dev;
+  if (!po.host_only) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) == hipSuccess) p->grid_cap = prop.multiProcessorCount * 8;
+    const int rc = materialize(p);
+    if (rc) {
+      const std::string keep = g_err;
+      free_plan_memory(p);
+      delete p;
+      g_err = keep;
+      return rc;
+    }
+  }
+  *out = p;
+  return MUON_OK;
+}
+
+int muon_plan_destroy(muon_plan* p) {
+  if (!p) return MUON_OK;
+  free_plan_memory(p);
+  delete p;
+  return MUON_OK;
+}
+
+int muon_step(muon_plan* p, void* const* params, const void* const* grads, float* const* momenta,
+              float lr, float beta, float wd, int ns_steps, const float* coeffs, void* stream) {
+  if (ns_steps < 0 || ns_steps > 64) return fail(MUON_EINVAL, "ns_steps must be in [0, 64]");
+  const float* c = coeffs ? coeffs : kQuintic;
+  std::vector<float> sched(3 * (size_t)ns_steps);
+  for (int k = 0; k < ns_steps; ++k) std::memcpy(&sched[3 * k], c, 3 * sizeof(float));
+  return step_impl(p, params, grads, momenta, lr, beta, wd, ns_steps, sched.data(), stream);
+}
+
+int muon_step_schedule(muon_plan* p, void* const* params, const void* const* grads,
+                       float* const* momenta, float lr, float beta, float wd, int ns_steps,
+                       const float* coeffs, void* stream) {
+  if (ns_steps > 0 && !coeffs) return fail(MUON_EINVAL, "coeffs is NULL");
+  return step_impl(p, params, grads, momenta, lr, beta, wd, ns_steps, coeffs ? coeffs : kQuintic, stream);
+}
+
+int muon_plan_set_update_capture(muon_plan* p, float* const* dst) {
+  if (!p) return fail(MUON_EINVAL, "plan is NULL");
+  for (size_t i = 0; i < p->capture.size(); ++i) p->capture[i] = dst ? dst[i] : nullptr;
+  return MUON_OK;
+}
+
+int muon_plan_get_flags(muon_plan* p, uint32_t* flags, int clear) {
+  if (!p || !flags) return fail(MUON_EINVAL, "NULL argument");
+  if (p->host.opts.host_only) return fail(MUON_ESTATE, "host-only plan");
+  HIP_TRY(hipDeviceSynchronize());
+  HIP_TRY(hipMemcpy(flags, p->flags, sizeof(uint32_t), hipMemcpyDeviceToHost));
+  if (clear) HIP_TRY(hipMemset(p->flags, 0, sizeof(uint32_t)));
+  return MUON_OK;
+}
+
+int muon_plan_serialize(const muon_plan* p, void* buf, size_t* len) {
+  if (!p || !len) return fail(MUON_EINVAL, "NULL argument");
+  const size_t need = p->serialized.size();
+  if (!buf) {
+    *len = need;
+    return MUON_OK;
+  }
+  if (*len < need) return fail(MUON_EINVAL, "buffer too small");
+  std::memcpy(buf, p->serialized.data(), need);
+  *len = need;
+  return MUON_OK;
+}
+
+int muon_plan_info_get(const muon_plan* p, muon_plan_info* info) {
+  if (!p || !info) return fail(MUON_EINVAL, "NULL argument");
+  std::memset(info, 0, sizeof *info);
+  info->n_matrices = (int32_t)p->host.mats.size();
+  info->n_groups = (int32_t)p->host.groups.size();
+  info->n_chunks = (int32_t)p->host.chunks.size();
+  info->n_gram = p->host.n_gram;
+  info->workspace_bytes = p->host.ws_bytes;
+  plan_flops(p->host, 5, &info->ns_flops_min, &info->ns_flops_issued);
+  info->ew_bytes = plan_ew_bytes(p->host);
+  info->plan_hash = p->hash;
+  return MUON_OK;
+}
+
+int muon_plan_matrix_choice(const muon_plan* p, int i, int32_t* form, int32_t* group, int32_t* chunk) {
+  if (!p || i < 0 || i >= (int)p->host.mats.size()) return fail(MUON_EINVAL, "bad plan or index");
+  const MatPlan& M = p->host.mats[i];
+  if (form) *form = M.form;
+  if (group) *group = M.group;
+  if (chunk) *chunk = M.chunk;
+  return MUON_OK;
+}
+
+int muon_plan_set_profiling(muon_plan* p, int enable) {
+  if (!p) return fail(MUON_EINVAL, "plan is NULL");
+  p->profiling = enable != 0;
+  return MUON_OK;
+}
+
+int muon_plan_get_kernel_times(muon_plan* p, muon_kernel_time* out, int max, int* n_out, int reset) {
+  if (!p || !n_out || (max > 0 && !out)) return fail(MUON_EINVAL, "NULL argument");
+  for (ProfRec& r : p->recs) {
+    HIP_TRY(hipEventSynchronize(r.b));
+    float ms = 0;
+    HIP_TRY(hipEventElapsedTime(&ms, r.a, r.b));
+    Totals& t = p->tot[r.kind];
+    t.launches++;
+    t.ms += ms;
+    t.flops += r.flops;
+    t.bytes += r.bytes;
+    p->ev_pool.push_back(r.a);
+    p->ev_pool.push_back(r.b);
+  }
+  p->recs.clear();
+  int k = 0;
+  for (int i = 0; i < kKinds; ++i) {
+    if (p->tot[i].launches == 0) continue;
+    if (k < max) {
+      muon_kernel_time& o = out[k];
+      std::memset(&o, 0, sizeof o);
+      std::strncpy(o.name, kKindNames[i], sizeof(o.name) - 1);
+      o.launches = p->tot[i].launches;
+      o.total_ms = p->tot[i].ms;
+      o.flops = p->tot[i].flops;
+      o.bytes = p->tot[i].bytes;
+    }
+    ++k;
+  }
+  *n_out = std::min(k, std::max(max, 0));
+  if (reset)
+    for (int i = 0; i < kKinds; ++i) p->tot[i] = Totals();
+  return MUON_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,590 @@
+// gfx950 kernels of the Muon update step.
+//
+//  k_ew_momentum  Nesterov momentum (the "momentum-based update" Muon
+//                 orthogonalizes, per "DeepSpeed now supports Muon",
+//                 technical deep dive), fused with the move of d into the
+//                 canonical NS workspace (transposed through LDS for tall
+//                 matrices) and per-tile partial sums of d^2.  HBM-bound.
+//  k_norm         fixed-order reduction of those partials: r = 1/(||d||_F + eps).
+//  k_gemm         the Newton-Schulz contractions on MFMA with fp32 accumulation:
+//                 A = X X^T, B = b A + c A^2, X <- a X + B X, and the m x m
+//                 Gram-space products (DMuon announcement, improvement 2,
+//                 item 1).  LDS-staged 128-byte k-tiles, double buffered.
+//  k_ew_apply     decoupled weight decay plus the RMS-matched orthogonal step
+//                 (same deep-dive section), transposing back through LDS.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.hpp"
+
+namespace muon {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------- conversions
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// Round to nearest, ties to even; NaN stays NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// 16 consecutive elements of dtype dt starting at element offset off (16-byte aligned).
+__device__ __forceinline__ void load16_vec(const void* base, int dt, int64_t off, float* v) {
+  if (dt == kBF16) {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + off);
+    uint4 a = p[0], b = p[1];
+    uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      v[2 * e] = bf16_to_f32(w[e] & 0xffffu);
+      v[2 * e + 1] = bf16_to_f32(w[e] >> 16);
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + off);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float4 t = p[q];
+      v[4 * q] = t.x; v[4 * q + 1] = t.y; v[4 * q + 2] = t.z; v[4 * q + 3] = t.w;
+    }
+  }
+}
+
+__device__ __forceinline__ void store16_vec(void* base, int dt, int64_t off, const float* v) {
+  if (dt == kBF16) {
+    uint4* p = reinterpret_cast<uint4*>(static_cast<uint16_t*>(base) + off);
+    p[0] = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                      pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+    p[1] = make_uint4(pack_bf16x2(v[8], v[9]), pack_bf16x2(v[10], v[11]),
+                      pack_bf16x2(v[12], v[13]), pack_bf16x2(v[14], v[15]));
+  } else {
+    float4* p = reinterpret_cast<float4*>(static_cast<float*>(base) + off);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) p[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+  }
+}
+
+__device__ __forceinline__ float load1(const void* base, int dt, int64_t off) {
+  if (dt == kBF16) return bf16_to_f32(static_cast<const uint16_t*>(base)[off]);
+  return static_cast<const float*>(base)[off];
+}
+
+__device__ __forceinline__ void store1(void* base, int dt, int64_t off, float v) {
+  if (dt == kBF16) static_cast<uint16_t*>(base)[off] = static_cast<uint16_t>(f32_to_bf16(v));
+  else static_cast<float*>(base)[off] = v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Matrix of chunk tile t: the last matrix whose first tile is <= t.
+__device__ __forceinline__ int find_mat(const int64_t* prefix, int nmats, int64_t t) {
+  int lo = 0, hi = nmats - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (prefix[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// ------------------------------------------------------------ elementwise: momentum
+
+// Thread layout on a 64 x 64 block (stored orientation): row r = tid / 4,
+// 16 consecutive columns from c0 = (tid % 4) * 16.
+__global__ __launch_bounds__(256) void k_ew_momentum(
+    const EwMat* __restrict__ mats, const EwDyn* __restrict__ dyn,
+    const int64_t* __restrict__ prefix, int nmats, int64_t total,
+    float* __restrict__ partials, float beta, int nesterov) {
+  __shared__ float tT[kEwTile][kEwTile + 1];
+  __shared__ float red[4];
+  const int tid = threadIdx.x;
+  const int r = tid >> 2, c0 = (tid & 3) * 16;
+  for (int64_t t = blockIdx.x; t < total; t += gridDim.x) {
+    const int mi = find_mat(prefix, nmats, t);
+    const EwMat& M = mats[mi];
+    const EwDyn& D = dyn[mi];
+    const int64_t lt = t - M.tile_begin;
+    const int64_t i0 = (lt / M.tiles_j) * kEwTile, j0 = (lt % M.tiles_j) * kEwTile;
+    const int64_t sr0 = M.trans ? j0 : i0, sc0 = M.trans ? i0 : j0;
+    const int64_t sr = sr0 + r;
+    float dv[16];
+    if (D.vec && sr0 + kEwTile <= M.rows && sc0 + kEwTile <= M.cols) {
+      const int64_t off = sr * M.cols + sc0 + c0;
+      float g[16], b[16];
+      load16_vec(D.g, M.pdtype, off, g);
+      load16_vec(D.buf, kF32, off, b);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        b[e] = beta * b[e] + g[e];
+        dv[e] = nesterov ? g[e] + beta * b[e] : b[e];
+      }
+      store16_vec(D.buf, kF32, off, b);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t sc = sc0 + c0 + e;
+        dv[e] = 0.f;
+        if (sr < M.rows && sc < M.cols) {
+          const int64_t off = sr * M.cols + sc;
+          const float g = load1(D.g, M.pdtype, off);
+          const float b = beta * D.buf[off] + g;
+          D.buf[off] = b;
+          dv[e] = nesterov ? g + beta * b : b;
+        }
+      }
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) ss += dv[e] * dv[e];
+    if (!M.trans) {
+      store16_vec(M.d, M.ddtype, (i0 + r) * M.ldd + j0 + c0, dv);
+    } else {
+      // stored (j0 + r, i0 + c0 + e) is canonical (i0 + c0 + e, j0 + r)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) tT[c0 + e][r] = dv[e];
+      __syncthreads();
+      float o[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[e] = tT[r][c0 + e];
+      store16_vec(M.d, M.ddtype, (i0 + r) * M.ldd + j0 + c0, o);
+    }
+    ss = wave_sum(ss);
+    if ((tid & 63) == 0) red[tid >> 6] = ss;
+    __syncthreads();
+    if (tid == 0) partials[t] = (red[0] + red[1]) + (red[2] + red[3]);
+    __syncthreads();
+  }
+}
+
+// One block per matrix: fixed-order sum of its tiles' partials.
+__global__ __launch_bounds__(256) void k_norm(const EwMat* __restrict__ mats,
+                                              const float* __restrict__ partials,
+                                              float* __restrict__ rscale,
+                                              uint32_t* __restrict__ flags, float eps) {
+  __shared__ float red[4];
+  const EwMat& M = mats[blockIdx.x];
+  const int64_t nt = (int64_t)M.tiles_i * M.tiles_j;
+  float ss = 0.f;
+  for (int64_t k = threadIdx.x; k < nt; k += blockDim.x) ss += partials[M.tile_begin + k];
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+    const float nu = sqrtf(tot);
+    rscale[M.mat] = 1.0f / (nu + eps);
+    if (!isfinite(tot)) atomicOr(flags, 1u);
+  }
+}
+
+// ------------------------------------------------------------ elementwise: apply
+
+__global__ __launch_bounds__(256) void k_ew_apply(
+    const EwMat* __restrict__ mats, const EwDyn* __restrict__ dyn,
+    const int64_t* __restrict__ prefix, int nmats, int64_t total,
+    const float* __restrict__ rscale, float lr, float wd, int src_is_d) {
+  __shared__ float tT[kEwTile][kEwTile + 1];
+  const int tid = threadIdx.x;
+  const int r = tid >> 2, c0 = (tid & 3) * 16;
+  for (int64_t t = blockIdx.x; t < total; t += gridDim.x) {
+    const int mi = find_mat(prefix, nmats, t);
+    const EwMat& M = mats[mi];
+    const EwDyn& D = dyn[mi];
+    const int64_t lt = t - M.tile_begin;
+    const int64_t i0 = (lt / M.tiles_j) * kEwTile, j0 = (lt % M.tiles_j) * kEwTile;
+    if (i0 >= M.m || j0 >= M.n) continue;   // padding-only tile (uniform per block)
+    const float sx = src_is_d ? rscale[M.mat] : 1.0f;
+    const void* src = src_is_d ? M.d : static_cast<const void*>(M.xt);
+    const int sdt = src_is_d ? M.ddtype : kF32;
+    float x[16];
+    int64_t sr, sc0;
+    if (!M.trans) {
+      load16_vec(src, sdt, (i0 + r) * M.ldd + j0 + c0, x);
+      sr = i0 + r;
+      sc0 = j0 + c0;
+    } else {
+      float o[16];
+      load16_vec(src, sdt, (i0 + r) * M.ldd + j0 + c0, o);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) tT[r][c0 + e] = o[e];
+      __syncthreads();
+#pragma unroll
+      for (int e = 0; e < 16; ++e) x[e] = tT[c0 + e][r];
+      __syncthreads();
+      sr = j0 + r;
+      sc0 = i0 + c0;
+    }
+    const float s = M.s;
+    if (D.vec && sr < M.rows && sc0 + 16 <= M.cols) {
+      const int64_t off = sr * M.cols + sc0;
+      float w[16], u[16];
+      load16_vec(D.w, M.pdtype, off, w);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        u[e] = -lr * (wd * w[e] + s * (sx * x[e]));
+        w[e] = w[e] + u[e];
+      }
+      store16_vec(D.w, M.pdtype, off, w);
+      if (D.upd) store16_vec(D.upd, kF32, off, u);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t sc = sc0 + e;
+        if (sr < M.rows && sc < M.cols) {
+          const int64_t off = sr * M.cols + sc;
+          const float w = load1(D.w, M.pdtype, off);
+          const float u = -lr * (wd * w + s * (sx * x[e]));
+          store1(D.w, M.pdtype, off, w + u);
+          if (D.upd) D.upd[off] = u;
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ NS contractions
+//
+// Block: 256 threads = 4 waves in a 2 x 2 grid, each wave a (BM/2) x (BN/2)
+// sub-tile made of 32 x 32 MFMA tiles.  k advances in 128-byte tiles (64 bf16
+// or 32 fp32).  Both operands sit in LDS as [row][k] with a 144-byte row pitch
+// (16 bytes of padding keep the 16-byte fragment reads conflict-free); the NN
+// operand is transposed on its way into LDS.  A lane's MFMA fragment is the
+// 16 bytes at row (lane % 32), byte (lane / 32) * 16 of a 32-byte k-group:
+// eight bf16 for one 32x32x16 MFMA, or four fp32 feeding four 32x32x2 MFMAs
+// (the k order inside a group is the same permutation for both operands, so
+// the sum is unchanged).
+
+template <typename TI>
+struct Mma;
+
+template <>
+struct Mma<uint16_t> {
+  static __device__ __forceinline__ void run(const u32x4_t& a, const u32x4_t& b, f32x16_t& c) {
+    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  }
+};
+
+template <>
+struct Mma<float> {
+  static __device__ __forceinline__ void run(const u32x4_t& a, const u32x4_t& b, f32x16_t& c) {
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a[0]), __uint_as_float(b[0]), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a[1]), __uint_as_float(b[1]), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a[2]), __uint_as_float(b[2]), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a[3]), __uint_as_float(b[3]), c, 0, 0, 0);
+  }
+};
+
+// Element access to workspace buffers (device global memory).
+template <typename T>
+__device__ __forceinline__ float ld_elem(const void* base, int64_t off) {
+  if constexpr (sizeof(T) == 2)
+    return bf16_to_f32(((__attribute__((address_space(1))) const uint16_t*)(base))[off]);
+  else return ((__attribute__((address_space(1))) const float*)(base))[off];
+}
+
+template <typename T>
+__device__ __forceinline__ void st_elem(void* base, int64_t off, float v) {
+  if constexpr (sizeof(T) == 2)
+    ((__attribute__((address_space(1))) uint16_t*)(base))[off] = static_cast<uint16_t>(f32_to_bf16(v));
+  else ((__attribute__((address_space(1))) float*)(base))[off] = v;
+}
+
+// Four consecutive elements (one row, columns off..off+3).
+template <typename T>
+__device__ __forceinline__ void st_elem4(void* base, int64_t off, const float* v) {
+  if constexpr (sizeof(T) == 2) {
+    *((__attribute__((address_space(1))) u32x2_t*)(static_cast<uint16_t*>(base) + off)) =
+        u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+  } else {
+    typedef float f32x4_t __attribute__((ext_vector_type(4)));
+    *((__attribute__((address_space(1))) f32x4_t*)(static_cast<float*>(base) + off)) =
+        f32x4_t{v[0], v[1], v[2], v[3]};
+  }
+}
+
+__device__ __forceinline__ uint32_t half16(const u32x4_t& v, int e) {
+  const uint32_t w = v[e >> 1];
+  return (e & 1) ? (w >> 16) : (w & 0xffffu);
+}
+__device__ __forceinline__ uint32_t word32(const u32x4_t& v, int e) { return v[e]; }
+
+#define GLOBAL_AS __attribute__((address_space(1)))
+typedef GLOBAL_AS const u32x4_t gu32x4_c;
+
+template <int BM, int BN, bool NN, int ES>
+struct GemmGeom {
+  static constexpr int V = 16 / ES;      // elements per 16-byte chunk
+  static constexpr int BK = 128 / ES;    // elements per k-tile
+  static constexpr int ROWB = 144;       // LDS row pitch (bytes)
+  static constexpr int WM = BM / 2, WN = BN / 2;
+  static constexpr int MT = WM / 32, NT = WN / 32;
+  static constexpr int PCH = BM / 32;    // 16-byte P chunks per thread per k-tile
+  static constexpr int QCH = BN / 32;    // Q chunks per thread (NN: consecutive k rows)
+  static constexpr int STAGE = (BM + BN) * ROWB;
+};
+
+template <int BM, int BN, bool NN, int ES>
+__device__ __forceinline__ void gemm_gload(u32x4_t (&pr)[BM / 32], u32x4_t (&qr)[BN / 32],
+                                           const char* Pg, const char* Qg, int ldp, int ldq,
+                                           int m0, int n0, int kt, int tid, int qcc, int qrg) {
+  using G = GemmGeom<BM, BN, NN, ES>;
+  const int64_t k0 = (int64_t)kt * G::BK;
+#pragma unroll
+  for (int u = 0; u < G::PCH; ++u) {
+    const int c = tid + 256 * u, row = c >> 3, cc = c & 7;
+    pr[u] = *(gu32x4_c*)(Pg + (((int64_t)(m0 + row) * ldp + k0) * ES) + cc * 16);
+  }
+  if constexpr (!NN) {
+#pragma unroll
+    for (int u = 0; u < G::QCH; ++u) {
+      const int c = tid + 256 * u, row = c >> 3, cc = c & 7;
+      qr[u] = *(gu32x4_c*)(Qg + (((int64_t)(n0 + row) * ldq + k0) * ES) + cc * 16);
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < G::QCH; ++u) {
+      const int64_t krow = k0 + qrg * G::QCH + u;
+      qr[u] = *(gu32x4_c*)(Qg + ((krow * ldq + n0) * ES) + qcc * 16);
+    }
+  }
+}
+
+template <int BM, int BN, bool NN, int ES>
+__device__ __forceinline__ void gemm_lstore(const u32x4_t (&pr)[BM / 32], const u32x4_t (&qr)[BN / 32],
+                                            char* Ps, int tid, int qcc, int qrg) {
+  using G = GemmGeom<BM, BN, NN, ES>;
+  char* Qs = Ps + BM * G::ROWB;
+#pragma unroll
+  for (int u = 0; u < G::PCH; ++u) {
+    const int c = tid + 256 * u, row = c >> 3, cc = c & 7;
+    *reinterpret_cast<u32x4_t*>(Ps + row * G::ROWB + cc * 16) = pr[u];
+  }
+  if constexpr (!NN) {
+#pragma unroll
+    for (int u = 0; u < G::QCH; ++u) {
+      const int c = tid + 256 * u, row = c >> 3, cc = c & 7;
+      *reinterpret_cast<u32x4_t*>(Qs + row * G::ROWB + cc * 16) = qr[u];
+    }
+  } else {
+    // element e of each loaded chunk is column n = qcc*V + e; its QCH k values
+    // (rows qrg*QCH ..) become one contiguous run of LDS row n.
+#pragma unroll
+    for (int e = 0; e < G::V; ++e) {
+      char* dst = Qs + (qcc * G::V + e) * G::ROWB + qrg * G::QCH * ES;
+      if constexpr (ES == 2) {
+        uint32_t w[G::QCH / 2];
+#pragma unroll
+        for (int h = 0; h < G::QCH / 2; ++h) w[h] = half16(qr[2 * h], e) | (half16(qr[2 * h + 1], e) << 16);
+        if constexpr (G::QCH == 4) {
+          *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{w[0], w[1]};
+        } else {
+#pragma unroll
+          for (int h = 0; h < G::QCH / 8; ++h)
+            *reinterpret_cast<u32x4_t*>(dst + 16 * h) = u32x4_t{w[4 * h], w[4 * h + 1], w[4 * h + 2], w[4 * h + 3]};
+        }
+      } else {
+#pragma unroll
+        for (int h = 0; h < G::QCH / 4; ++h)
+          *reinterpret_cast<u32x4_t*>(dst + 16 * h) =
+              u32x4_t{word32(qr[4 * h], e), word32(qr[4 * h + 1], e), word32(qr[4 * h + 2], e),
+                      word32(qr[4 * h + 3], e)};
+      }
+    }
+  }
+}
+
+template <typename TI, int BM, int BN, bool NN>
+__device__ __forceinline__ void gemm_compute(f32x16_t (&acc)[BM / 64][BN / 64], const char* Ps,
+                                             int lane, int wy, int wx) {
+  using G = GemmGeom<BM, BN, NN, (int)sizeof(TI)>;
+  const char* Qs = Ps + BM * G::ROWB;
+  const int lr = lane & 31, lk = (lane >> 5) * 16;
+#pragma unroll
+  for (int kg = 0; kg < 4; ++kg) {
+    u32x4_t af[G::MT], bfr[G::NT];
+#pragma unroll
+    for (int a = 0; a < G::MT; ++a)
+      af[a] = *reinterpret_cast<const u32x4_t*>(Ps + (wy * G::WM + a * 32 + lr) * G::ROWB + kg * 32 + lk);
+#pragma unroll
+    for (int b = 0; b < G::NT; ++b)
+      bfr[b] = *reinterpret_cast<const u32x4_t*>(Qs + (wx * G::WN + b * 32 + lr) * G::ROWB + kg * 32 + lk);
+#pragma unroll
+    for (int a = 0; a < G::MT; ++a)
+#pragma unroll
+      for (int b = 0; b < G::NT; ++b) Mma<TI>::run(af[a], bfr[b], acc[a][b]);
+  }
+}
+
+template <typename TI, typename TO, bool NN, int BM, int BN>
+__global__ __launch_bounds__(256) void k_gemm(const GemmParams p) {
+  constexpr int ES = sizeof(TI);
+  using G = GemmGeom<BM, BN, NN, ES>;
+  static_assert(BM % 64 == 0 && BN % 64 == 0, "tile");
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wy = wid >> 1, wx = wid & 1;
+  const WorkItem it = p.items[blockIdx.x];
+  const NsMat* nmp = p.mats + it.slot;
+  const int m_pad = nmp->m_pad, n_pad = nmp->n_pad;
+  const int shape = p.shape;
+  int K, ldp, ldq, ldc, Mr, Nr;
+  if (shape == kShapeGram) { K = n_pad; ldp = n_pad; ldq = n_pad; ldc = m_pad; Mr = nmp->m; Nr = nmp->m; }
+  else if (shape == kShapeSquare) { K = m_pad; ldp = m_pad; ldq = m_pad; ldc = m_pad; Mr = nmp->m; Nr = nmp->m; }
+  else { K = m_pad; ldp = m_pad; ldq = n_pad; ldc = n_pad; Mr = nmp->m; Nr = nmp->n; }
+  const char* Pg = static_cast<const char*>(nmp->buf[p.p_id]);
+  const char* Qg = static_cast<const char*>(nmp->buf[p.q_id]);
+  const int m0 = it.tm * BM, n0 = it.tn * BN;
+  const int nk = K / G::BK;
+  const int qcc = tid % (BN / G::V), qrg = tid / (BN / G::V);
+
+  u32x4_t pr[G::PCH], qr[G::QCH];
+  f32x16_t acc[G::MT][G::NT];
+#pragma unroll
+  for (int a = 0; a < G::MT; ++a)
+#pragma unroll
+    for (int b = 0; b < G::NT; ++b)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[a][b][q] = 0.f;
+
+  gemm_gload<BM, BN, NN, ES>(pr, qr, Pg, Qg, ldp, ldq, m0, n0, 0, tid, qcc, qrg);
+  gemm_lstore<BM, BN, NN, ES>(pr, qr, smem, tid, qcc, qrg);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    const bool more = kt + 1 < nk;
+    if (more) gemm_gload<BM, BN, NN, ES>(pr, qr, Pg, Qg, ldp, ldq, m0, n0, kt + 1, tid, qcc, qrg);
+    gemm_compute<TI, BM, BN, NN>(acc, smem + cur * G::STAGE, lane, wy, wx);
+    if (more) gemm_lstore<BM, BN, NN, ES>(pr, qr, smem + (cur ^ 1) * G::STAGE, tid, qcc, qrg);
+    __syncthreads();
+  }
+
+  // ---- epilogue
+  float s = 1.0f;
+  if (p.scale_pow) {
+    const float rr = p.rscale[nmp->mat];
+    s = p.scale_pow == 2 ? rr * rr : rr;
+  }
+  const float alpha = p.alpha, beta = p.beta, gamma = p.gamma;
+  void* Out = nmp->buf[p.o_id];
+  void* Out2 = p.o2_id >= 0 ? nmp->buf[p.o2_id] : nullptr;
+  const void* Cin = p.c_id >= 0 ? nmp->buf[p.c_id] : nullptr;
+  const int ldo = ldc;
+  const bool mirror = p.sym && it.tm != it.tn;
+#pragma unroll
+  for (int a = 0; a < G::MT; ++a) {
+#pragma unroll
+    for (int b = 0; b < G::NT; ++b) {
+      const int j = n0 + wx * G::WN + b * 32 + (lane & 31);
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int ib = m0 + wy * G::WM + a * 32 + rg * 8 + (lane >> 5) * 4;
+        float v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int i = ib + q;
+          float x = alpha * acc[a][b][rg * 4 + q];
+          if (Cin) x += beta * ld_elem<TI>(Cin, (int64_t)i * ldc + j);
+          x *= s;
+          if (i == j) x += gamma;
+          if (i >= Mr || j >= Nr) x = 0.f;
+          v[q] = x;
+          st_elem<TO>(Out, (int64_t)i * ldo + j, x);
+          if (Out2) st_elem<uint16_t>(Out2, (int64_t)i * ldo + j, x);
+        }
+        if (mirror) {
+          st_elem4<TO>(Out, (int64_t)j * ldo + ib, v);
+          if (Out2) st_elem4<uint16_t>(Out2, (int64_t)j * ldo + ib, v);
+        }
+      }
+    }
+  }
+}
+
+template <typename TI, typename TO, bool NN, int BM, int BN>
+hipError_t launch_gemm_t(const GemmParams& p, hipStream_t s) {
+  constexpr int smem = 2 * (BM + BN) * 144;
+  static bool attr_done = false;
+  auto kern = &k_gemm<TI, TO, NN, BM, BN>;
+  if (!attr_done) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+    if (e != hipSuccess) return e;
+    attr_done = true;
+  }
+  if (p.n_items <= 0) return hipSuccess;
+  hipLaunchKernelGGL(kern, dim3(p.n_items), dim3(256), smem, s, p);
+  return hipGetLastError();
+}
+
+template <int BM, int BN>
+hipError_t launch_gemm_cfg(int in_dt, int out_dt, const GemmParams& p, hipStream_t s) {
+  const bool nn = p.shape == kShapeApply;
+  if (in_dt == kBF16 && out_dt == kBF16)
+    return nn ? launch_gemm_t<uint16_t, uint16_t, true, BM, BN>(p, s)
+              : launch_gemm_t<uint16_t, uint16_t, false, BM, BN>(p, s);
+  if (in_dt == kBF16 && out_dt == kF32)
+    return nn ? launch_gemm_t<uint16_t, float, true, BM, BN>(p, s)
+              : launch_gemm_t<uint16_t, float, false, BM, BN>(p, s);
+  if (in_dt == kF32 && out_dt == kF32)
+    return nn ? launch_gemm_t<float, float, true, BM, BN>(p, s)
+              : launch_gemm_t<float, float, false, BM, BN>(p, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_ew_momentum(const EwMat* mats, const EwDyn* dyn, const int64_t* tile_prefix,
+                              int nmats, int64_t total_tiles, float* partials, float beta,
+                              int nesterov, int grid_cap, hipStream_t s) {
+  if (total_tiles <= 0) return hipSuccess;
+  const int64_t grid = total_tiles < grid_cap ? total_tiles : grid_cap;
+  hipLaunchKernelGGL(k_ew_momentum, dim3((unsigned)grid), dim3(256), 0, s, mats, dyn, tile_prefix,
+                     nmats, total_tiles, partials, beta, nesterov);
+  return hipGetLastError();
+}
+
+hipError_t launch_norm(const EwMat* mats, int nmats, const float* partials, float* rscale,
+                       uint32_t* flags, float eps, hipStream_t s) {
+  if (nmats <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_norm, dim3(nmats), dim3(256), 0, s, mats, partials, rscale, flags, eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_ew_apply(const EwMat* mats, const EwDyn* dyn, const int64_t* tile_prefix,
+                           int nmats, int64_t total_tiles, const float* rscale, float lr,
+                           float wd, int src_is_d, int grid_cap, hipStream_t s) {
+  if (total_tiles <= 0) return hipSuccess;
+  const int64_t grid = total_tiles < grid_cap ? total_tiles : grid_cap;
+  hipLaunchKernelGGL(k_ew_apply, dim3((unsigned)grid), dim3(256), 0, s, mats, dyn, tile_prefix,
+                     nmats, total_tiles, rscale, lr, wd, src_is_d);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm(int tile_cfg, int in_dtype, int out_dtype, const GemmParams& p,
+                       hipStream_t s) {
+  switch (tile_cfg) {
+    case 0: return launch_gemm_cfg<128, 128>(in_dtype, out_dtype, p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace muon

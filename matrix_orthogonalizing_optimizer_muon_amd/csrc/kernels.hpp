@@ -1,0 +1,122 @@
+// Device-side tables and kernel launchers of the Muon step (gfx950).
+//
+// Layout conventions shared by the planner, the sequencer and the kernels:
+//  * "canonical" orientation: m = min(rows, cols) rows, n = max(rows, cols)
+//    columns.  A tall stored matrix (rows > cols) is transposed while the
+//    elementwise kernels move it between the caller's buffers and the
+//    workspace, so every NS kernel sees one row-major layout.
+//  * every workspace matrix is zero-padded to multiples of the NS tile size in
+//    both dimensions (m_pad x n_pad, m_pad x m_pad); the kernels write the pads
+//    as exact zeros each step, so the NS contractions need no bounds checks.
+//  * the elementwise kernels walk 64 x 64 tiles of the padded canonical
+//    extent; tile t of a chunk belongs to the matrix whose tile range holds it.
+#pragma once
+#include <stdint.h>
+#include <hip/hip_runtime.h>
+
+namespace muon {
+
+constexpr int kEwTile = 64;   // elementwise tile edge (canonical elements)
+
+enum DType : int32_t { kF32 = 0, kBF16 = 1 };
+
+// Per matrix, static for the life of a plan (uploaded once).
+struct EwMat {
+  int64_t rows, cols;        // stored shape
+  int64_t m, n;              // canonical real shape
+  int64_t ldd;               // leading dimension of D and XT (n_pad)
+  int64_t tile_begin;        // first elementwise tile of this matrix in its chunk
+  int32_t tiles_i, tiles_j;  // 64-tiles along m_pad and n_pad
+  int32_t trans;             // 1: canonical = stored^T
+  int32_t pdtype;            // parameter / gradient dtype
+  int32_t ddtype;            // NS operand dtype (D buffer)
+  int32_t mat;               // index into the plan's per-matrix scale array
+  void* d;                   // D: canonical NS input (m_pad x n_pad, ddtype)
+  float* xt;                 // X_T: final NS output (m_pad x n_pad, fp32)
+  float s;                   // RMS-matching scale
+  float pad_;
+};
+
+// Per matrix, caller pointers of the current step (uploaded when they change).
+struct EwDyn {
+  void* w;           // params (pdtype), rows x cols
+  const void* g;     // grads (pdtype)
+  float* buf;        // momentum (fp32)
+  float* upd;        // optional fp32 capture of the update, or null
+  int32_t vec;       // 1: all four pointers 16-byte aligned and cols % 8 == 0
+  int32_t pad_;
+};
+
+// Workspace buffers of one matrix in NS (ids index NsMat::buf).
+enum BufId : int32_t {
+  kX0 = 0,  // D / X_0 (m_pad x n_pad, NS dtype); also X ping
+  kX1 = 1,  // X pong (m_pad x n_pad, NS dtype)
+  kXT = 2,  // X_T (m_pad x n_pad, fp32)
+  kA = 3,   // A = X X^T (direct, NS dtype) or G / A_k (Gram, fp32); m_pad x m_pad
+  kB = 4,   // B = b A + c A^2 (direct, NS dtype)
+  kH = 5,   // H = a I + b A + c A^2 (Gram, fp32)
+  kQX = 6,  // Q ping (Gram, fp32)
+  kQY = 7,  // Q pong (Gram, fp32)
+  kT1 = 8,  // H A (Gram, fp32)
+  kQH = 9,  // bf16 copy of Q_T (Gram, bf16 path)
+  kNumBufs = 10
+};
+
+// Per matrix of a launch set: its workspace buffers and extents.
+struct NsMat {
+  void* buf[kNumBufs];
+  int32_t m, n;          // canonical real extents
+  int32_t m_pad, n_pad;  // padded extents (multiples of the tile sizes)
+  int32_t mat;           // scale index
+  int32_t pad_;
+};
+
+// Contraction shapes, derived per matrix from (m_pad, n_pad):
+enum GemmShape : int32_t {
+  kShapeGram = 0,   // (m x n)(m x n)^T -> m x m, K = n_pad        (NT, symmetric)
+  kShapeSquare = 1, // (m x m)(m x m)   -> m x m, K = m_pad        (NT, Q symmetric)
+  kShapeApply = 2   // (m x m)(m x n)   -> m x n, K = m_pad        (NN)
+};
+
+struct WorkItem {
+  int32_t slot;      // NsMat index
+  int32_t tm, tn;    // output tile coordinates
+  int32_t pad_;
+};
+
+// out = s * (alpha * acc + beta * Cin) + gamma * [i == j],  s = rscale[mat]^scale_pow;
+// entries outside the real extents are written as 0.
+struct GemmParams {
+  const WorkItem* items;
+  const NsMat* mats;
+  const float* rscale;
+  int32_t n_items;
+  int32_t shape;       // GemmShape
+  int32_t scale_pow;   // 0, 1 or 2
+  int32_t sym;         // 1: items are upper-triangle tiles; off-diagonal tiles are mirrored
+  int32_t p_id, q_id, c_id, o_id, o2_id;   // BufId; c_id / o2_id may be -1 (none)
+  int32_t pad_;
+  float alpha, beta, gamma, pad2_;
+};
+
+// Kernel configurations (the planner's tile choices).
+struct TileCfg {
+  int32_t bm, bn;  // output tile (rows, cols); k-tile is always 128 bytes
+};
+constexpr int kNumTileCfgs = 1;
+constexpr TileCfg kTileCfgs[kNumTileCfgs] = {{128, 128}};
+
+// Launchers (kernels.hip).  All return hipError_t of the launch.
+hipError_t launch_ew_momentum(const EwMat* mats, const EwDyn* dyn, const int64_t* tile_prefix,
+                              int nmats, int64_t total_tiles, float* partials, float beta,
+                              int nesterov, int grid_cap, hipStream_t s);
+hipError_t launch_norm(const EwMat* mats, int nmats, const float* partials, float* rscale,
+                       uint32_t* flags, float eps, hipStream_t s);
+hipError_t launch_ew_apply(const EwMat* mats, const EwDyn* dyn, const int64_t* tile_prefix,
+                           int nmats, int64_t total_tiles, const float* rscale, float lr,
+                           float wd, int src_is_d, int grid_cap, hipStream_t s);
+// kShapeApply runs the NN kernel, the other shapes the NT kernel.
+hipError_t launch_gemm(int tile_cfg, int in_dtype, int out_dtype, const GemmParams& p,
+                       hipStream_t s);
+
+}  // namespace muon

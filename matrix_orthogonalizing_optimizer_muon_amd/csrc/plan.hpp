@@ -1,0 +1,141 @@
+// Host-side planner of the Muon step: pure C++, no device calls.
+//
+// The plan is a pure function of (matrix descriptors, options, per-shape
+// choices).  The per-shape choices (NS form and tile configuration) come from
+// the tune cache, one-time timing, or the analytic cost model; everything
+// downstream of them - groups, chunks, workspace offsets, work-item order - is
+// derived deterministically here, so equal inputs give byte-equal plans.
+//
+// DMuon announcement (wjxwpt.net), improvement 2 "shape-adaptive execution
+// stack": the mathematical form, the execution mode (alone or batched) and
+// the kernel are chosen per shape.  DMuon announcement (zaocj.com), second of
+// the three moves: a new shape is measured once and the winner is reused for
+// that shape.
+#pragma once
+#include <stdint.h>
+
+#include <map>
+#include <string>
+#include <tuple>
+#include <vector>
+
+namespace muon {
+
+enum PlanForm : int32_t { kFormDirect = 1, kFormGram = 2 };
+
+struct ShapeKey {
+  int64_t m, n;     // canonical (min, max)
+  int32_t path;     // NS dtype: 0 fp32, 1 bf16
+  bool operator<(const ShapeKey& o) const {
+    return std::tie(path, m, n) < std::tie(o.path, o.m, o.n);
+  }
+  bool operator==(const ShapeKey& o) const { return m == o.m && n == o.n && path == o.path; }
+};
+
+struct ShapeChoice {
+  int32_t form = kFormDirect;
+  int32_t tile = 0;
+  double us_direct = 0, us_gram = 0;  // measured (0: not timed)
+  bool timed = false;
+};
+
+struct PlanOptions {
+  int32_t nesterov = 1;
+  float eps = 1e-7f;
+  float rms_scale = 0.2f;
+  int32_t precision = 0;  // muon_precision
+  int32_t form = 0;       // muon_form
+  int32_t tune = 0;
+  int32_t host_only = 0;
+  uint64_t workspace_cap = 0;
+  std::string cache_path;
+};
+
+struct MatPlan {
+  int64_t rows = 0, cols = 0;
+  int32_t dtype = 0;       // parameter dtype
+  int32_t path = 0;        // NS dtype
+  int32_t trans = 0;
+  int64_t m = 0, n = 0, m_pad = 0, n_pad = 0;
+  int32_t form = kFormDirect;
+  int32_t tile = 0;
+  int32_t group = -1;
+  int32_t chunk = -1;
+  float s = 0.f;           // RMS-matching scale
+  uint64_t off[10] = {0};  // workspace byte offsets per buffer id (within the chunk region)
+  uint64_t ws_bytes = 0;
+  int64_t ew_tiles = 0;    // 64 x 64 tiles of the padded canonical extent
+};
+
+struct GroupPlan {
+  ShapeKey key;
+  int32_t form = kFormDirect, tile = 0;
+  std::vector<int32_t> members;  // matrix indices, ascending
+};
+
+struct ItemHost { int32_t slot, tm, tn; };
+
+// Matrices of one chunk that share (path, form, tile): one launch per NS stage.
+struct LaunchSetPlan {
+  int32_t path = 0, form = kFormDirect, tile = 0;
+  std::vector<int32_t> mats;         // matrix indices, in slot order
+  std::vector<ItemHost> items_sym;   // upper-triangle m x m tiles
+  std::vector<ItemHost> items_full;  // m x n tiles
+  double flops_gram_min = 0;         // symmetric-aware algorithmic flops of one X X^T over the set
+  double flops_square_min = 0;       // one symmetric m x m product over the set
+  double flops_apply_min = 0;        // one (m x m)(m x n) product over the set
+  double flops_gram_issued = 0, flops_square_issued = 0, flops_apply_issued = 0;
+};
+
+struct ChunkPlan {
+  std::vector<int32_t> mats;         // in group order
+  uint64_t ws_bytes = 0;
+  int64_t ew_tiles = 0;
+  std::vector<LaunchSetPlan> sets;
+};
+
+struct PlanHost {
+  PlanOptions opts;
+  std::vector<MatPlan> mats;
+  std::vector<GroupPlan> groups;
+  std::vector<ChunkPlan> chunks;
+  uint64_t ws_bytes = 0;       // max over chunks
+  int32_t n_gram = 0;
+};
+
+// Tile configuration (must match kernels.hpp kTileCfgs).
+struct TileShape { int32_t bm, bn; };
+TileShape tile_shape(int tile);
+int num_tiles();
+
+// Canonical key of a matrix under the options (path from dtype and precision).
+ShapeKey shape_key(int64_t rows, int64_t cols, int32_t dtype, int32_t precision);
+
+// Analytic cost of a shape for a form, in microseconds at nominal MI355X peaks
+// (used when not timing).  T = 5.
+double model_cost_us(const ShapeKey& k, int32_t form, int32_t tile);
+ShapeChoice model_choice(const ShapeKey& k, int32_t forced_form);
+
+// Builds the plan.  choices must hold an entry for every distinct key.
+// Returns "" on success or an error message (workspace cap exceeded by one matrix).
+std::string build_plan(const std::vector<int64_t>& rows, const std::vector<int64_t>& cols,
+                       const std::vector<int32_t>& dtypes, const PlanOptions& opts,
+                       const std::map<ShapeKey, ShapeChoice>& choices, PlanHost* out);
+
+// Canonical serialization (text) and its FNV-1a hash.
+std::string serialize_plan(const PlanHost& p);
+uint64_t fnv1a(const std::string& s);
+
+// Workspace bytes of one matrix of the given key/form/tile (as laid out by build_plan).
+uint64_t matrix_ws_bytes(const ShapeKey& k, int32_t form, int32_t tile);
+
+// Tune cache: one line per key; unknown or malformed lines are ignored.
+std::map<ShapeKey, ShapeChoice> read_cache(const std::string& path, const std::string& device_tag);
+bool write_cache(const std::string& path, const std::string& device_tag,
+                 const std::map<ShapeKey, ShapeChoice>& entries);
+
+// Per-step flops (T = 5) of the plan: symmetric-aware minimum and issued by the tiles.
+void plan_flops(const PlanHost& p, int ns_steps, double* min_flops, double* issued_flops);
+double plan_ew_bytes(const PlanHost& p);
+
+}  // namespace muon

@@ -1,0 +1,82 @@
+"""Helpers of the GPU parity tests: seeded inputs to device tensors, results back
+to exact fp64, and the oracle driven on the same stored values."""
+import numpy as np
+import torch
+
+import workloads as WL
+from oracle import muon_oracle as O
+
+REL_TOL = {WL.F32: 1e-4, WL.BF16: 2e-2}
+
+
+def to_device(stored):
+    if stored.dtype == WL.F32:
+        return torch.from_numpy(np.ascontiguousarray(stored.raw)).cuda()
+    bits = np.ascontiguousarray(stored.raw).view(np.int16)
+    return torch.from_numpy(bits).view(torch.bfloat16).cuda()
+
+
+def to_f64(t):
+    t = t.detach()
+    if t.dtype == torch.bfloat16:
+        bits = t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        return WL.bf16_bits_to_f64(bits)
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def rel(a, b):
+    nb = np.linalg.norm(b)
+    return float(np.linalg.norm(a - b) / nb) if nb > 0 else float(np.linalg.norm(a - b))
+
+
+def make_state(shapes, dtype, seed, grad_law="normal", grad_scale=0.02, w_scale=0.02,
+               buf_scale=0.0):
+    """Seeded params / grads / momenta for arbitrary shapes (edge and ragged cases)."""
+    Ws, Gs, Bs = [], [], []
+    for i, shp in enumerate(shapes):
+        Ws.append(WL.draw_custom([seed, i, 0], shp, dtype, "normal", w_scale))
+        Gs.append(WL.draw_custom([seed, i, 1], shp, dtype, grad_law, grad_scale))
+        if buf_scale:
+            Bs.append(WL.draw_custom([seed, i, 2], shp, WL.F32, "normal", buf_scale))
+        else:
+            Bs.append(WL.Stored(np.zeros(shp), np.zeros(shp, np.float32), WL.F32))
+    return Ws, Gs, Bs
+
+
+def device_state(Ws, Gs, Bs):
+    return [to_device(w) for w in Ws], [to_device(g) for g in Gs], [to_device(b) for b in Bs]
+
+
+def run_and_compare(plan, Ws, Gs, Bs, dtype, *, lr=0.02, beta=0.95, wd=0.01, ns_steps=5,
+                    coeffs=None, check=None, tol=None):
+    """One GPU step through the C ABI vs the oracle on the same stored inputs.
+
+    check: indices of matrices to compare (default all).  Returns per-matrix errors."""
+    P, G, M = device_state(Ws, Gs, Bs)
+    idx = range(len(Ws)) if check is None else check
+    cap = [None] * len(Ws)
+    for i in idx:
+        cap[i] = torch.empty(Ws[i].value.shape, dtype=torch.float32, device="cuda")
+    plan.set_update_capture(cap)
+    plan.step(P, G, M, lr=lr, beta=beta, wd=wd, ns_steps=ns_steps, coeffs=coeffs)
+    torch.cuda.synchronize()
+    plan.set_update_capture(None)
+    co = O.QUINTIC if coeffs is None else coeffs
+    tol = REL_TOL[dtype] if tol is None else tol
+    errs = []
+    for i in idx:
+        ref = O.muon_step_ref(Ws[i].value, Gs[i].value, Bs[i].value, lr=lr, beta=beta, wd=wd,
+                              ns_steps=ns_steps, coeffs=co, param_dtype=dtype)
+        U = cap[i].cpu().numpy().astype(np.float64)
+        e_u = rel(U, ref["U"])
+        e_buf = rel(to_f64(M[i]), ref["buf_new"])
+        Wn = to_f64(P[i])
+        e_dw = rel(Wn - Ws[i].value, ref["U"])
+        errs.append({"i": i, "err_U": e_u, "err_buf": e_buf, "err_dW": e_dw})
+        assert np.all(np.isfinite(U)), f"matrix {i}: non-finite update"
+        assert e_u <= tol, f"matrix {i} {Ws[i].value.shape}: rel err of U {e_u:.3e} > {tol}"
+        assert e_buf <= 1e-6, f"matrix {i}: momentum rel err {e_buf:.3e}"
+        # the stored weights are W + U rounded to the parameter dtype
+        round_floor = 0.0 if dtype == WL.F32 else 2e-2
+        assert e_dw <= tol + round_floor, f"matrix {i}: weight delta rel err {e_dw:.3e}"
+    return errs

@@ -1,0 +1,142 @@
+"""The C-ABI library on the CPU: it loads, exports every function include/muon.h
+declares, and its host-only planner is deterministic and validates input.
+No compute call is made (no GPU here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import matrix_orthogonalizing_optimizer_muon_amd as M
+from matrix_orthogonalizing_optimizer_muon_amd import _lib as L
+import workloads as WL
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "muon.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(muon_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_every_declared_function_is_exported_and_bound():
+    lib = L.lib()
+    names = _declared()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in L.PROTOTYPES, f"{n} has no ctypes prototype"
+    assert set(L.PROTOTYPES) == set(names)
+    assert lib.muon_abi_version() == 1
+
+
+def test_struct_sizes_match_header_layout():
+    assert ctypes.sizeof(L.MatrixDesc) == 24
+    assert ctypes.sizeof(L.PlanOpts) == 48
+    opts = L.PlanOpts()
+    assert L.lib().muon_plan_opts_default(ctypes.byref(opts)) == 0
+    assert opts.struct_size == ctypes.sizeof(L.PlanOpts)
+    assert opts.nesterov == 1 and abs(opts.eps - 1e-7) < 1e-12 and abs(opts.rms_scale - 0.2) < 1e-7
+
+
+def _host(shapes, dtype="bf16", **kw):
+    return M.MuonPlan(shapes, dtype, host_only=True, **kw)
+
+
+def test_grouping_of_c2_and_plan_determinism():
+    wl = WL.workload(2)
+    a = _host(wl.shapes)
+    b = _host(wl.shapes)
+    assert a.serialize() == b.serialize()
+    info = a.info()
+    assert info["n_matrices"] == 16 and info["n_chunks"] == 1
+    # canonical keys: 1024x1024, 1024x3072, 1024x4096 (up is the transposed down shape)
+    assert info["n_groups"] == 3
+    assert a.matrix_choice(2)["group"] == a.matrix_choice(3)["group"]
+    assert a.matrix_choice(0)["group"] != a.matrix_choice(1)["group"]
+    # symmetric-aware flops at T = 5: T (m^2 n + m^2(m+1)... ) summed per matrix
+    want = 0.0
+    for r, c in wl.shapes:
+        m, n = min(r, c), max(r, c)
+        want += 5 * (n * m * (m + 1) + m * m * (m + 1) + 2.0 * m * m * n)
+    assert info["ns_flops_min"] == pytest.approx(want, rel=1e-12)
+    assert info["ns_flops_issued"] >= info["ns_flops_min"]
+
+
+def test_plan_is_invariant_to_repeat_and_records_order():
+    shapes = [(300, 100), (100, 300), (64, 64), (300, 100)]
+    p1 = _host(shapes)
+    for _ in range(20):
+        assert _host(shapes).serialize() == p1.serialize()
+    # equal shapes share a group; the transposed shape shares its canonical key
+    g = [p1.matrix_choice(i)["group"] for i in range(4)]
+    assert g[0] == g[1] == g[3] and g[2] != g[0]
+
+
+def test_workspace_cap_makes_chunks_and_rejects_oversize():
+    shapes = [(1024, 4096)] * 6
+    one = _host(shapes)
+    ws1 = one.info()["workspace_bytes"] // 6
+    p = _host(shapes, workspace_cap=2 * ws1)
+    info = p.info()
+    assert info["n_chunks"] == 3
+    assert info["workspace_bytes"] == 2 * ws1
+    assert [p.matrix_choice(i)["chunk"] for i in range(6)] == [0, 0, 1, 1, 2, 2]
+    with pytest.raises(M.MuonError) as e:
+        _host(shapes, workspace_cap=ws1 - 1)
+    assert e.value.code == L.MUON_ENOMEM
+
+
+def test_invalid_arguments():
+    lib = L.lib()
+    out = ctypes.c_void_p()
+    assert lib.muon_plan_create(None, 1, None, ctypes.byref(out)) == L.MUON_EINVAL
+    descs = (L.MatrixDesc * 1)()
+    descs[0].rows, descs[0].cols, descs[0].dtype = 0, 8, 1
+    assert lib.muon_plan_create(descs, 1, None, ctypes.byref(out)) in (L.MUON_EUNSUPPORTED, L.MUON_EINVAL)
+    descs[0].rows, descs[0].dtype = 8, 7
+    assert lib.muon_plan_create(descs, 1, None, ctypes.byref(out)) == L.MUON_EUNSUPPORTED
+    assert lib.muon_plan_create(descs, 0, None, ctypes.byref(out)) == L.MUON_EINVAL
+    descs[0].dtype, descs[0].reserved = 1, 3
+    assert lib.muon_plan_create(descs, 1, None, ctypes.byref(out)) == L.MUON_EINVAL
+    assert lib.muon_last_error()
+    with pytest.raises(M.MuonError):
+        _host([(8, 8)], eps=-1.0)
+    assert lib.muon_plan_destroy(None) == L.MUON_OK
+
+
+def test_step_refuses_host_only_plan():
+    p = _host([(16, 32)])
+    lib = L.lib()
+    arr = (ctypes.c_void_p * 1)(1)
+    rc = lib.muon_step(p._h, arr, arr, arr, 0.02, 0.95, 0.01, 5, None, None)
+    assert rc == L.MUON_ESTATE
+
+
+def test_forced_forms_and_cost_model():
+    p = _host([(512, 16384), (1024, 1024)], form="gram")
+    assert p.matrix_choice(0)["form"] == "gram" and p.matrix_choice(1)["form"] == "gram"
+    q = _host([(512, 16384), (1024, 1024)], form="direct")
+    assert q.info()["n_gram"] == 0
+    # the cost model never picks Gram for a square matrix
+    r = _host([(2048, 2048)])
+    assert r.matrix_choice(0)["form"] == "direct"
+
+
+def test_tune_cache_is_read_and_bad_lines_ignored(tmp_path):
+    path = tmp_path / "tune.txt"
+    path.write_text(
+        "garbage line\n"
+        "muon-tune-v1 host m=512 n=16384 path=1 form=2 tile=0 us_direct=900 us_gram=400\n"
+        "muon-tune-v1 host m=1024 n=1024 path=1 form=9 tile=0 us_direct=1 us_gram=1\n"
+        "muon-tune-v1 otherdev m=64 n=64 path=1 form=2 tile=0 us_direct=1 us_gram=1\n")
+    p = _host([(512, 16384), (1024, 1024), (64, 64)], cache_path=str(path))
+    assert p.matrix_choice(0)["form"] == "gram"      # from the cache
+    assert p.matrix_choice(1)["form"] == "direct"    # malformed entry ignored -> model
+    assert p.matrix_choice(2)["form"] == "direct"    # other device's line ignored
+    p2 = _host([(512, 16384), (1024, 1024), (64, 64)], cache_path=str(path))
+    assert p2.serialize() == p.serialize()
+    # tune off ignores the cache
+    p3 = _host([(512, 16384)], cache_path=str(path), tune="off")
+    assert p3.matrix_choice(0)["form"] == "direct"

@@ -1,0 +1,178 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Tolerance (relative Frobenius error of the fp32 pre-rounding update U):
+1e-4 on the fp32 path, 2e-2 on the bf16-MFMA path."""
+import numpy as np
+import pytest
+
+import workloads as WL
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def M():
+    import matrix_orthogonalizing_optimizer_muon_amd as mod
+    return mod
+
+
+def _plan(M, shapes, dtype, **kw):
+    kw.setdefault("tune", "off")
+    return M.MuonPlan(shapes, dtype, **kw)
+
+
+def test_c1_single_fp32_matrix(M):
+    from gpu_util import run_and_compare
+    wl = WL.workload(1)
+    Ws = [WL.draw(wl, 0, 0, WL.KIND_W)]
+    Gs = [WL.draw(wl, 0, 0, WL.KIND_G)]
+    Bs = [WL.Stored(np.zeros((256, 512)), np.zeros((256, 512), np.float32), WL.F32)]
+    plan = _plan(M, wl.shapes, "f32")
+    errs = run_and_compare(plan, Ws, Gs, Bs, WL.F32)
+    print("c1", errs)
+
+
+@pytest.mark.parametrize("coeffs,T", [((1.0, 0.0, 0.0), 1), ((0.0, 1.0, 0.0), 1),
+                                      ((0.0, 0.0, 1.0), 1), ((3.4445, -4.7750, 2.0315), 2),
+                                      ((1.5, -0.5, 0.0), 7)])
+@pytest.mark.parametrize("dtype", [WL.F32, WL.BF16])
+def test_single_stage_isolation(M, coeffs, T, dtype):
+    """(1,0,0): X_T = X0 (elementwise + transpose paths); (0,1,0): A X; (0,0,1): A^2 X."""
+    from gpu_util import make_state, run_and_compare
+    shapes = [(200, 136), (136, 200)]
+    Ws, Gs, Bs = make_state(shapes, dtype, seed=11)
+    plan = _plan(M, shapes, dtype)
+    run_and_compare(plan, Ws, Gs, Bs, dtype, ns_steps=T, coeffs=coeffs)
+
+
+@pytest.mark.parametrize("dtype", [WL.F32, WL.BF16])
+def test_ragged_mixed_shapes_one_plan(M, dtype):
+    from gpu_util import make_state, run_and_compare
+    shapes = [(100, 300), (300, 100), (129, 257), (1, 64), (64, 1), (513, 77), (7, 7),
+              (256, 256), (300, 100)]
+    Ws, Gs, Bs = make_state(shapes, dtype, seed=3, buf_scale=0.01)
+    plan = _plan(M, shapes, dtype)
+    run_and_compare(plan, Ws, Gs, Bs, dtype)
+
+
+@pytest.mark.parametrize("dtype", [WL.F32, WL.BF16])
+def test_gram_form_matches_oracle(M, dtype):
+    from gpu_util import make_state, run_and_compare
+    shapes = [(64, 1000), (1000, 64), (256, 2048), (130, 700)]
+    Ws, Gs, Bs = make_state(shapes, dtype, seed=5)
+    plan = _plan(M, shapes, dtype, form="gram")
+    assert all(plan.matrix_choice(i)["form"] == "gram" for i in range(len(shapes)))
+    run_and_compare(plan, Ws, Gs, Bs, dtype)
+    for T in (1, 2, 0):
+        run_and_compare(plan, Ws, Gs, Bs, dtype, ns_steps=T)
+
+
+def test_ns_steps_zero_and_schedule(M):
+    from gpu_util import make_state, run_and_compare
+    shapes = [(96, 160), (160, 96)]
+    Ws, Gs, Bs = make_state(shapes, WL.F32, seed=8)
+    plan = _plan(M, shapes, "f32")
+    run_and_compare(plan, Ws, Gs, Bs, WL.F32, ns_steps=0)
+    sched = [(3.4445, -4.7750, 2.0315), (1.5, -0.5, 0.0), (2.0, -1.5, 0.5)]
+    run_and_compare(plan, Ws, Gs, Bs, WL.F32, ns_steps=3, coeffs=sched)
+
+
+def test_c2_three_steps_all_matrices(M):
+    """The transformer-block workload as the bench runs it: 16 bf16 matrices, 3 steps,
+    fresh gradients each step, momentum and weights carried over."""
+    import torch
+    from gpu_util import to_device, to_f64, rel
+    from oracle import muon_oracle as O
+    wl = WL.workload(2)
+    plan = _plan(M, wl.shapes, "bf16")
+    P = [to_device(WL.draw(wl, i, 0, WL.KIND_W)) for i in range(wl.n_matrices)]
+    B = [torch.zeros(s, dtype=torch.float32, device="cuda") for s in wl.shapes]
+    cap = [torch.empty(s, dtype=torch.float32, device="cuda") for s in wl.shapes]
+    worst = 0.0
+    for step in range(wl.steps):
+        Gst = [WL.draw(wl, i, step, WL.KIND_G) for i in range(wl.n_matrices)]
+        G = [to_device(g) for g in Gst]
+        W_before = [to_f64(p) for p in P]
+        buf_before = [to_f64(b) for b in B]
+        plan.set_update_capture(cap)
+        plan.step(P, G, B)
+        torch.cuda.synchronize()
+        for i in range(wl.n_matrices):
+            ref = O.muon_step_ref(W_before[i], Gst[i].value, buf_before[i], param_dtype="bf16")
+            e = rel(cap[i].cpu().numpy().astype(np.float64), ref["U"])
+            worst = max(worst, e)
+            assert e <= 2e-2, f"step {step} matrix {i}: {e:.3e}"
+            assert rel(to_f64(B[i]), ref["buf_new"]) <= 1e-6
+            # weights: the GPU stores RNE(W + U_gpu); within one bf16 ulp of RNE(W + U_ref)
+            Wn = to_f64(P[i])
+            ulp = np.abs(ref["W_new_stored"]) * 2.0 ** -7 + 1e-30
+            assert np.mean(np.abs(Wn - ref["W_new_stored"]) <= ulp) > 0.97
+    plan.set_update_capture(None)
+    print("c2 worst rel err", worst)
+
+
+def test_bitwise_determinism(M):
+    import torch
+    from gpu_util import make_state, device_state
+    shapes = [(384, 640), (640, 384), (128, 1024)]
+    Ws, Gs, Bs = make_state(shapes, WL.BF16, seed=21, buf_scale=0.01)
+    plan = _plan(M, shapes, "bf16")
+    outs = []
+    for _ in range(2):
+        P, G, B = device_state(Ws, Gs, Bs)
+        plan.step(P, G, B)
+        torch.cuda.synchronize()
+        outs.append([p.view(torch.int16).cpu().numpy().copy() for p in P] +
+                    [b.cpu().numpy().copy() for b in B])
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)
+
+
+def test_zero_grad_lr_zero_and_nonfinite_flag(M):
+    import torch
+    from gpu_util import make_state, device_state, to_f64
+    shapes = [(64, 96), (96, 64)]
+    Ws, Gs, Bs = make_state(shapes, WL.F32, seed=2)
+    plan = _plan(M, shapes, "f32")
+    # zero gradient and zero momentum: pure decoupled decay
+    P, G, B = device_state(Ws, Gs, Bs)
+    for g in G:
+        g.zero_()
+    cap = [torch.empty(s, dtype=torch.float32, device="cuda") for s in shapes]
+    plan.set_update_capture(cap)
+    plan.step(P, G, B, lr=0.02, wd=0.01)
+    torch.cuda.synchronize()
+    for i in range(2):
+        want = -0.02 * 0.01 * Ws[i].value
+        assert np.max(np.abs(cap[i].cpu().numpy() - want)) <= 1e-9
+    # lr = 0 leaves weights bit-identical and still moves the momentum
+    P, G, B = device_state(Ws, Gs, Bs)
+    before = [p.clone() for p in P]
+    plan.step(P, G, B, lr=0.0)
+    torch.cuda.synchronize()
+    for a, b in zip(P, before):
+        assert torch.equal(a, b)
+    assert np.allclose(to_f64(B[0]), Gs[0].value, rtol=0, atol=0)
+    plan.set_update_capture(None)
+    assert plan.flags(clear=True) == 0
+    # a NaN gradient raises the non-finite flag
+    P, G, B = device_state(Ws, Gs, Bs)
+    G[1][3, 5] = float("nan")
+    plan.step(P, G, B)
+    assert plan.flags(clear=True) & 1
+    assert plan.flags() == 0
+
+
+def test_plan_errors_and_host_checks(M):
+    import torch
+    with pytest.raises(M.MuonError):
+        _plan(M, [(0, 5)], "bf16")
+    plan = _plan(M, [(32, 64)], "bf16")
+    good = [torch.zeros(32, 64, dtype=torch.bfloat16, device="cuda")]
+    mom = [torch.zeros(32, 64, dtype=torch.float32, device="cuda")]
+    with pytest.raises(ValueError):
+        plan.step([torch.zeros(64, 32, dtype=torch.bfloat16, device="cuda")], good, mom)
+    with pytest.raises(ValueError):
+        plan.step(good, [torch.zeros(32, 64, dtype=torch.float32, device="cuda")], mom)
+    with pytest.raises(M.MuonError):
+        plan.step([good[0].clone()], good, mom, ns_steps=-1)
