@@ -76,7 +76,10 @@ def run_and_compare(plan, Ws, Gs, Bs, dtype, *, lr=0.02, beta=0.95, wd=0.01, ns_
         assert np.all(np.isfinite(U)), f"matrix {i}: non-finite update"
         assert e_u <= tol, f"matrix {i} {Ws[i].value.shape}: rel err of U {e_u:.3e} > {tol}"
         assert e_buf <= 1e-6, f"matrix {i}: momentum rel err {e_buf:.3e}"
-        # the stored weights are W + U rounded to the parameter dtype
-        round_floor = 0.0 if dtype == WL.F32 else 2e-2
-        assert e_dw <= tol + round_floor, f"matrix {i}: weight delta rel err {e_dw:.3e}"
+        # the stored weights are W + U rounded to the parameter dtype: allow the error of U
+        # plus twice the rounding floor that the oracle's own rounding of W + U shows
+        floor = rel(ref["W_new_stored"] - ref["W_new"], np.zeros_like(ref["U"])) / max(
+            np.linalg.norm(ref["U"]), 1e-300)
+        assert e_dw <= tol + 2.5 * floor + 1e-7, \
+            f"matrix {i}: weight delta rel err {e_dw:.3e} (rounding floor {floor:.3e})"
     return errs

@@ -103,10 +103,12 @@ def test_c2_three_steps_all_matrices(M):
             worst = max(worst, e)
             assert e <= 2e-2, f"step {step} matrix {i}: {e:.3e}"
             assert rel(to_f64(B[i]), ref["buf_new"]) <= 1e-6
-            # weights: the GPU stores RNE(W + U_gpu); within one bf16 ulp of RNE(W + U_ref)
+            # weights: the GPU stores RNE(W + U_gpu); its delta carries the error of U plus
+            # the bf16 rounding floor the oracle's own rounding of W + U shows
             Wn = to_f64(P[i])
-            ulp = np.abs(ref["W_new_stored"]) * 2.0 ** -7 + 1e-30
-            assert np.mean(np.abs(Wn - ref["W_new_stored"]) <= ulp) > 0.97
+            nU = np.linalg.norm(ref["U"])
+            floor = np.linalg.norm(ref["W_new_stored"] - ref["W_new"]) / nU
+            assert rel(Wn - W_before[i], ref["U"]) <= 2e-2 + 2.5 * floor
     plan.set_update_capture(None)
     print("c2 worst rel err", worst)
 
