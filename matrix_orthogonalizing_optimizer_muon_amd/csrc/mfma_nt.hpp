@@ -1,0 +1,245 @@
+// bf16 "NT" contraction core for gfx950: acc(i, j) += sum_k P[i][k] * Q[j][k]
+// with P and Q row-major and k contiguous in both, fp32 accumulation on
+// v_mfma_f32_32x32x16_bf16.
+//
+// Block: 256 threads = 4 waves in a 2 x 2 grid; wave tile (BM/2) x (BN/2)
+// made of 32 x 32 MFMA tiles, accumulators in AGPRs (one wave per SIMD).
+// k advances in 64-element (128-byte) tiles.  Each k-tile of P (BM rows) and
+// Q (BN rows) is copied global -> LDS by buffer_load ... lds (16 bytes per
+// lane, no VGPR staging), two stages in flight.  LDS rows are 128 bytes with
+// no padding; 16-byte chunk c of row r is stored at slot c ^ ((r >> 1) & 7),
+// so the 16-byte fragment reads of any 16 consecutive lanes (16 rows, one
+// chunk) hit 16 distinct 16-byte bank groups.  A lane's MFMA fragment is the
+// 16 bytes of chunk (2*kg + lane/32) of row (lane % 32) of a 32-row slab.
+//
+// The buffer descriptors carry the byte size of each operand, so an access
+// outside it reads zeros instead of faulting; the callers still only issue
+// in-bounds tiles (every extent is padded to the tile size).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace muon {
+namespace nt {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+#define MUON_LDS __attribute__((address_space(3)))
+
+constexpr int kThreads = 256;
+
+// Raw buffer descriptor word 3 for gfx9-class targets: 32-bit untyped data.
+constexpr int kRsrcWord3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
+}
+
+// s_waitcnt immediate that waits for vmcnt <= n only (gfx9 encoding: vmcnt
+// bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+constexpr int waitcnt_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | 0x70 | 0xF00; }
+static_assert(waitcnt_vm(0) == 0xF70, "encoding");
+constexpr int kWaitVmLgkm0 = 0x0070;   // vmcnt(0) lgkmcnt(0)
+
+// BM x BN output tile, BK bf16 per k-tile (32 or 64), S LDS stages.
+template <int BM, int BN, int BK, int S>
+struct Geom {
+  static constexpr int ROWB = BK * 2;                  // bytes per LDS row
+  static constexpr int CPR = ROWB / 16;                // 16-byte chunks per row
+  static constexpr int R256 = 256 / ROWB;              // rows per 256 bytes
+  static constexpr int KG = BK / 16;                   // MFMA k-groups per k-tile
+  static constexpr int WM = BM / 2, WN = BN / 2;       // wave tile
+  static constexpr int MT = WM / 32, NT = WN / 32;     // MFMA tiles per wave
+  static constexpr int PB = BM * ROWB, QB = BN * ROWB;
+  static constexpr int STAGE = PB + QB;                // bytes per stage
+  static constexpr int LDS = S * STAGE;
+  static constexpr int RPI = 1024 / ROWB;              // rows per wave copy instruction
+  static constexpr int RPR = 4 * RPI;                  // rows per round of the 4 waves
+  static constexpr int PR = BM / RPR, QR = BN / RPR;   // copy rounds per operand
+  static constexpr int NI = PR + QR;                   // copy instructions per wave per tile
+  static_assert(BK == 32 || BK == 64, "k-tile");
+  static_assert(BM % 64 == 0 && BN % 64 == 0 && BM % RPR == 0 && BN % RPR == 0, "tile edges");
+  static_assert(S >= 2 && LDS <= 160 * 1024, "LDS budget");
+  static_assert((S - 1) * NI <= 63, "vmcnt range");
+};
+
+// LDS slot of 16-byte chunk c of tile row r: c ^ swz(r).  Any 16 consecutive
+// rows read at one chunk hit 16 distinct 16-byte bank groups.
+template <int ROWB>
+__device__ __forceinline__ int swz(int r) {
+  return (r / (256 / ROWB)) % (ROWB / 16);
+}
+
+// Global -> LDS copies of one operand.  Wave w copies the contiguous run of
+// tile rows [w * NR * RPI, (w+1) * NR * RPI): copy u writes LDS bytes
+// [(w*NR + u) KiB, +1 KiB), i.e. RPI whole rows, lane l into row l / CPR,
+// slot l % CPR, so it fetches chunk (l % CPR) ^ swz(row) of that row.  M0
+// (the LDS base) changes every fourth copy; the 12-bit immediate supplies the
+// 1 KiB steps in between.  The immediate also advances the global address, so
+// the scalar offset takes it back out.
+template <class G, int NR>
+struct Copier {
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t voff[2];   // per-lane offsets for even / odd copies (swizzle phase)
+  uint32_t soff;      // bytes to the wave's first row (row-block origin added per call)
+  uint32_t step;      // bytes per copy (RPI rows)
+
+  __device__ __forceinline__ void init(__amdgpu_buffer_rsrc_t r, uint32_t ld_bytes, int lane, int w) {
+    rsrc = r;
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+      const int row = (w * NR + par) * G::RPI + lane / G::CPR;   // any copy of this parity
+      const int chunk = (lane % G::CPR) ^ swz<G::ROWB>(row);
+      voff[par] = (uint32_t)(lane / G::CPR) * ld_bytes + (uint32_t)chunk * 16u;
+    }
+    step = (uint32_t)G::RPI * ld_bytes;
+    soff = (uint32_t)(w * NR) * step;
+  }
+
+  // Copy U of the run (the immediate must be a compile-time constant).
+  template <int U>
+  __device__ __forceinline__ void issue_from(MUON_LDS char* dst, uint32_t origin, int w) const {
+    if constexpr (U < NR) {
+      constexpr int kImm = (U & 3) * 1024;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst + (w * NR + (U & ~3)) * 1024, 16,
+                                               voff[U & 1], origin + soff + U * step - kImm, kImm, 0);
+      issue_from<U + 1>(dst, origin, w);
+    }
+  }
+
+  // Copies rows [0, NR*4*RPI) of the row block whose byte origin is `origin`
+  // (row-block start + k offset) into `dst` (this operand's region of a stage).
+  __device__ __forceinline__ void issue(MUON_LDS char* dst, uint32_t origin, int w) const {
+    issue_from<0>(dst, origin, w);
+  }
+};
+
+template <class G>
+struct Frags {
+  u32x4_t a[G::MT], b[G::NT];
+};
+
+// Fragments of k-group kg (16 k values) of the stage at `st`: lane l reads
+// chunk (2 kg + l / 32) of row (l % 32) of every 32-row slab of its wave tile.
+template <class G>
+__device__ __forceinline__ void load_frags(Frags<G>& f, const MUON_LDS char* st, int kg, int lane,
+                                           int wy, int wx) {
+  const int lr = lane & 31, hi = lane >> 5;
+  const int q = ((kg * 2 + hi) ^ swz<G::ROWB>(lr)) * 16;
+  const MUON_LDS char* pa = st + (wy * G::WM + lr) * G::ROWB + q;
+  const MUON_LDS char* qa = st + G::PB + (wx * G::WN + lr) * G::ROWB + q;
+#pragma unroll
+  for (int i = 0; i < G::MT; ++i) f.a[i] = *(const MUON_LDS u32x4_t*)(pa + i * 32 * G::ROWB);
+#pragma unroll
+  for (int j = 0; j < G::NT; ++j) f.b[j] = *(const MUON_LDS u32x4_t*)(qa + j * 32 * G::ROWB);
+}
+
+template <class G>
+__device__ __forceinline__ void mfma_group(f32x16_t (&acc)[G::MT][G::NT], const Frags<G>& f) {
+#pragma unroll
+  for (int i = 0; i < G::MT; ++i)
+#pragma unroll
+    for (int j = 0; j < G::NT; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, f.a[i]),
+                                                         __builtin_bit_cast(bf16x8_t, f.b[j]),
+                                                         acc[i][j], 0, 0, 0);
+}
+
+// Scheduling hints: keep `n` instructions of class `mask` in this slot of the
+// schedule (classes: 0x008 MFMA, 0x020 VMEM read, 0x100 DS read).
+#define MUON_SCHED(mask, n) __builtin_amdgcn_sched_group_barrier(mask, n, 0)
+
+// MFMAs of one k-group interleaved with `nvm` copy instructions and `nds`
+// LDS fragment reads issued by the surrounding code (one of each per MFMA
+// until they run out).
+template <class G, int NVM, int NDS>
+__device__ __forceinline__ void interleave_hint() {
+#pragma unroll
+  for (int i = 0; i < G::MT * G::NT; ++i) {
+    MUON_SCHED(0x008, 1);
+    if (i < NVM) MUON_SCHED(0x020, 1);
+    if (i < NDS) MUON_SCHED(0x100, 1);
+  }
+}
+
+// Workgroup barrier without the memory-model fences of __syncthreads (those
+// would force vmcnt(0) and drain every copy in flight).  Callers wait on the
+// counters they need first; the "memory" clobber keeps the compiler from
+// moving LDS accesses across it.
+__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Full k loop: acc = P[m0 : m0+BM, 0:K] * Q[n0 : n0+BN, 0:K]^T.
+// ldp / ldq: leading dimensions in elements; K a multiple of BK.
+// lds: Geom::LDS bytes of dynamic shared memory.
+//
+// Tile kt sits in stage kt % S.  Its k-groups run on fragments loaded one
+// group ahead.  After the reads of its last group have been issued, the wave
+// waits for those reads and for its copies of tile kt+1, then one barrier:
+// every wave is done with stage kt % S and tile kt+1 has landed everywhere.
+// The copies of tile kt+S then go into stage kt % S, interleaved with the
+// last group's MFMAs and the reads of group 0 of tile kt+1.  Copies past the
+// last tile re-read the last tile (in bounds, never consumed) so the steady
+// state has no branches and always S-1 tiles in flight.
+template <int BM, int BN, int BK, int S>
+__device__ __forceinline__ void mainloop(f32x16_t (&acc)[BM / 64][BN / 64], MUON_LDS char* lds,
+                                         __amdgpu_buffer_rsrc_t P, __amdgpu_buffer_rsrc_t Q,
+                                         uint32_t ldp, uint32_t ldq, uint32_t m0, uint32_t n0,
+                                         int K) {
+  using G = Geom<BM, BN, BK, S>;
+  static_assert(G::KG % 2 == 0, "the last group's fragments are in f1");
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wy = w >> 1, wx = w & 1;
+#pragma unroll
+  for (int i = 0; i < G::MT; ++i)
+#pragma unroll
+    for (int j = 0; j < G::NT; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  Copier<G, G::PR> cp;
+  Copier<G, G::QR> cq;
+  cp.init(P, ldp * 2u, lane, w);
+  cq.init(Q, ldq * 2u, lane, w);
+  const uint32_t sp = m0 * ldp * 2u, sq = n0 * ldq * 2u;
+  const int nk = K / BK;
+  const uint32_t klast = (uint32_t)(nk - 1) * G::ROWB;
+#pragma unroll
+  for (int t = 0; t < S; ++t) {
+    const uint32_t kb = t < nk ? (uint32_t)t * G::ROWB : klast;
+    cp.issue(lds + t * G::STAGE, sp + kb, w);
+    cq.issue(lds + t * G::STAGE + G::PB, sq + kb, w);
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm((S - 1) * G::NI));   // tile 0 landed
+  block_barrier();
+  Frags<G> f0, f1;
+  load_frags<G>(f0, lds, 0, lane, wy, wx);
+  int stage = 0;
+  uint32_t knext = (uint32_t)S * G::ROWB;
+  for (int kt = 0; kt < nk; ++kt) {
+    const MUON_LDS char* st = lds + stage * G::STAGE;
+#pragma unroll
+    for (int g = 0; g + 1 < G::KG; ++g) {
+      if (g & 1) { load_frags<G>(f0, st, g + 1, lane, wy, wx); mfma_group<G>(acc, f1); }
+      else       { load_frags<G>(f1, st, g + 1, lane, wy, wx); mfma_group<G>(acc, f0); }
+      interleave_hint<G, 0, G::MT + G::NT>();
+    }
+    // tile kt+1 landed (S-2 later tiles may stay in flight), own reads done
+    constexpr int kWait = waitcnt_vm((S - 2) * G::NI) & ~0xF00;
+    __builtin_amdgcn_s_waitcnt(kWait);
+    block_barrier();
+    const uint32_t kb = knext <= klast ? knext : klast;
+    knext += G::ROWB;
+    MUON_LDS char* dst = lds + stage * G::STAGE;
+    cp.issue(dst, sp + kb, w);
+    cq.issue(dst + G::PB, sq + kb, w);
+    stage = stage + 1 == S ? 0 : stage + 1;
+    load_frags<G>(f0, lds + stage * G::STAGE, 0, lane, wy, wx);
+    mfma_group<G>(acc, f1);
+    interleave_hint<G, G::NI, G::MT + G::NT>();
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitVmLgkm0);   // no copy outlives the loop
+}
+
+}  // namespace nt
+}  // namespace muon
