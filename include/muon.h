@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define MUON_ABI_VERSION 1
+#define MUON_ABI_VERSION 2
 
 typedef enum muon_status {
   MUON_OK = 0,
@@ -88,6 +88,11 @@ typedef struct muon_plan_opts {
   float rms_scale;              /* s = rms_scale * sqrt(max(rows, cols)); default 0.2 */
   int32_t precision;            /* muon_precision, default AUTO */
   int32_t form;                 /* muon_form, default AUTO */
+  int32_t tile;                 /* tile plan of the bf16 NS kernels, -1 (default): chosen per
+                                   shape; 0..4 force one plan for every bf16 matrix (the
+                                   symmetric and the m x n products' output tiles:
+                                   0: 128/128x128, 1: 128/256x256, 2: 256/256x256,
+                                   3: 128/256x128, 4: 128/128x256).  Ignored on the fp32 path */
   int32_t tune;                 /* muon_tune, default ONCE (OFF when no cache path is known) */
   int32_t host_only;            /* 1: plan on the host only - no device, no workspace, no
                                    timing; muon_step refuses such a plan (planner tests) */
@@ -126,13 +131,15 @@ int muon_plan_opts_default(muon_plan_opts* opts);
 /*
  * Builds a plan for n matrices (descs: host array of n).  Groups matrices by
  * canonical shape (m = min(rows, cols), n = max) and precision; picks per group
- * the NS form and tile configuration (timed once and cached, or by the cost
- * model); lays the groups out in chunks under the workspace cap; allocates the
- * device workspace on the current HIP device (except host_only).  The plan owns
- * its workspace; release it with muon_plan_destroy.  Given the same descs,
- * options and cache contents the plan is byte-identical (muon_plan_serialize).
- * opts NULL: defaults.  Errors: EINVAL (NULL descs/out, n <= 0, reserved != 0),
- * EUNSUPPORTED (dtype, rows or cols < 1, no gfx950 device), ENOMEM, EHIP.
+ * the NS form and tile plan (timed once and cached, or by the cost model); lays
+ * the groups out in chunks under the workspace cap; allocates the device
+ * workspace on the current HIP device (except host_only).  The plan owns its
+ * workspace; release it with muon_plan_destroy.  Given the same descs, options
+ * and cache contents the plan is byte-identical (muon_plan_serialize).
+ * opts NULL: defaults.  Errors: EINVAL (NULL descs/out, n <= 0, reserved != 0,
+ * an option out of range), EUNSUPPORTED (dtype; rows or cols < 1; the smaller
+ * side over 16384, the larger over 2^20, or min * max (each rounded up to 256)
+ * over 2^30; no gfx950 device), ENOMEM, EHIP.
  */
 int muon_plan_create(const muon_matrix_desc* descs, int n, const muon_plan_opts* opts,
                      muon_plan** out);
@@ -187,11 +194,12 @@ int muon_plan_serialize(const muon_plan* plan, void* buf, size_t* len);
 int muon_plan_info_get(const muon_plan* plan, muon_plan_info* info);
 
 /*
- * Per-matrix decision: form (muon_form DIRECT or GRAM), group index and chunk
- * index of matrix i.  Any out pointer may be NULL.
+ * Per-matrix decision: form (muon_form DIRECT or GRAM), tile plan (see
+ * muon_plan_opts.tile; 0 on the fp32 path), group index and chunk index of
+ * matrix i.  Any out pointer may be NULL.  EINVAL: NULL plan or i out of range.
  */
-int muon_plan_matrix_choice(const muon_plan* plan, int i, int32_t* form, int32_t* group,
-                            int32_t* chunk);
+int muon_plan_matrix_choice(const muon_plan* plan, int i, int32_t* form, int32_t* tile,
+                            int32_t* group, int32_t* chunk);
 
 /*
  * Profiling: while enabled, muon_step records a hipEvent pair around each

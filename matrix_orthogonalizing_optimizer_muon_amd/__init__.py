@@ -36,7 +36,7 @@ class MuonPlan:
     """A plan over a fixed list of matrix shapes (see muon_plan_create)."""
 
     def __init__(self, shapes, dtypes, *, nesterov=True, eps=1e-7, rms_scale=0.2,
-                 precision="auto", form="auto", tune="once", cache_path=None,
+                 precision="auto", form="auto", tile=None, tune="once", cache_path=None,
                  workspace_cap=0, host_only=False):
         lib = L.lib()
         shapes = [(int(r), int(c)) for r, c in shapes]
@@ -59,6 +59,7 @@ class MuonPlan:
         opts.rms_scale = rms_scale
         opts.precision = L.PRECISION[precision]
         opts.form = L.FORM[form]
+        opts.tile = -1 if tile is None else int(tile)
         opts.tune = L.TUNE[tune]
         opts.host_only = 1 if host_only else 0
         opts.workspace_cap_bytes = int(workspace_cap)
@@ -191,10 +192,11 @@ class MuonPlan:
         return {k: getattr(i, k) for k, _ in L.PlanInfo._fields_}
 
     def matrix_choice(self, i):
-        f, g, c = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
-        L.check(L.lib().muon_plan_matrix_choice(self._h, int(i), ctypes.byref(f), ctypes.byref(g),
-                                                ctypes.byref(c)))
-        return {"form": {1: "direct", 2: "gram"}[f.value], "group": g.value, "chunk": c.value}
+        f, t, g, c = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        L.check(L.lib().muon_plan_matrix_choice(self._h, int(i), ctypes.byref(f), ctypes.byref(t),
+                                                ctypes.byref(g), ctypes.byref(c)))
+        return {"form": {1: "direct", 2: "gram"}[f.value], "tile": t.value, "group": g.value,
+                "chunk": c.value}
 
     def set_profiling(self, enable=True):
         L.check(L.lib().muon_plan_set_profiling(self._h, 1 if enable else 0))

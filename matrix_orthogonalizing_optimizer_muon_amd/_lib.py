@@ -26,6 +26,7 @@ class PlanOpts(ctypes.Structure):
     _fields_ = [("struct_size", ctypes.c_uint32), ("nesterov", ctypes.c_int32),
                 ("eps", ctypes.c_float), ("rms_scale", ctypes.c_float),
                 ("precision", ctypes.c_int32), ("form", ctypes.c_int32),
+                ("tile", ctypes.c_int32),
                 ("tune", ctypes.c_int32), ("host_only", ctypes.c_int32),
                 ("workspace_cap_bytes", ctypes.c_uint64), ("cache_path", ctypes.c_char_p)]
 
@@ -67,6 +68,7 @@ PROTOTYPES = {
                                            ctypes.POINTER(ctypes.c_size_t)]),
     "muon_plan_info_get": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(PlanInfo)]),
     "muon_plan_matrix_choice": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int,
+                                               ctypes.POINTER(ctypes.c_int32),
                                                ctypes.POINTER(ctypes.c_int32),
                                                ctypes.POINTER(ctypes.c_int32),
                                                ctypes.POINTER(ctypes.c_int32)]),

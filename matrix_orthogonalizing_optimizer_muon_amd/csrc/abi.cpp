@@ -35,16 +35,28 @@ enum Kind { kEwMom = 0, kNorm, kNsSyrk, kNsComb, kNsApply, kGramXxt, kGramSquare
 const char* kKindNames[kKinds] = {"ew_momentum", "ew_norm", "ns_syrk", "ns_comb", "ns_apply",
                                   "gram_xxt", "gram_square", "gram_final", "ew_apply"};
 
+// One list of work items on the device.
+struct Items {
+  WorkItem* d = nullptr;
+  int n = 0;
+};
+
 struct SetDev {
   int path = 0, form = kFormDirect, tile = 0;
   int nmats = 0;
   NsMat* mats = nullptr;
-  WorkItem* sym = nullptr;
-  int n_sym = 0;
-  WorkItem* full = nullptr;
-  int n_full = 0;
+  Items nt_sym, nt_full, old_sym, old_full;
   double fl_gram = 0, fl_square = 0, fl_apply = 0;   // algorithmic (symmetric-aware) flops
 };
+
+static_assert(kNumNtCfgs == 4 && sizeof(kNtTileShapes) / sizeof(kNtTileShapes[0]) == 4, "tables");
+static_assert(kNtCfgs[0].bm == kNtTileShapes[0].bm && kNtCfgs[0].bn == kNtTileShapes[0].bn &&
+              kNtCfgs[1].bm == kNtTileShapes[1].bm && kNtCfgs[1].bn == kNtTileShapes[1].bn &&
+              kNtCfgs[2].bm == kNtTileShapes[2].bm && kNtCfgs[2].bn == kNtTileShapes[2].bn &&
+              kNtCfgs[3].bm == kNtTileShapes[3].bm && kNtCfgs[3].bn == kNtTileShapes[3].bn,
+              "planner and kernel tile tables agree");
+static_assert((int)kPlanBufs == (int)kNumBufs && (int)bX0T == (int)kX0T && (int)bX1T == (int)kX1T &&
+              (int)bQH == (int)kQH, "buffer ids agree");
 
 struct ChunkDev {
   std::vector<int> mats;          // global indices, chunk order
@@ -180,12 +192,14 @@ int materialize(muon_plan* p) {
       E.ddtype = M.path;
       E.mat = C.mats[k];
       E.d = p->ws + M.off[kX0];
+      E.dt = M.has[bX0T] ? static_cast<void*>(p->ws + M.off[kX0T]) : nullptr;
+      E.ldt = M.m_pad;
       E.xt = reinterpret_cast<float*>(p->ws + M.off[kXT]);
       E.s = M.s;
       prefix[k] = tb;
       tb += M.ew_tiles;
       const double e = (double)M.rows * M.cols, pes = M.dtype ? 2 : 4, es = M.path ? 2 : 4;
-      C.bytes_mom += e * (pes + 8 + es);
+      C.bytes_mom += e * (pes + 8 + es + (M.has[bX0T] ? es : 0));
       C.bytes_apply += e * (4 + 2 * pes);
     }
     C.total_tiles = tb;
@@ -208,30 +222,31 @@ int materialize(muon_plan* p) {
         const MatPlan& M = H.mats[S.mats[k]];
         NsMat& N = nsm[k];
         std::memset(&N, 0, sizeof N);
-        for (int b = 0; b < kNumBufs; ++b) N.buf[b] = p->ws + M.off[b];
+        for (int b = 0; b < kNumBufs; ++b) N.buf[b] = M.has[b] ? p->ws + M.off[b] : nullptr;
         N.m = (int32_t)M.m;
         N.n = (int32_t)M.n;
         N.m_pad = (int32_t)M.m_pad;
         N.n_pad = (int32_t)M.n_pad;
         N.mat = S.mats[k];
       }
-      auto items = [](const std::vector<ItemHost>& v) {
-        std::vector<WorkItem> w(v.size());
-        for (size_t i = 0; i < v.size(); ++i) w[i] = WorkItem{v[i].slot, v[i].tm, v[i].tn, 0};
-        return w;
-      };
-      const std::vector<WorkItem> sym = items(S.items_sym), full = items(S.items_full);
-      D.n_sym = (int)sym.size();
-      D.n_full = (int)full.size();
       D.fl_gram = S.flops_gram_min;
       D.fl_square = S.flops_square_min;
       D.fl_apply = S.flops_apply_min;
       if ((rc = dev_alloc(p, &D.mats, nsm.size() * sizeof(NsMat)))) return rc;
-      if ((rc = dev_alloc(p, &D.sym, sym.size() * sizeof(WorkItem)))) return rc;
-      if ((rc = dev_alloc(p, &D.full, full.size() * sizeof(WorkItem)))) return rc;
       HIP_TRY(hipMemcpy(D.mats, nsm.data(), nsm.size() * sizeof(NsMat), hipMemcpyHostToDevice));
-      HIP_TRY(hipMemcpy(D.sym, sym.data(), sym.size() * sizeof(WorkItem), hipMemcpyHostToDevice));
-      HIP_TRY(hipMemcpy(D.full, full.data(), full.size() * sizeof(WorkItem), hipMemcpyHostToDevice));
+      auto upload = [&](const std::vector<ItemHost>& v, Items* out) -> int {
+        out->n = (int)v.size();
+        if (v.empty()) return MUON_OK;
+        std::vector<WorkItem> w(v.size());
+        for (size_t i = 0; i < v.size(); ++i) w[i] = WorkItem{v[i].slot, v[i].tm, v[i].tn, 0};
+        int r = dev_alloc(p, &out->d, w.size() * sizeof(WorkItem));
+        if (r) return r;
+        HIP_TRY(hipMemcpy(out->d, w.data(), w.size() * sizeof(WorkItem), hipMemcpyHostToDevice));
+        return MUON_OK;
+      };
+      if ((rc = upload(S.nt_sym, &D.nt_sym)) || (rc = upload(S.nt_full, &D.nt_full)) ||
+          (rc = upload(S.old_sym, &D.old_sym)) || (rc = upload(S.old_full, &D.old_full)))
+        return rc;
       C.sets.push_back(D);
     }
   }
@@ -268,12 +283,13 @@ int run(muon_plan* p, int kind, double flops, double bytes, hipStream_t s, F&& l
   return MUON_OK;
 }
 
-GemmParams gp(const SetDev& S, bool sym, int shape, int pid, int qid, int cid, int oid, int o2id,
-              float alpha, float beta, float gamma, int scale_pow, const float* rscale) {
+GemmParams gp(const SetDev& S, const Items& it, bool sym, int shape, int pid, int qid, int cid,
+              int oid, int o2id, int otid, float alpha, float beta, float gamma, int scale_pow,
+              const float* rscale) {
   GemmParams g;
   std::memset(&g, 0, sizeof g);
-  g.items = sym ? S.sym : S.full;
-  g.n_items = sym ? S.n_sym : S.n_full;
+  g.items = it.d;
+  g.n_items = it.n;
   g.mats = S.mats;
   g.rscale = rscale;
   g.shape = shape;
@@ -284,6 +300,7 @@ GemmParams gp(const SetDev& S, bool sym, int shape, int pid, int qid, int cid, i
   g.c_id = cid;
   g.o_id = oid;
   g.o2_id = o2id;
+  g.ot_id = otid;
   g.alpha = alpha;
   g.beta = beta;
   g.gamma = gamma;
@@ -291,53 +308,109 @@ GemmParams gp(const SetDev& S, bool sym, int shape, int pid, int qid, int cid, i
 }
 
 // The NS stages of one launch set (T steps, coefficient schedule sched[3*T]).
+//
+// bf16 path, direct form, step k (X = X_k, X^T kept alongside):
+//   A  = s_k X X^T                     NT, symmetric tiles           (s_0 = r^2, else 1)
+//   B  = b A + c A A                   NT, symmetric tiles
+//   X' = t_k (a X + B X)               NT with Q = X^T; writes X' and X'^T (t_0 = r, else 1)
+//   the last step writes X' in fp32 to X_T instead.
+// bf16 path, Gram form: G = r^2 X0 X0^T (NT, fp32 out); the m x m recursion in
+// fp32 on the register-staged kernel; X_T = r Q_T X0 (NT, Q_T rounded to bf16).
+// fp32 path: every product on the register-staged fp32 kernel.
 int enqueue_ns(muon_plan* p, const SetDev& S, int T, const float* sched, hipStream_t s) {
   if (T <= 0) return MUON_OK;
-  const int pdt = S.path ? kBF16 : kF32;
   int rc;
+  const float* rs = p->rscale;
+  if (S.path) {
+    const TilePlan tp = tile_plan(S.tile);
+    if (S.form == kFormDirect) {
+      for (int k = 0; k < T; ++k) {
+        const float a = sched[3 * k], b = sched[3 * k + 1], c = sched[3 * k + 2];
+        const bool even = k % 2 == 0, last = k == T - 1;
+        const int src = even ? kX0 : kX1, srcT = even ? kX0T : kX1T;
+        const int dst = last ? kXT : (even ? kX1 : kX0);
+        const int dstT = last ? -1 : (even ? kX1T : kX0T);
+        GemmParams g1 = gp(S, S.nt_sym, true, kShapeGram, src, src, -1, kA, -1, -1, 1.f, 0.f, 0.f,
+                           k == 0 ? 2 : 0, rs);
+        if ((rc = run(p, kNsSyrk, S.fl_gram, 0, s, [&] { return launch_gemm_nt(tp.sym, kBF16, g1, s); }))) return rc;
+        GemmParams g2 = gp(S, S.nt_sym, true, kShapeSquare, kA, kA, kA, kB, -1, -1, c, b, 0.f, 0, rs);
+        if ((rc = run(p, kNsComb, S.fl_square, 0, s, [&] { return launch_gemm_nt(tp.sym, kBF16, g2, s); }))) return rc;
+        GemmParams g3 = gp(S, S.nt_full, false, kShapeApplyT, kB, srcT, src, dst, -1, dstT, 1.f, a, 0.f,
+                           k == 0 ? 1 : 0, rs);
+        const int odt = last ? kF32 : kBF16;
+        if ((rc = run(p, kNsApply, S.fl_apply, 0, s, [&] { return launch_gemm_nt(tp.apply, odt, g3, s); }))) return rc;
+      }
+      return MUON_OK;
+    }
+    // Gram space
+    GemmParams g0 = gp(S, S.nt_sym, true, kShapeGram, kX0, kX0, -1, kA, -1, -1, 1.f, 0.f, 0.f, 2, rs);
+    if ((rc = run(p, kGramXxt, S.fl_gram, 0, s, [&] { return launch_gemm_nt(tp.sym, kF32, g0, s); }))) return rc;
+    int cur = kQX;
+    for (int k = 0; k < T; ++k) {
+      const float a = sched[3 * k], b = sched[3 * k + 1], c = sched[3 * k + 2];
+      const bool last = k == T - 1;
+      const int hbuf = (k == 0) ? kQX : kH;
+      // H = a I + b A + c A^2 (at k = 0 this is Q_1 itself)
+      GemmParams gh = gp(S, S.old_sym, true, kShapeSquare, kA, kA, kA, hbuf, (k == 0 && last) ? kQH : -1,
+                         -1, c, b, a, 0, rs);
+      if ((rc = run(p, kGramSquare, S.fl_square, 0, s, [&] { return launch_gemm(0, kF32, kF32, gh, s); }))) return rc;
+      if (k > 0) {
+        const int nxt = cur == kQX ? kQY : kQX;
+        GemmParams gq = gp(S, S.old_sym, true, kShapeSquare, kH, cur, -1, nxt, last ? kQH : -1, -1, 1.f,
+                           0.f, 0.f, 0, rs);
+        if ((rc = run(p, kGramSquare, S.fl_square, 0, s, [&] { return launch_gemm(0, kF32, kF32, gq, s); }))) return rc;
+        cur = nxt;
+      }
+      if (!last) {
+        GemmParams gt = gp(S, S.old_sym, true, kShapeSquare, hbuf, kA, -1, kT1, -1, -1, 1.f, 0.f, 0.f, 0, rs);
+        if ((rc = run(p, kGramSquare, S.fl_square, 0, s, [&] { return launch_gemm(0, kF32, kF32, gt, s); }))) return rc;
+        GemmParams ga = gp(S, S.old_sym, true, kShapeSquare, kT1, hbuf, -1, kA, -1, -1, 1.f, 0.f, 0.f, 0, rs);
+        if ((rc = run(p, kGramSquare, S.fl_square, 0, s, [&] { return launch_gemm(0, kF32, kF32, ga, s); }))) return rc;
+      }
+    }
+    GemmParams gf = gp(S, S.nt_full, false, kShapeApplyT, kQH, kX0T, -1, kXT, -1, -1, 1.f, 0.f, 0.f, 1, rs);
+    if ((rc = run(p, kGramFinal, S.fl_apply, 0, s, [&] { return launch_gemm_nt(tp.apply, kF32, gf, s); }))) return rc;
+    return MUON_OK;
+  }
+  // fp32 path
   if (S.form == kFormDirect) {
     for (int k = 0; k < T; ++k) {
       const float a = sched[3 * k], b = sched[3 * k + 1], c = sched[3 * k + 2];
       const int src = (k % 2 == 0) ? kX0 : kX1;
       const int dst = (k == T - 1) ? kXT : (src == kX0 ? kX1 : kX0);
-      GemmParams g1 = gp(S, true, kShapeGram, src, src, -1, kA, -1, 1.f, 0.f, 0.f, k == 0 ? 2 : 0, p->rscale);
-      if ((rc = run(p, kNsSyrk, S.fl_gram, 0, s, [&] { return launch_gemm(S.tile, pdt, pdt, g1, s); }))) return rc;
-      GemmParams g2 = gp(S, true, kShapeSquare, kA, kA, kA, kB, -1, c, b, 0.f, 0, p->rscale);
-      if ((rc = run(p, kNsComb, S.fl_square, 0, s, [&] { return launch_gemm(S.tile, pdt, pdt, g2, s); }))) return rc;
-      GemmParams g3 = gp(S, false, kShapeApply, kB, src, src, dst, -1, 1.f, a, 0.f, k == 0 ? 1 : 0, p->rscale);
-      const int odt = dst == kXT ? kF32 : pdt;
-      if ((rc = run(p, kNsApply, S.fl_apply, 0, s, [&] { return launch_gemm(S.tile, pdt, odt, g3, s); }))) return rc;
+      GemmParams g1 = gp(S, S.old_sym, true, kShapeGram, src, src, -1, kA, -1, -1, 1.f, 0.f, 0.f, k == 0 ? 2 : 0, rs);
+      if ((rc = run(p, kNsSyrk, S.fl_gram, 0, s, [&] { return launch_gemm(0, kF32, kF32, g1, s); }))) return rc;
+      GemmParams g2 = gp(S, S.old_sym, true, kShapeSquare, kA, kA, kA, kB, -1, -1, c, b, 0.f, 0, rs);
+      if ((rc = run(p, kNsComb, S.fl_square, 0, s, [&] { return launch_gemm(0, kF32, kF32, g2, s); }))) return rc;
+      GemmParams g3 = gp(S, S.old_full, false, kShapeApply, kB, src, src, dst, -1, -1, 1.f, a, 0.f, k == 0 ? 1 : 0, rs);
+      if ((rc = run(p, kNsApply, S.fl_apply, 0, s, [&] { return launch_gemm(0, kF32, kF32, g3, s); }))) return rc;
     }
     return MUON_OK;
   }
-  // Gram space: G = X0 X0^T (scaled by r^2), m x m iterates in fp32, X_T = r * Q_T D.
-  const bool bf = S.path != 0;
-  GemmParams g0 = gp(S, true, kShapeGram, kX0, kX0, -1, kA, -1, 1.f, 0.f, 0.f, 2, p->rscale);
-  if ((rc = run(p, kGramXxt, S.fl_gram, 0, s, [&] { return launch_gemm(S.tile, pdt, kF32, g0, s); }))) return rc;
+  GemmParams g0 = gp(S, S.old_sym, true, kShapeGram, kX0, kX0, -1, kA, -1, -1, 1.f, 0.f, 0.f, 2, rs);
+  if ((rc = run(p, kGramXxt, S.fl_gram, 0, s, [&] { return launch_gemm(0, kF32, kF32, g0, s); }))) return rc;
   int cur = kQX;
   for (int k = 0; k < T; ++k) {
     const float a = sched[3 * k], b = sched[3 * k + 1], c = sched[3 * k + 2];
     const bool last = k == T - 1;
     const int hbuf = (k == 0) ? kQX : kH;
-    // H = a I + b A + c A^2 (at k = 0 this is Q_1 itself)
-    GemmParams gh = gp(S, true, kShapeSquare, kA, kA, kA, hbuf, (k == 0 && last && bf) ? kQH : -1, c, b, a, 0, p->rscale);
-    if ((rc = run(p, kGramSquare, S.fl_square, 0, s, [&] { return launch_gemm(S.tile, kF32, kF32, gh, s); }))) return rc;
+    GemmParams gh = gp(S, S.old_sym, true, kShapeSquare, kA, kA, kA, hbuf, -1, -1, c, b, a, 0, rs);
+    if ((rc = run(p, kGramSquare, S.fl_square, 0, s, [&] { return launch_gemm(0, kF32, kF32, gh, s); }))) return rc;
     if (k > 0) {
       const int nxt = cur == kQX ? kQY : kQX;
-      GemmParams gq = gp(S, true, kShapeSquare, kH, cur, -1, nxt, (last && bf) ? kQH : -1, 1.f, 0.f, 0.f, 0, p->rscale);
-      if ((rc = run(p, kGramSquare, S.fl_square, 0, s, [&] { return launch_gemm(S.tile, kF32, kF32, gq, s); }))) return rc;
+      GemmParams gq = gp(S, S.old_sym, true, kShapeSquare, kH, cur, -1, nxt, -1, -1, 1.f, 0.f, 0.f, 0, rs);
+      if ((rc = run(p, kGramSquare, S.fl_square, 0, s, [&] { return launch_gemm(0, kF32, kF32, gq, s); }))) return rc;
       cur = nxt;
     }
     if (!last) {
-      GemmParams gt = gp(S, true, kShapeSquare, hbuf, kA, -1, kT1, -1, 1.f, 0.f, 0.f, 0, p->rscale);
-      if ((rc = run(p, kGramSquare, S.fl_square, 0, s, [&] { return launch_gemm(S.tile, kF32, kF32, gt, s); }))) return rc;
-      GemmParams ga = gp(S, true, kShapeSquare, kT1, hbuf, -1, kA, -1, 1.f, 0.f, 0.f, 0, p->rscale);
-      if ((rc = run(p, kGramSquare, S.fl_square, 0, s, [&] { return launch_gemm(S.tile, kF32, kF32, ga, s); }))) return rc;
+      GemmParams gt = gp(S, S.old_sym, true, kShapeSquare, hbuf, kA, -1, kT1, -1, -1, 1.f, 0.f, 0.f, 0, rs);
+      if ((rc = run(p, kGramSquare, S.fl_square, 0, s, [&] { return launch_gemm(0, kF32, kF32, gt, s); }))) return rc;
+      GemmParams ga = gp(S, S.old_sym, true, kShapeSquare, kT1, hbuf, -1, kA, -1, -1, 1.f, 0.f, 0.f, 0, rs);
+      if ((rc = run(p, kGramSquare, S.fl_square, 0, s, [&] { return launch_gemm(0, kF32, kF32, ga, s); }))) return rc;
     }
   }
-  const int qsrc = bf ? kQH : cur;
-  GemmParams gf = gp(S, false, kShapeApply, qsrc, kX0, -1, kXT, -1, 1.f, 0.f, 0.f, 1, p->rscale);
-  if ((rc = run(p, kGramFinal, S.fl_apply, 0, s, [&] { return launch_gemm(S.tile, pdt, kF32, gf, s); }))) return rc;
+  GemmParams gf = gp(S, S.old_full, false, kShapeApply, cur, kX0, -1, kXT, -1, -1, 1.f, 0.f, 0.f, 1, rs);
+  if ((rc = run(p, kGramFinal, S.fl_apply, 0, s, [&] { return launch_gemm(0, kF32, kF32, gf, s); }))) return rc;
   return MUON_OK;
 }
 
@@ -407,16 +480,22 @@ int step_impl(muon_plan* p, void* const* params, const void* const* grads, float
 
 const float kQuintic[3] = {3.4445f, -4.7750f, 2.0315f};
 
-// Times both forms of one shape on a batch of up to 8 matrices (NS stages only, T = 5).
-int time_shape(const ShapeKey& k, const PlanOptions& base, int count, ShapeChoice* out) {
-  const int batch = std::max(1, std::min(count, 8));
-  double us[3] = {0, 0, 0};
-  for (int form : {kFormDirect, kFormGram}) {
+// Times every candidate (form, tile plan) of one shape on a batch of equal
+// matrices (NS stages only, T = 5, bounded synthetic operands) and keeps the
+// fastest; a later candidate must beat the best so far by 3% to replace it.
+int time_shape(const ShapeKey& k, const PlanOptions& base, int count,
+               const std::vector<std::pair<int32_t, int32_t>>& cands, ShapeChoice* out) {
+  double best_us = 0;
+  bool have = false;
+  for (const auto& cand : cands) {
+    const uint64_t per = matrix_ws_bytes(k, cand.first, cand.second);
+    const int by_mem = (int)std::max<uint64_t>(1, (2ull << 30) / std::max<uint64_t>(per, 1));
+    const int batch = std::max(1, std::min({count, 32, by_mem}));
     PlanHost H;
     std::map<ShapeKey, ShapeChoice> ch;
     ShapeChoice c;
-    c.form = form;
-    c.tile = 0;
+    c.form = cand.first;
+    c.tile = cand.second;
     ch[k] = c;
     PlanOptions o = base;
     o.workspace_cap = 0;
@@ -429,7 +508,8 @@ int time_shape(const ShapeKey& k, const PlanOptions& base, int count, ShapeChoic
     tp.host = std::move(H);
     int rc = materialize(&tp);
     if (rc) { free_plan_memory(&tp); return rc; }
-    // bounded, finite inputs: every X0 byte 0x3C (bf16 ~0.0115), scaled to unit Frobenius norm
+    // bounded, finite inputs: every workspace byte 0x3C (bf16 and fp32 ~0.0115),
+    // X0 scaled to unit Frobenius norm
     const MatPlan& M0 = tp.host.mats[0];
     const double v = k.path ? 0.011474609375 : 0.011483338475227356;
     std::vector<float> r(batch, (float)(1.0 / (v * std::sqrt((double)M0.m_pad * M0.n_pad))));
@@ -462,12 +542,15 @@ int time_shape(const ShapeKey& k, const PlanOptions& base, int count, ShapeChoic
       if (rep > 0) best = std::min(best, ms);
     }
     cleanup();
-    us[form] = best * 1000.0 / batch;
+    const double us = best * 1000.0 / batch;
+    if (!have || us < 0.97 * best_us) {
+      out->form = cand.first;
+      out->tile = cand.second;
+      best_us = us;
+      have = true;
+    }
   }
-  out->us_direct = us[kFormDirect];
-  out->us_gram = us[kFormGram];
-  out->form = us[kFormGram] < 0.97 * us[kFormDirect] ? kFormGram : kFormDirect;
-  out->tile = 0;
+  out->us = best_us;
   out->timed = true;
   return MUON_OK;
 }
@@ -489,6 +572,7 @@ int muon_plan_opts_default(muon_plan_opts* o) {
   o->rms_scale = 0.2f;
   o->precision = MUON_PRECISION_AUTO;
   o->form = MUON_FORM_AUTO;
+  o->tile = -1;
   o->tune = MUON_TUNE_ONCE;
   o->host_only = 0;
   o->workspace_cap_bytes = 0;
@@ -510,8 +594,9 @@ int muon_plan_create(const muon_matrix_desc* descs, int n, const muon_plan_opts*
   }
   if (!(o.eps >= 0.f) || !std::isfinite(o.eps) || !(o.rms_scale > 0.f) || !std::isfinite(o.rms_scale))
     return fail(MUON_EINVAL, "eps must be >= 0 and rms_scale > 0, both finite");
-  if (o.precision < 0 || o.precision > 2 || o.form < 0 || o.form > 2 || o.tune < 0 || o.tune > 2)
-    return fail(MUON_EINVAL, "precision, form or tune out of range");
+  if (o.precision < 0 || o.precision > 2 || o.form < 0 || o.form > 2 || o.tune < 0 || o.tune > 2 ||
+      o.tile < -1 || o.tile >= num_tile_plans())
+    return fail(MUON_EINVAL, "precision, form, tile or tune out of range");
   std::vector<int64_t> rows(n), cols(n);
   std::vector<int32_t> dts(n);
   for (int i = 0; i < n; ++i) {
@@ -520,7 +605,7 @@ int muon_plan_create(const muon_matrix_desc* descs, int n, const muon_plan_opts*
       return fail(MUON_EUNSUPPORTED, "unsupported dtype at index " + std::to_string(i));
     if (descs[i].rows < 1 || descs[i].cols < 1)
       return fail(MUON_EUNSUPPORTED, "zero-size matrix at index " + std::to_string(i));
-    if (std::min(descs[i].rows, descs[i].cols) > 32768 || std::max(descs[i].rows, descs[i].cols) > (1 << 20))
+    if (!dims_supported(descs[i].rows, descs[i].cols))
       return fail(MUON_EUNSUPPORTED, "matrix too large at index " + std::to_string(i));
     rows[i] = descs[i].rows;
     cols[i] = descs[i].cols;
@@ -532,6 +617,7 @@ int muon_plan_create(const muon_matrix_desc* descs, int n, const muon_plan_opts*
   po.rms_scale = o.rms_scale;
   po.precision = o.precision;
   po.form = o.form;
+  po.tile = o.tile;
   po.host_only = o.host_only ? 1 : 0;
   po.workspace_cap = o.workspace_cap_bytes;
   if (o.cache_path) po.cache_path = o.cache_path;
@@ -560,25 +646,32 @@ int muon_plan_create(const muon_matrix_desc* descs, int n, const muon_plan_opts*
   bool cache_dirty = false;
   for (const auto& kv : counts) {
     const ShapeKey& k = kv.first;
-    if (po.form == MUON_FORM_DIRECT || po.form == MUON_FORM_GRAM) {
-      choices[k] = model_choice(k, po.form);
+    const auto cands = candidates(k, po.form, po.tile);
+    const bool forced = po.form != MUON_FORM_AUTO || (po.tile >= 0 && k.path);
+    if (cands.size() == 1) {
+      ShapeChoice c;
+      c.form = cands[0].first;
+      c.tile = cands[0].second;
+      choices[k] = c;
       continue;
     }
     auto it = cache.find(k);
-    if (it != cache.end() && (po.tune == MUON_TUNE_ONCE || po.host_only)) {
+    if (!forced && it != cache.end() && (po.tune == MUON_TUNE_ONCE || po.host_only)) {
       choices[k] = it->second;
       continue;
     }
     if (po.tune == MUON_TUNE_OFF || po.host_only) {
-      choices[k] = model_choice(k, 0);
+      choices[k] = model_choice(k, po.form, po.tile, kv.second);
       continue;
     }
     ShapeChoice c;
-    const int rc = time_shape(k, po, kv.second, &c);
+    const int rc = time_shape(k, po, kv.second, cands, &c);
     if (rc) return rc;
     choices[k] = c;
-    cache[k] = c;
-    cache_dirty = true;
+    if (!forced) {
+      cache[k] = c;
+      cache_dirty = true;
+    }
   }
   if (cache_dirty) (void)write_cache(po.cache_path, tag, cache);
 
@@ -672,10 +765,12 @@ int muon_plan_info_get(const muon_plan* p, muon_plan_info* info) {
   return MUON_OK;
 }
 
-int muon_plan_matrix_choice(const muon_plan* p, int i, int32_t* form, int32_t* group, int32_t* chunk) {
+int muon_plan_matrix_choice(const muon_plan* p, int i, int32_t* form, int32_t* tile, int32_t* group,
+                            int32_t* chunk) {
   if (!p || i < 0 || i >= (int)p->host.mats.size()) return fail(MUON_EINVAL, "bad plan or index");
   const MatPlan& M = p->host.mats[i];
   if (form) *form = M.form;
+  if (tile) *tile = M.tile;
   if (group) *group = M.group;
   if (chunk) *chunk = M.chunk;
   return MUON_OK;

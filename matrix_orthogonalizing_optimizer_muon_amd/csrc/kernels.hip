@@ -16,6 +16,7 @@
 #include <stdint.h>
 
 #include "kernels.hpp"
+#include "mfma_nt.hpp"
 
 namespace muon {
 namespace {
@@ -153,17 +154,23 @@ __global__ __launch_bounds__(256) void k_ew_momentum(
     float ss = 0.f;
 #pragma unroll
     for (int e = 0; e < 16; ++e) ss += dv[e] * dv[e];
-    if (!M.trans) {
-      store16_vec(M.d, M.ddtype, (i0 + r) * M.ldd + j0 + c0, dv);
-    } else {
-      // stored (j0 + r, i0 + c0 + e) is canonical (i0 + c0 + e, j0 + r)
+    // dv is row r of the tile in stored orientation: canonical row i0 + r of
+    // D (stored = canonical) or canonical column j0 + r, i.e. row j0 + r of
+    // D^T (tall matrices).  That orientation is stored directly; the other
+    // one, when the NS path uses it, goes through an LDS transpose.
+    void* direct = M.trans ? M.dt : M.d;
+    void* other = M.trans ? M.d : M.dt;
+    const int64_t ld_dir = M.trans ? M.ldt : M.ldd, ld_oth = M.trans ? M.ldd : M.ldt;
+    const int64_t r0_dir = M.trans ? j0 : i0, c0_dir = M.trans ? i0 : j0;
+    if (direct) store16_vec(direct, M.ddtype, (r0_dir + r) * ld_dir + c0_dir + c0, dv);
+    if (other) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) tT[c0 + e][r] = dv[e];
       __syncthreads();
       float o[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e) o[e] = tT[r][c0 + e];
-      store16_vec(M.d, M.ddtype, (i0 + r) * M.ldd + j0 + c0, o);
+      store16_vec(other, M.ddtype, (c0_dir + r) * ld_oth + r0_dir + c0, o);
     }
     ss = wave_sum(ss);
     if ((tid & 63) == 0) red[tid >> 6] = ss;
@@ -550,6 +557,110 @@ hipError_t launch_gemm_cfg(int in_dt, int out_dt, const GemmParams& p, hipStream
   return hipErrorInvalidValue;
 }
 
+// ------------------------------------------------------- bf16 NT contractions
+//
+// The NS products on the LDS-DMA MFMA core of mfma_nt.hpp.  Both operands are
+// row-major with k contiguous:
+//   kShapeGram    A = X X^T       P = Q = X (m_pad x n_pad), K = n_pad, out m x m
+//   kShapeSquare  C = A A         P = Q = A (m_pad x m_pad, symmetric), K = m_pad
+//   kShapeApplyT  C = B X         P = B (m_pad x m_pad), Q = X^T (n_pad x m_pad), K = m_pad
+// (B X needs X^T because its k index runs down the columns of X; every NS
+// step therefore keeps X in both orientations.)  Epilogue as GemmParams: the
+// output in TO, optionally its transpose (bf16) and, for upper-triangle
+// symmetric tiles, the mirrored tile.
+
+__device__ __forceinline__ void st_bf16x4(void* base, int64_t off, const float* v) {
+  *((GLOBAL_AS u32x2_t*)(static_cast<uint16_t*>(base) + off)) =
+      u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+}
+
+template <int BM, int BN, typename TO>
+__global__ __launch_bounds__(256) void k_nt(const GemmParams p) {
+  extern __shared__ __attribute__((aligned(1024))) char nt_smem[];
+  using G = nt::Geom<BM, BN, 64, 2>;
+  const WorkItem it = p.items[blockIdx.x];
+  const NsMat* nmp = p.mats + it.slot;
+  const int m_pad = nmp->m_pad, n_pad = nmp->n_pad;
+  int K, ldp, ldq, ldo, Mr, Nr;
+  uint32_t p_rows, q_rows;
+  if (p.shape == kShapeGram) {
+    K = n_pad; ldp = ldq = n_pad; ldo = m_pad; Mr = Nr = nmp->m; p_rows = q_rows = m_pad;
+  } else if (p.shape == kShapeSquare) {
+    K = m_pad; ldp = ldq = m_pad; ldo = m_pad; Mr = Nr = nmp->m; p_rows = q_rows = m_pad;
+  } else {
+    K = m_pad; ldp = ldq = m_pad; ldo = n_pad; Mr = nmp->m; Nr = nmp->n; p_rows = m_pad; q_rows = n_pad;
+  }
+  const void* Pg = nmp->buf[p.p_id];
+  const void* Qg = nmp->buf[p.q_id];
+  const __amdgpu_buffer_rsrc_t Pr = nt::make_rsrc(Pg, p_rows * (uint32_t)ldp * 2u);
+  const __amdgpu_buffer_rsrc_t Qr = nt::make_rsrc(Qg, q_rows * (uint32_t)ldq * 2u);
+  const int m0 = it.tm * BM, n0 = it.tn * BN;
+  nt::f32x16_t acc[G::MT][G::NT];
+  nt::mainloop<BM, BN, 64, 2>(acc, (MUON_LDS char*)nt_smem, Pr, Qr, (uint32_t)ldp, (uint32_t)ldq,
+                              (uint32_t)m0, (uint32_t)n0, K);
+
+  // ---- epilogue
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wy = w >> 1, wx = w & 1;
+  float s = 1.0f;
+  if (p.scale_pow) {
+    const float rr = p.rscale[nmp->mat];
+    s = p.scale_pow == 2 ? rr * rr : rr;
+  }
+  const float alpha = p.alpha, beta = p.beta, gamma = p.gamma;
+  void* Out = nmp->buf[p.o_id];
+  void* OutT = p.ot_id >= 0 ? nmp->buf[p.ot_id] : nullptr;
+  const void* Cin = p.c_id >= 0 ? nmp->buf[p.c_id] : nullptr;
+  const bool mirror = p.sym && it.tm != it.tn;
+#pragma unroll
+  for (int a = 0; a < G::MT; ++a) {
+#pragma unroll
+    for (int b = 0; b < G::NT; ++b) {
+      const int j = n0 + wx * G::WN + b * 32 + (lane & 31);
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int ib = m0 + wy * G::WM + a * 32 + rg * 8 + (lane >> 5) * 4;
+        float v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int i = ib + q;
+          float x = alpha * acc[a][b][rg * 4 + q];
+          if (Cin) x += beta * ld_elem<uint16_t>(Cin, (int64_t)i * ldo + j);
+          x *= s;
+          if (i == j) x += gamma;
+          if (i >= Mr || j >= Nr) x = 0.f;
+          v[q] = x;
+          st_elem<TO>(Out, (int64_t)i * ldo + j, x);
+        }
+        if (mirror) st_elem4<TO>(Out, (int64_t)j * ldo + ib, v);
+        if (OutT) st_bf16x4(OutT, (int64_t)j * m_pad + ib, v);
+      }
+    }
+  }
+}
+
+template <int BM, int BN, typename TO>
+hipError_t launch_nt_t(const GemmParams& p, hipStream_t s) {
+  constexpr int smem = nt::Geom<BM, BN, 64, 2>::LDS;
+  static bool attr_done = false;
+  auto kern = &k_nt<BM, BN, TO>;
+  if (!attr_done) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+    if (e != hipSuccess) return e;
+    attr_done = true;
+  }
+  if (p.n_items <= 0) return hipSuccess;
+  hipLaunchKernelGGL(kern, dim3(p.n_items), dim3(256), smem, s, p);
+  return hipGetLastError();
+}
+
+template <int BM, int BN>
+hipError_t launch_nt_cfg(int out_dt, const GemmParams& p, hipStream_t s) {
+  if (out_dt == kBF16) return launch_nt_t<BM, BN, uint16_t>(p, s);
+  if (out_dt == kF32) return launch_nt_t<BM, BN, float>(p, s);
+  return hipErrorInvalidValue;
+}
+
 }  // namespace
 
 hipError_t launch_ew_momentum(const EwMat* mats, const EwDyn* dyn, const int64_t* tile_prefix,
@@ -583,6 +694,18 @@ hipError_t launch_gemm(int tile_cfg, int in_dtype, int out_dtype, const GemmPara
                        hipStream_t s) {
   switch (tile_cfg) {
     case 0: return launch_gemm_cfg<128, 128>(in_dtype, out_dtype, p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_gemm_nt(int nt_cfg, int out_dtype, const GemmParams& p, hipStream_t s) {
+  if (p.shape != kShapeGram && p.shape != kShapeSquare && p.shape != kShapeApplyT)
+    return hipErrorInvalidValue;
+  switch (nt_cfg) {
+    case kNt128: return launch_nt_cfg<128, 128>(out_dtype, p, s);
+    case kNt256: return launch_nt_cfg<256, 256>(out_dtype, p, s);
+    case kNt256x128: return launch_nt_cfg<256, 128>(out_dtype, p, s);
+    case kNt128x256: return launch_nt_cfg<128, 256>(out_dtype, p, s);
     default: return hipErrorInvalidValue;
   }
 }

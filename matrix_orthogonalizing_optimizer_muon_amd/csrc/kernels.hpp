@@ -32,6 +32,8 @@ struct EwMat {
   int32_t ddtype;            // NS operand dtype (D buffer)
   int32_t mat;               // index into the plan's per-matrix scale array
   void* d;                   // D: canonical NS input (m_pad x n_pad, ddtype)
+  void* dt;                  // D^T (n_pad x m_pad, ddtype) or null when the NS path does not use it
+  int64_t ldt;               // leading dimension of D^T (m_pad)
   float* xt;                 // X_T: final NS output (m_pad x n_pad, fp32)
   float s;                   // RMS-matching scale
   float pad_;
@@ -59,7 +61,9 @@ enum BufId : int32_t {
   kQY = 7,  // Q pong (Gram, fp32)
   kT1 = 8,  // H A (Gram, fp32)
   kQH = 9,  // bf16 copy of Q_T (Gram, bf16 path)
-  kNumBufs = 10
+  kX0T = 10, // D^T / X_0^T (n_pad x m_pad, bf16 path): the k-contiguous operand of B X
+  kX1T = 11, // X pong, transposed (bf16 direct path)
+  kNumBufs = 12
 };
 
 // Per matrix of a launch set: its workspace buffers and extents.
@@ -75,7 +79,8 @@ struct NsMat {
 enum GemmShape : int32_t {
   kShapeGram = 0,   // (m x n)(m x n)^T -> m x m, K = n_pad        (NT, symmetric)
   kShapeSquare = 1, // (m x m)(m x m)   -> m x m, K = m_pad        (NT, Q symmetric)
-  kShapeApply = 2   // (m x m)(m x n)   -> m x n, K = m_pad        (NN)
+  kShapeApply = 2,  // (m x m)(m x n)   -> m x n, K = m_pad        (NN)
+  kShapeApplyT = 3  // (m x m)(n x m)^T -> m x n, K = m_pad        (NT, Q = X^T)
 };
 
 struct WorkItem {
@@ -95,7 +100,7 @@ struct GemmParams {
   int32_t scale_pow;   // 0, 1 or 2
   int32_t sym;         // 1: items are upper-triangle tiles; off-diagonal tiles are mirrored
   int32_t p_id, q_id, c_id, o_id, o2_id;   // BufId; c_id / o2_id may be -1 (none)
-  int32_t pad_;
+  int32_t ot_id;       // NT kernel: also store out^T (bf16) into this buffer, or -1
   float alpha, beta, gamma, pad2_;
 };
 
@@ -105,6 +110,11 @@ struct TileCfg {
 };
 constexpr int kNumTileCfgs = 1;
 constexpr TileCfg kTileCfgs[kNumTileCfgs] = {{128, 128}};
+
+// Tile configurations of the bf16 NT kernel (mfma_nt.hpp): output tile BM x BN,
+// 64-element k-tiles, two LDS stages.
+enum NtCfg : int32_t { kNt128 = 0, kNt256 = 1, kNt256x128 = 2, kNt128x256 = 3, kNumNtCfgs = 4 };
+constexpr TileCfg kNtCfgs[kNumNtCfgs] = {{128, 128}, {256, 256}, {256, 128}, {128, 256}};
 
 // Launchers (kernels.hip).  All return hipError_t of the launch.
 hipError_t launch_ew_momentum(const EwMat* mats, const EwDyn* dyn, const int64_t* tile_prefix,
@@ -118,5 +128,8 @@ hipError_t launch_ew_apply(const EwMat* mats, const EwDyn* dyn, const int64_t* t
 // kShapeApply runs the NN kernel, the other shapes the NT kernel.
 hipError_t launch_gemm(int tile_cfg, int in_dtype, int out_dtype, const GemmParams& p,
                        hipStream_t s);
+// bf16 operands on the LDS-DMA MFMA core; shapes kShapeGram, kShapeSquare, kShapeApplyT.
+// out_dtype: kF32 or kBF16; Cin (c_id) and out^T (ot_id) are bf16.
+hipError_t launch_gemm_nt(int nt_cfg, int out_dtype, const GemmParams& p, hipStream_t s);
 
 }  // namespace muon

@@ -14,36 +14,43 @@ namespace {
 constexpr uint64_t kAlign = 256;
 constexpr uint64_t kDefaultCap = 48ull << 30;
 constexpr int kEw = 64;           // elementwise tile edge
+constexpr int kOld = 128;         // tile edge of the fp32 (register-staged) kernel
 constexpr int kXcds = 8;          // MI355X: 8 XCDs, workgroups dealt round-robin
+constexpr int kCus = 256;
 constexpr double kLaunchUs = 4.0; // per-launch cost used by the model
+
+// Tile plans: (sym config, apply config).
+constexpr TilePlan kTilePlans[5] = {{0, 0}, {0, 1}, {1, 1}, {0, 2}, {0, 3}};
 
 uint64_t align_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
 int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 
-// Buffer ids (same numbering as kernels.hpp BufId).
-enum { bX0 = 0, bX1, bXT, bA, bB, bH, bQX, bQY, bT1, bQH };
-
-// Byte offsets of each buffer of one matrix, relative to its start; returns the total.
-uint64_t layout(const ShapeKey& k, int32_t form, int32_t tile, uint64_t* off) {
-  const TileShape t = tile_shape(tile);
-  const int64_t pad = std::max(t.bm, t.bn);
-  const uint64_t mp = (uint64_t)round_up(k.m, pad), np = (uint64_t)round_up(k.n, pad);
+// Byte sizes of each buffer of one matrix; returns the total with offsets.
+uint64_t layout(const ShapeKey& k, int32_t form, int32_t tile, uint64_t* off, bool* has) {
+  int64_t mp64 = 0, np64 = 0;
+  padded_dims(k, form, tile, &mp64, &np64);
+  const uint64_t mp = (uint64_t)mp64, np = (uint64_t)np64;
   const uint64_t es = k.path ? 2 : 4;
   const uint64_t mn = mp * np, mm = mp * mp;
-  uint64_t sizes[10] = {0};
+  uint64_t sizes[kPlanBufs] = {0};
   sizes[bX0] = es * mn;
   sizes[bXT] = 4 * mn;
   if (form == kFormDirect) {
     sizes[bX1] = es * mn;
     sizes[bA] = es * mm;
     sizes[bB] = es * mm;
+    if (k.path) sizes[bX0T] = sizes[bX1T] = 2 * mn;
   } else {
     sizes[bA] = sizes[bH] = sizes[bQX] = sizes[bQY] = sizes[bT1] = 4 * mm;
-    if (k.path) sizes[bQH] = 2 * mm;
+    if (k.path) {
+      sizes[bQH] = 2 * mm;
+      sizes[bX0T] = 2 * mn;
+    }
   }
   uint64_t cur = 0;
-  for (int b = 0; b < 10; ++b) {
+  for (int b = 0; b < kPlanBufs; ++b) {
     if (off) off[b] = sizes[b] ? cur : 0;
+    if (has) has[b] = sizes[b] != 0;
     cur = align_up(cur + sizes[b], kAlign);
   }
   return cur;
@@ -62,15 +69,56 @@ void remap_xcd(std::vector<ItemHost>& v) {
   v.swap(out);
 }
 
-}  // namespace
+void add_sym(std::vector<ItemHost>& v, int32_t slot, int64_t m_pad, int edge) {
+  const int32_t nt = (int32_t)(m_pad / edge);
+  for (int32_t a = 0; a < nt; ++a)
+    for (int32_t b = a; b < nt; ++b) v.push_back({slot, a, b});
+}
 
-TileShape tile_shape(int tile) {
-  switch (tile) {
-    default:
-    case 0: return {128, 128};
+void add_full(std::vector<ItemHost>& v, int32_t slot, int64_t m_pad, int64_t n_pad, TileShape t) {
+  const int32_t ntm = (int32_t)(m_pad / t.bm), ntn = (int32_t)(n_pad / t.bn);
+  for (int32_t a = 0; a < ntm; ++a)
+    for (int32_t b = 0; b < ntn; ++b) v.push_back({slot, a, b});
+}
+
+double sym_tiles(int64_t m_pad, int edge) {
+  const double nt = (double)(m_pad / edge);
+  return nt * (nt + 1) / 2;
+}
+
+// Per-block rate (flop/s) and blocks per CU of each NT configuration, as measured
+// on MI355X for large bf16 products; the fp32 kernel for the fp32 path.
+double nt_rate(int cfg) {
+  switch (cfg) {
+    case 1: return 4.0e12;
+    case 2: case 3: return 3.4e12;
+    default: return 1.8e12;
   }
 }
-int num_tiles() { return 1; }
+int nt_blocks_per_cu(int cfg) { return cfg == 0 ? 2 : 1; }
+constexpr double kOldRateBf16 = 0.9e12;   // fp32-kernel blocks, bf16 operands
+constexpr double kOldRateF32 = 0.25e12;   // fp32-kernel blocks, fp32 operands (per block, 2 per CU)
+
+// Time of one launch of `tiles` blocks each doing `flops_per_tile`.
+double launch_us(double tiles, double flops_per_tile, double rate, int per_cu) {
+  if (tiles <= 0) return 0;
+  const double waves = std::ceil(tiles / (double)(kCus * per_cu));
+  return waves * flops_per_tile / rate * 1e6 + kLaunchUs;
+}
+
+}  // namespace
+
+TileShape nt_cfg_shape(int cfg) {
+  if (cfg < 0 || cfg >= 4) cfg = 0;
+  return kNtTileShapes[cfg];
+}
+
+int num_tile_plans() { return (int)(sizeof kTilePlans / sizeof kTilePlans[0]); }
+
+TilePlan tile_plan(int t) {
+  if (t < 0 || t >= num_tile_plans()) t = 0;
+  return kTilePlans[t];
+}
 
 ShapeKey shape_key(int64_t rows, int64_t cols, int32_t dtype, int32_t precision) {
   ShapeKey k;
@@ -82,37 +130,97 @@ ShapeKey shape_key(int64_t rows, int64_t cols, int32_t dtype, int32_t precision)
   return k;
 }
 
-uint64_t matrix_ws_bytes(const ShapeKey& k, int32_t form, int32_t tile) {
-  return layout(k, form, tile, nullptr);
-}
-
-double model_cost_us(const ShapeKey& k, int32_t form, int32_t tile) {
-  const int T = 5;
-  const TileShape t = tile_shape(tile);
-  const double mp = (double)round_up(k.m, std::max(t.bm, t.bn));
-  const double np = (double)round_up(k.n, std::max(t.bm, t.bn));
-  const double ntm = mp / t.bm;
-  const double sym_tiles = ntm * (ntm + 1) / 2;
-  const double tile_flops = 2.0 * t.bm * t.bn;
-  const double gram = sym_tiles * tile_flops * np;
-  const double square = sym_tiles * tile_flops * mp;
-  const double apply = ntm * (np / t.bn) * tile_flops * mp;
-  const double fast = (k.path ? 2.5e15 : 157e12) * 0.5;   // NS dtype rate
-  const double f32 = 157e12 * 0.5;                          // Gram iterates run in fp32
-  if (form == kFormDirect) return T * (gram + square + apply) / fast * 1e6 + 3 * T * kLaunchUs;
-  return (gram + apply) / fast * 1e6 + (4 * T - 3) * square / f32 * 1e6 + (4 * T - 1) * kLaunchUs;
-}
-
-ShapeChoice model_choice(const ShapeKey& k, int32_t forced_form) {
-  ShapeChoice c;
-  c.tile = 0;
-  if (forced_form == kFormDirect || forced_form == kFormGram) {
-    c.form = forced_form;
-    return c;
+void padded_dims(const ShapeKey& k, int32_t form, int32_t tile, int64_t* m_pad, int64_t* n_pad) {
+  (void)form;
+  int64_t em = kOld, en = kOld;
+  if (k.path) {
+    const TilePlan tp = tile_plan(tile);
+    const TileShape s = nt_cfg_shape(tp.sym), a = nt_cfg_shape(tp.apply);
+    em = std::max<int64_t>({em, s.bm, a.bm});
+    en = std::max<int64_t>(en, a.bn);
   }
-  const double d = model_cost_us(k, kFormDirect, 0), g = model_cost_us(k, kFormGram, 0);
-  c.form = g < 0.97 * d ? kFormGram : kFormDirect;
-  return c;
+  *m_pad = round_up(k.m, em);
+  *n_pad = round_up(k.n, en);
+}
+
+bool dims_supported(int64_t rows, int64_t cols) {
+  const int64_t m = std::min(rows, cols), n = std::max(rows, cols);
+  if (m < 1 || m > 16384 || n > (1 << 20)) return false;
+  // every bf16 operand and each fp32 m x m iterate stays under 2^31 bytes
+  return round_up(m, 256) * round_up(n, 256) <= (int64_t(1) << 30);
+}
+
+uint64_t matrix_ws_bytes(const ShapeKey& k, int32_t form, int32_t tile) {
+  return layout(k, form, tile, nullptr, nullptr);
+}
+
+std::vector<std::pair<int32_t, int32_t>> candidates(const ShapeKey& k, int32_t forced_form,
+                                                    int32_t forced_tile) {
+  std::vector<std::pair<int32_t, int32_t>> out;
+  const bool dir = forced_form != kFormGram, gram = forced_form != kFormDirect;
+  if (!k.path) {
+    if (dir) out.push_back({kFormDirect, 0});
+    if (gram) out.push_back({kFormGram, 0});
+    return out;
+  }
+  auto want = [&](int t) { return forced_tile < 0 || forced_tile == t; };
+  if (dir)
+    for (int t = 0; t < num_tile_plans(); ++t)
+      if (want(t)) out.push_back({kFormDirect, t});
+  if (gram)
+    for (int t : {0, 1, 2})
+      if (want(t)) out.push_back({kFormGram, t});
+  return out;
+}
+
+double model_cost_us(const ShapeKey& k, int32_t form, int32_t tile, int count) {
+  const int T = 5;
+  const double c = std::max(count, 1);
+  int64_t mp64 = 0, np64 = 0;
+  padded_dims(k, form, tile, &mp64, &np64);
+  const double mp = (double)mp64, np = (double)np64;
+  double us = 0;
+  if (!k.path) {
+    const double st = sym_tiles(mp64, kOld) * c, ft = (mp / kOld) * (np / kOld) * c;
+    const double tf = 2.0 * kOld * kOld;
+    const double g = launch_us(st, tf * np, kOldRateF32, 2);
+    const double sq = launch_us(st, tf * mp, kOldRateF32, 2);
+    const double ap = launch_us(ft, tf * mp, kOldRateF32, 2);
+    us = form == kFormDirect ? T * (g + sq + ap) : g + ap + (4 * T - 3) * sq;
+    return us / c;
+  }
+  const TilePlan tp = tile_plan(tile);
+  const TileShape s = nt_cfg_shape(tp.sym), a = nt_cfg_shape(tp.apply);
+  const double st = sym_tiles(mp64, s.bm) * c, ft = (mp / a.bm) * (np / a.bn) * c;
+  const double g = launch_us(st, 2.0 * s.bm * s.bn * np, nt_rate(tp.sym), nt_blocks_per_cu(tp.sym));
+  const double ap = launch_us(ft, 2.0 * a.bm * a.bn * mp, nt_rate(tp.apply), nt_blocks_per_cu(tp.apply));
+  if (form == kFormDirect) {
+    const double sq = launch_us(st, 2.0 * s.bm * s.bn * mp, nt_rate(tp.sym), nt_blocks_per_cu(tp.sym));
+    us = T * (g + sq + ap);
+  } else {
+    const double ost = sym_tiles(mp64, kOld) * c;
+    const double sq = launch_us(ost, 2.0 * kOld * kOld * mp, kOldRateBf16 * 0.3, 2);  // fp32 iterates
+    us = g + ap + (4 * T - 3) * sq;
+  }
+  return us / c;
+}
+
+ShapeChoice model_choice(const ShapeKey& k, int32_t forced_form, int32_t forced_tile, int count) {
+  ShapeChoice best;
+  double best_us = 0;
+  bool first = true;
+  for (const auto& cand : candidates(k, forced_form, forced_tile)) {
+    const double us = model_cost_us(k, cand.first, cand.second, count);
+    if (first || us < 0.97 * best_us) {
+      best.form = cand.first;
+      best.tile = cand.second;
+      best_us = us;
+      first = false;
+    }
+  }
+  best.us = 0;
+  best.timed = false;
+  return best;
 }
 
 std::string build_plan(const std::vector<int64_t>& rows, const std::vector<int64_t>& cols,
@@ -142,7 +250,7 @@ std::string build_plan(const std::vector<int64_t>& rows, const std::vector<int64
     GroupPlan g;
     g.key = kv.first;
     g.form = it->second.form;
-    g.tile = it->second.tile;
+    g.tile = kv.first.path ? it->second.tile : 0;
     g.members = kv.second;
     const int32_t gi = (int32_t)P.groups.size();
     for (int32_t i : g.members) {
@@ -150,11 +258,8 @@ std::string build_plan(const std::vector<int64_t>& rows, const std::vector<int64
       M.form = g.form;
       M.tile = g.tile;
       M.group = gi;
-      const TileShape t = tile_shape(g.tile);
-      const int64_t pad = std::max(t.bm, t.bn);
-      M.m_pad = round_up(M.m, pad);
-      M.n_pad = round_up(M.n, pad);
-      M.ws_bytes = layout(kv.first, g.form, g.tile, M.off);
+      padded_dims(kv.first, g.form, g.tile, &M.m_pad, &M.n_pad);
+      M.ws_bytes = layout(kv.first, g.form, g.tile, M.off, M.has);
       M.ew_tiles = (M.m_pad / kEw) * (M.n_pad / kEw);
       if (g.form == kFormGram) P.n_gram++;
     }
@@ -173,7 +278,7 @@ std::string build_plan(const std::vector<int64_t>& rows, const std::vector<int64
       }
       if (P.chunks.empty() || P.chunks.back().ws_bytes + M.ws_bytes > cap) P.chunks.emplace_back();
       ChunkPlan& C = P.chunks.back();
-      for (int b = 0; b < 10; ++b) M.off[b] += C.ws_bytes;
+      for (int b = 0; b < kPlanBufs; ++b) M.off[b] += C.ws_bytes;
       C.ws_bytes += M.ws_bytes;
       C.ew_tiles += M.ew_tiles;
       M.chunk = (int32_t)(P.chunks.size() - 1);
@@ -196,31 +301,49 @@ std::string build_plan(const std::vector<int64_t>& rows, const std::vector<int64
       }
       const int32_t slot = (int32_t)S->mats.size();
       S->mats.push_back(i);
-      const TileShape t = tile_shape(M.tile);
-      const int32_t ntm = (int32_t)(M.m_pad / t.bm), ntn = (int32_t)(M.n_pad / t.bn);
-      for (int32_t a = 0; a < ntm; ++a)
-        for (int32_t b = a; b < ntm; ++b) S->items_sym.push_back({slot, a, b});
-      for (int32_t a = 0; a < ntm; ++a)
-        for (int32_t b = 0; b < ntn; ++b) S->items_full.push_back({slot, a, b});
       const double m = (double)M.m, nn = (double)M.n, mp = (double)M.m_pad, np = (double)M.n_pad;
-      const double symt = (double)ntm * (ntm + 1) / 2, tf = 2.0 * t.bm * t.bn;
       S->flops_gram_min += nn * m * (m + 1);
       S->flops_square_min += m * m * (m + 1);
       S->flops_apply_min += 2.0 * m * m * nn;
-      S->flops_gram_issued += symt * tf * np;
-      S->flops_square_issued += symt * tf * mp;
-      S->flops_apply_issued += (double)ntm * ntn * tf * mp;
+      const double old_tf = 2.0 * kOld * kOld;
+      if (M.path) {
+        const TilePlan tp = tile_plan(M.tile);
+        const TileShape s = nt_cfg_shape(tp.sym), a = nt_cfg_shape(tp.apply);
+        add_sym(S->nt_sym, slot, M.m_pad, s.bm);
+        add_full(S->nt_full, slot, M.m_pad, M.n_pad, a);
+        const double st = sym_tiles(M.m_pad, s.bm);
+        S->flops_gram_issued += st * 2.0 * s.bm * s.bn * np;
+        S->flops_apply_issued += (mp / a.bm) * (np / a.bn) * 2.0 * a.bm * a.bn * mp;
+        if (M.form == kFormDirect) {
+          S->flops_square_issued += st * 2.0 * s.bm * s.bn * mp;
+        } else {
+          add_sym(S->old_sym, slot, M.m_pad, kOld);
+          S->flops_square_issued_fp32 += sym_tiles(M.m_pad, kOld) * old_tf * mp;
+        }
+      } else {
+        add_sym(S->old_sym, slot, M.m_pad, kOld);
+        add_full(S->old_full, slot, M.m_pad, M.n_pad, TileShape{kOld, kOld});
+        const double st = sym_tiles(M.m_pad, kOld);
+        S->flops_gram_issued += st * old_tf * np;
+        S->flops_apply_issued += (mp / kOld) * (np / kOld) * old_tf * mp;
+        if (M.form == kFormDirect) S->flops_square_issued += st * old_tf * mp;
+        else S->flops_square_issued_fp32 += st * old_tf * mp;
+      }
     }
     for (LaunchSetPlan& S : C.sets) {
       // longest contraction first, then XCD-contiguous placement
-      auto kgram = [&](const ItemHost& it) { return P.mats[S.mats[it.slot]].n_pad; };
-      auto kfull = [&](const ItemHost& it) { return P.mats[S.mats[it.slot]].m_pad; };
-      std::stable_sort(S.items_sym.begin(), S.items_sym.end(),
-                       [&](const ItemHost& x, const ItemHost& y) { return kgram(x) > kgram(y); });
-      std::stable_sort(S.items_full.begin(), S.items_full.end(),
-                       [&](const ItemHost& x, const ItemHost& y) { return kfull(x) > kfull(y); });
-      remap_xcd(S.items_sym);
-      remap_xcd(S.items_full);
+      auto kn = [&](const ItemHost& it) { return P.mats[S.mats[it.slot]].n_pad; };
+      auto km = [&](const ItemHost& it) { return P.mats[S.mats[it.slot]].m_pad; };
+      for (std::vector<ItemHost>* v : {&S.nt_sym, &S.old_sym}) {
+        std::stable_sort(v->begin(), v->end(),
+                         [&](const ItemHost& x, const ItemHost& y) { return kn(x) > kn(y); });
+        remap_xcd(*v);
+      }
+      for (std::vector<ItemHost>* v : {&S.nt_full, &S.old_full}) {
+        std::stable_sort(v->begin(), v->end(),
+                         [&](const ItemHost& x, const ItemHost& y) { return km(x) > km(y); });
+        remap_xcd(*v);
+      }
     }
   }
   *out = std::move(P);
@@ -229,10 +352,10 @@ std::string build_plan(const std::vector<int64_t>& rows, const std::vector<int64
 
 std::string serialize_plan(const PlanHost& p) {
   std::ostringstream o;
-  o << "muon-plan v1\n";
+  o << "muon-plan v2\n";
   o << "opts nesterov=" << p.opts.nesterov << " eps=" << std::hexfloat << p.opts.eps
     << " rms=" << p.opts.rms_scale << std::defaultfloat << " precision=" << p.opts.precision
-    << " form=" << p.opts.form << " cap=" << p.opts.workspace_cap << "\n";
+    << " form=" << p.opts.form << " tile=" << p.opts.tile << " cap=" << p.opts.workspace_cap << "\n";
   for (size_t i = 0; i < p.mats.size(); ++i) {
     const MatPlan& M = p.mats[i];
     o << "mat " << i << " " << M.rows << "x" << M.cols << " dtype=" << M.dtype << " path=" << M.path
@@ -251,11 +374,12 @@ std::string serialize_plan(const PlanHost& p) {
       << "\n";
     for (const LaunchSetPlan& S : C.sets) {
       o << " set path=" << S.path << " form=" << S.form << " tile=" << S.tile << " mats=" << S.mats.size()
-        << " sym=" << S.items_sym.size() << " full=" << S.items_full.size() << " order=";
+        << " items=" << S.nt_sym.size() << "/" << S.nt_full.size() << "/" << S.old_sym.size() << "/"
+        << S.old_full.size() << " order=";
       uint64_t h = 1469598103934665603ull;
       auto mix = [&](int32_t v) { for (int b = 0; b < 4; ++b) { h ^= (uint8_t)(v >> (8 * b)); h *= 1099511628211ull; } };
-      for (const ItemHost& it : S.items_sym) { mix(it.slot); mix(it.tm); mix(it.tn); }
-      for (const ItemHost& it : S.items_full) { mix(it.slot); mix(it.tm); mix(it.tn); }
+      for (const std::vector<ItemHost>* v : {&S.nt_sym, &S.nt_full, &S.old_sym, &S.old_full})
+        for (const ItemHost& it : *v) { mix(it.slot); mix(it.tm); mix(it.tn); }
       o << std::hex << h << std::dec << "\n";
     }
   }
@@ -279,7 +403,7 @@ std::map<ShapeKey, ShapeChoice> read_cache(const std::string& path, const std::s
   while (std::getline(f, line)) {
     std::istringstream is(line);
     std::string magic, tag;
-    if (!(is >> magic >> tag) || magic != "muon-tune-v1" || tag != device_tag) continue;
+    if (!(is >> magic >> tag) || magic != "muon-tune-v2" || tag != device_tag) continue;
     ShapeKey k{-1, -1, -1};
     ShapeChoice c;
     c.form = -1;
@@ -298,11 +422,11 @@ std::map<ShapeKey, ShapeChoice> read_cache(const std::string& path, const std::s
       else if (key == "path") k.path = (int32_t)v;
       else if (key == "form") c.form = (int32_t)v;
       else if (key == "tile") c.tile = (int32_t)v;
-      else if (key == "us_direct") c.us_direct = v;
-      else if (key == "us_gram") c.us_gram = v;
+      else if (key == "us") c.us = v;
     }
     if (bad || k.m < 1 || k.n < k.m || (k.path != 0 && k.path != 1)) continue;
-    if ((c.form != kFormDirect && c.form != kFormGram) || c.tile < 0 || c.tile >= num_tiles()) continue;
+    if ((c.form != kFormDirect && c.form != kFormGram) || c.tile < 0 || c.tile >= num_tile_plans()) continue;
+    if (k.path == 0 && c.tile != 0) continue;
     c.timed = true;
     out[k] = c;
   }
@@ -320,7 +444,7 @@ bool write_cache(const std::string& path, const std::string& device_tag,
     while (std::getline(f, line)) {
       std::istringstream is(line);
       std::string magic, tag;
-      if ((is >> magic >> tag) && magic == "muon-tune-v1" && tag == device_tag) continue;
+      if ((is >> magic >> tag) && magic == "muon-tune-v2" && tag == device_tag) continue;
       if (!line.empty()) keep.push_back(line);
     }
   }
@@ -331,9 +455,9 @@ bool write_cache(const std::string& path, const std::string& device_tag,
     for (const std::string& l : keep) f << l << "\n";
     for (const auto& kv : entries) {
       char buf[256];
-      snprintf(buf, sizeof buf, "muon-tune-v1 %s m=%lld n=%lld path=%d form=%d tile=%d us_direct=%.3f us_gram=%.3f\n",
+      snprintf(buf, sizeof buf, "muon-tune-v2 %s m=%lld n=%lld path=%d form=%d tile=%d us=%.3f\n",
                device_tag.c_str(), (long long)kv.first.m, (long long)kv.first.n, kv.first.path,
-               kv.second.form, kv.second.tile, kv.second.us_direct, kv.second.us_gram);
+               kv.second.form, kv.second.tile, kv.second.us);
       f << buf;
     }
     if (!f) return false;
@@ -351,7 +475,7 @@ void plan_flops(const PlanHost& p, int T, double* min_flops, double* issued_flop
         is += T * (S.flops_gram_issued + S.flops_square_issued + S.flops_apply_issued);
       } else {
         mn += S.flops_gram_min + S.flops_apply_min + (4.0 * T - 3) * S.flops_square_min;
-        is += S.flops_gram_issued + S.flops_apply_issued + (4.0 * T - 3) * S.flops_square_issued;
+        is += S.flops_gram_issued + S.flops_apply_issued + (4.0 * T - 3) * S.flops_square_issued_fp32;
       }
     }
   if (min_flops) *min_flops = mn;
@@ -363,8 +487,9 @@ double plan_ew_bytes(const PlanHost& p) {
   for (const MatPlan& M : p.mats) {
     const double e = (double)M.rows * M.cols;
     const double pes = M.dtype ? 2 : 4, es = M.path ? 2 : 4;
-    b += e * (pes + 8 + es);    // momentum: g, buf in/out, d out
-    b += e * (4 + 2 * pes);     // apply: X_T in, W in/out
+    const double dt = M.has[bX0T] ? es : 0;   // transposed copy of d for the bf16 path
+    b += e * (pes + 8 + es + dt);  // momentum: g, buf in/out, d (and d^T) out
+    b += e * (4 + 2 * pes);        // apply: X_T in, W in/out
   }
   return b;
 }

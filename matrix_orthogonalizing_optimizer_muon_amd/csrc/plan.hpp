@@ -1,10 +1,10 @@
 // Host-side planner of the Muon step: pure C++, no device calls.
 //
 // The plan is a pure function of (matrix descriptors, options, per-shape
-// choices).  The per-shape choices (NS form and tile configuration) come from
-// the tune cache, one-time timing, or the analytic cost model; everything
-// downstream of them - groups, chunks, workspace offsets, work-item order - is
-// derived deterministically here, so equal inputs give byte-equal plans.
+// choices).  The per-shape choices (NS form and tile plan) come from the tune
+// cache, one-time timing, or the analytic cost model; everything downstream
+// of them - groups, chunks, workspace offsets, work-item order - is derived
+// deterministically here, so equal inputs give byte-equal plans.
 //
 // DMuon announcement (wjxwpt.net), improvement 2 "shape-adaptive execution
 // stack": the mathematical form, the execution mode (alone or batched) and
@@ -23,6 +23,24 @@ namespace muon {
 
 enum PlanForm : int32_t { kFormDirect = 1, kFormGram = 2 };
 
+// Buffer ids of a matrix's workspace (same numbering as kernels.hpp BufId).
+enum PlanBuf : int32_t {
+  bX0 = 0, bX1, bXT, bA, bB, bH, bQX, bQY, bT1, bQH, bX0T, bX1T, kPlanBufs
+};
+
+// Output tiles of the bf16 NT kernel configurations (kernels.hpp NtCfg; abi.cpp
+// checks at compile time that the two tables agree).
+struct TileShape { int32_t bm, bn; };
+constexpr TileShape kNtTileShapes[4] = {{128, 128}, {256, 256}, {256, 128}, {128, 256}};
+TileShape nt_cfg_shape(int cfg);
+
+// A tile plan: the NT kernel configuration of the symmetric m x m products
+// (X X^T, A A; square tiles) and of the m x n product B X.  The fp32 path runs
+// the 128 x 128 register-staged kernel and has the single plan 0.
+struct TilePlan { int32_t sym, apply; };
+int num_tile_plans();
+TilePlan tile_plan(int t);
+
 struct ShapeKey {
   int64_t m, n;     // canonical (min, max)
   int32_t path;     // NS dtype: 0 fp32, 1 bf16
@@ -35,7 +53,7 @@ struct ShapeKey {
 struct ShapeChoice {
   int32_t form = kFormDirect;
   int32_t tile = 0;
-  double us_direct = 0, us_gram = 0;  // measured (0: not timed)
+  double us = 0;        // measured NS time per matrix of the chosen candidate (0: not timed)
   bool timed = false;
 };
 
@@ -45,6 +63,7 @@ struct PlanOptions {
   float rms_scale = 0.2f;
   int32_t precision = 0;  // muon_precision
   int32_t form = 0;       // muon_form
+  int32_t tile = -1;      // forced tile plan, -1: chosen per shape
   int32_t tune = 0;
   int32_t host_only = 0;
   uint64_t workspace_cap = 0;
@@ -61,10 +80,11 @@ struct MatPlan {
   int32_t tile = 0;
   int32_t group = -1;
   int32_t chunk = -1;
-  float s = 0.f;           // RMS-matching scale
-  uint64_t off[10] = {0};  // workspace byte offsets per buffer id (within the chunk region)
+  float s = 0.f;                  // RMS-matching scale
+  uint64_t off[kPlanBufs] = {0};  // workspace byte offsets per buffer id (within the chunk region)
+  bool has[kPlanBufs] = {false};  // buffer present
   uint64_t ws_bytes = 0;
-  int64_t ew_tiles = 0;    // 64 x 64 tiles of the padded canonical extent
+  int64_t ew_tiles = 0;           // 64 x 64 tiles of the padded canonical extent
 };
 
 struct GroupPlan {
@@ -78,13 +98,16 @@ struct ItemHost { int32_t slot, tm, tn; };
 // Matrices of one chunk that share (path, form, tile): one launch per NS stage.
 struct LaunchSetPlan {
   int32_t path = 0, form = kFormDirect, tile = 0;
-  std::vector<int32_t> mats;         // matrix indices, in slot order
-  std::vector<ItemHost> items_sym;   // upper-triangle m x m tiles
-  std::vector<ItemHost> items_full;  // m x n tiles
-  double flops_gram_min = 0;         // symmetric-aware algorithmic flops of one X X^T over the set
-  double flops_square_min = 0;       // one symmetric m x m product over the set
-  double flops_apply_min = 0;        // one (m x m)(m x n) product over the set
+  std::vector<int32_t> mats;       // matrix indices, in slot order
+  std::vector<ItemHost> nt_sym;    // upper-triangle m x m tiles of the NT sym config
+  std::vector<ItemHost> nt_full;   // m x n tiles of the NT apply config
+  std::vector<ItemHost> old_sym;   // upper-triangle 128-tiles (fp32 kernel)
+  std::vector<ItemHost> old_full;  // m x n 128-tiles (fp32 kernel)
+  double flops_gram_min = 0;       // symmetric-aware algorithmic flops of one X X^T over the set
+  double flops_square_min = 0;     // one symmetric m x m product over the set
+  double flops_apply_min = 0;      // one (m x m)(m x n) product over the set
   double flops_gram_issued = 0, flops_square_issued = 0, flops_apply_issued = 0;
+  double flops_square_issued_fp32 = 0;   // Gram iterates on the fp32 kernel
 };
 
 struct ChunkPlan {
@@ -103,18 +126,23 @@ struct PlanHost {
   int32_t n_gram = 0;
 };
 
-// Tile configuration (must match kernels.hpp kTileCfgs).
-struct TileShape { int32_t bm, bn; };
-TileShape tile_shape(int tile);
-int num_tiles();
-
 // Canonical key of a matrix under the options (path from dtype and precision).
 ShapeKey shape_key(int64_t rows, int64_t cols, int32_t dtype, int32_t precision);
 
-// Analytic cost of a shape for a form, in microseconds at nominal MI355X peaks
-// (used when not timing).  T = 5.
-double model_cost_us(const ShapeKey& k, int32_t form, int32_t tile);
-ShapeChoice model_choice(const ShapeKey& k, int32_t forced_form);
+// Candidates (form, tile plan) of a key, in the fixed tie-break order.
+std::vector<std::pair<int32_t, int32_t>> candidates(const ShapeKey& k, int32_t forced_form,
+                                                    int32_t forced_tile);
+
+// Analytic cost of one matrix of `count` equal ones for a (form, tile plan),
+// in microseconds at the rates the kernels reach on MI355X (used when not timing).
+double model_cost_us(const ShapeKey& k, int32_t form, int32_t tile, int count);
+ShapeChoice model_choice(const ShapeKey& k, int32_t forced_form, int32_t forced_tile, int count);
+
+// Padded canonical extents of a key under a (form, tile plan).
+void padded_dims(const ShapeKey& k, int32_t form, int32_t tile, int64_t* m_pad, int64_t* n_pad);
+
+// Largest canonical extents the kernels address (32-bit byte offsets per operand).
+bool dims_supported(int64_t rows, int64_t cols);
 
 // Builds the plan.  choices must hold an entry for every distinct key.
 // Returns "" on success or an error message (workspace cap exceeded by one matrix).
@@ -134,7 +162,7 @@ std::map<ShapeKey, ShapeChoice> read_cache(const std::string& path, const std::s
 bool write_cache(const std::string& path, const std::string& device_tag,
                  const std::map<ShapeKey, ShapeChoice>& entries);
 
-// Per-step flops (T = 5) of the plan: symmetric-aware minimum and issued by the tiles.
+// Per-step flops of the plan at ns_steps T: symmetric-aware minimum and issued by the tiles.
 void plan_flops(const PlanHost& p, int ns_steps, double* min_flops, double* issued_flops);
 double plan_ew_bytes(const PlanHost& p);
 

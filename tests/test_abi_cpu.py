@@ -28,16 +28,17 @@ def test_every_declared_function_is_exported_and_bound():
         assert hasattr(lib, n), n
         assert n in L.PROTOTYPES, f"{n} has no ctypes prototype"
     assert set(L.PROTOTYPES) == set(names)
-    assert lib.muon_abi_version() == 1
+    assert lib.muon_abi_version() == 2
 
 
 def test_struct_sizes_match_header_layout():
     assert ctypes.sizeof(L.MatrixDesc) == 24
-    assert ctypes.sizeof(L.PlanOpts) == 48
+    assert ctypes.sizeof(L.PlanOpts) == 56
     opts = L.PlanOpts()
     assert L.lib().muon_plan_opts_default(ctypes.byref(opts)) == 0
     assert opts.struct_size == ctypes.sizeof(L.PlanOpts)
     assert opts.nesterov == 1 and abs(opts.eps - 1e-7) < 1e-12 and abs(opts.rms_scale - 0.2) < 1e-7
+    assert opts.tile == -1 and opts.form == 0 and opts.precision == 0
 
 
 def _host(shapes, dtype="bf16", **kw):
@@ -128,15 +129,24 @@ def test_tune_cache_is_read_and_bad_lines_ignored(tmp_path):
     path = tmp_path / "tune.txt"
     path.write_text(
         "garbage line\n"
-        "muon-tune-v1 host m=512 n=16384 path=1 form=2 tile=0 us_direct=900 us_gram=400\n"
-        "muon-tune-v1 host m=1024 n=1024 path=1 form=9 tile=0 us_direct=1 us_gram=1\n"
-        "muon-tune-v1 otherdev m=64 n=64 path=1 form=2 tile=0 us_direct=1 us_gram=1\n")
-    p = _host([(512, 16384), (1024, 1024), (64, 64)], cache_path=str(path))
-    assert p.matrix_choice(0)["form"] == "gram"      # from the cache
-    assert p.matrix_choice(1)["form"] == "direct"    # malformed entry ignored -> model
-    assert p.matrix_choice(2)["form"] == "direct"    # other device's line ignored
-    p2 = _host([(512, 16384), (1024, 1024), (64, 64)], cache_path=str(path))
+        "muon-tune-v2 host m=512 n=16384 path=1 form=2 tile=1 us=400\n"
+        "muon-tune-v2 host m=1024 n=1024 path=1 form=9 tile=0 us=1\n"
+        "muon-tune-v2 host m=2048 n=2048 path=1 form=1 tile=7 us=1\n"
+        "muon-tune-v1 host m=256 n=256 path=1 form=2 tile=0 us_direct=1 us_gram=1\n"
+        "muon-tune-v2 otherdev m=64 n=64 path=1 form=2 tile=0 us=1\n")
+    shapes = [(512, 16384), (1024, 1024), (64, 64), (2048, 2048), (256, 256)]
+    p = _host(shapes, cache_path=str(path))
+    model = _host(shapes, tune="off")
+    c0 = p.matrix_choice(0)
+    assert (c0["form"], c0["tile"]) == ("gram", 1)   # from the cache
+    for i in range(1, 5):                            # malformed, other device, old format -> model
+        got, want = p.matrix_choice(i), model.matrix_choice(i)
+        assert (got["form"], got["tile"]) == (want["form"], want["tile"])
+    p2 = _host(shapes, cache_path=str(path))
     assert p2.serialize() == p.serialize()
     # tune off ignores the cache
     p3 = _host([(512, 16384)], cache_path=str(path), tune="off")
-    assert p3.matrix_choice(0)["form"] == "direct"
+    assert p3.serialize() == _host([(512, 16384)], tune="off").serialize()
+    # a forced form or tile never takes a cached choice that violates it
+    p4 = _host([(512, 16384)], cache_path=str(path), form="direct")
+    assert p4.matrix_choice(0)["form"] == "direct"

@@ -178,3 +178,27 @@ def test_plan_errors_and_host_checks(M):
         plan.step(good, [torch.zeros(32, 64, dtype=torch.float32, device="cuda")], mom)
     with pytest.raises(M.MuonError):
         plan.step([good[0].clone()], good, mom, ns_steps=-1)
+
+
+@pytest.mark.parametrize("tile", [0, 1, 2, 3, 4])
+def test_bf16_direct_every_tile_plan(M, tile):
+    """Each NT tile plan (symmetric / m x n output tiles), ragged and tall shapes
+    in one batched plan, T = 5, 1 and 2."""
+    from gpu_util import make_state, run_and_compare
+    shapes = [(300, 700), (700, 300), (129, 1000), (520, 520), (64, 2048), (300, 700)]
+    Ws, Gs, Bs = make_state(shapes, WL.BF16, seed=40 + tile, buf_scale=0.01)
+    plan = _plan(M, shapes, "bf16", tile=tile, form="direct")
+    assert all(plan.matrix_choice(i)["tile"] == tile for i in range(len(shapes)))
+    for T in (5, 1, 2):
+        run_and_compare(plan, Ws, Gs, Bs, WL.BF16, ns_steps=T)
+
+
+@pytest.mark.parametrize("tile", [0, 1, 2])
+def test_bf16_gram_every_tile_plan(M, tile):
+    from gpu_util import make_state, run_and_compare
+    shapes = [(200, 1500), (1500, 200), (256, 4096)]
+    Ws, Gs, Bs = make_state(shapes, WL.BF16, seed=60 + tile)
+    plan = _plan(M, shapes, "bf16", tile=tile, form="gram")
+    assert all(plan.matrix_choice(i)["form"] == "gram" for i in range(len(shapes)))
+    for T in (5, 1):
+        run_and_compare(plan, Ws, Gs, Bs, WL.BF16, ns_steps=T)
