@@ -32,10 +32,44 @@ def parse():
     ap.add_argument("--config", type=int, default=2, help="workload number 1..5")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--tune", default="once", choices=["off", "once", "force"])
+    ap.add_argument("--form", default="auto", choices=["auto", "direct", "gram"])
+    ap.add_argument("--tile", type=int, default=None, help="force a tile plan (0..4)")
     ap.add_argument("--cache", default=os.path.join(os.path.expanduser("~"), ".cache", "muon_mi355x",
                                                     "tune.txt"))
     ap.add_argument("--no-kernel-times", action="store_true")
     return ap.parse_args()
+
+
+def source_digest():
+    """sha256 of the kernel sources: a recorded traffic figure is only valid for them."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "matrix_orthogonalizing_optimizer_muon_amd", "csrc")
+    for f in ("kernels.hip", "mfma_nt.hpp", "kernels.hpp"):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel, workload, launches_per_step):
+    """HBM bytes per launch of `kernel` from a committed counter summary
+    (profiles/traffic.json, written from two rocprofv3 --pmc passes), or None
+    when none matches this kernel, workload and kernel-source digest."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    digest = source_digest()
+    for r in rec.get("entries", []):
+        if r.get("kernel") == kernel and r.get("workload") == workload and r.get("source") == digest:
+            return {"fetch_bytes": r["fetch_bytes_per_launch"], "write_bytes": r["write_bytes_per_launch"],
+                    "bytes": r["fetch_bytes_per_launch"] + r["write_bytes_per_launch"],
+                    "copy_factor": r.get("copy_factor"), "source": digest}
+    return None
 
 
 def make_inputs(wl, torch):
@@ -104,9 +138,14 @@ def main():
     torch.cuda.init()
     os.makedirs(os.path.dirname(args.cache), exist_ok=True)
     t0 = time.perf_counter()
-    plan = MU.MuonPlan(wl.shapes, wl.dtype, tune=args.tune, cache_path=args.cache)
+    plan = MU.MuonPlan(wl.shapes, wl.dtype, tune=args.tune, cache_path=args.cache, form=args.form,
+                       tile=args.tile)
     plan_s = time.perf_counter() - t0
     info = plan.info()
+    choices = {}
+    for i, (r, c) in enumerate(wl.shapes):
+        ch = plan.matrix_choice(i)
+        choices.setdefault(f"{min(r, c)}x{max(r, c)}", f"{ch['form']}/tile{ch['tile']}")
     P, G, B = make_inputs(wl, torch)
     h = wl.hyper
     stream = torch.cuda.current_stream()
@@ -150,24 +189,38 @@ def main():
     ns_flops = info["ns_flops_min"]
     bf16 = wl.dtype == "bf16"
     peak = PEAK_BF16_TFLOPS if bf16 else PEAK_FP32_TFLOPS
-    ns_kinds = [k for k in kt if k["flops"] > 0]
-    ew_kinds = [k for k in kt if k["bytes"] > 0]
-    ns_ms = sum(k["total_ms"] for k in ns_kinds) / max(args.steps, 1)
+    # per kernel instance (what rocprofv3 lists as one kernel), summed over stages
+    by_kernel = {}
+    for k in kt:
+        d = by_kernel.setdefault(k["kernel"], {"launches": 0, "total_ms": 0.0, "flops": 0.0,
+                                               "bytes": 0.0, "stages": []})
+        d["launches"] += k["launches"]
+        d["total_ms"] += k["total_ms"]
+        d["flops"] += k["flops"]
+        d["bytes"] += k["bytes"]
+        d["stages"].append(k["name"])
+    ns_kern = {n: d for n, d in by_kernel.items() if d["flops"] > 0}
+    ew_kern = {n: d for n, d in by_kernel.items() if d["bytes"] > 0}
+    ns_ms = sum(d["total_ms"] for d in ns_kern.values()) / max(args.steps, 1)
     roofline = None
-    if ns_kinds:
-        dom = max(ns_kinds, key=lambda k: k["total_ms"])
+    if ns_kern:
+        name, dom = max(ns_kern.items(), key=lambda kv: kv[1]["total_ms"])
         avg_ms = dom["total_ms"] / dom["launches"]
-        ach = dom["flops"] / dom["launches"] / (avg_ms * 1e-3) / 1e12
-        roofline = {"bound": "mfma", "kernel": dom["name"], "achieved": round(ach, 2),
-                    "peak": peak, "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": None,
-                    "avg_launch_us": round(avg_ms * 1e3, 2),
-                    "flops_per_launch": dom["flops"] / dom["launches"]}
+        fpl = dom["flops"] / dom["launches"]
+        ach = fpl / (avg_ms * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "kernel": name, "stages": sorted(set(dom["stages"])),
+                    "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
+                    "frac": round(ach / peak, 4),
+                    "traffic": traffic_for(name, wl.name, dom["launches"] / args.steps),
+                    "avg_launch_us": round(avg_ms * 1e3, 2), "flops_per_launch": fpl,
+                    "launches_per_step": dom["launches"] / args.steps,
+                    "share_of_step": round(dom["total_ms"] / args.steps / ms, 4)}
     ew = {}
-    for k in ew_kinds:
-        avg_ms = k["total_ms"] / k["launches"]
-        gbs = k["bytes"] / k["launches"] / (avg_ms * 1e-3) / 1e9
-        ew[k["name"]] = {"GB/s": round(gbs, 1), "frac_of_hbm": round(gbs / PEAK_HBM_GBS, 4),
-                         "avg_launch_us": round(avg_ms * 1e3, 2)}
+    for n, d in ew_kern.items():
+        avg_ms = d["total_ms"] / d["launches"]
+        gbs = d["bytes"] / d["launches"] / (avg_ms * 1e-3) / 1e9
+        ew[n] = {"GB/s": round(gbs, 1), "frac_of_hbm": round(gbs / PEAK_HBM_GBS, 4),
+                 "avg_launch_us": round(avg_ms * 1e3, 2), "bytes_per_launch": d["bytes"] / d["launches"]}
     value = ns_flops / (ms * 1e-3) / 1e12
     out = {
         "metric": "Muon optimizer-step ms + NS TFLOP/s (% of MI355X bf16 MFMA peak)",
@@ -185,9 +238,10 @@ def main():
         "ns_frac_of_peak": round(ns_flops / (ns_ms * 1e-3) / 1e12 / peak, 4) if ns_ms else None,
         "step_frac_of_peak": round(value / peak, 4),
         "elementwise": ew, "roofline": roofline,
-        "kernels": [{"name": k["name"], "launches_per_step": k["launches"] / args.steps,
+        "kernels": [{"stage": k["name"], "kernel": k["kernel"],
+                     "launches_per_step": k["launches"] / args.steps,
                      "ms_per_step": round(k["total_ms"] / args.steps, 4)} for k in kt],
-        "plan": {"groups": info["n_groups"], "chunks": info["n_chunks"], "gram": info["n_gram"],
+        "plan": {"choices": choices, "groups": info["n_groups"], "chunks": info["n_chunks"], "gram": info["n_gram"],
                  "workspace_gb": round(info["workspace_bytes"] / 1e9, 3),
                  "create_s": round(plan_s, 3), "hash": info["plan_hash"]},
         "wall_s_timed": round(wall, 3),

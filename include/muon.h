@@ -116,9 +116,11 @@ typedef struct muon_plan_info {
   uint64_t plan_hash;         /* FNV-1a of the canonical serialization */
 } muon_plan_info;
 
-/* Per-kernel timing collected while profiling is on (see muon_plan_set_profiling). */
+/* Per-kernel timing collected while profiling is on (see muon_plan_set_profiling):
+ * one entry per (stage, kernel) pair. */
 typedef struct muon_kernel_time {
-  char name[32];        /* kernel kind, e.g. "ns_apply", "ew_momentum" */
+  char name[32];        /* stage, e.g. "ns_apply", "ew_momentum" */
+  char kernel[32];      /* kernel instance, e.g. "k_nt<256,256,bf16>" */
   int64_t launches;     /* launches timed */
   double total_ms;      /* summed hipEvent time of those launches */
   double flops;         /* summed algorithmic flops of those launches (0 for elementwise) */
@@ -204,8 +206,9 @@ int muon_plan_matrix_choice(const muon_plan* plan, int i, int32_t* form, int32_t
 /*
  * Profiling: while enabled, muon_step records a hipEvent pair around each
  * kernel launch on the step's stream.  muon_plan_get_kernel_times synchronizes,
- * folds the recorded pairs into per-kind totals and writes up to max entries to
- * out (host array), the count to *n_out.  reset != 0 clears the totals after.
+ * folds the recorded pairs into per-(stage, kernel) totals, sorted by stage then
+ * kernel name, and writes up to max entries to out (host array), the count to
+ * *n_out.  reset != 0 clears the totals after.
  */
 int muon_plan_set_profiling(muon_plan* plan, int enable);
 int muon_plan_get_kernel_times(muon_plan* plan, muon_kernel_time* out, int max, int* n_out,

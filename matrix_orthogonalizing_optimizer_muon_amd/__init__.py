@@ -202,9 +202,10 @@ class MuonPlan:
         L.check(L.lib().muon_plan_set_profiling(self._h, 1 if enable else 0))
 
     def kernel_times(self, reset=True):
-        arr = (L.KernelTime * 32)()
+        arr = (L.KernelTime * 64)()
         n = ctypes.c_int()
-        L.check(L.lib().muon_plan_get_kernel_times(self._h, arr, 32, ctypes.byref(n), 1 if reset else 0))
-        return [{"name": arr[k].name.decode(), "launches": arr[k].launches,
+        L.check(L.lib().muon_plan_get_kernel_times(self._h, arr, 64, ctypes.byref(n), 1 if reset else 0))
+        return [{"name": arr[k].name.decode(), "kernel": arr[k].kernel.decode(),
+                 "launches": arr[k].launches,
                  "total_ms": arr[k].total_ms, "flops": arr[k].flops, "bytes": arr[k].bytes}
                 for k in range(n.value)]

@@ -40,7 +40,8 @@ class PlanInfo(ctypes.Structure):
 
 
 class KernelTime(ctypes.Structure):
-    _fields_ = [("name", ctypes.c_char * 32), ("launches", ctypes.c_int64),
+    _fields_ = [("name", ctypes.c_char * 32), ("kernel", ctypes.c_char * 32),
+                ("launches", ctypes.c_int64),
                 ("total_ms", ctypes.c_double), ("flops", ctypes.c_double),
                 ("bytes", ctypes.c_double)]
 

@@ -74,8 +74,22 @@ struct ChunkDev {
   std::vector<SetDev> sets;
 };
 
+// Kernel symbol labels for the profiling records (one per template instance).
+const char* nt_name(int cfg, int odt) {
+  static const char* names[kNumNtCfgs][2] = {
+      {"k_nt<128,128,f32>", "k_nt<128,128,bf16>"}, {"k_nt<256,256,f32>", "k_nt<256,256,bf16>"},
+      {"k_nt<256,128,f32>", "k_nt<256,128,bf16>"}, {"k_nt<128,256,f32>", "k_nt<128,256,bf16>"}};
+  return names[cfg][odt == kBF16 ? 1 : 0];
+}
+const char* rs_name(bool nn, int idt, int odt) {
+  if (idt == kF32) return nn ? "k_gemm<f32,f32,NN>" : "k_gemm<f32,f32,NT>";
+  if (odt == kF32) return nn ? "k_gemm<bf16,f32,NN>" : "k_gemm<bf16,f32,NT>";
+  return nn ? "k_gemm<bf16,bf16,NN>" : "k_gemm<bf16,bf16,NT>";
+}
+
 struct ProfRec {
   int kind;
+  const char* kern;
   double flops, bytes;
   hipEvent_t a, b;
 };
@@ -103,7 +117,7 @@ struct muon_plan {
   bool profiling = false;
   std::vector<ProfRec> recs;
   std::vector<hipEvent_t> ev_pool;
-  Totals tot[kKinds];
+  std::map<std::pair<int, std::string>, Totals> tot;   // (stage, kernel) -> totals
 };
 
 namespace {
@@ -265,7 +279,8 @@ hipEvent_t pool_event(muon_plan* p) {
 }
 
 template <typename F>
-int run(muon_plan* p, int kind, double flops, double bytes, hipStream_t s, F&& launch) {
+int run(muon_plan* p, int kind, const char* kern, double flops, double bytes, hipStream_t s,
+        F&& launch) {
   hipEvent_t a = nullptr, b = nullptr;
   if (p->profiling) {
     a = pool_event(p);
@@ -278,7 +293,7 @@ int run(muon_plan* p, int kind, double flops, double bytes, hipStream_t s, F&& l
     return fail(MUON_EHIP, std::string(kKindNames[kind]) + " launch: " + hipGetErrorString(e));
   if (p->profiling) {
     HIP_TRY(hipEventRecord(b, s));
-    p->recs.push_back({kind, flops, bytes, a, b});
+    p->recs.push_back({kind, kern, flops, bytes, a, b});
   }
   return MUON_OK;
 }
@@ -332,19 +347,19 @@ int enqueue_ns(muon_plan* p, const SetDev& S, int T, const float* sched, hipStre
         const int dstT = last ? -1 : (even ? kX1T : kX0T);
         GemmParams g1 = gp(S, S.nt_sym, true, kShapeGram, src, src, -1, kA, -1, -1, 1.f, 0.f, 0.f,
                            k == 0 ? 2 : 0, rs);
-        if ((rc = run(p, kNsSyrk, S.fl_gram, 0, s, [&] { return launch_gemm_nt(tp.sym, kBF16, g1, s); }))) return rc;
+        if ((rc = run(p, kNsSyrk, nt_name(tp.sym, kBF16), S.fl_gram, 0, s, [&] { return launch_gemm_nt(tp.sym, kBF16, g1, s); }))) return rc;
         GemmParams g2 = gp(S, S.nt_sym, true, kShapeSquare, kA, kA, kA, kB, -1, -1, c, b, 0.f, 0, rs);
-        if ((rc = run(p, kNsComb, S.fl_square, 0, s, [&] { return launch_gemm_nt(tp.sym, kBF16, g2, s); }))) return rc;
+        if ((rc = run(p, kNsComb, nt_name(tp.sym, kBF16), S.fl_square, 0, s, [&] { return launch_gemm_nt(tp.sym, kBF16, g2, s); }))) return rc;
         GemmParams g3 = gp(S, S.nt_full, false, kShapeApplyT, kB, srcT, src, dst, -1, dstT, 1.f, a, 0.f,
                            k == 0 ? 1 : 0, rs);
         const int odt = last ? kF32 : kBF16;
-        if ((rc = run(p, kNsApply, S.fl_apply, 0, s, [&] { return launch_gemm_nt(tp.apply, odt, g3, s); }))) return rc;
+        if ((rc = run(p, kNsApply, nt_name(tp.apply, odt), S.fl_apply, 0, s, [&] { return launch_gemm_nt(tp.apply, odt, g3, s); }))) return rc;
       }
       return MUON_OK;
     }
     // Gram space
     GemmParams g0 = gp(S, S.nt_sym, true, kShapeGram, kX0, kX0, -1, kA, -1, -1, 1.f, 0.f, 0.f, 2, rs);
-    if ((rc = run(p, kGramXxt, S.fl_gram, 0, s, [&] { return launch_gemm_nt(tp.sym, kF32, g0, s); }))) return rc;
+    if ((rc = run(p, kGramXxt, nt_name(tp.sym, kF32), S.fl_gram, 0, s, [&] { return launch_gemm_nt(tp.sym, kF32, g0, s); }))) return rc;
     int cur = kQX;
     for (int k = 0; k < T; ++k) {
       const float a = sched[3 * k], b = sched[3 * k + 1], c = sched[3 * k + 2];
@@ -353,23 +368,23 @@ int enqueue_ns(muon_plan* p, const SetDev& S, int T, const float* sched, hipStre
       // H = a I + b A + c A^2 (at k = 0 this is Q_1 itself)
       GemmParams gh = gp(S, S.old_sym, true, kShapeSquare, kA, kA, kA, hbuf, (k == 0 && last) ? kQH : -1,
                          -1, c, b, a, 0, rs);
-      if ((rc = run(p, kGramSquare, S.fl_square, 0, s, [&] { return launch_gemm(0, kF32, kF32, gh, s); }))) return rc;
+      if ((rc = run(p, kGramSquare, rs_name(false, kF32, kF32), S.fl_square, 0, s, [&] { return launch_gemm(0, kF32, kF32, gh, s); }))) return rc;
       if (k > 0) {
         const int nxt = cur == kQX ? kQY : kQX;
         GemmParams gq = gp(S, S.old_sym, true, kShapeSquare, kH, cur, -1, nxt, last ? kQH : -1, -1, 1.f,
                            0.f, 0.f, 0, rs);
-        if ((rc = run(p, kGramSquare, S.fl_square, 0, s, [&] { return launch_gemm(0, kF32, kF32, gq, s); }))) return rc;
+        if ((rc = run(p, kGramSquare, rs_name(false, kF32, kF32), S.fl_square, 0, s, [&] { return launch_gemm(0, kF32, kF32, gq, s); }))) return rc;
         cur = nxt;
       }
       if (!last) {
         GemmParams gt = gp(S, S.old_sym, true, kShapeSquare, hbuf, kA, -1, kT1, -1, -1, 1.f, 0.f, 0.f, 0, rs);
-        if ((rc = run(p, kGramSquare, S.fl_square, 0, s, [&] { return launch_gemm(0, kF32, kF32, gt, s); }))) return rc;
+        if ((rc = run(p, kGramSquare, rs_name(false, kF32, kF32), S.fl_square, 0, s, [&] { return launch_gemm(0, kF32, kF32, gt, s); }))) return rc;
         GemmParams ga = gp(S, S.old_sym, true, kShapeSquare, kT1, hbuf, -1, kA, -1, -1, 1.f, 0.f, 0.f, 0, rs);
-        if ((rc = run(p, kGramSquare, S.fl_square, 0, s, [&] { return launch_gemm(0, kF32, kF32, ga, s); }))) return rc;
+        if ((rc = run(p, kGramSquare, rs_name(false, kF32, kF32), S.fl_square, 0, s, [&] { return launch_gemm(0, kF32, kF32, ga, s); }))) return rc;
       }
     }
     GemmParams gf = gp(S, S.nt_full, false, kShapeApplyT, kQH, kX0T, -1, kXT, -1, -1, 1.f, 0.f, 0.f, 1, rs);
-    if ((rc = run(p, kGramFinal, S.fl_apply, 0, s, [&] { return launch_gemm_nt(tp.apply, kF32, gf, s); }))) return rc;
+    if ((rc = run(p, kGramFinal, nt_name(tp.apply, kF32), S.fl_apply, 0, s, [&] { return launch_gemm_nt(tp.apply, kF32, gf, s); }))) return rc;
     return MUON_OK;
   }
   // fp32 path
@@ -379,38 +394,38 @@ int enqueue_ns(muon_plan* p, const SetDev& S, int T, const float* sched, hipStre
       const int src = (k % 2 == 0) ? kX0 : kX1;
       const int dst = (k == T - 1) ? kXT : (src == kX0 ? kX1 : kX0);
       GemmParams g1 = gp(S, S.old_sym, true, kShapeGram, src, src, -1, kA, -1, -1, 1.f, 0.f, 0.f, k == 0 ? 2 : 0, rs);
-      if ((rc = run(p, kNsSyrk, S.fl_gram, 0, s, [&] { return launch_gemm(0, kF32, kF32, g1, s); }))) return rc;
+      if ((rc = run(p, kNsSyrk, rs_name(false, kF32, kF32), S.fl_gram, 0, s, [&] { return launch_gemm(0, kF32, kF32, g1, s); }))) return rc;
       GemmParams g2 = gp(S, S.old_sym, true, kShapeSquare, kA, kA, kA, kB, -1, -1, c, b, 0.f, 0, rs);
-      if ((rc = run(p, kNsComb, S.fl_square, 0, s, [&] { return launch_gemm(0, kF32, kF32, g2, s); }))) return rc;
+      if ((rc = run(p, kNsComb, rs_name(false, kF32, kF32), S.fl_square, 0, s, [&] { return launch_gemm(0, kF32, kF32, g2, s); }))) return rc;
       GemmParams g3 = gp(S, S.old_full, false, kShapeApply, kB, src, src, dst, -1, -1, 1.f, a, 0.f, k == 0 ? 1 : 0, rs);
-      if ((rc = run(p, kNsApply, S.fl_apply, 0, s, [&] { return launch_gemm(0, kF32, kF32, g3, s); }))) return rc;
+      if ((rc = run(p, kNsApply, rs_name(true, kF32, kF32), S.fl_apply, 0, s, [&] { return launch_gemm(0, kF32, kF32, g3, s); }))) return rc;
     }
     return MUON_OK;
   }
   GemmParams g0 = gp(S, S.old_sym, true, kShapeGram, kX0, kX0, -1, kA, -1, -1, 1.f, 0.f, 0.f, 2, rs);
-  if ((rc = run(p, kGramXxt, S.fl_gram, 0, s, [&] { return launch_gemm(0, kF32, kF32, g0, s); }))) return rc;
+  if ((rc = run(p, kGramXxt, rs_name(false, kF32, kF32), S.fl_gram, 0, s, [&] { return launch_gemm(0, kF32, kF32, g0, s); }))) return rc;
   int cur = kQX;
   for (int k = 0; k < T; ++k) {
     const float a = sched[3 * k], b = sched[3 * k + 1], c = sched[3 * k + 2];
     const bool last = k == T - 1;
     const int hbuf = (k == 0) ? kQX : kH;
     GemmParams gh = gp(S, S.old_sym, true, kShapeSquare, kA, kA, kA, hbuf, -1, -1, c, b, a, 0, rs);
-    if ((rc = run(p, kGramSquare, S.fl_square, 0, s, [&] { return launch_gemm(0, kF32, kF32, gh, s); }))) return rc;
+    if ((rc = run(p, kGramSquare, rs_name(false, kF32, kF32), S.fl_square, 0, s, [&] { return launch_gemm(0, kF32, kF32, gh, s); }))) return rc;
     if (k > 0) {
       const int nxt = cur == kQX ? kQY : kQX;
       GemmParams gq = gp(S, S.old_sym, true, kShapeSquare, kH, cur, -1, nxt, -1, -1, 1.f, 0.f, 0.f, 0, rs);
-      if ((rc = run(p, kGramSquare, S.fl_square, 0, s, [&] { return launch_gemm(0, kF32, kF32, gq, s); }))) return rc;
+      if ((rc = run(p, kGramSquare, rs_name(false, kF32, kF32), S.fl_square, 0, s, [&] { return launch_gemm(0, kF32, kF32, gq, s); }))) return rc;
       cur = nxt;
     }
     if (!last) {
       GemmParams gt = gp(S, S.old_sym, true, kShapeSquare, hbuf, kA, -1, kT1, -1, -1, 1.f, 0.f, 0.f, 0, rs);
-      if ((rc = run(p, kGramSquare, S.fl_square, 0, s, [&] { return launch_gemm(0, kF32, kF32, gt, s); }))) return rc;
+      if ((rc = run(p, kGramSquare, rs_name(false, kF32, kF32), S.fl_square, 0, s, [&] { return launch_gemm(0, kF32, kF32, gt, s); }))) return rc;
       GemmParams ga = gp(S, S.old_sym, true, kShapeSquare, kT1, hbuf, -1, kA, -1, -1, 1.f, 0.f, 0.f, 0, rs);
-      if ((rc = run(p, kGramSquare, S.fl_square, 0, s, [&] { return launch_gemm(0, kF32, kF32, ga, s); }))) return rc;
+      if ((rc = run(p, kGramSquare, rs_name(false, kF32, kF32), S.fl_square, 0, s, [&] { return launch_gemm(0, kF32, kF32, ga, s); }))) return rc;
     }
   }
   GemmParams gf = gp(S, S.old_full, false, kShapeApply, cur, kX0, -1, kXT, -1, -1, 1.f, 0.f, 0.f, 1, rs);
-  if ((rc = run(p, kGramFinal, S.fl_apply, 0, s, [&] { return launch_gemm(0, kF32, kF32, gf, s); }))) return rc;
+  if ((rc = run(p, kGramFinal, rs_name(true, kF32, kF32), S.fl_apply, 0, s, [&] { return launch_gemm(0, kF32, kF32, gf, s); }))) return rc;
   return MUON_OK;
 }
 
@@ -461,16 +476,16 @@ int step_impl(muon_plan* p, void* const* params, const void* const* grads, float
   for (ChunkDev& C : p->chunks) {
     if ((rc = upload_dyn(p, C, params, grads, momenta, s))) return rc;
     const int nm = (int)C.mats.size();
-    if ((rc = run(p, kEwMom, 0, C.bytes_mom, s, [&] {
+    if ((rc = run(p, kEwMom, "k_ew_momentum", 0, C.bytes_mom, s, [&] {
            return launch_ew_momentum(C.ew, C.dyn, C.prefix, nm, C.total_tiles, C.partials, beta,
                                      p->host.opts.nesterov, p->grid_cap, s);
          }))) return rc;
-    if ((rc = run(p, kNorm, 0, 0, s, [&] {
+    if ((rc = run(p, kNorm, "k_norm", 0, 0, s, [&] {
            return launch_norm(C.ew, nm, C.partials, p->rscale, p->flags, p->host.opts.eps, s);
          }))) return rc;
     for (const SetDev& S : C.sets)
       if ((rc = enqueue_ns(p, S, T, sched, s))) return rc;
-    if ((rc = run(p, kEwApply, 0, C.bytes_apply, s, [&] {
+    if ((rc = run(p, kEwApply, "k_ew_apply", 0, C.bytes_apply, s, [&] {
            return launch_ew_apply(C.ew, C.dyn, C.prefix, nm, C.total_tiles, p->rscale, lr, wd,
                                   T == 0 ? 1 : 0, p->grid_cap, s);
          }))) return rc;
@@ -788,7 +803,7 @@ int muon_plan_get_kernel_times(muon_plan* p, muon_kernel_time* out, int max, int
     HIP_TRY(hipEventSynchronize(r.b));
     float ms = 0;
     HIP_TRY(hipEventElapsedTime(&ms, r.a, r.b));
-    Totals& t = p->tot[r.kind];
+    Totals& t = p->tot[{r.kind, std::string(r.kern)}];
     t.launches++;
     t.ms += ms;
     t.flops += r.flops;
@@ -798,22 +813,22 @@ int muon_plan_get_kernel_times(muon_plan* p, muon_kernel_time* out, int max, int
   }
   p->recs.clear();
   int k = 0;
-  for (int i = 0; i < kKinds; ++i) {
-    if (p->tot[i].launches == 0) continue;
+  for (const auto& kv : p->tot) {
+    if (kv.second.launches == 0) continue;
     if (k < max) {
       muon_kernel_time& o = out[k];
       std::memset(&o, 0, sizeof o);
-      std::strncpy(o.name, kKindNames[i], sizeof(o.name) - 1);
-      o.launches = p->tot[i].launches;
-      o.total_ms = p->tot[i].ms;
-      o.flops = p->tot[i].flops;
-      o.bytes = p->tot[i].bytes;
+      std::strncpy(o.name, kKindNames[kv.first.first], sizeof(o.name) - 1);
+      std::strncpy(o.kernel, kv.first.second.c_str(), sizeof(o.kernel) - 1);
+      o.launches = kv.second.launches;
+      o.total_ms = kv.second.ms;
+      o.flops = kv.second.flops;
+      o.bytes = kv.second.bytes;
     }
     ++k;
   }
   *n_out = std::min(k, std::max(max, 0));
-  if (reset)
-    for (int i = 0; i < kKinds; ++i) p->tot[i] = Totals();
+  if (reset) p->tot.clear();
   return MUON_OK;
 }
 

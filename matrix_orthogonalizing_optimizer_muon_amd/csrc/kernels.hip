@@ -574,6 +574,128 @@ __device__ __forceinline__ void st_bf16x4(void* base, int64_t off, const float* 
       u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
 }
 
+// Rows of the output tile staged in LDS at a time: the largest power of two
+// whose fp32 slab (row pitch BN + 4 floats) fits the mainloop's LDS.
+template <int BM, int BN>
+constexpr int slab_rows() {
+  int sh = BM;
+  while (sh > 8 && sh * (BN + 4) * 4 > nt::Geom<BM, BN, 64, 2>::LDS) sh /= 2;
+  return sh;
+}
+
+__device__ __forceinline__ void ld8_bf16(const void* base, int64_t off, float* v) {
+  const u32x4_t q = *(GLOBAL_AS const u32x4_t*)(static_cast<const uint16_t*>(base) + off);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    v[2 * e] = bf16_to_f32(q[e] & 0xffffu);
+    v[2 * e + 1] = bf16_to_f32(q[e] >> 16);
+  }
+}
+
+template <typename TO>
+__device__ __forceinline__ void st8(void* base, int64_t off, const float* v) {
+  if constexpr (sizeof(TO) == 2) {
+    *(GLOBAL_AS u32x4_t*)(static_cast<uint16_t*>(base) + off) =
+        u32x4_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                pack_bf16x2(v[6], v[7])};
+  } else {
+    typedef float f32x4_t __attribute__((ext_vector_type(4)));
+    GLOBAL_AS f32x4_t* d = (GLOBAL_AS f32x4_t*)(static_cast<float*>(base) + off);
+    d[0] = f32x4_t{v[0], v[1], v[2], v[3]};
+    d[1] = f32x4_t{v[4], v[5], v[6], v[7]};
+  }
+}
+
+// Epilogue of the NT kernel through LDS, in slabs of SH rows:
+//  1. each wave writes its accumulators of the slab's rows into an fp32 tile;
+//  2. row pass: every thread takes 8 consecutive columns of a row, applies
+//     out = s (alpha acc + beta Cin) + gamma [i == j] (0 outside the real
+//     extents) and stores 16-byte runs of the output (Cin read the same way);
+//  3. column pass (transposed copy or mirrored tile only): every thread takes 8
+//     consecutive rows of one column and stores them as a 16-byte run.
+template <int BM, int BN, typename TO>
+__device__ __forceinline__ void nt_epilogue(const nt::f32x16_t (&acc)[BM / 64][BN / 64],
+                                            MUON_LDS float* C, const GemmParams& p,
+                                            const NsMat* nmp, int m0, int n0, int ldo, int Mr,
+                                            int Nr) {
+  using G = nt::Geom<BM, BN, 64, 2>;
+  constexpr int SH = slab_rows<BM, BN>();
+  constexpr int PITCH = BN + 4;
+  constexpr int TPR = BN / 8, RPP = 256 / TPR;
+  static_assert(SH % 8 == 0 && SH * PITCH * 4 <= G::LDS && 256 % TPR == 0, "slab");
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wy = w >> 1, wx = w & 1;
+  float sc = 1.0f;
+  if (p.scale_pow) {
+    const float rr = p.rscale[nmp->mat];
+    sc = p.scale_pow == 2 ? rr * rr : rr;
+  }
+  const float alpha = p.alpha, beta = p.beta, gamma = p.gamma;
+  void* Out = nmp->buf[p.o_id];
+  void* OutT = p.ot_id >= 0 ? nmp->buf[p.ot_id] : nullptr;
+  const void* Cin = p.c_id >= 0 ? nmp->buf[p.c_id] : nullptr;
+  const WorkItem it = p.items[blockIdx.x];
+  const bool mirror = p.sym && it.tm != it.tn;
+  const bool colpass = mirror || OutT != nullptr;
+  const int m_pad = nmp->m_pad;
+  __syncthreads();   // every wave is done with the main loop's LDS
+#pragma unroll 1
+  for (int s0 = 0; s0 < BM; s0 += SH) {
+#pragma unroll
+    for (int a = 0; a < G::MT; ++a)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int rbase = wy * G::WM + a * 32 + rg * 8;   // 8-row group, uniform per wave
+        if (rbase < s0 || rbase >= s0 + SH) continue;
+        const int r = rbase - s0 + (lane >> 5) * 4;
+#pragma unroll
+        for (int b = 0; b < G::NT; ++b) {
+          const int c = wx * G::WN + b * 32 + (lane & 31);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) C[(r + q) * PITCH + c] = acc[a][b][rg * 4 + q];
+        }
+      }
+    __syncthreads();
+#pragma unroll 1
+    for (int r = tid / TPR; r < SH; r += RPP) {
+      const int c = (tid % TPR) * 8;
+      const int i = m0 + s0 + r, j = n0 + c;
+      float v[8], cin[8];
+      MUON_LDS float* src = C + r * PITCH + c;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = src[e];
+      if (Cin) ld8_bf16(Cin, (int64_t)i * ldo + j, cin);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float x = alpha * v[e];
+        if (Cin) x += beta * cin[e];
+        x *= sc;
+        if (i == j + e) x += gamma;
+        if (i >= Mr || j + e >= Nr) x = 0.f;
+        v[e] = x;
+      }
+      st8<TO>(Out, (int64_t)i * ldo + j, v);
+      if (colpass) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) src[e] = v[e];
+      }
+    }
+    if (colpass) {
+      __syncthreads();
+#pragma unroll 1
+      for (int wi = tid; wi < BN * (SH / 8); wi += 256) {
+        const int jc = wi % BN, r0 = (wi / BN) * 8;
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = C[(r0 + e) * PITCH + jc];
+        const int j = n0 + jc, i0 = m0 + s0 + r0;
+        if (OutT) st8<uint16_t>(OutT, (int64_t)j * m_pad + i0, v);
+        if (mirror) st8<TO>(Out, (int64_t)j * ldo + i0, v);
+      }
+    }
+    __syncthreads();   // the slab buffer is reused
+  }
+}
+
 template <int BM, int BN, typename TO>
 __global__ __launch_bounds__(256) void k_nt(const GemmParams p) {
   extern __shared__ __attribute__((aligned(1024))) char nt_smem[];
@@ -599,43 +721,7 @@ __global__ __launch_bounds__(256) void k_nt(const GemmParams p) {
   nt::mainloop<BM, BN, 64, 2>(acc, (MUON_LDS char*)nt_smem, Pr, Qr, (uint32_t)ldp, (uint32_t)ldq,
                               (uint32_t)m0, (uint32_t)n0, K);
 
-  // ---- epilogue
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wy = w >> 1, wx = w & 1;
-  float s = 1.0f;
-  if (p.scale_pow) {
-    const float rr = p.rscale[nmp->mat];
-    s = p.scale_pow == 2 ? rr * rr : rr;
-  }
-  const float alpha = p.alpha, beta = p.beta, gamma = p.gamma;
-  void* Out = nmp->buf[p.o_id];
-  void* OutT = p.ot_id >= 0 ? nmp->buf[p.ot_id] : nullptr;
-  const void* Cin = p.c_id >= 0 ? nmp->buf[p.c_id] : nullptr;
-  const bool mirror = p.sym && it.tm != it.tn;
-#pragma unroll
-  for (int a = 0; a < G::MT; ++a) {
-#pragma unroll
-    for (int b = 0; b < G::NT; ++b) {
-      const int j = n0 + wx * G::WN + b * 32 + (lane & 31);
-#pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const int ib = m0 + wy * G::WM + a * 32 + rg * 8 + (lane >> 5) * 4;
-        float v[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int i = ib + q;
-          float x = alpha * acc[a][b][rg * 4 + q];
-          if (Cin) x += beta * ld_elem<uint16_t>(Cin, (int64_t)i * ldo + j);
-          x *= s;
-          if (i == j) x += gamma;
-          if (i >= Mr || j >= Nr) x = 0.f;
-          v[q] = x;
-          st_elem<TO>(Out, (int64_t)i * ldo + j, x);
-        }
-        if (mirror) st_elem4<TO>(Out, (int64_t)j * ldo + ib, v);
-        if (OutT) st_bf16x4(OutT, (int64_t)j * m_pad + ib, v);
-      }
-    }
-  }
+  nt_epilogue<BM, BN, TO>(acc, (MUON_LDS float*)nt_smem, p, nmp, m0, n0, ldo, Mr, Nr);
 }
 
 template <int BM, int BN, typename TO>

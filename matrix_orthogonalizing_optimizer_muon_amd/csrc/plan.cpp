@@ -69,16 +69,26 @@ void remap_xcd(std::vector<ItemHost>& v) {
   v.swap(out);
 }
 
+// Tiles of one product in super-tile order: 4 x 8 blocks of output tiles are
+// consecutive, so the 32 work items an XCD runs side by side (remap_xcd hands
+// each XCD a contiguous run) share 4 row panels and 8 column panels in its L2.
+constexpr int kSuperM = 4, kSuperN = 8;
+
+void add_tiles(std::vector<ItemHost>& v, int32_t slot, int32_t ntm, int32_t ntn, bool upper) {
+  for (int32_t sm = 0; sm < ntm; sm += kSuperM)
+    for (int32_t sn = 0; sn < ntn; sn += kSuperN)
+      for (int32_t a = sm; a < std::min(sm + kSuperM, ntm); ++a)
+        for (int32_t b = sn; b < std::min(sn + kSuperN, ntn); ++b)
+          if (!upper || b >= a) v.push_back({slot, a, b});
+}
+
 void add_sym(std::vector<ItemHost>& v, int32_t slot, int64_t m_pad, int edge) {
   const int32_t nt = (int32_t)(m_pad / edge);
-  for (int32_t a = 0; a < nt; ++a)
-    for (int32_t b = a; b < nt; ++b) v.push_back({slot, a, b});
+  add_tiles(v, slot, nt, nt, true);
 }
 
 void add_full(std::vector<ItemHost>& v, int32_t slot, int64_t m_pad, int64_t n_pad, TileShape t) {
-  const int32_t ntm = (int32_t)(m_pad / t.bm), ntn = (int32_t)(n_pad / t.bn);
-  for (int32_t a = 0; a < ntm; ++a)
-    for (int32_t b = 0; b < ntn; ++b) v.push_back({slot, a, b});
+  add_tiles(v, slot, (int32_t)(m_pad / t.bm), (int32_t)(n_pad / t.bn), false);
 }
 
 double sym_tiles(int64_t m_pad, int edge) {
