@@ -34,6 +34,12 @@ def parse():
     ap.add_argument("--tune", default="once", choices=["off", "once", "force"])
     ap.add_argument("--form", default="auto", choices=["auto", "direct", "gram"])
     ap.add_argument("--tile", type=int, default=None, help="force a tile plan (0..4)")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="run 2 steps and a 1 GiB device copy (for rocprofv3 --pmc passes), print nothing")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two rocprofv3 --pmc output dirs (FETCH_SIZE, WRITE_SIZE passes over "
+                         "--traffic-probe) into profiles/traffic.json for the workload's dominant kernel")
+    ap.add_argument("--kernel", default=None, help="kernel instance for --traffic-from, e.g. k_nt<128,128,bf16>")
     ap.add_argument("--cache", default=os.path.join(os.path.expanduser("~"), ".cache", "muon_mi355x",
                                                     "tune.txt"))
     ap.add_argument("--no-kernel-times", action="store_true")
@@ -70,6 +76,63 @@ def traffic_for(kernel, workload, launches_per_step):
                     "bytes": r["fetch_bytes_per_launch"] + r["write_bytes_per_launch"],
                     "copy_factor": r.get("copy_factor"), "source": digest}
     return None
+
+
+COPY_BYTES = 1 << 30   # bytes read and written by the calibration copy
+
+
+def demangled(label):
+    """rocprofv3's name of a kernel instance label such as k_nt<128,128,bf16>."""
+    base, _, args = label.partition("<")
+    args = args.rstrip(">").split(",") if args else []
+    conv = {"bf16": "unsigned short", "f32": "float"}
+    if base == "k_nt":
+        return f"k_nt<{args[0]}, {args[1]}, {conv[args[2]]}>"
+    return base
+
+
+def counter_rows(dirpath, counter):
+    import csv
+    import glob
+    out = []
+    for path in glob.glob(os.path.join(dirpath, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] == counter:
+                    out.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    return out
+
+
+def write_traffic(args, wl):
+    """Per-launch HBM bytes of one kernel from FETCH_SIZE / WRITE_SIZE (KiB per
+    dispatch), each scaled so that the calibration copy reads as COPY_BYTES."""
+    import statistics
+    name = demangled(args.kernel)
+    entry = {"kernel": args.kernel, "workload": wl.name, "source": source_digest()}
+    for key, d, counter in (("fetch", args.traffic_from[0], "FETCH_SIZE"),
+                            ("write", args.traffic_from[1], "WRITE_SIZE")):
+        rows = counter_rows(d, counter)
+        kern = [v for n, v in rows if name in n]
+        copy = [v for n, v in rows if "elementwise_kernel" in n]
+        copy = [v for v in copy if v * 1024 > COPY_BYTES / 2]
+        if not kern or not copy:
+            raise SystemExit(f"{counter}: no rows for {name} or for the calibration copy in {d}")
+        factor = COPY_BYTES / (statistics.median(copy) * 1024)
+        entry[f"{key}_bytes_per_launch"] = statistics.mean(kern) * 1024 * factor
+        entry[f"{key}_copy_factor"] = factor
+        entry[f"{key}_dispatches"] = len(kern)
+    entry["copy_factor"] = [entry["fetch_copy_factor"], entry["write_copy_factor"]]
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    rec = {"entries": []}
+    if os.path.exists(path):
+        with open(path) as fh:
+            rec = json.load(fh)
+    rec["entries"] = [e for e in rec["entries"]
+                      if not (e["kernel"] == entry["kernel"] and e["workload"] == entry["workload"])]
+    rec["entries"].append(entry)
+    with open(path, "w") as fh:
+        json.dump(rec, fh, indent=1, sort_keys=True)
+    print(json.dumps(entry))
 
 
 def make_inputs(wl, torch):
@@ -130,11 +193,14 @@ def main():
         print(json.dumps({"error": "this build runs on one GPU only; multi-GPU runs are not "
                                    "supported (matrices would be sharded whole across owners)"}))
         sys.exit(2)
-    import torch
     import workloads as WL
+    wl = WL.workload(args.config)
+    if args.traffic_from:
+        write_traffic(args, wl)
+        return
+    import torch
     import matrix_orthogonalizing_optimizer_muon_amd as MU
 
-    wl = WL.workload(args.config)
     torch.cuda.init()
     os.makedirs(os.path.dirname(args.cache), exist_ok=True)
     t0 = time.perf_counter()
@@ -156,6 +222,17 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    if args.traffic_probe:
+        for _ in range(2):
+            step()
+        torch.cuda.synchronize()
+        src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)   # one plain read and one plain write of COPY_BYTES
+        torch.cuda.synchronize()
+        plan.close()
+        return
     print(f"# warmup done ({args.warmup} steps), timing {args.steps}", file=sys.stderr, flush=True)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     per = []
