@@ -576,10 +576,10 @@ __device__ __forceinline__ void st_bf16x4(void* base, int64_t off, const float* 
 
 // Rows of the output tile staged in LDS at a time: the largest power of two
 // whose fp32 slab (row pitch BN + 4 floats) fits the mainloop's LDS.
-template <int BM, int BN>
+template <int BM, int BN, int WGM, int WGN>
 constexpr int slab_rows() {
   int sh = BM;
-  while (sh > 8 && sh * (BN + 4) * 4 > nt::Geom<BM, BN, 64, 2>::LDS) sh /= 2;
+  while (sh > 8 && sh * (BN + 4) * 4 > nt::Geom<BM, BN, 64, 2, WGM, WGN>::LDS) sh /= 2;
   return sh;
 }
 
@@ -613,17 +613,18 @@ __device__ __forceinline__ void st8(void* base, int64_t off, const float* v) {
 //     extents) and stores 16-byte runs of the output (Cin read the same way);
 //  3. column pass (transposed copy or mirrored tile only): every thread takes 8
 //     consecutive rows of one column and stores them as a 16-byte run.
-template <int BM, int BN, typename TO>
-__device__ __forceinline__ void nt_epilogue(const nt::f32x16_t (&acc)[BM / 64][BN / 64],
+template <int BM, int BN, int WGM, int WGN, typename TO>
+__device__ __forceinline__ void nt_epilogue(const nt::f32x16_t (&acc)[BM / 32 / WGM][BN / 32 / WGN],
                                             MUON_LDS float* C, const GemmParams& p,
                                             const NsMat* nmp, int m0, int n0, int ldo, int Mr,
                                             int Nr) {
-  using G = nt::Geom<BM, BN, 64, 2>;
-  constexpr int SH = slab_rows<BM, BN>();
+  using G = nt::Geom<BM, BN, 64, 2, WGM, WGN>;
+  constexpr int NT = G::THREADS;
+  constexpr int SH = slab_rows<BM, BN, WGM, WGN>();
   constexpr int PITCH = BN + 4;
-  constexpr int TPR = BN / 8, RPP = 256 / TPR;
-  static_assert(SH % 8 == 0 && SH * PITCH * 4 <= G::LDS && 256 % TPR == 0, "slab");
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wy = w >> 1, wx = w & 1;
+  constexpr int TPR = BN / 8, RPP = NT / TPR;
+  static_assert(SH % 8 == 0 && SH * PITCH * 4 <= G::LDS && NT % TPR == 0, "slab");
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wy = w / WGN, wx = w % WGN;
   float sc = 1.0f;
   if (p.scale_pow) {
     const float rr = p.rscale[nmp->mat];
@@ -682,7 +683,7 @@ __device__ __forceinline__ void nt_epilogue(const nt::f32x16_t (&acc)[BM / 64][B
     if (colpass) {
       __syncthreads();
 #pragma unroll 1
-      for (int wi = tid; wi < BN * (SH / 8); wi += 256) {
+      for (int wi = tid; wi < BN * (SH / 8); wi += NT) {
         const int jc = wi % BN, r0 = (wi / BN) * 8;
         float v[8];
 #pragma unroll
@@ -696,10 +697,10 @@ __device__ __forceinline__ void nt_epilogue(const nt::f32x16_t (&acc)[BM / 64][B
   }
 }
 
-template <int BM, int BN, typename TO>
-__global__ __launch_bounds__(256) void k_nt(const GemmParams p) {
+template <int BM, int BN, int WGM, int WGN, typename TO>
+__global__ __launch_bounds__(64 * WGM * WGN) void k_nt(const GemmParams p) {
   extern __shared__ __attribute__((aligned(1024))) char nt_smem[];
-  using G = nt::Geom<BM, BN, 64, 2>;
+  using G = nt::Geom<BM, BN, 64, 2, WGM, WGN>;
   const WorkItem it = p.items[blockIdx.x];
   const NsMat* nmp = p.mats + it.slot;
   const int m_pad = nmp->m_pad, n_pad = nmp->n_pad;
@@ -718,17 +719,18 @@ __global__ __launch_bounds__(256) void k_nt(const GemmParams p) {
   const __amdgpu_buffer_rsrc_t Qr = nt::make_rsrc(Qg, q_rows * (uint32_t)ldq * 2u);
   const int m0 = it.tm * BM, n0 = it.tn * BN;
   nt::f32x16_t acc[G::MT][G::NT];
-  nt::mainloop<BM, BN, 64, 2>(acc, (MUON_LDS char*)nt_smem, Pr, Qr, (uint32_t)ldp, (uint32_t)ldq,
-                              (uint32_t)m0, (uint32_t)n0, K);
+  nt::mainloop<BM, BN, 64, 2, WGM, WGN>(acc, (MUON_LDS char*)nt_smem, Pr, Qr, (uint32_t)ldp,
+                                        (uint32_t)ldq, (uint32_t)m0, (uint32_t)n0, K);
 
-  nt_epilogue<BM, BN, TO>(acc, (MUON_LDS float*)nt_smem, p, nmp, m0, n0, ldo, Mr, Nr);
+  nt_epilogue<BM, BN, WGM, WGN, TO>(acc, (MUON_LDS float*)nt_smem, p, nmp, m0, n0, ldo, Mr, Nr);
 }
 
-template <int BM, int BN, typename TO>
+template <int BM, int BN, int WGM, int WGN, typename TO>
 hipError_t launch_nt_t(const GemmParams& p, hipStream_t s) {
-  constexpr int smem = nt::Geom<BM, BN, 64, 2>::LDS;
+  using G = nt::Geom<BM, BN, 64, 2, WGM, WGN>;
+  constexpr int smem = G::LDS;
   static bool attr_done = false;
-  auto kern = &k_nt<BM, BN, TO>;
+  auto kern = &k_nt<BM, BN, WGM, WGN, TO>;
   if (!attr_done) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, smem);
@@ -736,14 +738,14 @@ hipError_t launch_nt_t(const GemmParams& p, hipStream_t s) {
     attr_done = true;
   }
   if (p.n_items <= 0) return hipSuccess;
-  hipLaunchKernelGGL(kern, dim3(p.n_items), dim3(256), smem, s, p);
+  hipLaunchKernelGGL(kern, dim3(p.n_items), dim3(G::THREADS), smem, s, p);
   return hipGetLastError();
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int WGM, int WGN>
 hipError_t launch_nt_cfg(int out_dt, const GemmParams& p, hipStream_t s) {
-  if (out_dt == kBF16) return launch_nt_t<BM, BN, uint16_t>(p, s);
-  if (out_dt == kF32) return launch_nt_t<BM, BN, float>(p, s);
+  if (out_dt == kBF16) return launch_nt_t<BM, BN, WGM, WGN, uint16_t>(p, s);
+  if (out_dt == kF32) return launch_nt_t<BM, BN, WGM, WGN, float>(p, s);
   return hipErrorInvalidValue;
 }
 
@@ -788,10 +790,11 @@ hipError_t launch_gemm_nt(int nt_cfg, int out_dtype, const GemmParams& p, hipStr
   if (p.shape != kShapeGram && p.shape != kShapeSquare && p.shape != kShapeApplyT)
     return hipErrorInvalidValue;
   switch (nt_cfg) {
-    case kNt128: return launch_nt_cfg<128, 128>(out_dtype, p, s);
-    case kNt256: return launch_nt_cfg<256, 256>(out_dtype, p, s);
-    case kNt256x128: return launch_nt_cfg<256, 128>(out_dtype, p, s);
-    case kNt128x256: return launch_nt_cfg<128, 256>(out_dtype, p, s);
+    // 256 x 256 runs 8 waves (2 per SIMD, 128 x 64 each); the others 4 waves
+    case kNt128: return launch_nt_cfg<128, 128, 2, 2>(out_dtype, p, s);
+    case kNt256: return launch_nt_cfg<256, 256, 2, 4>(out_dtype, p, s);
+    case kNt256x128: return launch_nt_cfg<256, 128, 2, 2>(out_dtype, p, s);
+    case kNt128x256: return launch_nt_cfg<128, 256, 2, 2>(out_dtype, p, s);
     default: return hipErrorInvalidValue;
   }
 }

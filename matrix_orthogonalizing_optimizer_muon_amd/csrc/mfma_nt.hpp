@@ -42,24 +42,27 @@ constexpr int waitcnt_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | 0x70 | 0
 static_assert(waitcnt_vm(0) == 0xF70, "encoding");
 constexpr int kWaitVmLgkm0 = 0x0070;   // vmcnt(0) lgkmcnt(0)
 
-// BM x BN output tile, BK bf16 per k-tile (32 or 64), S LDS stages.
-template <int BM, int BN, int BK, int S>
+// BM x BN output tile, BK bf16 per k-tile (32 or 64), S LDS stages, a WGM x WGN
+// grid of waves (each owns a (BM/WGM) x (BN/WGN) tile).
+template <int BM, int BN, int BK, int S, int WGM = 2, int WGN = 2>
 struct Geom {
+  static constexpr int NW = WGM * WGN;                 // waves per block
+  static constexpr int THREADS = 64 * NW;
   static constexpr int ROWB = BK * 2;                  // bytes per LDS row
   static constexpr int CPR = ROWB / 16;                // 16-byte chunks per row
   static constexpr int R256 = 256 / ROWB;              // rows per 256 bytes
   static constexpr int KG = BK / 16;                   // MFMA k-groups per k-tile
-  static constexpr int WM = BM / 2, WN = BN / 2;       // wave tile
+  static constexpr int WM = BM / WGM, WN = BN / WGN;   // wave tile
   static constexpr int MT = WM / 32, NT = WN / 32;     // MFMA tiles per wave
   static constexpr int PB = BM * ROWB, QB = BN * ROWB;
   static constexpr int STAGE = PB + QB;                // bytes per stage
   static constexpr int LDS = S * STAGE;
   static constexpr int RPI = 1024 / ROWB;              // rows per wave copy instruction
-  static constexpr int RPR = 4 * RPI;                  // rows per round of the 4 waves
+  static constexpr int RPR = NW * RPI;                 // rows per round of all waves
   static constexpr int PR = BM / RPR, QR = BN / RPR;   // copy rounds per operand
   static constexpr int NI = PR + QR;                   // copy instructions per wave per tile
   static_assert(BK == 32 || BK == 64, "k-tile");
-  static_assert(BM % 64 == 0 && BN % 64 == 0 && BM % RPR == 0 && BN % RPR == 0, "tile edges");
+  static_assert(WM % 32 == 0 && WN % 32 == 0 && BM % RPR == 0 && BN % RPR == 0, "tile edges");
   static_assert(S >= 2 && LDS <= 160 * 1024, "LDS budget");
   static_assert((S - 1) * NI <= 63, "vmcnt range");
 };
@@ -80,6 +83,7 @@ __device__ __forceinline__ int swz(int r) {
 // the scalar offset takes it back out.
 template <class G, int NR>
 struct Copier {
+  static_assert(NR % 2 == 0 || G::ROWB == 64, "the swizzle phase must follow the copy index");
   __amdgpu_buffer_rsrc_t rsrc;
   uint32_t voff[2];   // per-lane offsets for even / odd copies (swizzle phase)
   uint32_t soff;      // bytes to the wave's first row (row-block origin added per call)
@@ -181,16 +185,16 @@ __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "
 // last group's MFMAs and the reads of group 0 of tile kt+1.  Copies past the
 // last tile re-read the last tile (in bounds, never consumed) so the steady
 // state has no branches and always S-1 tiles in flight.
-template <int BM, int BN, int BK, int S>
-__device__ __forceinline__ void mainloop(f32x16_t (&acc)[BM / 64][BN / 64], MUON_LDS char* lds,
-                                         __amdgpu_buffer_rsrc_t P, __amdgpu_buffer_rsrc_t Q,
-                                         uint32_t ldp, uint32_t ldq, uint32_t m0, uint32_t n0,
-                                         int K) {
-  using G = Geom<BM, BN, BK, S>;
+template <int BM, int BN, int BK, int S, int WGM = 2, int WGN = 2>
+__device__ __forceinline__ void mainloop(
+    f32x16_t (&acc)[BM / 32 / WGM][BN / 32 / WGN],
+    MUON_LDS char* lds, __amdgpu_buffer_rsrc_t P, __amdgpu_buffer_rsrc_t Q, uint32_t ldp,
+    uint32_t ldq, uint32_t m0, uint32_t n0, int K) {
+  using G = Geom<BM, BN, BK, S, WGM, WGN>;
   static_assert(G::KG % 2 == 0, "the last group's fragments are in f1");
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wy = w >> 1, wx = w & 1;
+  const int wy = w / WGN, wx = w % WGN;
 #pragma unroll
   for (int i = 0; i < G::MT; ++i)
 #pragma unroll
