@@ -503,9 +503,12 @@ int time_shape(const ShapeKey& k, const PlanOptions& base, int count,
   double best_us = 0;
   bool have = false;
   for (const auto& cand : cands) {
+    // the shape's real count of matrices (at most 64 and 16 GiB of workspace), so
+    // the timed launches have the real launch's tile count and wave quantization
     const uint64_t per = matrix_ws_bytes(k, cand.first, cand.second);
-    const int by_mem = (int)std::max<uint64_t>(1, (2ull << 30) / std::max<uint64_t>(per, 1));
-    const int batch = std::max(1, std::min({count, 32, by_mem}));
+    const int by_mem = (int)std::max<uint64_t>(1, (16ull << 30) / std::max<uint64_t>(per, 1));
+    const int want = 64;
+    const int batch = std::max(1, std::min({want, count, by_mem}));
     PlanHost H;
     std::map<ShapeKey, ShapeChoice> ch;
     ShapeChoice c;
@@ -661,7 +664,18 @@ int muon_plan_create(const muon_matrix_desc* descs, int n, const muon_plan_opts*
   bool cache_dirty = false;
   for (const auto& kv : counts) {
     const ShapeKey& k = kv.first;
-    const auto cands = candidates(k, po.form, po.tile);
+    // candidates worth timing: within 2x of the cost model's best
+    std::vector<std::pair<int32_t, int32_t>> cands;
+    {
+      const auto all = candidates(k, po.form, po.tile);
+      double best = 0;
+      for (const auto& c : all) {
+        const double us = model_cost_us(k, c.first, c.second, kv.second);
+        best = (best == 0 || us < best) ? us : best;
+      }
+      for (const auto& c : all)
+        if (model_cost_us(k, c.first, c.second, kv.second) <= 2.0 * best) cands.push_back(c);
+    }
     const bool forced = po.form != MUON_FORM_AUTO || (po.tile >= 0 && k.path);
     if (cands.size() == 1) {
       ShapeChoice c;
