@@ -71,6 +71,8 @@ struct ChunkDev {
   float* partials = nullptr;
   int64_t total_tiles = 0;
   double bytes_mom = 0, bytes_apply = 0;
+  bool all_fused = false;     // every matrix's update is applied by its last NS product
+  double bytes_apply_unfused = 0;   // k_ew_apply bytes when fused matrices are skipped
   std::vector<SetDev> sets;
 };
 
@@ -210,6 +212,7 @@ int materialize(muon_plan* p) {
       E.ldt = M.m_pad;
       E.xt = reinterpret_cast<float*>(p->ws + M.off[kXT]);
       E.s = M.s;
+      E.fused = M.path ? 1 : 0;
       prefix[k] = tb;
       tb += M.ew_tiles;
       const double e = (double)M.rows * M.cols, pes = M.dtype ? 2 : 4, es = M.path ? 2 : 4;
@@ -217,6 +220,15 @@ int materialize(muon_plan* p) {
       C.bytes_apply += e * (4 + 2 * pes);
     }
     C.total_tiles = tb;
+    C.all_fused = true;
+    for (size_t k = 0; k < nm; ++k) {
+      const MatPlan& M = H.mats[C.mats[k]];
+      if (!M.path) {
+        C.all_fused = false;
+        const double e = (double)M.rows * M.cols, pes = M.dtype ? 2 : 4;
+        C.bytes_apply_unfused += e * (4 + 2 * pes);
+      }
+    }
     if ((rc = dev_alloc(p, &C.ew, nm * sizeof(EwMat)))) return rc;
     if ((rc = dev_alloc(p, &C.prefix, nm * sizeof(int64_t)))) return rc;
     if ((rc = dev_alloc(p, &C.dyn, nm * sizeof(EwDyn)))) return rc;
@@ -242,6 +254,11 @@ int materialize(muon_plan* p) {
         N.m_pad = (int32_t)M.m_pad;
         N.n_pad = (int32_t)M.n_pad;
         N.mat = S.mats[k];
+        N.dyn = (int32_t)(std::find(C.mats.begin(), C.mats.end(), S.mats[k]) - C.mats.begin());
+        N.trans = M.trans;
+        N.pdtype = M.dtype;
+        N.cols = M.cols;
+        N.s = M.s;
       }
       D.fl_gram = S.flops_gram_min;
       D.fl_square = S.flops_square_min;
@@ -322,6 +339,14 @@ GemmParams gp(const SetDev& S, const Items& it, bool sym, int shape, int pid, in
   return g;
 }
 
+// Makes the last NS product apply the parameter update instead of storing X_T.
+void fuse_update(GemmParams* g, const EwDyn* dyn, float lr, float wd) {
+  g->fuse = 1;
+  g->dyn = dyn;
+  g->lr = lr;
+  g->wd = wd;
+}
+
 // The NS stages of one launch set (T steps, coefficient schedule sched[3*T]).
 //
 // bf16 path, direct form, step k (X = X_k, X^T kept alongside):
@@ -332,7 +357,9 @@ GemmParams gp(const SetDev& S, const Items& it, bool sym, int shape, int pid, in
 // bf16 path, Gram form: G = r^2 X0 X0^T (NT, fp32 out); the m x m recursion in
 // fp32 on the register-staged kernel; X_T = r Q_T X0 (NT, Q_T rounded to bf16).
 // fp32 path: every product on the register-staged fp32 kernel.
-int enqueue_ns(muon_plan* p, const SetDev& S, int T, const float* sched, hipStream_t s) {
+// dyn: the chunk's caller pointers, or null (tuning: no parameters to update).
+int enqueue_ns(muon_plan* p, const SetDev& S, int T, const float* sched, const EwDyn* dyn,
+               float lr, float wd, hipStream_t s) {
   if (T <= 0) return MUON_OK;
   int rc;
   const float* rs = p->rscale;
@@ -352,6 +379,7 @@ int enqueue_ns(muon_plan* p, const SetDev& S, int T, const float* sched, hipStre
         if ((rc = run(p, kNsComb, nt_name(tp.sym, kBF16), S.fl_square, 0, s, [&] { return launch_gemm_nt(tp.sym, kBF16, g2, s); }))) return rc;
         GemmParams g3 = gp(S, S.nt_full, false, kShapeApplyT, kB, srcT, src, dst, -1, dstT, 1.f, a, 0.f,
                            k == 0 ? 1 : 0, rs);
+        if (last && dyn) fuse_update(&g3, dyn, lr, wd);
         const int odt = last ? kF32 : kBF16;
         if ((rc = run(p, kNsApply, nt_name(tp.apply, odt), S.fl_apply, 0, s, [&] { return launch_gemm_nt(tp.apply, odt, g3, s); }))) return rc;
       }
@@ -384,6 +412,7 @@ int enqueue_ns(muon_plan* p, const SetDev& S, int T, const float* sched, hipStre
       }
     }
     GemmParams gf = gp(S, S.nt_full, false, kShapeApplyT, kQH, kX0T, -1, kXT, -1, -1, 1.f, 0.f, 0.f, 1, rs);
+    if (dyn) fuse_update(&gf, dyn, lr, wd);
     if ((rc = run(p, kGramFinal, nt_name(tp.apply, kF32), S.fl_apply, 0, s, [&] { return launch_gemm_nt(tp.apply, kF32, gf, s); }))) return rc;
     return MUON_OK;
   }
@@ -484,10 +513,12 @@ int step_impl(muon_plan* p, void* const* params, const void* const* grads, float
            return launch_norm(C.ew, nm, C.partials, p->rscale, p->flags, p->host.opts.eps, s);
          }))) return rc;
     for (const SetDev& S : C.sets)
-      if ((rc = enqueue_ns(p, S, T, sched, s))) return rc;
-    if ((rc = run(p, kEwApply, "k_ew_apply", 0, C.bytes_apply, s, [&] {
+      if ((rc = enqueue_ns(p, S, T, sched, C.dyn, lr, wd, s))) return rc;
+    // with T >= 1 the last NS product of every bf16-path matrix applied its update
+    if (T >= 1 && C.all_fused) continue;
+    if ((rc = run(p, kEwApply, "k_ew_apply", 0, T >= 1 ? C.bytes_apply_unfused : C.bytes_apply, s, [&] {
            return launch_ew_apply(C.ew, C.dyn, C.prefix, nm, C.total_tiles, p->rscale, lr, wd,
-                                  T == 0 ? 1 : 0, p->grid_cap, s);
+                                  T == 0 ? 1 : 0, T >= 1 ? 1 : 0, p->grid_cap, s);
          }))) return rc;
   }
   return MUON_OK;
@@ -552,7 +583,7 @@ int time_shape(const ShapeKey& k, const PlanOptions& base, int count,
     for (int rep = 0; rep < 4; ++rep) {
       (void)hipEventRecord(e0, s);
       for (const SetDev& S : tp.chunks[0].sets)
-        if ((rc = enqueue_ns(&tp, S, 5, sched, s))) { cleanup(); return rc; }
+        if ((rc = enqueue_ns(&tp, S, 5, sched, nullptr, 0.f, 0.f, s))) { cleanup(); return rc; }
       (void)hipEventRecord(e1, s);
       if (hipEventSynchronize(e1) != hipSuccess) { cleanup(); return fail(MUON_EHIP, "tuning sync failed"); }
       float ms = 0;

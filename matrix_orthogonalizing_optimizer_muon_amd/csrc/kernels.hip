@@ -206,7 +206,7 @@ __global__ __launch_bounds__(256) void k_norm(const EwMat* __restrict__ mats,
 __global__ __launch_bounds__(256) void k_ew_apply(
     const EwMat* __restrict__ mats, const EwDyn* __restrict__ dyn,
     const int64_t* __restrict__ prefix, int nmats, int64_t total,
-    const float* __restrict__ rscale, float lr, float wd, int src_is_d) {
+    const float* __restrict__ rscale, float lr, float wd, int src_is_d, int skip_fused) {
   __shared__ float tT[kEwTile][kEwTile + 1];
   const int tid = threadIdx.x;
   const int r = tid >> 2, c0 = (tid & 3) * 16;
@@ -217,6 +217,7 @@ __global__ __launch_bounds__(256) void k_ew_apply(
     const int64_t lt = t - M.tile_begin;
     const int64_t i0 = (lt / M.tiles_j) * kEwTile, j0 = (lt % M.tiles_j) * kEwTile;
     if (i0 >= M.m || j0 >= M.n) continue;   // padding-only tile (uniform per block)
+    if (skip_fused && M.fused) continue;     // the last NS product applied this matrix
     const float sx = src_is_d ? rscale[M.mat] : 1.0f;
     const void* src = src_is_d ? M.d : static_cast<const void*>(M.xt);
     const int sdt = src_is_d ? M.ddtype : kF32;
@@ -606,6 +607,61 @@ __device__ __forceinline__ void st8(void* base, int64_t off, const float* v) {
   }
 }
 
+// Decoupled weight decay and the RMS-scaled orthogonal step on `nvalid` (<= 8)
+// consecutive stored elements of W starting at (row, col0), from the final NS
+// values x: U = -lr (wd W + s x), W <- RNE(W + U); U also goes to the
+// capture buffer when one is set.
+__device__ __forceinline__ void apply_update8(const GemmParams& p, const NsMat* nmp, int64_t row,
+                                              int64_t col0, int nvalid, const float* x) {
+  if (nvalid <= 0) return;
+  const EwDyn& D = p.dyn[nmp->dyn];
+  const int64_t off = row * nmp->cols + col0;
+  const float sc = nmp->s, lr = p.lr, wd = p.wd;
+  const int dt = nmp->pdtype;
+  if (D.vec && nvalid == 8) {
+    float w[8], u[8];
+    if (dt == kBF16) {
+      const uint4 q = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(D.w) + off);
+      const uint32_t qq[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        w[2 * e] = bf16_to_f32(qq[e] & 0xffffu);
+        w[2 * e + 1] = bf16_to_f32(qq[e] >> 16);
+      }
+    } else {
+      const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(D.w) + off);
+      const float4 a = src[0], b = src[1];
+      w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w; w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      u[e] = -lr * (wd * w[e] + sc * x[e]);
+      w[e] = w[e] + u[e];
+    }
+    if (dt == kBF16) {
+      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(D.w) + off) =
+          make_uint4(pack_bf16x2(w[0], w[1]), pack_bf16x2(w[2], w[3]), pack_bf16x2(w[4], w[5]),
+                     pack_bf16x2(w[6], w[7]));
+    } else {
+      float4* dst = reinterpret_cast<float4*>(static_cast<float*>(D.w) + off);
+      dst[0] = make_float4(w[0], w[1], w[2], w[3]);
+      dst[1] = make_float4(w[4], w[5], w[6], w[7]);
+    }
+    if (D.upd) {
+      float4* dst = reinterpret_cast<float4*>(D.upd + off);
+      dst[0] = make_float4(u[0], u[1], u[2], u[3]);
+      dst[1] = make_float4(u[4], u[5], u[6], u[7]);
+    }
+    return;
+  }
+  for (int e = 0; e < nvalid; ++e) {
+    const float w = load1(D.w, dt, off + e);
+    const float u = -lr * (wd * w + sc * x[e]);
+    store1(D.w, dt, off + e, w + u);
+    if (D.upd) D.upd[off + e] = u;
+  }
+}
+
 // Epilogue of the NT kernel through LDS, in slabs of SH rows:
 //  1. each wave writes its accumulators of the slab's rows into an fp32 tile;
 //  2. row pass: every thread takes 8 consecutive columns of a row, applies
@@ -636,7 +692,8 @@ __device__ __forceinline__ void nt_epilogue(const nt::f32x16_t (&acc)[BM / 32 / 
   const void* Cin = p.c_id >= 0 ? nmp->buf[p.c_id] : nullptr;
   const WorkItem it = p.items[blockIdx.x];
   const bool mirror = p.sym && it.tm != it.tn;
-  const bool colpass = mirror || OutT != nullptr;
+  const bool fuse = p.fuse != 0, ftrans = fuse && nmp->trans;
+  const bool colpass = mirror || OutT != nullptr || ftrans;
   const int m_pad = nmp->m_pad;
   __syncthreads();   // every wave is done with the main loop's LDS
 #pragma unroll 1
@@ -656,25 +713,42 @@ __device__ __forceinline__ void nt_epilogue(const nt::f32x16_t (&acc)[BM / 32 / 
         }
       }
     __syncthreads();
-#pragma unroll 1
-    for (int r = tid / TPR; r < SH; r += RPP) {
-      const int c = (tid % TPR) * 8;
-      const int i = m0 + s0 + r, j = n0 + c;
-      float v[8], cin[8];
+    // row pass: this thread's SH / RPP rows, 8 columns each; Cin for all of
+    // them is requested before any is used
+    constexpr int RPT = SH / RPP;
+    static_assert(SH % RPP == 0, "rows per thread");
+    const int c = (tid % TPR) * 8, r_first = tid / TPR;
+    const int j = n0 + c;
+    u32x4_t craw[RPT];
+    if (Cin) {
+#pragma unroll
+      for (int t = 0; t < RPT; ++t)
+        craw[t] = *(GLOBAL_AS const u32x4_t*)(static_cast<const uint16_t*>(Cin) +
+                                              (int64_t)(m0 + s0 + r_first + t * RPP) * ldo + j);
+    }
+#pragma unroll
+    for (int t = 0; t < RPT; ++t) {
+      const int r = r_first + t * RPP;
+      const int i = m0 + s0 + r;
+      float v[8];
       MUON_LDS float* src = C + r * PITCH + c;
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] = src[e];
-      if (Cin) ld8_bf16(Cin, (int64_t)i * ldo + j, cin);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         float x = alpha * v[e];
-        if (Cin) x += beta * cin[e];
+        if (Cin) x += beta * bf16_to_f32((e & 1) ? (craw[t][e >> 1] >> 16) : (craw[t][e >> 1] & 0xffffu));
         x *= sc;
         if (i == j + e) x += gamma;
         if (i >= Mr || j + e >= Nr) x = 0.f;
         v[e] = x;
       }
-      st8<TO>(Out, (int64_t)i * ldo + j, v);
+      if (!fuse) {
+        st8<TO>(Out, (int64_t)i * ldo + j, v);
+      } else if (!ftrans && i < Mr) {
+        const int nv = Nr - j;
+        apply_update8(p, nmp, i, j, nv < 8 ? nv : 8, v);
+      }
       if (colpass) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) src[e] = v[e];
@@ -691,6 +765,10 @@ __device__ __forceinline__ void nt_epilogue(const nt::f32x16_t (&acc)[BM / 32 / 
         const int j = n0 + jc, i0 = m0 + s0 + r0;
         if (OutT) st8<uint16_t>(OutT, (int64_t)j * m_pad + i0, v);
         if (mirror) st8<TO>(Out, (int64_t)j * ldo + i0, v);
+        if (ftrans && j < Nr) {
+          const int nv = Mr - i0;
+          apply_update8(p, nmp, j, i0, nv < 8 ? nv : 8, v);
+        }
       }
     }
     __syncthreads();   // the slab buffer is reused
@@ -770,11 +848,11 @@ hipError_t launch_norm(const EwMat* mats, int nmats, const float* partials, floa
 
 hipError_t launch_ew_apply(const EwMat* mats, const EwDyn* dyn, const int64_t* tile_prefix,
                            int nmats, int64_t total_tiles, const float* rscale, float lr,
-                           float wd, int src_is_d, int grid_cap, hipStream_t s) {
+                           float wd, int src_is_d, int skip_fused, int grid_cap, hipStream_t s) {
   if (total_tiles <= 0) return hipSuccess;
   const int64_t grid = total_tiles < grid_cap ? total_tiles : grid_cap;
   hipLaunchKernelGGL(k_ew_apply, dim3((unsigned)grid), dim3(256), 0, s, mats, dyn, tile_prefix,
-                     nmats, total_tiles, rscale, lr, wd, src_is_d);
+                     nmats, total_tiles, rscale, lr, wd, src_is_d, skip_fused);
   return hipGetLastError();
 }
 

@@ -36,7 +36,7 @@ struct EwMat {
   int64_t ldt;               // leading dimension of D^T (m_pad)
   float* xt;                 // X_T: final NS output (m_pad x n_pad, fp32)
   float s;                   // RMS-matching scale
-  float pad_;
+  int32_t fused;             // 1: the last NS product applies the update (bf16 NT path)
 };
 
 // Per matrix, caller pointers of the current step (uploaded when they change).
@@ -72,6 +72,11 @@ struct NsMat {
   int32_t m, n;          // canonical real extents
   int32_t m_pad, n_pad;  // padded extents (multiples of the tile sizes)
   int32_t mat;           // scale index
+  int32_t dyn;           // index of the matrix's EwDyn in its chunk
+  int32_t trans;         // 1: stored = canonical^T
+  int32_t pdtype;        // parameter dtype
+  int64_t cols;          // stored columns (row pitch of W)
+  float s;               // RMS-matching scale
   int32_t pad_;
 };
 
@@ -101,7 +106,13 @@ struct GemmParams {
   int32_t sym;         // 1: items are upper-triangle tiles; off-diagonal tiles are mirrored
   int32_t p_id, q_id, c_id, o_id, o2_id;   // BufId; c_id / o2_id may be -1 (none)
   int32_t ot_id;       // NT kernel: also store out^T (bf16) into this buffer, or -1
-  float alpha, beta, gamma, pad2_;
+  float alpha, beta, gamma;
+  // NT kernel, last NS product: instead of storing X_T, apply
+  // W <- W - lr (wd W + s X_T) to the caller's parameters (and write the
+  // update to the capture buffer when one is set).
+  int32_t fuse;
+  const EwDyn* dyn;
+  float lr, wd;
 };
 
 // Kernel configurations (the planner's tile choices).
@@ -122,9 +133,10 @@ hipError_t launch_ew_momentum(const EwMat* mats, const EwDyn* dyn, const int64_t
                               int nesterov, int grid_cap, hipStream_t s);
 hipError_t launch_norm(const EwMat* mats, int nmats, const float* partials, float* rscale,
                        uint32_t* flags, float eps, hipStream_t s);
+// skip_fused != 0: matrices whose update the last NS product applied are skipped.
 hipError_t launch_ew_apply(const EwMat* mats, const EwDyn* dyn, const int64_t* tile_prefix,
                            int nmats, int64_t total_tiles, const float* rscale, float lr,
-                           float wd, int src_is_d, int grid_cap, hipStream_t s);
+                           float wd, int src_is_d, int skip_fused, int grid_cap, hipStream_t s);
 // kShapeApply runs the NN kernel, the other shapes the NT kernel.
 hipError_t launch_gemm(int tile_cfg, int in_dtype, int out_dtype, const GemmParams& p,
                        hipStream_t s);
