@@ -42,14 +42,17 @@ struct Items {
 };
 
 struct SetDev {
-  int path = 0, form = kFormDirect, tile = 0;
+  int path = 0, form = kFormDirect;
   int nmats = 0;
   NsMat* mats = nullptr;
-  Items nt_sym, nt_full, old_sym, old_full;
-  double fl_gram = 0, fl_square = 0, fl_apply = 0;   // algorithmic (symmetric-aware) flops
+  Items nt_sym[kNumNtCfgs], nt_full[kNumNtCfgs], old_sym, old_full;
+  // algorithmic (symmetric-aware) flops of each launch: per NT configuration
+  // on the bf16 path, index 0 for the fp32 kernel
+  double fl_gram[kNumNtCfgs] = {0}, fl_square[kNumNtCfgs] = {0}, fl_apply[kNumNtCfgs] = {0};
 };
 
-static_assert(kNumNtCfgs == 4 && sizeof(kNtTileShapes) / sizeof(kNtTileShapes[0]) == 4, "tables");
+static_assert(kNumNtCfgs == kNtTiles && sizeof(kNtTileShapes) / sizeof(kNtTileShapes[0]) == kNtTiles,
+              "tables");
 static_assert(kNtCfgs[0].bm == kNtTileShapes[0].bm && kNtCfgs[0].bn == kNtTileShapes[0].bn &&
               kNtCfgs[1].bm == kNtTileShapes[1].bm && kNtCfgs[1].bn == kNtTileShapes[1].bn &&
               kNtCfgs[2].bm == kNtTileShapes[2].bm && kNtCfgs[2].bn == kNtTileShapes[2].bn &&
@@ -241,7 +244,6 @@ int materialize(muon_plan* p) {
       SetDev D;
       D.path = S.path;
       D.form = S.form;
-      D.tile = S.tile;
       D.nmats = (int)S.mats.size();
       std::vector<NsMat> nsm(S.mats.size());
       for (size_t k = 0; k < S.mats.size(); ++k) {
@@ -260,9 +262,11 @@ int materialize(muon_plan* p) {
         N.cols = M.cols;
         N.s = M.s;
       }
-      D.fl_gram = S.flops_gram_min;
-      D.fl_square = S.flops_square_min;
-      D.fl_apply = S.flops_apply_min;
+      for (int c = 0; c < kNumNtCfgs; ++c) {
+        D.fl_gram[c] = S.fl_gram[c];
+        D.fl_square[c] = S.fl_square[c];
+        D.fl_apply[c] = S.fl_apply[c];
+      }
       if ((rc = dev_alloc(p, &D.mats, nsm.size() * sizeof(NsMat)))) return rc;
       HIP_TRY(hipMemcpy(D.mats, nsm.data(), nsm.size() * sizeof(NsMat), hipMemcpyHostToDevice));
       auto upload = [&](const std::vector<ItemHost>& v, Items* out) -> int {
@@ -275,9 +279,10 @@ int materialize(muon_plan* p) {
         HIP_TRY(hipMemcpy(out->d, w.data(), w.size() * sizeof(WorkItem), hipMemcpyHostToDevice));
         return MUON_OK;
       };
-      if ((rc = upload(S.nt_sym, &D.nt_sym)) || (rc = upload(S.nt_full, &D.nt_full)) ||
-          (rc = upload(S.old_sym, &D.old_sym)) || (rc = upload(S.old_full, &D.old_full)))
-        return rc;
+      for (int c = 0; c < kNumNtCfgs; ++c)
+        if ((rc = upload(S.nt_sym[c], &D.nt_sym[c])) || (rc = upload(S.nt_full[c], &D.nt_full[c])))
+          return rc;
+      if ((rc = upload(S.old_sym, &D.old_sym)) || (rc = upload(S.old_full, &D.old_full))) return rc;
       C.sets.push_back(D);
     }
   }
@@ -348,23 +353,26 @@ void fuse_update(GemmParams* g, const EwDyn* dyn, float lr, float wd) {
 }
 
 // The NS stages of one launch set (T steps, coefficient schedule sched[3*T]).
+// On the bf16 path each stage is one launch per NT configuration that the
+// set's matrices use for it.
 //
 // bf16 path, direct form, step k (X = X_k, X^T kept alongside):
 //   A  = s_k X X^T                     NT, symmetric tiles           (s_0 = r^2, else 1)
-//   B  = b A + c A A                   NT, symmetric tiles
-//   X' = t_k (a X + B X)               NT with Q = X^T; writes X' and X'^T (t_0 = r, else 1)
-//   the last step writes X' in fp32 to X_T instead.
+//   B  = a I + b A + c A A             NT, symmetric tiles
+//   X' = t_k B X                       NT with Q = X^T; writes X' and X'^T (t_0 = r, else 1)
+//   the last step applies the update from X' (or, without parameters, writes
+//   X' in fp32 to X_T).  B carries the a X term as a I: in exact arithmetic
+//   B X equals a X + (b A + c A A) X, and the product then reads no third
+//   operand.  Rounding B to bf16 perturbs a X no more than rounding X' does.
 // bf16 path, Gram form: G = r^2 X0 X0^T (NT, fp32 out); the m x m recursion in
 // fp32 on the register-staged kernel; X_T = r Q_T X0 (NT, Q_T rounded to bf16).
-// fp32 path: every product on the register-staged fp32 kernel.
-// dyn: the chunk's caller pointers, or null (tuning: no parameters to update).
+// fp32 path: the same stages on the register-staged kernel.
 int enqueue_ns(muon_plan* p, const SetDev& S, int T, const float* sched, const EwDyn* dyn,
                float lr, float wd, hipStream_t s) {
   if (T <= 0) return MUON_OK;
   int rc;
   const float* rs = p->rscale;
   if (S.path) {
-    const TilePlan tp = tile_plan(S.tile);
     if (S.form == kFormDirect) {
       for (int k = 0; k < T; ++k) {
         const float a = sched[3 * k], b = sched[3 * k + 1], c = sched[3 * k + 2];
@@ -372,22 +380,36 @@ int enqueue_ns(muon_plan* p, const SetDev& S, int T, const float* sched, const E
         const int src = even ? kX0 : kX1, srcT = even ? kX0T : kX1T;
         const int dst = last ? kXT : (even ? kX1 : kX0);
         const int dstT = last ? -1 : (even ? kX1T : kX0T);
-        GemmParams g1 = gp(S, S.nt_sym, true, kShapeGram, src, src, -1, kA, -1, -1, 1.f, 0.f, 0.f,
-                           k == 0 ? 2 : 0, rs);
-        if ((rc = run(p, kNsSyrk, nt_name(tp.sym, kBF16), S.fl_gram, 0, s, [&] { return launch_gemm_nt(tp.sym, kBF16, g1, s); }))) return rc;
-        GemmParams g2 = gp(S, S.nt_sym, true, kShapeSquare, kA, kA, kA, kB, -1, -1, c, b, 0.f, 0, rs);
-        if ((rc = run(p, kNsComb, nt_name(tp.sym, kBF16), S.fl_square, 0, s, [&] { return launch_gemm_nt(tp.sym, kBF16, g2, s); }))) return rc;
-        GemmParams g3 = gp(S, S.nt_full, false, kShapeApplyT, kB, srcT, src, dst, -1, dstT, 1.f, a, 0.f,
-                           k == 0 ? 1 : 0, rs);
-        if (last && dyn) fuse_update(&g3, dyn, lr, wd);
+        for (int cfg = 0; cfg < kNumNtCfgs; ++cfg) {
+          if (!S.nt_sym[cfg].n) continue;
+          GemmParams g1 = gp(S, S.nt_sym[cfg], true, kShapeGram, src, src, -1, kA, -1, -1, 1.f, 0.f,
+                             0.f, k == 0 ? 2 : 0, rs);
+          if ((rc = run(p, kNsSyrk, nt_name(cfg, kBF16), S.fl_gram[cfg], 0, s, [&] { return launch_gemm_nt(cfg, kBF16, g1, s); }))) return rc;
+        }
+        for (int cfg = 0; cfg < kNumNtCfgs; ++cfg) {
+          if (!S.nt_sym[cfg].n) continue;
+          GemmParams g2 = gp(S, S.nt_sym[cfg], true, kShapeSquare, kA, kA, kA, kB, -1, -1, c, b, a, 0, rs);
+          if ((rc = run(p, kNsComb, nt_name(cfg, kBF16), S.fl_square[cfg], 0, s, [&] { return launch_gemm_nt(cfg, kBF16, g2, s); }))) return rc;
+        }
         const int odt = last ? kF32 : kBF16;
-        if ((rc = run(p, kNsApply, nt_name(tp.apply, odt), S.fl_apply, 0, s, [&] { return launch_gemm_nt(tp.apply, odt, g3, s); }))) return rc;
+        for (int cfg = 0; cfg < kNumNtCfgs; ++cfg) {
+          if (!S.nt_full[cfg].n) continue;
+          GemmParams g3 = gp(S, S.nt_full[cfg], false, kShapeApplyT, kB, srcT, -1, dst, -1, dstT, 1.f,
+                             0.f, 0.f, k == 0 ? 1 : 0, rs);
+          if (last && dyn) fuse_update(&g3, dyn, lr, wd);
+          if ((rc = run(p, kNsApply, nt_name(cfg, odt), S.fl_apply[cfg], 0, s, [&] { return launch_gemm_nt(cfg, odt, g3, s); }))) return rc;
+        }
       }
       return MUON_OK;
     }
     // Gram space
-    GemmParams g0 = gp(S, S.nt_sym, true, kShapeGram, kX0, kX0, -1, kA, -1, -1, 1.f, 0.f, 0.f, 2, rs);
-    if ((rc = run(p, kGramXxt, nt_name(tp.sym, kF32), S.fl_gram, 0, s, [&] { return launch_gemm_nt(tp.sym, kF32, g0, s); }))) return rc;
+    double fl_square = 0;
+    for (int cfg = 0; cfg < kNumNtCfgs; ++cfg) {
+      fl_square += S.fl_square[cfg];
+      if (!S.nt_sym[cfg].n) continue;
+      GemmParams g0 = gp(S, S.nt_sym[cfg], true, kShapeGram, kX0, kX0, -1, kA, -1, -1, 1.f, 0.f, 0.f, 2, rs);
+      if ((rc = run(p, kGramXxt, nt_name(cfg, kF32), S.fl_gram[cfg], 0, s, [&] { return launch_gemm_nt(cfg, kF32, g0, s); }))) return rc;
+    }
     int cur = kQX;
     for (int k = 0; k < T; ++k) {
       const float a = sched[3 * k], b = sched[3 * k + 1], c = sched[3 * k + 2];
@@ -396,24 +418,27 @@ int enqueue_ns(muon_plan* p, const SetDev& S, int T, const float* sched, const E
       // H = a I + b A + c A^2 (at k = 0 this is Q_1 itself)
       GemmParams gh = gp(S, S.old_sym, true, kShapeSquare, kA, kA, kA, hbuf, (k == 0 && last) ? kQH : -1,
                          -1, c, b, a, 0, rs);
-      if ((rc = run(p, kGramSquare, rs_name(false, kF32, kF32), S.fl_square, 0, s, [&] { return launch_gemm(0, kF32, kF32, gh, s); }))) return rc;
+      if ((rc = run(p, kGramSquare, rs_name(false, kF32, kF32), fl_square, 0, s, [&] { return launch_gemm(0, kF32, kF32, gh, s); }))) return rc;
       if (k > 0) {
         const int nxt = cur == kQX ? kQY : kQX;
         GemmParams gq = gp(S, S.old_sym, true, kShapeSquare, kH, cur, -1, nxt, last ? kQH : -1, -1, 1.f,
                            0.f, 0.f, 0, rs);
-        if ((rc = run(p, kGramSquare, rs_name(false, kF32, kF32), S.fl_square, 0, s, [&] { return launch_gemm(0, kF32, kF32, gq, s); }))) return rc;
+        if ((rc = run(p, kGramSquare, rs_name(false, kF32, kF32), fl_square, 0, s, [&] { return launch_gemm(0, kF32, kF32, gq, s); }))) return rc;
         cur = nxt;
       }
       if (!last) {
         GemmParams gt = gp(S, S.old_sym, true, kShapeSquare, hbuf, kA, -1, kT1, -1, -1, 1.f, 0.f, 0.f, 0, rs);
-        if ((rc = run(p, kGramSquare, rs_name(false, kF32, kF32), S.fl_square, 0, s, [&] { return launch_gemm(0, kF32, kF32, gt, s); }))) return rc;
+        if ((rc = run(p, kGramSquare, rs_name(false, kF32, kF32), fl_square, 0, s, [&] { return launch_gemm(0, kF32, kF32, gt, s); }))) return rc;
         GemmParams ga = gp(S, S.old_sym, true, kShapeSquare, kT1, hbuf, -1, kA, -1, -1, 1.f, 0.f, 0.f, 0, rs);
-        if ((rc = run(p, kGramSquare, rs_name(false, kF32, kF32), S.fl_square, 0, s, [&] { return launch_gemm(0, kF32, kF32, ga, s); }))) return rc;
+        if ((rc = run(p, kGramSquare, rs_name(false, kF32, kF32), fl_square, 0, s, [&] { return launch_gemm(0, kF32, kF32, ga, s); }))) return rc;
       }
     }
-    GemmParams gf = gp(S, S.nt_full, false, kShapeApplyT, kQH, kX0T, -1, kXT, -1, -1, 1.f, 0.f, 0.f, 1, rs);
-    if (dyn) fuse_update(&gf, dyn, lr, wd);
-    if ((rc = run(p, kGramFinal, nt_name(tp.apply, kF32), S.fl_apply, 0, s, [&] { return launch_gemm_nt(tp.apply, kF32, gf, s); }))) return rc;
+    for (int cfg = 0; cfg < kNumNtCfgs; ++cfg) {
+      if (!S.nt_full[cfg].n) continue;
+      GemmParams gf = gp(S, S.nt_full[cfg], false, kShapeApplyT, kQH, kX0T, -1, kXT, -1, -1, 1.f, 0.f, 0.f, 1, rs);
+      if (dyn) fuse_update(&gf, dyn, lr, wd);
+      if ((rc = run(p, kGramFinal, nt_name(cfg, kF32), S.fl_apply[cfg], 0, s, [&] { return launch_gemm_nt(cfg, kF32, gf, s); }))) return rc;
+    }
     return MUON_OK;
   }
   // fp32 path
@@ -423,38 +448,38 @@ int enqueue_ns(muon_plan* p, const SetDev& S, int T, const float* sched, const E
       const int src = (k % 2 == 0) ? kX0 : kX1;
       const int dst = (k == T - 1) ? kXT : (src == kX0 ? kX1 : kX0);
       GemmParams g1 = gp(S, S.old_sym, true, kShapeGram, src, src, -1, kA, -1, -1, 1.f, 0.f, 0.f, k == 0 ? 2 : 0, rs);
-      if ((rc = run(p, kNsSyrk, rs_name(false, kF32, kF32), S.fl_gram, 0, s, [&] { return launch_gemm(0, kF32, kF32, g1, s); }))) return rc;
+      if ((rc = run(p, kNsSyrk, rs_name(false, kF32, kF32), S.fl_gram[0], 0, s, [&] { return launch_gemm(0, kF32, kF32, g1, s); }))) return rc;
       GemmParams g2 = gp(S, S.old_sym, true, kShapeSquare, kA, kA, kA, kB, -1, -1, c, b, 0.f, 0, rs);
-      if ((rc = run(p, kNsComb, rs_name(false, kF32, kF32), S.fl_square, 0, s, [&] { return launch_gemm(0, kF32, kF32, g2, s); }))) return rc;
+      if ((rc = run(p, kNsComb, rs_name(false, kF32, kF32), S.fl_square[0], 0, s, [&] { return launch_gemm(0, kF32, kF32, g2, s); }))) return rc;
       GemmParams g3 = gp(S, S.old_full, false, kShapeApply, kB, src, src, dst, -1, -1, 1.f, a, 0.f, k == 0 ? 1 : 0, rs);
-      if ((rc = run(p, kNsApply, rs_name(true, kF32, kF32), S.fl_apply, 0, s, [&] { return launch_gemm(0, kF32, kF32, g3, s); }))) return rc;
+      if ((rc = run(p, kNsApply, rs_name(true, kF32, kF32), S.fl_apply[0], 0, s, [&] { return launch_gemm(0, kF32, kF32, g3, s); }))) return rc;
     }
     return MUON_OK;
   }
   GemmParams g0 = gp(S, S.old_sym, true, kShapeGram, kX0, kX0, -1, kA, -1, -1, 1.f, 0.f, 0.f, 2, rs);
-  if ((rc = run(p, kGramXxt, rs_name(false, kF32, kF32), S.fl_gram, 0, s, [&] { return launch_gemm(0, kF32, kF32, g0, s); }))) return rc;
+  if ((rc = run(p, kGramXxt, rs_name(false, kF32, kF32), S.fl_gram[0], 0, s, [&] { return launch_gemm(0, kF32, kF32, g0, s); }))) return rc;
   int cur = kQX;
   for (int k = 0; k < T; ++k) {
     const float a = sched[3 * k], b = sched[3 * k + 1], c = sched[3 * k + 2];
     const bool last = k == T - 1;
     const int hbuf = (k == 0) ? kQX : kH;
     GemmParams gh = gp(S, S.old_sym, true, kShapeSquare, kA, kA, kA, hbuf, -1, -1, c, b, a, 0, rs);
-    if ((rc = run(p, kGramSquare, rs_name(false, kF32, kF32), S.fl_square, 0, s, [&] { return launch_gemm(0, kF32, kF32, gh, s); }))) return rc;
+    if ((rc = run(p, kGramSquare, rs_name(false, kF32, kF32), S.fl_square[0], 0, s, [&] { return launch_gemm(0, kF32, kF32, gh, s); }))) return rc;
     if (k > 0) {
       const int nxt = cur == kQX ? kQY : kQX;
       GemmParams gq = gp(S, S.old_sym, true, kShapeSquare, kH, cur, -1, nxt, -1, -1, 1.f, 0.f, 0.f, 0, rs);
-      if ((rc = run(p, kGramSquare, rs_name(false, kF32, kF32), S.fl_square, 0, s, [&] { return launch_gemm(0, kF32, kF32, gq, s); }))) return rc;
+      if ((rc = run(p, kGramSquare, rs_name(false, kF32, kF32), S.fl_square[0], 0, s, [&] { return launch_gemm(0, kF32, kF32, gq, s); }))) return rc;
       cur = nxt;
     }
     if (!last) {
       GemmParams gt = gp(S, S.old_sym, true, kShapeSquare, hbuf, kA, -1, kT1, -1, -1, 1.f, 0.f, 0.f, 0, rs);
-      if ((rc = run(p, kGramSquare, rs_name(false, kF32, kF32), S.fl_square, 0, s, [&] { return launch_gemm(0, kF32, kF32, gt, s); }))) return rc;
+      if ((rc = run(p, kGramSquare, rs_name(false, kF32, kF32), S.fl_square[0], 0, s, [&] { return launch_gemm(0, kF32, kF32, gt, s); }))) return rc;
       GemmParams ga = gp(S, S.old_sym, true, kShapeSquare, kT1, hbuf, -1, kA, -1, -1, 1.f, 0.f, 0.f, 0, rs);
-      if ((rc = run(p, kGramSquare, rs_name(false, kF32, kF32), S.fl_square, 0, s, [&] { return launch_gemm(0, kF32, kF32, ga, s); }))) return rc;
+      if ((rc = run(p, kGramSquare, rs_name(false, kF32, kF32), S.fl_square[0], 0, s, [&] { return launch_gemm(0, kF32, kF32, ga, s); }))) return rc;
     }
   }
   GemmParams gf = gp(S, S.old_full, false, kShapeApply, cur, kX0, -1, kXT, -1, -1, 1.f, 0.f, 0.f, 1, rs);
-  if ((rc = run(p, kGramFinal, rs_name(true, kF32, kF32), S.fl_apply, 0, s, [&] { return launch_gemm(0, kF32, kF32, gf, s); }))) return rc;
+  if ((rc = run(p, kGramFinal, rs_name(true, kF32, kF32), S.fl_apply[0], 0, s, [&] { return launch_gemm(0, kF32, kF32, gf, s); }))) return rc;
   return MUON_OK;
 }
 

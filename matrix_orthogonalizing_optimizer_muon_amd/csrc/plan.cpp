@@ -301,26 +301,29 @@ std::string build_plan(const std::vector<int64_t>& rows, const std::vector<int64
       const MatPlan& M = P.mats[i];
       LaunchSetPlan* S = nullptr;
       for (LaunchSetPlan& s : C.sets)
-        if (s.path == M.path && s.form == M.form && s.tile == M.tile) S = &s;
+        if (s.path == M.path && s.form == M.form) S = &s;
       if (!S) {
         C.sets.emplace_back();
         S = &C.sets.back();
         S->path = M.path;
         S->form = M.form;
-        S->tile = M.tile;
       }
       const int32_t slot = (int32_t)S->mats.size();
       S->mats.push_back(i);
       const double m = (double)M.m, nn = (double)M.n, mp = (double)M.m_pad, np = (double)M.n_pad;
-      S->flops_gram_min += nn * m * (m + 1);
-      S->flops_square_min += m * m * (m + 1);
-      S->flops_apply_min += 2.0 * m * m * nn;
+      const double fg = nn * m * (m + 1), fs = m * m * (m + 1), fa = 2.0 * m * m * nn;
+      S->flops_gram_min += fg;
+      S->flops_square_min += fs;
+      S->flops_apply_min += fa;
       const double old_tf = 2.0 * kOld * kOld;
       if (M.path) {
         const TilePlan tp = tile_plan(M.tile);
         const TileShape s = nt_cfg_shape(tp.sym), a = nt_cfg_shape(tp.apply);
-        add_sym(S->nt_sym, slot, M.m_pad, s.bm);
-        add_full(S->nt_full, slot, M.m_pad, M.n_pad, a);
+        add_sym(S->nt_sym[tp.sym], slot, M.m_pad, s.bm);
+        add_full(S->nt_full[tp.apply], slot, M.m_pad, M.n_pad, a);
+        S->fl_gram[tp.sym] += fg;
+        S->fl_square[tp.sym] += fs;
+        S->fl_apply[tp.apply] += fa;
         const double st = sym_tiles(M.m_pad, s.bm);
         S->flops_gram_issued += st * 2.0 * s.bm * s.bn * np;
         S->flops_apply_issued += (mp / a.bm) * (np / a.bn) * 2.0 * a.bm * a.bn * mp;
@@ -333,6 +336,9 @@ std::string build_plan(const std::vector<int64_t>& rows, const std::vector<int64
       } else {
         add_sym(S->old_sym, slot, M.m_pad, kOld);
         add_full(S->old_full, slot, M.m_pad, M.n_pad, TileShape{kOld, kOld});
+        S->fl_gram[0] += fg;
+        S->fl_square[0] += fs;
+        S->fl_apply[0] += fa;
         const double st = sym_tiles(M.m_pad, kOld);
         S->flops_gram_issued += st * old_tf * np;
         S->flops_apply_issued += (mp / kOld) * (np / kOld) * old_tf * mp;
@@ -344,12 +350,17 @@ std::string build_plan(const std::vector<int64_t>& rows, const std::vector<int64
       // longest contraction first, then XCD-contiguous placement
       auto kn = [&](const ItemHost& it) { return P.mats[S.mats[it.slot]].n_pad; };
       auto km = [&](const ItemHost& it) { return P.mats[S.mats[it.slot]].m_pad; };
-      for (std::vector<ItemHost>* v : {&S.nt_sym, &S.old_sym}) {
+      std::vector<std::vector<ItemHost>*> sym{&S.old_sym}, full{&S.old_full};
+      for (int c = 0; c < kNtTiles; ++c) {
+        sym.push_back(&S.nt_sym[c]);
+        full.push_back(&S.nt_full[c]);
+      }
+      for (std::vector<ItemHost>* v : sym) {
         std::stable_sort(v->begin(), v->end(),
                          [&](const ItemHost& x, const ItemHost& y) { return kn(x) > kn(y); });
         remap_xcd(*v);
       }
-      for (std::vector<ItemHost>* v : {&S.nt_full, &S.old_full}) {
+      for (std::vector<ItemHost>* v : full) {
         std::stable_sort(v->begin(), v->end(),
                          [&](const ItemHost& x, const ItemHost& y) { return km(x) > km(y); });
         remap_xcd(*v);
@@ -362,7 +373,7 @@ std::string build_plan(const std::vector<int64_t>& rows, const std::vector<int64
 
 std::string serialize_plan(const PlanHost& p) {
   std::ostringstream o;
-  o << "muon-plan v2\n";
+  o << "muon-plan v3\n";
   o << "opts nesterov=" << p.opts.nesterov << " eps=" << std::hexfloat << p.opts.eps
     << " rms=" << p.opts.rms_scale << std::defaultfloat << " precision=" << p.opts.precision
     << " form=" << p.opts.form << " tile=" << p.opts.tile << " cap=" << p.opts.workspace_cap << "\n";
@@ -383,12 +394,19 @@ std::string serialize_plan(const PlanHost& p) {
     o << "chunk " << c << " mats=" << C.mats.size() << " ws=" << C.ws_bytes << " ew_tiles=" << C.ew_tiles
       << "\n";
     for (const LaunchSetPlan& S : C.sets) {
-      o << " set path=" << S.path << " form=" << S.form << " tile=" << S.tile << " mats=" << S.mats.size()
-        << " items=" << S.nt_sym.size() << "/" << S.nt_full.size() << "/" << S.old_sym.size() << "/"
-        << S.old_full.size() << " order=";
+      o << " set path=" << S.path << " form=" << S.form << " mats=" << S.mats.size() << " items=";
+      for (int c = 0; c < kNtTiles; ++c) o << S.nt_sym[c].size() << "/" << S.nt_full[c].size() << ",";
+      o << S.old_sym.size() << "/" << S.old_full.size() << " order=";
       uint64_t h = 1469598103934665603ull;
       auto mix = [&](int32_t v) { for (int b = 0; b < 4; ++b) { h ^= (uint8_t)(v >> (8 * b)); h *= 1099511628211ull; } };
-      for (const std::vector<ItemHost>* v : {&S.nt_sym, &S.nt_full, &S.old_sym, &S.old_full})
+      std::vector<const std::vector<ItemHost>*> lists;
+      for (int c = 0; c < kNtTiles; ++c) {
+        lists.push_back(&S.nt_sym[c]);
+        lists.push_back(&S.nt_full[c]);
+      }
+      lists.push_back(&S.old_sym);
+      lists.push_back(&S.old_full);
+      for (const std::vector<ItemHost>* v : lists)
         for (const ItemHost& it : *v) { mix(it.slot); mix(it.tm); mix(it.tn); }
       o << std::hex << h << std::dec << "\n";
     }

@@ -31,7 +31,8 @@ enum PlanBuf : int32_t {
 // Output tiles of the bf16 NT kernel configurations (kernels.hpp NtCfg; abi.cpp
 // checks at compile time that the two tables agree).
 struct TileShape { int32_t bm, bn; };
-constexpr TileShape kNtTileShapes[4] = {{128, 128}, {256, 256}, {256, 128}, {128, 256}};
+constexpr int kNtTiles = 4;
+constexpr TileShape kNtTileShapes[kNtTiles] = {{128, 128}, {256, 256}, {256, 128}, {128, 256}};
 TileShape nt_cfg_shape(int cfg);
 
 // A tile plan: the NT kernel configuration of the symmetric m x m products
@@ -95,15 +96,22 @@ struct GroupPlan {
 
 struct ItemHost { int32_t slot, tm, tn; };
 
-// Matrices of one chunk that share (path, form, tile): one launch per NS stage.
+// Matrices of one chunk that share (path, form): one launch per NS stage and
+// kernel configuration.  On the bf16 path every NT configuration has its own
+// item lists, so matrices whose tile plans differ in one product still share
+// the launches of the other (a plan {128 sym, 256 apply} and a plan {128, 128}
+// run X X^T and A A together).
 struct LaunchSetPlan {
-  int32_t path = 0, form = kFormDirect, tile = 0;
-  std::vector<int32_t> mats;       // matrix indices, in slot order
-  std::vector<ItemHost> nt_sym;    // upper-triangle m x m tiles of the NT sym config
-  std::vector<ItemHost> nt_full;   // m x n tiles of the NT apply config
-  std::vector<ItemHost> old_sym;   // upper-triangle 128-tiles (fp32 kernel)
-  std::vector<ItemHost> old_full;  // m x n 128-tiles (fp32 kernel)
-  double flops_gram_min = 0;       // symmetric-aware algorithmic flops of one X X^T over the set
+  int32_t path = 0, form = kFormDirect;
+  std::vector<int32_t> mats;               // matrix indices, in slot order
+  std::vector<ItemHost> nt_sym[kNtTiles];  // upper-triangle m x m tiles per NT configuration
+  std::vector<ItemHost> nt_full[kNtTiles]; // m x n tiles per NT configuration
+  std::vector<ItemHost> old_sym;           // upper-triangle 128-tiles (fp32 kernel)
+  std::vector<ItemHost> old_full;          // m x n 128-tiles (fp32 kernel)
+  // symmetric-aware algorithmic flops of one product over the matrices of each
+  // NT configuration's launch (bf16 path) or of the whole set (fp32 path: index 0)
+  double fl_gram[kNtTiles] = {0}, fl_square[kNtTiles] = {0}, fl_apply[kNtTiles] = {0};
+  double flops_gram_min = 0;       // one X X^T over the set
   double flops_square_min = 0;     // one symmetric m x m product over the set
   double flops_apply_min = 0;      // one (m x m)(m x n) product over the set
   double flops_gram_issued = 0, flops_square_issued = 0, flops_apply_issued = 0;
