@@ -551,9 +551,58 @@ int step_impl(muon_plan* p, void* const* params, const void* const* grads, float
 
 const float kQuintic[3] = {3.4445f, -4.7750f, 2.0315f};
 
+// Times the NS stages (T = 5) of a host plan on bounded synthetic operands:
+// every workspace byte 0x3C (bf16 and fp32 ~0.0115), X0 scaled to unit
+// Frobenius norm.  4 runs over all chunks, best of the last 3, in ms.
+int time_ns(PlanHost&& H, float* best_ms) {
+  muon_plan tp;
+  tp.host = std::move(H);
+  int rc = materialize(&tp);
+  if (rc) { free_plan_memory(&tp); return rc; }
+  const size_t n = tp.host.mats.size();
+  std::vector<float> r(n);
+  for (size_t i = 0; i < n; ++i) {
+    const MatPlan& M = tp.host.mats[i];
+    const double v = M.path ? 0.011474609375 : 0.011483338475227356;
+    r[i] = (float)(1.0 / (v * std::sqrt((double)M.m_pad * M.n_pad)));
+  }
+  hipStream_t s = nullptr;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  auto cleanup = [&] {
+    if (e0) (void)hipEventDestroy(e0);
+    if (e1) (void)hipEventDestroy(e1);
+    if (s) (void)hipStreamDestroy(s);
+    free_plan_memory(&tp);
+  };
+  if (hipMemset(tp.ws, 0x3C, tp.host.ws_bytes) != hipSuccess ||
+      hipMemcpy(tp.rscale, r.data(), n * sizeof(float), hipMemcpyHostToDevice) != hipSuccess ||
+      hipStreamCreate(&s) != hipSuccess || hipEventCreate(&e0) != hipSuccess ||
+      hipEventCreate(&e1) != hipSuccess) {
+    cleanup();
+    return fail(MUON_EHIP, "tuning setup failed");
+  }
+  float sched[15];
+  for (int i = 0; i < 5; ++i) std::memcpy(sched + 3 * i, kQuintic, sizeof kQuintic);
+  float best = 1e30f;
+  for (int rep = 0; rep < 4; ++rep) {
+    (void)hipEventRecord(e0, s);
+    for (const ChunkDev& C : tp.chunks)
+      for (const SetDev& S : C.sets)
+        if ((rc = enqueue_ns(&tp, S, 5, sched, nullptr, 0.f, 0.f, s))) { cleanup(); return rc; }
+    (void)hipEventRecord(e1, s);
+    if (hipEventSynchronize(e1) != hipSuccess) { cleanup(); return fail(MUON_EHIP, "tuning sync failed"); }
+    float ms = 0;
+    (void)hipEventElapsedTime(&ms, e0, e1);
+    if (rep > 0) best = std::min(best, ms);
+  }
+  cleanup();
+  *best_ms = best;
+  return MUON_OK;
+}
+
 // Times every candidate (form, tile plan) of one shape on a batch of equal
-// matrices (NS stages only, T = 5, bounded synthetic operands) and keeps the
-// fastest; a later candidate must beat the best so far by 3% to replace it.
+// matrices and keeps the fastest; a later candidate must beat the best so far
+// by 3% to replace it.
 int time_shape(const ShapeKey& k, const PlanOptions& base, int count,
                const std::vector<std::pair<int32_t, int32_t>>& cands, ShapeChoice* out) {
   double best_us = 0;
@@ -563,8 +612,7 @@ int time_shape(const ShapeKey& k, const PlanOptions& base, int count,
     // the timed launches have the real launch's tile count and wave quantization
     const uint64_t per = matrix_ws_bytes(k, cand.first, cand.second);
     const int by_mem = (int)std::max<uint64_t>(1, (16ull << 30) / std::max<uint64_t>(per, 1));
-    const int want = 64;
-    const int batch = std::max(1, std::min({want, count, by_mem}));
+    const int batch = std::max(1, std::min({64, count, by_mem}));
     PlanHost H;
     std::map<ShapeKey, ShapeChoice> ch;
     ShapeChoice c;
@@ -578,45 +626,10 @@ int time_shape(const ShapeKey& k, const PlanOptions& base, int count,
     o.precision = k.path ? MUON_PRECISION_BF16 : MUON_PRECISION_FP32;
     std::string err = build_plan(rows, cols, dts, o, ch, &H);
     if (!err.empty()) return fail(MUON_ENOMEM, "tuning: " + err);
-    muon_plan tp;
-    tp.host = std::move(H);
-    int rc = materialize(&tp);
-    if (rc) { free_plan_memory(&tp); return rc; }
-    // bounded, finite inputs: every workspace byte 0x3C (bf16 and fp32 ~0.0115),
-    // X0 scaled to unit Frobenius norm
-    const MatPlan& M0 = tp.host.mats[0];
-    const double v = k.path ? 0.011474609375 : 0.011483338475227356;
-    std::vector<float> r(batch, (float)(1.0 / (v * std::sqrt((double)M0.m_pad * M0.n_pad))));
-    hipStream_t s = nullptr;
-    hipEvent_t e0 = nullptr, e1 = nullptr;
-    auto cleanup = [&] {
-      if (e0) (void)hipEventDestroy(e0);
-      if (e1) (void)hipEventDestroy(e1);
-      if (s) (void)hipStreamDestroy(s);
-      free_plan_memory(&tp);
-    };
-    if (hipMemset(tp.ws, 0x3C, tp.host.ws_bytes) != hipSuccess ||
-        hipMemcpy(tp.rscale, r.data(), batch * sizeof(float), hipMemcpyHostToDevice) != hipSuccess ||
-        hipStreamCreate(&s) != hipSuccess || hipEventCreate(&e0) != hipSuccess ||
-        hipEventCreate(&e1) != hipSuccess) {
-      cleanup();
-      return fail(MUON_EHIP, "tuning setup failed");
-    }
-    float sched[15];
-    for (int i = 0; i < 5; ++i) std::memcpy(sched + 3 * i, kQuintic, sizeof kQuintic);
-    float best = 1e30f;
-    for (int rep = 0; rep < 4; ++rep) {
-      (void)hipEventRecord(e0, s);
-      for (const SetDev& S : tp.chunks[0].sets)
-        if ((rc = enqueue_ns(&tp, S, 5, sched, nullptr, 0.f, 0.f, s))) { cleanup(); return rc; }
-      (void)hipEventRecord(e1, s);
-      if (hipEventSynchronize(e1) != hipSuccess) { cleanup(); return fail(MUON_EHIP, "tuning sync failed"); }
-      float ms = 0;
-      (void)hipEventElapsedTime(&ms, e0, e1);
-      if (rep > 0) best = std::min(best, ms);
-    }
-    cleanup();
-    const double us = best * 1000.0 / batch;
+    float ms = 0;
+    const int rc = time_ns(std::move(H), &ms);
+    if (rc) return rc;
+    const double us = ms * 1000.0 / batch;
     if (!have || us < 0.97 * best_us) {
       out->form = cand.first;
       out->tile = cand.second;
@@ -626,6 +639,49 @@ int time_shape(const ShapeKey& k, const PlanOptions& base, int count,
   }
   out->us = best_us;
   out->timed = true;
+  return MUON_OK;
+}
+
+// Whole-set refinement.  Shapes are timed one at a time, but a stage's launch
+// is shared by every matrix that uses the same kernel configuration for it, so
+// the plan that gives all bf16 direct-form shapes one tile plan can beat the
+// per-shape choices (fewer, fuller launches).  Each such uniform plan is timed
+// as a whole against the per-shape plan; it must be 1.5% faster to be kept
+// (whole-set timings repeat to well under 1%).
+// Returns the kept tile plan (-1: per-shape) through *tile.
+int refine_set(const std::vector<int64_t>& rows, const std::vector<int64_t>& cols,
+               const std::vector<int32_t>& dts, const PlanOptions& po,
+               const std::map<ShapeKey, ShapeChoice>& choices, SetChoice* out) {
+  auto uniform = [&](int t) {
+    std::map<ShapeKey, ShapeChoice> u = choices;
+    for (auto& kv : u)
+      if (kv.first.path && kv.second.form == kFormDirect) kv.second.tile = t;
+    return u;
+  };
+  auto time_of = [&](const std::map<ShapeKey, ShapeChoice>& ch, float* ms) -> int {
+    PlanHost H;
+    const std::string err = build_plan(rows, cols, dts, po, ch, &H);
+    if (!err.empty()) return fail(MUON_ENOMEM, "tuning: " + err);
+    return time_ns(std::move(H), ms);
+  };
+  float best = 0;
+  int rc = time_of(choices, &best);
+  if (rc) return rc;
+  out->tile = -1;
+  out->us = best * 1000.0;
+  for (int t = 0; t < num_tile_plans(); ++t) {
+    bool same = true;
+    for (const auto& kv : choices)
+      if (kv.first.path && kv.second.form == kFormDirect && kv.second.tile != t) same = false;
+    if (same) continue;
+    float ms = 0;
+    if ((rc = time_of(uniform(t), &ms))) return rc;
+    if (ms < 0.985f * best) {
+      best = ms;
+      out->tile = t;
+      out->us = ms * 1000.0;
+    }
+  }
   return MUON_OK;
 }
 
@@ -714,7 +770,7 @@ int muon_plan_create(const muon_matrix_desc* descs, int n, const muon_plan_opts*
   std::map<ShapeKey, int> counts;
   for (int i = 0; i < n; ++i) counts[shape_key(rows[i], cols[i], dts[i], po.precision)]++;
   // a host-only plan reads the cache (tag "host") but never times
-  std::map<ShapeKey, ShapeChoice> cache;
+  TuneCache cache;
   if (po.tune != MUON_TUNE_OFF) cache = read_cache(po.cache_path, tag);
   std::map<ShapeKey, ShapeChoice> choices;
   bool cache_dirty = false;
@@ -740,8 +796,8 @@ int muon_plan_create(const muon_matrix_desc* descs, int n, const muon_plan_opts*
       choices[k] = c;
       continue;
     }
-    auto it = cache.find(k);
-    if (!forced && it != cache.end() && (po.tune == MUON_TUNE_ONCE || po.host_only)) {
+    auto it = cache.shapes.find(k);
+    if (!forced && it != cache.shapes.end() && (po.tune == MUON_TUNE_ONCE || po.host_only)) {
       choices[k] = it->second;
       continue;
     }
@@ -754,8 +810,36 @@ int muon_plan_create(const muon_matrix_desc* descs, int n, const muon_plan_opts*
     if (rc) return rc;
     choices[k] = c;
     if (!forced) {
-      cache[k] = c;
+      cache.shapes[k] = c;
       cache_dirty = true;
+    }
+  }
+  // whole-set refinement (tuned plans without a forced form or tile): the
+  // cached set choice, or a timing when the set's workspace fits 16 GiB
+  if (po.tune != MUON_TUNE_OFF && po.form == MUON_FORM_AUTO && po.tile < 0) {
+    bool direct_bf16 = false;
+    for (const auto& kv : choices) direct_bf16 |= kv.first.path && kv.second.form == kFormDirect;
+    if (direct_bf16) {
+      const std::string sk = set_key(counts, choices);
+      const auto it = cache.sets.find(sk);
+      SetChoice sc;
+      bool have = false;
+      if (it != cache.sets.end() && (po.tune == MUON_TUNE_ONCE || po.host_only)) {
+        sc = it->second;
+        have = true;
+      } else if (!po.host_only) {
+        PlanHost probe;
+        if (build_plan(rows, cols, dts, po, choices, &probe).empty() && probe.ws_bytes <= (16ull << 30)) {
+          const int rc = refine_set(rows, cols, dts, po, choices, &sc);
+          if (rc) return rc;
+          cache.sets[sk] = sc;
+          cache_dirty = true;
+          have = true;
+        }
+      }
+      if (have && sc.tile >= 0)
+        for (auto& kv : choices)
+          if (kv.first.path && kv.second.form == kFormDirect) kv.second.tile = sc.tile;
     }
   }
   if (cache_dirty) (void)write_cache(po.cache_path, tag, cache);

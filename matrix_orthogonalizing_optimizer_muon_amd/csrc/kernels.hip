@@ -607,58 +607,81 @@ __device__ __forceinline__ void st8(void* base, int64_t off, const float* v) {
   }
 }
 
-// Decoupled weight decay and the RMS-scaled orthogonal step on `nvalid` (<= 8)
-// consecutive stored elements of W starting at (row, col0), from the final NS
-// values x: U = -lr (wd W + s x), W <- RNE(W + U); U also goes to the
+// What the weight update applied in an epilogue needs, read once per block
+// (the output stores may alias the descriptor tables, so nothing is re-read).
+struct UpdCtx {
+  void* w;          // stored W (rows x cols, row-major)
+  float* upd;       // capture of U, or null
+  int64_t cols;
+  float s, lr, wd;  // RMS-matching scale, learning rate, weight decay
+  int32_t pdtype;
+  int32_t vec;      // W (and the capture) aligned for 16-byte runs, cols % 8 == 0
+};
+
+// Decoupled weight decay and the RMS-scaled orthogonal step on 8 consecutive
+// stored bf16 elements of W at element offset `off`, whose current values wq
+// were loaded ahead: U = -lr (wd W + s x), W <- RNE(W + U); U also goes to the
 // capture buffer when one is set.
-__device__ __forceinline__ void apply_update8(const GemmParams& p, const NsMat* nmp, int64_t row,
-                                              int64_t col0, int nvalid, const float* x) {
-  if (nvalid <= 0) return;
-  const EwDyn& D = p.dyn[nmp->dyn];
-  const int64_t off = row * nmp->cols + col0;
-  const float sc = nmp->s, lr = p.lr, wd = p.wd;
-  const int dt = nmp->pdtype;
-  if (D.vec && nvalid == 8) {
-    float w[8], u[8];
-    if (dt == kBF16) {
-      const uint4 q = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(D.w) + off);
-      const uint32_t qq[4] = {q.x, q.y, q.z, q.w};
+__device__ __forceinline__ void apply_update8_bf16(const UpdCtx& c, int64_t off, u32x4_t wq,
+                                                   const float* x) {
+  float w[8], u[8];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        w[2 * e] = bf16_to_f32(qq[e] & 0xffffu);
-        w[2 * e + 1] = bf16_to_f32(qq[e] >> 16);
-      }
-    } else {
-      const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(D.w) + off);
-      const float4 a = src[0], b = src[1];
-      w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w; w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+  for (int e = 0; e < 4; ++e) {
+    w[2 * e] = bf16_to_f32(wq[e] & 0xffffu);
+    w[2 * e + 1] = bf16_to_f32(wq[e] >> 16);
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    u[e] = -c.lr * (c.wd * w[e] + c.s * x[e]);
+    w[e] = w[e] + u[e];
+  }
+  *(GLOBAL_AS u32x4_t*)(static_cast<uint16_t*>(c.w) + off) =
+      u32x4_t{pack_bf16x2(w[0], w[1]), pack_bf16x2(w[2], w[3]), pack_bf16x2(w[4], w[5]),
+              pack_bf16x2(w[6], w[7])};
+  if (c.upd) {
+    typedef float f32x4_t __attribute__((ext_vector_type(4)));
+    GLOBAL_AS f32x4_t* dst = (GLOBAL_AS f32x4_t*)(c.upd + off);
+    dst[0] = f32x4_t{u[0], u[1], u[2], u[3]};
+    dst[1] = f32x4_t{u[4], u[5], u[6], u[7]};
+  }
+}
+
+// The same update on `nvalid` (<= 8) consecutive stored elements of W starting
+// at (row, col0), loading W itself (any parameter dtype, any alignment).
+__device__ __forceinline__ void apply_update8(const UpdCtx& c, int64_t row, int64_t col0, int nvalid,
+                                              const float* x) {
+  if (nvalid <= 0) return;
+  const int64_t off = row * c.cols + col0;
+  const float sc = c.s, lr = c.lr, wd = c.wd;
+  const int dt = c.pdtype;
+  if (c.vec && nvalid == 8) {
+    if (dt == kBF16) {
+      apply_update8_bf16(c, off, *(GLOBAL_AS const u32x4_t*)(static_cast<const uint16_t*>(c.w) + off), x);
+      return;
     }
+    typedef float f32x4_t __attribute__((ext_vector_type(4)));
+    GLOBAL_AS f32x4_t* src = (GLOBAL_AS f32x4_t*)(static_cast<float*>(c.w) + off);
+    const f32x4_t a = src[0], b = src[1];
+    float w[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]}, u[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       u[e] = -lr * (wd * w[e] + sc * x[e]);
       w[e] = w[e] + u[e];
     }
-    if (dt == kBF16) {
-      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(D.w) + off) =
-          make_uint4(pack_bf16x2(w[0], w[1]), pack_bf16x2(w[2], w[3]), pack_bf16x2(w[4], w[5]),
-                     pack_bf16x2(w[6], w[7]));
-    } else {
-      float4* dst = reinterpret_cast<float4*>(static_cast<float*>(D.w) + off);
-      dst[0] = make_float4(w[0], w[1], w[2], w[3]);
-      dst[1] = make_float4(w[4], w[5], w[6], w[7]);
-    }
-    if (D.upd) {
-      float4* dst = reinterpret_cast<float4*>(D.upd + off);
-      dst[0] = make_float4(u[0], u[1], u[2], u[3]);
-      dst[1] = make_float4(u[4], u[5], u[6], u[7]);
+    src[0] = f32x4_t{w[0], w[1], w[2], w[3]};
+    src[1] = f32x4_t{w[4], w[5], w[6], w[7]};
+    if (c.upd) {
+      GLOBAL_AS f32x4_t* dst = (GLOBAL_AS f32x4_t*)(c.upd + off);
+      dst[0] = f32x4_t{u[0], u[1], u[2], u[3]};
+      dst[1] = f32x4_t{u[4], u[5], u[6], u[7]};
     }
     return;
   }
   for (int e = 0; e < nvalid; ++e) {
-    const float w = load1(D.w, dt, off + e);
+    const float w = load1(c.w, dt, off + e);
     const float u = -lr * (wd * w + sc * x[e]);
-    store1(D.w, dt, off + e, w + u);
-    if (D.upd) D.upd[off + e] = u;
+    store1(c.w, dt, off + e, w + u);
+    if (c.upd) c.upd[off + e] = u;
   }
 }
 
@@ -695,6 +718,14 @@ __device__ __forceinline__ void nt_epilogue(const nt::f32x16_t (&acc)[BM / 32 / 
   const bool fuse = p.fuse != 0, ftrans = fuse && nmp->trans;
   const bool colpass = mirror || OutT != nullptr || ftrans;
   const int m_pad = nmp->m_pad;
+  UpdCtx uc = {nullptr, nullptr, 0, 0.f, 0.f, 0.f, 0, 0};
+  if (fuse) {
+    const EwDyn* d = p.dyn + nmp->dyn;
+    uc = UpdCtx{d->w, d->upd, nmp->cols, nmp->s, p.lr, p.wd, nmp->pdtype, d->vec};
+  }
+  // the update's W runs are loaded ahead when they are aligned bf16 runs
+  const bool wvec = fuse && uc.pdtype == kBF16 && uc.vec;
+  const bool wrow = wvec && !ftrans, wcol = wvec && ftrans;
   __syncthreads();   // every wave is done with the main loop's LDS
 #pragma unroll 1
   for (int s0 = 0; s0 < BM; s0 += SH) {
@@ -714,7 +745,8 @@ __device__ __forceinline__ void nt_epilogue(const nt::f32x16_t (&acc)[BM / 32 / 
       }
     __syncthreads();
     // row pass: this thread's SH / RPP rows, 8 columns each; Cin for all of
-    // them is requested before any is used
+    // them (or, for an update applied here, the bf16 W rows) is requested
+    // before any is used
     constexpr int RPT = SH / RPP;
     static_assert(SH % RPP == 0, "rows per thread");
     const int c = (tid % TPR) * 8, r_first = tid / TPR;
@@ -725,6 +757,14 @@ __device__ __forceinline__ void nt_epilogue(const nt::f32x16_t (&acc)[BM / 32 / 
       for (int t = 0; t < RPT; ++t)
         craw[t] = *(GLOBAL_AS const u32x4_t*)(static_cast<const uint16_t*>(Cin) +
                                               (int64_t)(m0 + s0 + r_first + t * RPP) * ldo + j);
+    } else if (wrow) {
+#pragma unroll
+      for (int t = 0; t < RPT; ++t) {
+        const int i = m0 + s0 + r_first + t * RPP;
+        if (i < Mr && j + 8 <= Nr)
+          craw[t] = *(GLOBAL_AS const u32x4_t*)(static_cast<const uint16_t*>(uc.w) +
+                                                (int64_t)i * uc.cols + j);
+      }
     }
 #pragma unroll
     for (int t = 0; t < RPT; ++t) {
@@ -747,7 +787,8 @@ __device__ __forceinline__ void nt_epilogue(const nt::f32x16_t (&acc)[BM / 32 / 
         st8<TO>(Out, (int64_t)i * ldo + j, v);
       } else if (!ftrans && i < Mr) {
         const int nv = Nr - j;
-        apply_update8(p, nmp, i, j, nv < 8 ? nv : 8, v);
+        if (wrow && nv >= 8) apply_update8_bf16(uc, (int64_t)i * uc.cols + j, craw[t], v);
+        else apply_update8(uc, i, j, nv < 8 ? nv : 8, v);
       }
       if (colpass) {
 #pragma unroll
@@ -756,8 +797,11 @@ __device__ __forceinline__ void nt_epilogue(const nt::f32x16_t (&acc)[BM / 32 / 
     }
     if (colpass) {
       __syncthreads();
-#pragma unroll 1
-      for (int wi = tid; wi < BN * (SH / 8); wi += NT) {
+      // every thread takes CI (column, 8-row group) items
+      constexpr int CI = BN * (SH / 8) / NT;
+      static_assert(BN * (SH / 8) % NT == 0 && CI % 2 == 0, "column items per thread");
+      auto item = [&](int ci, bool have_w, u32x4_t wq) {
+        const int wi = tid + ci * NT;
         const int jc = wi % BN, r0 = (wi / BN) * 8;
         float v[8];
 #pragma unroll
@@ -767,8 +811,31 @@ __device__ __forceinline__ void nt_epilogue(const nt::f32x16_t (&acc)[BM / 32 / 
         if (mirror) st8<TO>(Out, (int64_t)j * ldo + i0, v);
         if (ftrans && j < Nr) {
           const int nv = Mr - i0;
-          apply_update8(p, nmp, j, i0, nv < 8 ? nv : 8, v);
+          if (have_w && nv >= 8) apply_update8_bf16(uc, (int64_t)j * uc.cols + i0, wq, v);
+          else apply_update8(uc, j, i0, nv < 8 ? nv : 8, v);
         }
+      };
+      if (wcol) {
+        // the update of a tall matrix: items in pairs, both bf16 W runs
+        // requested before either is used
+        auto wrun = [&](int ci) {
+          const int wi = tid + ci * NT;
+          const int j = n0 + wi % BN, i0 = m0 + s0 + (wi / BN) * 8;
+          u32x4_t q = {0, 0, 0, 0};
+          if (j < Nr && i0 + 8 <= Mr)
+            q = *(GLOBAL_AS const u32x4_t*)(static_cast<const uint16_t*>(uc.w) +
+                                            (int64_t)j * uc.cols + i0);
+          return q;
+        };
+#pragma unroll 1
+        for (int ci = 0; ci < CI; ci += 2) {
+          const u32x4_t q0 = wrun(ci), q1 = wrun(ci + 1);
+          item(ci, true, q0);
+          item(ci + 1, true, q1);
+        }
+      } else {
+#pragma unroll 1
+        for (int ci = 0; ci < CI; ++ci) item(ci, false, u32x4_t{0, 0, 0, 0});
       }
     }
     __syncthreads();   // the slab buffer is reused

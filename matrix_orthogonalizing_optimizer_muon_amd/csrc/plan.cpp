@@ -423,8 +423,8 @@ uint64_t fnv1a(const std::string& s) {
   return h;
 }
 
-std::map<ShapeKey, ShapeChoice> read_cache(const std::string& path, const std::string& device_tag) {
-  std::map<ShapeKey, ShapeChoice> out;
+TuneCache read_cache(const std::string& path, const std::string& device_tag) {
+  TuneCache out;
   if (path.empty()) return out;
   std::ifstream f(path);
   std::string line;
@@ -436,33 +436,43 @@ std::map<ShapeKey, ShapeChoice> read_cache(const std::string& path, const std::s
     ShapeChoice c;
     c.form = -1;
     c.tile = -1;
-    std::string kv;
-    bool bad = false;
+    std::string set, kv;
+    bool bad = false, have_tile = false;
     while (is >> kv) {
       const size_t eq = kv.find('=');
       if (eq == std::string::npos) { bad = true; break; }
       const std::string key = kv.substr(0, eq), val = kv.substr(eq + 1);
+      if (key == "set") {
+        set = val;
+        continue;
+      }
       char* end = nullptr;
       const double v = std::strtod(val.c_str(), &end);
-      if (!end || *end) { bad = true; break; }
+      if (val.empty() || !end || *end) { bad = true; break; }
       if (key == "m") k.m = (int64_t)v;
       else if (key == "n") k.n = (int64_t)v;
       else if (key == "path") k.path = (int32_t)v;
       else if (key == "form") c.form = (int32_t)v;
-      else if (key == "tile") c.tile = (int32_t)v;
+      else if (key == "tile") { c.tile = (int32_t)v; have_tile = true; }
       else if (key == "us") c.us = v;
     }
-    if (bad || k.m < 1 || k.n < k.m || (k.path != 0 && k.path != 1)) continue;
+    if (bad) continue;
+    if (!set.empty()) {
+      if (set.size() != 16 || set.find_first_not_of("0123456789abcdef") != std::string::npos) continue;
+      if (!have_tile || c.tile < -1 || c.tile >= num_tile_plans()) continue;
+      out.sets[set] = SetChoice{c.tile, c.us};
+      continue;
+    }
+    if (k.m < 1 || k.n < k.m || (k.path != 0 && k.path != 1)) continue;
     if ((c.form != kFormDirect && c.form != kFormGram) || c.tile < 0 || c.tile >= num_tile_plans()) continue;
     if (k.path == 0 && c.tile != 0) continue;
     c.timed = true;
-    out[k] = c;
+    out.shapes[k] = c;
   }
   return out;
 }
 
-bool write_cache(const std::string& path, const std::string& device_tag,
-                 const std::map<ShapeKey, ShapeChoice>& entries) {
+bool write_cache(const std::string& path, const std::string& device_tag, const TuneCache& entries) {
   if (path.empty()) return false;
   // keep other devices' lines, replace this device's
   std::vector<std::string> keep;
@@ -481,16 +491,35 @@ bool write_cache(const std::string& path, const std::string& device_tag,
     std::ofstream f(tmp, std::ios::trunc);
     if (!f) return false;
     for (const std::string& l : keep) f << l << "\n";
-    for (const auto& kv : entries) {
-      char buf[256];
+    char buf[256];
+    for (const auto& kv : entries.shapes) {
       snprintf(buf, sizeof buf, "muon-tune-v2 %s m=%lld n=%lld path=%d form=%d tile=%d us=%.3f\n",
                device_tag.c_str(), (long long)kv.first.m, (long long)kv.first.n, kv.first.path,
                kv.second.form, kv.second.tile, kv.second.us);
       f << buf;
     }
+    for (const auto& kv : entries.sets) {
+      snprintf(buf, sizeof buf, "muon-tune-v2 %s set=%s tile=%d us=%.3f\n", device_tag.c_str(),
+               kv.first.c_str(), kv.second.tile, kv.second.us);
+      f << buf;
+    }
     if (!f) return false;
   }
   return std::rename(tmp.c_str(), path.c_str()) == 0;
+}
+
+std::string set_key(const std::map<ShapeKey, int>& counts,
+                    const std::map<ShapeKey, ShapeChoice>& choices) {
+  std::ostringstream o;
+  for (const auto& kv : counts) {
+    const auto it = choices.find(kv.first);
+    o << kv.first.m << "," << kv.first.n << "," << kv.first.path << "," << kv.second << ","
+      << (it == choices.end() ? -1 : it->second.form) << "," << (it == choices.end() ? -1 : it->second.tile)
+      << ";";
+  }
+  char buf[17];
+  snprintf(buf, sizeof buf, "%016llx", (unsigned long long)fnv1a(o.str()));
+  return buf;
 }
 
 void plan_flops(const PlanHost& p, int T, double* min_flops, double* issued_flops) {

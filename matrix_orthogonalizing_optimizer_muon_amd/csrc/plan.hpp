@@ -165,10 +165,27 @@ uint64_t fnv1a(const std::string& s);
 // Workspace bytes of one matrix of the given key/form/tile (as laid out by build_plan).
 uint64_t matrix_ws_bytes(const ShapeKey& k, int32_t form, int32_t tile);
 
-// Tune cache: one line per key; unknown or malformed lines are ignored.
-std::map<ShapeKey, ShapeChoice> read_cache(const std::string& path, const std::string& device_tag);
-bool write_cache(const std::string& path, const std::string& device_tag,
-                 const std::map<ShapeKey, ShapeChoice>& entries);
+// Whole-set choice: one tile plan for every bf16 direct-form shape of a
+// matrix set (-1: the per-shape choices stand).
+struct SetChoice {
+  int32_t tile = -1;
+  double us = 0;   // measured NS time of the whole set
+};
+
+// Tune cache: one line per shape key and one per matrix set (keyed by
+// set_key of the set's per-shape choices); unknown or malformed lines are
+// ignored.
+struct TuneCache {
+  std::map<ShapeKey, ShapeChoice> shapes;
+  std::map<std::string, SetChoice> sets;
+};
+TuneCache read_cache(const std::string& path, const std::string& device_tag);
+bool write_cache(const std::string& path, const std::string& device_tag, const TuneCache& entries);
+
+// Key of a matrix set: hex FNV-1a of its shape keys, their counts and their
+// per-shape choices.
+std::string set_key(const std::map<ShapeKey, int>& counts,
+                    const std::map<ShapeKey, ShapeChoice>& choices);
 
 // Per-step flops of the plan at ns_steps T: symmetric-aware minimum and issued by the tiles.
 void plan_flops(const PlanHost& p, int ns_steps, double* min_flops, double* issued_flops);

@@ -125,6 +125,42 @@ def test_forced_forms_and_cost_model():
     assert r.matrix_choice(0)["form"] == "direct"
 
 
+def _set_key(entries):
+    """Key of a matrix set in the tune cache: FNV-1a (64-bit) of
+    "m,n,path,count,form,tile;" per canonical shape key, keys in (path, m, n) order."""
+    text = "".join(f"{m},{n},{p},{c},{f},{t};" for (p, m, n, c, f, t) in sorted(entries))
+    h = 1469598103934665603
+    for b in text.encode():
+        h = ((h ^ b) * 1099511628211) % (1 << 64)
+    return f"{h:016x}"
+
+
+def test_tune_cache_set_line_gives_every_direct_shape_one_tile_plan(tmp_path):
+    shapes = [(3072, 1024), (1024, 3072), (1024, 1024), (1024, 1024), (4096, 1024)]
+    shape_lines = ("muon-tune-v2 host m=1024 n=1024 path=1 form=1 tile=0 us=1\n"
+                   "muon-tune-v2 host m=1024 n=3072 path=1 form=1 tile=0 us=1\n"
+                   "muon-tune-v2 host m=1024 n=4096 path=1 form=1 tile=1 us=1\n")
+    key = _set_key([(1, 1024, 1024, 2, 1, 0), (1, 1024, 3072, 2, 1, 0), (1, 1024, 4096, 1, 1, 1)])
+    other = _set_key([(1, 1024, 1024, 2, 1, 0)])
+    path = tmp_path / "tune.txt"
+    path.write_text(shape_lines)
+    per_shape = _host(shapes, cache_path=str(path))
+    assert [per_shape.matrix_choice(i)["tile"] for i in range(5)] == [0, 0, 0, 0, 1]
+    path.write_text(shape_lines + f"muon-tune-v2 host set={key} tile=2 us=5\n")
+    p = _host(shapes, cache_path=str(path))
+    assert [p.matrix_choice(i)["tile"] for i in range(5)] == [2] * 5
+    # -1 keeps the per-shape choices; other sets, bad keys and bad tiles are ignored
+    for line in (f"set={key} tile=-1 us=5", f"set={other} tile=2 us=5", f"set={key[:-1]} tile=2 us=5",
+                 f"set={key.upper()} tile=2 us=5", f"set={key} tile=9 us=5", f"set={key} us=5"):
+        path.write_text(shape_lines + f"muon-tune-v2 host {line}\n")
+        q = _host(shapes, cache_path=str(path))
+        assert q.serialize() == per_shape.serialize(), line
+    # a forced tile plan ignores the set line
+    path.write_text(shape_lines + f"muon-tune-v2 host set={key} tile=2 us=5\n")
+    f = _host(shapes, cache_path=str(path), tile=1)
+    assert [f.matrix_choice(i)["tile"] for i in range(5)] == [1] * 5
+
+
 def test_tune_cache_is_read_and_bad_lines_ignored(tmp_path):
     path = tmp_path / "tune.txt"
     path.write_text(
