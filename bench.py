@@ -34,6 +34,7 @@ def parse():
     ap.add_argument("--tune", default="once", choices=["off", "once", "force"])
     ap.add_argument("--form", default="auto", choices=["auto", "direct", "gram"])
     ap.add_argument("--tile", type=int, default=None, help="force a tile plan (0..4)")
+    ap.add_argument("--lanes", type=int, default=None, help="force the NS lane count (1..4)")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run 2 steps and a 1 GiB device copy (for rocprofv3 --pmc passes), print nothing")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -205,7 +206,7 @@ def main():
     os.makedirs(os.path.dirname(args.cache), exist_ok=True)
     t0 = time.perf_counter()
     plan = MU.MuonPlan(wl.shapes, wl.dtype, tune=args.tune, cache_path=args.cache, form=args.form,
-                       tile=args.tile)
+                       tile=args.tile, lanes=args.lanes)
     plan_s = time.perf_counter() - t0
     info = plan.info()
     choices = {}
@@ -319,6 +320,7 @@ def main():
                      "launches_per_step": k["launches"] / args.steps,
                      "ms_per_step": round(k["total_ms"] / args.steps, 4)} for k in kt],
         "plan": {"choices": choices, "groups": info["n_groups"], "chunks": info["n_chunks"], "gram": info["n_gram"],
+                 "lanes": info["n_lanes"],
                  "workspace_gb": round(info["workspace_bytes"] / 1e9, 3),
                  "create_s": round(plan_s, 3), "hash": info["plan_hash"]},
         "wall_s_timed": round(wall, 3),

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define MUON_ABI_VERSION 2
+#define MUON_ABI_VERSION 3
 
 typedef enum muon_status {
   MUON_OK = 0,
@@ -96,6 +96,11 @@ typedef struct muon_plan_opts {
   int32_t tune;                 /* muon_tune, default ONCE (OFF when no cache path is known) */
   int32_t host_only;            /* 1: plan on the host only - no device, no workspace, no
                                    timing; muon_step refuses such a plan (planner tests) */
+  int32_t lanes;                /* concurrent NS lanes per chunk: the chunk's matrices are cut
+                                   into this many runs of about equal work whose NS stages go
+                                   to their own streams (forked from and joined back into the
+                                   caller's stream).  0 (default): 1, or the count the
+                                   whole-set timing picks when tuning; 1..4: forced */
   uint64_t workspace_cap_bytes; /* 0: default (48 GiB).  Matrices are processed in chunks
                                    whose workspace fits the cap; one matrix over it: ENOMEM */
   const char* cache_path;       /* tune cache file; NULL: $MUON_TUNE_CACHE, else no cache */
@@ -114,6 +119,8 @@ typedef struct muon_plan_info {
   double ns_flops_issued;     /* per step at T = 5: flops the chosen tiles actually issue */
   double ew_bytes;            /* per step: algorithmic HBM bytes of the elementwise kernels */
   uint64_t plan_hash;         /* FNV-1a of the canonical serialization */
+  int32_t n_lanes;            /* concurrent NS lanes per chunk (muon_plan_opts.lanes) */
+  int32_t reserved;
 } muon_plan_info;
 
 /* Per-kernel timing collected while profiling is on (see muon_plan_set_profiling):
@@ -197,15 +204,18 @@ int muon_plan_info_get(const muon_plan* plan, muon_plan_info* info);
 
 /*
  * Per-matrix decision: form (muon_form DIRECT or GRAM), tile plan (see
- * muon_plan_opts.tile; 0 on the fp32 path), group index and chunk index of
- * matrix i.  Any out pointer may be NULL.  EINVAL: NULL plan or i out of range.
+ * muon_plan_opts.tile; 0 on the fp32 path), group index, chunk index and NS
+ * lane (0 .. n_lanes-1; lane 0 runs on the caller's stream) of matrix i.  Any
+ * out pointer may be NULL.  EINVAL: NULL plan or i out of range.
  */
 int muon_plan_matrix_choice(const muon_plan* plan, int i, int32_t* form, int32_t* tile,
-                            int32_t* group, int32_t* chunk);
+                            int32_t* group, int32_t* chunk, int32_t* lane);
 
 /*
  * Profiling: while enabled, muon_step records a hipEvent pair around each
- * kernel launch on the step's stream.  muon_plan_get_kernel_times synchronizes,
+ * kernel launch on the stream it is launched on (the step's stream or an NS
+ * lane's; concurrent lanes share the GPU, so their pairs overlap in time).
+ * muon_plan_get_kernel_times synchronizes,
  * folds the recorded pairs into per-(stage, kernel) totals, sorted by stage then
  * kernel name, and writes up to max entries to out (host array), the count to
  * *n_out.  reset != 0 clears the totals after.

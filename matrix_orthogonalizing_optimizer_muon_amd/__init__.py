@@ -37,7 +37,7 @@ class MuonPlan:
 
     def __init__(self, shapes, dtypes, *, nesterov=True, eps=1e-7, rms_scale=0.2,
                  precision="auto", form="auto", tile=None, tune="once", cache_path=None,
-                 workspace_cap=0, host_only=False):
+                 workspace_cap=0, host_only=False, lanes=None):
         lib = L.lib()
         shapes = [(int(r), int(c)) for r, c in shapes]
         if isinstance(dtypes, (list, tuple)):
@@ -62,6 +62,7 @@ class MuonPlan:
         opts.tile = -1 if tile is None else int(tile)
         opts.tune = L.TUNE[tune]
         opts.host_only = 1 if host_only else 0
+        opts.lanes = 0 if lanes is None else int(lanes)
         opts.workspace_cap_bytes = int(workspace_cap)
         self._cache = cache_path.encode() if cache_path else None
         opts.cache_path = self._cache
@@ -192,11 +193,11 @@ class MuonPlan:
         return {k: getattr(i, k) for k, _ in L.PlanInfo._fields_}
 
     def matrix_choice(self, i):
-        f, t, g, c = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        f, t, g, c, ln = (ctypes.c_int32() for _ in range(5))
         L.check(L.lib().muon_plan_matrix_choice(self._h, int(i), ctypes.byref(f), ctypes.byref(t),
-                                                ctypes.byref(g), ctypes.byref(c)))
+                                                ctypes.byref(g), ctypes.byref(c), ctypes.byref(ln)))
         return {"form": {1: "direct", 2: "gram"}[f.value], "tile": t.value, "group": g.value,
-                "chunk": c.value}
+                "chunk": c.value, "lane": ln.value}
 
     def set_profiling(self, enable=True):
         L.check(L.lib().muon_plan_set_profiling(self._h, 1 if enable else 0))

@@ -28,6 +28,7 @@ class PlanOpts(ctypes.Structure):
                 ("precision", ctypes.c_int32), ("form", ctypes.c_int32),
                 ("tile", ctypes.c_int32),
                 ("tune", ctypes.c_int32), ("host_only", ctypes.c_int32),
+                ("lanes", ctypes.c_int32),
                 ("workspace_cap_bytes", ctypes.c_uint64), ("cache_path", ctypes.c_char_p)]
 
 
@@ -36,7 +37,8 @@ class PlanInfo(ctypes.Structure):
                 ("n_chunks", ctypes.c_int32), ("n_gram", ctypes.c_int32),
                 ("workspace_bytes", ctypes.c_uint64), ("ns_flops_min", ctypes.c_double),
                 ("ns_flops_issued", ctypes.c_double), ("ew_bytes", ctypes.c_double),
-                ("plan_hash", ctypes.c_uint64)]
+                ("plan_hash", ctypes.c_uint64), ("n_lanes", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 class KernelTime(ctypes.Structure):
@@ -69,6 +71,7 @@ PROTOTYPES = {
                                            ctypes.POINTER(ctypes.c_size_t)]),
     "muon_plan_info_get": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(PlanInfo)]),
     "muon_plan_matrix_choice": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int,
+                                               ctypes.POINTER(ctypes.c_int32),
                                                ctypes.POINTER(ctypes.c_int32),
                                                ctypes.POINTER(ctypes.c_int32),
                                                ctypes.POINTER(ctypes.c_int32),

@@ -43,6 +43,7 @@ struct Items {
 
 struct SetDev {
   int path = 0, form = kFormDirect;
+  int lane = 0;
   int nmats = 0;
   NsMat* mats = nullptr;
   Items nt_sym[kNumNtCfgs], nt_full[kNumNtCfgs], old_sym, old_full;
@@ -77,6 +78,7 @@ struct ChunkDev {
   bool all_fused = false;     // every matrix's update is applied by its last NS product
   double bytes_apply_unfused = 0;   // k_ew_apply bytes when fused matrices are skipped
   std::vector<SetDev> sets;
+  int n_lanes = 1;
 };
 
 // Kernel symbol labels for the profiling records (one per template instance).
@@ -118,6 +120,11 @@ struct muon_plan {
   std::vector<void*> dev_allocs;
   std::vector<void*> host_allocs;
   std::vector<ChunkDev> chunks;
+  // NS lanes 1 .. lanes-1: a stream each (default priority, non-blocking) and
+  // the events that fork them from and join them into the caller's stream
+  std::vector<hipStream_t> lane_streams;
+  std::vector<hipEvent_t> lane_join;
+  hipEvent_t lane_fork = nullptr;
   std::vector<float*> capture;
   bool profiling = false;
   std::vector<ProfRec> recs;
@@ -159,6 +166,12 @@ void free_plan_memory(muon_plan* p) {
     (void)hipEventDestroy(r.b);
   }
   for (hipEvent_t e : p->ev_pool) (void)hipEventDestroy(e);
+  for (hipEvent_t e : p->lane_join) (void)hipEventDestroy(e);
+  if (p->lane_fork) (void)hipEventDestroy(p->lane_fork);
+  for (hipStream_t st : p->lane_streams) (void)hipStreamDestroy(st);
+  p->lane_join.clear();
+  p->lane_fork = nullptr;
+  p->lane_streams.clear();
   for (void* v : p->dev_allocs) (void)hipFree(v);
   for (void* v : p->host_allocs) (void)hipHostFree(v);
   p->dev_allocs.clear();
@@ -240,10 +253,12 @@ int materialize(muon_plan* p) {
     HIP_TRY(hipMemcpy(C.ew, ew.data(), nm * sizeof(EwMat), hipMemcpyHostToDevice));
     HIP_TRY(hipMemcpy(C.prefix, prefix.data(), nm * sizeof(int64_t), hipMemcpyHostToDevice));
     HIP_TRY(hipEventCreateWithFlags(&C.upload_ev, hipEventDisableTiming));
+    C.n_lanes = CP.n_lanes;
     for (const LaunchSetPlan& S : CP.sets) {
       SetDev D;
       D.path = S.path;
       D.form = S.form;
+      D.lane = S.lane;
       D.nmats = (int)S.mats.size();
       std::vector<NsMat> nsm(S.mats.size());
       for (size_t k = 0; k < S.mats.size(); ++k) {
@@ -284,6 +299,17 @@ int materialize(muon_plan* p) {
           return rc;
       if ((rc = upload(S.old_sym, &D.old_sym)) || (rc = upload(S.old_full, &D.old_full))) return rc;
       C.sets.push_back(D);
+    }
+  }
+  if (H.lanes > 1) {
+    HIP_TRY(hipEventCreateWithFlags(&p->lane_fork, hipEventDisableTiming));
+    for (int l = 1; l < H.lanes; ++l) {
+      hipStream_t st = nullptr;
+      hipEvent_t ev = nullptr;
+      HIP_TRY(hipStreamCreateWithFlags(&st, hipStreamNonBlocking));
+      p->lane_streams.push_back(st);
+      HIP_TRY(hipEventCreateWithFlags(&ev, hipEventDisableTiming));
+      p->lane_join.push_back(ev);
     }
   }
   return MUON_OK;
@@ -483,6 +509,30 @@ int enqueue_ns(muon_plan* p, const SetDev& S, int T, const float* sched, const E
   return MUON_OK;
 }
 
+// The NS stages of a chunk: with one lane all sets go to s; with more, lanes
+// 1.. run on their own streams, forked from s before and joined into s after.
+int enqueue_chunk_ns(muon_plan* p, const ChunkDev& C, int T, const float* sched, const EwDyn* dyn,
+                     float lr, float wd, hipStream_t s) {
+  int rc;
+  const int L = std::min<int>(C.n_lanes, (int)p->lane_streams.size() + 1);
+  if (T <= 0 || L <= 1) {
+    for (const SetDev& S : C.sets)
+      if ((rc = enqueue_ns(p, S, T, sched, dyn, lr, wd, s))) return rc;
+    return MUON_OK;
+  }
+  HIP_TRY(hipEventRecord(p->lane_fork, s));
+  for (int l = 1; l < L; ++l) HIP_TRY(hipStreamWaitEvent(p->lane_streams[l - 1], p->lane_fork, 0));
+  for (const SetDev& S : C.sets) {
+    hipStream_t ls = S.lane == 0 ? s : p->lane_streams[S.lane - 1];
+    if ((rc = enqueue_ns(p, S, T, sched, dyn, lr, wd, ls))) return rc;
+  }
+  for (int l = 1; l < L; ++l) {
+    HIP_TRY(hipEventRecord(p->lane_join[l - 1], p->lane_streams[l - 1]));
+    HIP_TRY(hipStreamWaitEvent(s, p->lane_join[l - 1], 0));
+  }
+  return MUON_OK;
+}
+
 bool aligned16(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; }
 
 int upload_dyn(muon_plan* p, ChunkDev& C, void* const* params, const void* const* grads,
@@ -537,8 +587,7 @@ int step_impl(muon_plan* p, void* const* params, const void* const* grads, float
     if ((rc = run(p, kNorm, "k_norm", 0, 0, s, [&] {
            return launch_norm(C.ew, nm, C.partials, p->rscale, p->flags, p->host.opts.eps, s);
          }))) return rc;
-    for (const SetDev& S : C.sets)
-      if ((rc = enqueue_ns(p, S, T, sched, C.dyn, lr, wd, s))) return rc;
+    if ((rc = enqueue_chunk_ns(p, C, T, sched, C.dyn, lr, wd, s))) return rc;
     // with T >= 1 the last NS product of every bf16-path matrix applied its update
     if (T >= 1 && C.all_fused) continue;
     if ((rc = run(p, kEwApply, "k_ew_apply", 0, T >= 1 ? C.bytes_apply_unfused : C.bytes_apply, s, [&] {
@@ -587,8 +636,7 @@ int time_ns(PlanHost&& H, float* best_ms) {
   for (int rep = 0; rep < 4; ++rep) {
     (void)hipEventRecord(e0, s);
     for (const ChunkDev& C : tp.chunks)
-      for (const SetDev& S : C.sets)
-        if ((rc = enqueue_ns(&tp, S, 5, sched, nullptr, 0.f, 0.f, s))) { cleanup(); return rc; }
+      if ((rc = enqueue_chunk_ns(&tp, C, 5, sched, nullptr, 0.f, 0.f, s))) { cleanup(); return rc; }
     (void)hipEventRecord(e1, s);
     if (hipEventSynchronize(e1) != hipSuccess) { cleanup(); return fail(MUON_EHIP, "tuning sync failed"); }
     float ms = 0;
@@ -643,45 +691,53 @@ int time_shape(const ShapeKey& k, const PlanOptions& base, int count,
 }
 
 // Whole-set refinement.  Shapes are timed one at a time, but a stage's launch
-// is shared by every matrix that uses the same kernel configuration for it, so
-// the plan that gives all bf16 direct-form shapes one tile plan can beat the
-// per-shape choices (fewer, fuller launches).  Each such uniform plan is timed
-// as a whole against the per-shape plan; it must be 1.5% faster to be kept
-// (whole-set timings repeat to well under 1%).
-// Returns the kept tile plan (-1: per-shape) through *tile.
+// is shared by every matrix that uses the same kernel configuration for it, and
+// lanes overlap one lane's launches with another's tails; neither shows in a
+// one-shape timing.  So the whole set is timed with the per-shape choices and
+// with every uniform tile plan (all bf16 direct-form shapes on plan t), each at
+// 1, 2 and 4 lanes (when free), and the fastest is kept; a candidate must be
+// 1.5% faster than the best so far (whole-set timings repeat to well under 1%).
 int refine_set(const std::vector<int64_t>& rows, const std::vector<int64_t>& cols,
                const std::vector<int32_t>& dts, const PlanOptions& po,
-               const std::map<ShapeKey, ShapeChoice>& choices, SetChoice* out) {
-  auto uniform = [&](int t) {
+               const std::map<ShapeKey, ShapeChoice>& choices, bool tiles_free, bool lanes_free,
+               SetChoice* out) {
+  auto with_tile = [&](int t) {
     std::map<ShapeKey, ShapeChoice> u = choices;
-    for (auto& kv : u)
-      if (kv.first.path && kv.second.form == kFormDirect) kv.second.tile = t;
+    if (t >= 0)
+      for (auto& kv : u)
+        if (kv.first.path && kv.second.form == kFormDirect) kv.second.tile = t;
     return u;
   };
-  auto time_of = [&](const std::map<ShapeKey, ShapeChoice>& ch, float* ms) -> int {
-    PlanHost H;
-    const std::string err = build_plan(rows, cols, dts, po, ch, &H);
-    if (!err.empty()) return fail(MUON_ENOMEM, "tuning: " + err);
-    return time_ns(std::move(H), ms);
-  };
-  float best = 0;
-  int rc = time_of(choices, &best);
-  if (rc) return rc;
-  out->tile = -1;
-  out->us = best * 1000.0;
-  for (int t = 0; t < num_tile_plans(); ++t) {
-    bool same = true;
-    for (const auto& kv : choices)
-      if (kv.first.path && kv.second.form == kFormDirect && kv.second.tile != t) same = false;
-    if (same) continue;
-    float ms = 0;
-    if ((rc = time_of(uniform(t), &ms))) return rc;
-    if (ms < 0.985f * best) {
-      best = ms;
-      out->tile = t;
-      out->us = ms * 1000.0;
+  std::vector<int> tiles{-1};
+  if (tiles_free)
+    for (int t = 0; t < num_tile_plans(); ++t) {
+      bool same = true;
+      for (const auto& kv : choices)
+        if (kv.first.path && kv.second.form == kFormDirect && kv.second.tile != t) same = false;
+      if (!same) tiles.push_back(t);
     }
-  }
+  std::vector<int> lanes{std::max(po.lanes, 1)};
+  if (lanes_free) lanes = {1, 2, 4};
+  bool have = false;
+  float best = 0;
+  for (int t : tiles)
+    for (int L : lanes) {
+      PlanOptions o = po;
+      o.lanes = L;
+      PlanHost H;
+      const std::string err = build_plan(rows, cols, dts, o, with_tile(t), &H);
+      if (!err.empty()) return fail(MUON_ENOMEM, "tuning: " + err);
+      float ms = 0;
+      const int rc = time_ns(std::move(H), &ms);
+      if (rc) return rc;
+      if (!have || ms < 0.985f * best) {
+        best = ms;
+        out->tile = t;
+        out->lanes = L;
+        out->us = ms * 1000.0;
+        have = true;
+      }
+    }
   return MUON_OK;
 }
 
@@ -705,6 +761,7 @@ int muon_plan_opts_default(muon_plan_opts* o) {
   o->tile = -1;
   o->tune = MUON_TUNE_ONCE;
   o->host_only = 0;
+  o->lanes = 0;
   o->workspace_cap_bytes = 0;
   o->cache_path = nullptr;
   return MUON_OK;
@@ -725,8 +782,8 @@ int muon_plan_create(const muon_matrix_desc* descs, int n, const muon_plan_opts*
   if (!(o.eps >= 0.f) || !std::isfinite(o.eps) || !(o.rms_scale > 0.f) || !std::isfinite(o.rms_scale))
     return fail(MUON_EINVAL, "eps must be >= 0 and rms_scale > 0, both finite");
   if (o.precision < 0 || o.precision > 2 || o.form < 0 || o.form > 2 || o.tune < 0 || o.tune > 2 ||
-      o.tile < -1 || o.tile >= num_tile_plans())
-    return fail(MUON_EINVAL, "precision, form, tile or tune out of range");
+      o.tile < -1 || o.tile >= num_tile_plans() || o.lanes < 0 || o.lanes > kMaxLanes)
+    return fail(MUON_EINVAL, "precision, form, tile, lanes or tune out of range");
   std::vector<int64_t> rows(n), cols(n);
   std::vector<int32_t> dts(n);
   for (int i = 0; i < n; ++i) {
@@ -749,6 +806,7 @@ int muon_plan_create(const muon_matrix_desc* descs, int n, const muon_plan_opts*
   po.form = o.form;
   po.tile = o.tile;
   po.host_only = o.host_only ? 1 : 0;
+  po.lanes = o.lanes;
   po.workspace_cap = o.workspace_cap_bytes;
   if (o.cache_path) po.cache_path = o.cache_path;
   else if (const char* env = std::getenv("MUON_TUNE_CACHE")) po.cache_path = env;
@@ -814,33 +872,37 @@ int muon_plan_create(const muon_matrix_desc* descs, int n, const muon_plan_opts*
       cache_dirty = true;
     }
   }
-  // whole-set refinement (tuned plans without a forced form or tile): the
-  // cached set choice, or a timing when the set's workspace fits 16 GiB
-  if (po.tune != MUON_TUNE_OFF && po.form == MUON_FORM_AUTO && po.tile < 0) {
+  // whole-set refinement (tuned plans; the tile plan when neither form nor tile
+  // is forced, the lane count when not forced): the cached set choice, or a
+  // timing when the set's workspace fits 16 GiB
+  {
     bool direct_bf16 = false;
     for (const auto& kv : choices) direct_bf16 |= kv.first.path && kv.second.form == kFormDirect;
-    if (direct_bf16) {
-      const std::string sk = set_key(counts, choices);
+    const bool tiles_free = po.form == MUON_FORM_AUTO && po.tile < 0 && direct_bf16;
+    const bool lanes_free = po.lanes == 0;
+    SetChoice sc;
+    sc.lanes = std::max(po.lanes, 1);
+    if (po.tune != MUON_TUNE_OFF && (tiles_free || lanes_free)) {
+      const std::string sk = set_key(counts, choices, po.lanes);
       const auto it = cache.sets.find(sk);
-      SetChoice sc;
-      bool have = false;
       if (it != cache.sets.end() && (po.tune == MUON_TUNE_ONCE || po.host_only)) {
         sc = it->second;
-        have = true;
       } else if (!po.host_only) {
         PlanHost probe;
         if (build_plan(rows, cols, dts, po, choices, &probe).empty() && probe.ws_bytes <= (16ull << 30)) {
-          const int rc = refine_set(rows, cols, dts, po, choices, &sc);
+          const int rc = refine_set(rows, cols, dts, po, choices, tiles_free, lanes_free, &sc);
           if (rc) return rc;
           cache.sets[sk] = sc;
           cache_dirty = true;
-          have = true;
         }
       }
-      if (have && sc.tile >= 0)
-        for (auto& kv : choices)
-          if (kv.first.path && kv.second.form == kFormDirect) kv.second.tile = sc.tile;
+      if (!tiles_free) sc.tile = -1;
+      if (!lanes_free) sc.lanes = std::max(po.lanes, 1);
     }
+    if (sc.tile >= 0)
+      for (auto& kv : choices)
+        if (kv.first.path && kv.second.form == kFormDirect) kv.second.tile = sc.tile;
+    po.lanes = sc.lanes;
   }
   if (cache_dirty) (void)write_cache(po.cache_path, tag, cache);
 
@@ -931,17 +993,19 @@ int muon_plan_info_get(const muon_plan* p, muon_plan_info* info) {
   plan_flops(p->host, 5, &info->ns_flops_min, &info->ns_flops_issued);
   info->ew_bytes = plan_ew_bytes(p->host);
   info->plan_hash = p->hash;
+  info->n_lanes = p->host.lanes;
   return MUON_OK;
 }
 
 int muon_plan_matrix_choice(const muon_plan* p, int i, int32_t* form, int32_t* tile, int32_t* group,
-                            int32_t* chunk) {
+                            int32_t* chunk, int32_t* lane) {
   if (!p || i < 0 || i >= (int)p->host.mats.size()) return fail(MUON_EINVAL, "bad plan or index");
   const MatPlan& M = p->host.mats[i];
   if (form) *form = M.form;
   if (tile) *tile = M.tile;
   if (group) *group = M.group;
   if (chunk) *chunk = M.chunk;
+  if (lane) *lane = M.lane;
   return MUON_OK;
 }
 

@@ -295,18 +295,39 @@ std::string build_plan(const std::vector<int64_t>& rows, const std::vector<int64
       C.mats.push_back(i);
     }
   }
+  const int32_t lanes = std::min<int32_t>(std::max<int32_t>(opts.lanes, 1), kMaxLanes);
+  P.lanes = lanes;
   for (ChunkPlan& C : P.chunks) {
     P.ws_bytes = std::max(P.ws_bytes, C.ws_bytes);
+    // lane of each matrix: the chunk's matrices in order, cut where the running
+    // NS work crosses multiples of total / lanes (by each matrix's midpoint)
+    std::vector<double> work(C.mats.size());
+    double total = 0;
+    for (size_t k = 0; k < C.mats.size(); ++k) {
+      const MatPlan& M = P.mats[C.mats[k]];
+      const double m = (double)M.m, nn = (double)M.n;
+      work[k] = nn * m * (m + 1) + m * m * (m + 1) + 2.0 * m * m * nn;
+      total += work[k];
+    }
+    double run = 0;
+    for (size_t k = 0; k < C.mats.size(); ++k) {
+      MatPlan& M = P.mats[C.mats[k]];
+      const double mid = run + 0.5 * work[k];
+      run += work[k];
+      M.lane = total > 0 ? std::min<int32_t>(lanes - 1, (int32_t)(mid * lanes / total)) : 0;
+      C.n_lanes = std::max(C.n_lanes, M.lane + 1);
+    }
     for (int32_t i : C.mats) {
       const MatPlan& M = P.mats[i];
       LaunchSetPlan* S = nullptr;
       for (LaunchSetPlan& s : C.sets)
-        if (s.path == M.path && s.form == M.form) S = &s;
+        if (s.path == M.path && s.form == M.form && s.lane == M.lane) S = &s;
       if (!S) {
         C.sets.emplace_back();
         S = &C.sets.back();
         S->path = M.path;
         S->form = M.form;
+        S->lane = M.lane;
       }
       const int32_t slot = (int32_t)S->mats.size();
       S->mats.push_back(i);
@@ -376,12 +397,14 @@ std::string serialize_plan(const PlanHost& p) {
   o << "muon-plan v3\n";
   o << "opts nesterov=" << p.opts.nesterov << " eps=" << std::hexfloat << p.opts.eps
     << " rms=" << p.opts.rms_scale << std::defaultfloat << " precision=" << p.opts.precision
-    << " form=" << p.opts.form << " tile=" << p.opts.tile << " cap=" << p.opts.workspace_cap << "\n";
+    << " form=" << p.opts.form << " tile=" << p.opts.tile << " cap=" << p.opts.workspace_cap
+    << " lanes=" << p.lanes << "\n";
   for (size_t i = 0; i < p.mats.size(); ++i) {
     const MatPlan& M = p.mats[i];
     o << "mat " << i << " " << M.rows << "x" << M.cols << " dtype=" << M.dtype << " path=" << M.path
       << " trans=" << M.trans << " pad=" << M.m_pad << "x" << M.n_pad << " form=" << M.form
-      << " tile=" << M.tile << " group=" << M.group << " chunk=" << M.chunk << " ws=" << M.ws_bytes
+      << " tile=" << M.tile << " group=" << M.group << " chunk=" << M.chunk << " lane=" << M.lane
+      << " ws=" << M.ws_bytes
       << " off=" << M.off[0] << "\n";
   }
   for (size_t g = 0; g < p.groups.size(); ++g) {
@@ -392,9 +415,9 @@ std::string serialize_plan(const PlanHost& p) {
   for (size_t c = 0; c < p.chunks.size(); ++c) {
     const ChunkPlan& C = p.chunks[c];
     o << "chunk " << c << " mats=" << C.mats.size() << " ws=" << C.ws_bytes << " ew_tiles=" << C.ew_tiles
-      << "\n";
+      << " lanes=" << C.n_lanes << "\n";
     for (const LaunchSetPlan& S : C.sets) {
-      o << " set path=" << S.path << " form=" << S.form << " mats=" << S.mats.size() << " items=";
+      o << " set path=" << S.path << " form=" << S.form << " lane=" << S.lane << " mats=" << S.mats.size() << " items=";
       for (int c = 0; c < kNtTiles; ++c) o << S.nt_sym[c].size() << "/" << S.nt_full[c].size() << ",";
       o << S.old_sym.size() << "/" << S.old_full.size() << " order=";
       uint64_t h = 1469598103934665603ull;
@@ -438,6 +461,7 @@ TuneCache read_cache(const std::string& path, const std::string& device_tag) {
     c.tile = -1;
     std::string set, kv;
     bool bad = false, have_tile = false;
+    int32_t lanes = 1;
     while (is >> kv) {
       const size_t eq = kv.find('=');
       if (eq == std::string::npos) { bad = true; break; }
@@ -454,13 +478,14 @@ TuneCache read_cache(const std::string& path, const std::string& device_tag) {
       else if (key == "path") k.path = (int32_t)v;
       else if (key == "form") c.form = (int32_t)v;
       else if (key == "tile") { c.tile = (int32_t)v; have_tile = true; }
+      else if (key == "lanes") lanes = (int32_t)v;
       else if (key == "us") c.us = v;
     }
     if (bad) continue;
     if (!set.empty()) {
       if (set.size() != 16 || set.find_first_not_of("0123456789abcdef") != std::string::npos) continue;
-      if (!have_tile || c.tile < -1 || c.tile >= num_tile_plans()) continue;
-      out.sets[set] = SetChoice{c.tile, c.us};
+      if (!have_tile || c.tile < -1 || c.tile >= num_tile_plans() || lanes < 1 || lanes > kMaxLanes) continue;
+      out.sets[set] = SetChoice{c.tile, lanes, c.us};
       continue;
     }
     if (k.m < 1 || k.n < k.m || (k.path != 0 && k.path != 1)) continue;
@@ -499,8 +524,8 @@ bool write_cache(const std::string& path, const std::string& device_tag, const T
       f << buf;
     }
     for (const auto& kv : entries.sets) {
-      snprintf(buf, sizeof buf, "muon-tune-v2 %s set=%s tile=%d us=%.3f\n", device_tag.c_str(),
-               kv.first.c_str(), kv.second.tile, kv.second.us);
+      snprintf(buf, sizeof buf, "muon-tune-v2 %s set=%s tile=%d lanes=%d us=%.3f\n",
+               device_tag.c_str(), kv.first.c_str(), kv.second.tile, kv.second.lanes, kv.second.us);
       f << buf;
     }
     if (!f) return false;
@@ -509,7 +534,7 @@ bool write_cache(const std::string& path, const std::string& device_tag, const T
 }
 
 std::string set_key(const std::map<ShapeKey, int>& counts,
-                    const std::map<ShapeKey, ShapeChoice>& choices) {
+                    const std::map<ShapeKey, ShapeChoice>& choices, int32_t forced_lanes) {
   std::ostringstream o;
   for (const auto& kv : counts) {
     const auto it = choices.find(kv.first);
@@ -517,6 +542,7 @@ std::string set_key(const std::map<ShapeKey, int>& counts,
       << (it == choices.end() ? -1 : it->second.form) << "," << (it == choices.end() ? -1 : it->second.tile)
       << ";";
   }
+  o << "lanes=" << forced_lanes;
   char buf[17];
   snprintf(buf, sizeof buf, "%016llx", (unsigned long long)fnv1a(o.str()));
   return buf;

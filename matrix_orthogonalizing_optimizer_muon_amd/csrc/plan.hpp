@@ -67,6 +67,7 @@ struct PlanOptions {
   int32_t tile = -1;      // forced tile plan, -1: chosen per shape
   int32_t tune = 0;
   int32_t host_only = 0;
+  int32_t lanes = 0;      // NS lanes per chunk; 0: 1 (build_plan) or tuned (plan creation)
   uint64_t workspace_cap = 0;
   std::string cache_path;
 };
@@ -81,6 +82,7 @@ struct MatPlan {
   int32_t tile = 0;
   int32_t group = -1;
   int32_t chunk = -1;
+  int32_t lane = 0;
   float s = 0.f;                  // RMS-matching scale
   uint64_t off[kPlanBufs] = {0};  // workspace byte offsets per buffer id (within the chunk region)
   bool has[kPlanBufs] = {false};  // buffer present
@@ -96,13 +98,14 @@ struct GroupPlan {
 
 struct ItemHost { int32_t slot, tm, tn; };
 
-// Matrices of one chunk that share (path, form): one launch per NS stage and
+// Matrices of one chunk that share (path, form, lane): one launch per NS stage and
 // kernel configuration.  On the bf16 path every NT configuration has its own
 // item lists, so matrices whose tile plans differ in one product still share
 // the launches of the other (a plan {128 sym, 256 apply} and a plan {128, 128}
 // run X X^T and A A together).
 struct LaunchSetPlan {
   int32_t path = 0, form = kFormDirect;
+  int32_t lane = 0;                        // NS lane (stream) the set's launches go to
   std::vector<int32_t> mats;               // matrix indices, in slot order
   std::vector<ItemHost> nt_sym[kNtTiles];  // upper-triangle m x m tiles per NT configuration
   std::vector<ItemHost> nt_full[kNtTiles]; // m x n tiles per NT configuration
@@ -118,8 +121,14 @@ struct LaunchSetPlan {
   double flops_square_issued_fp32 = 0;   // Gram iterates on the fp32 kernel
 };
 
+// NS lanes: a chunk's matrices (in group order) are cut into runs of about
+// equal NS work, one per lane; each lane's sets are enqueued on a stream of
+// their own, so one lane's launch fills the CUs another lane's tail leaves idle.
+constexpr int kMaxLanes = 4;
+
 struct ChunkPlan {
   std::vector<int32_t> mats;         // in group order
+  int32_t n_lanes = 1;               // lanes holding at least one matrix are 0 .. n_lanes-1
   uint64_t ws_bytes = 0;
   int64_t ew_tiles = 0;
   std::vector<LaunchSetPlan> sets;
@@ -127,6 +136,7 @@ struct ChunkPlan {
 
 struct PlanHost {
   PlanOptions opts;
+  int32_t lanes = 1;           // lanes per chunk the plan was cut for
   std::vector<MatPlan> mats;
   std::vector<GroupPlan> groups;
   std::vector<ChunkPlan> chunks;
@@ -166,9 +176,10 @@ uint64_t fnv1a(const std::string& s);
 uint64_t matrix_ws_bytes(const ShapeKey& k, int32_t form, int32_t tile);
 
 // Whole-set choice: one tile plan for every bf16 direct-form shape of a
-// matrix set (-1: the per-shape choices stand).
+// matrix set (-1: the per-shape choices stand) and the NS lane count.
 struct SetChoice {
   int32_t tile = -1;
+  int32_t lanes = 1;
   double us = 0;   // measured NS time of the whole set
 };
 
@@ -182,10 +193,10 @@ struct TuneCache {
 TuneCache read_cache(const std::string& path, const std::string& device_tag);
 bool write_cache(const std::string& path, const std::string& device_tag, const TuneCache& entries);
 
-// Key of a matrix set: hex FNV-1a of its shape keys, their counts and their
-// per-shape choices.
+// Key of a matrix set: hex FNV-1a of its shape keys, their counts, their
+// per-shape choices and the forced lane count (0: free).
 std::string set_key(const std::map<ShapeKey, int>& counts,
-                    const std::map<ShapeKey, ShapeChoice>& choices);
+                    const std::map<ShapeKey, ShapeChoice>& choices, int32_t forced_lanes);
 
 // Per-step flops of the plan at ns_steps T: symmetric-aware minimum and issued by the tiles.
 void plan_flops(const PlanHost& p, int ns_steps, double* min_flops, double* issued_flops);

@@ -28,7 +28,7 @@ def test_every_declared_function_is_exported_and_bound():
         assert hasattr(lib, n), n
         assert n in L.PROTOTYPES, f"{n} has no ctypes prototype"
     assert set(L.PROTOTYPES) == set(names)
-    assert lib.muon_abi_version() == 2
+    assert lib.muon_abi_version() == 3
 
 
 def test_struct_sizes_match_header_layout():
@@ -38,7 +38,8 @@ def test_struct_sizes_match_header_layout():
     assert L.lib().muon_plan_opts_default(ctypes.byref(opts)) == 0
     assert opts.struct_size == ctypes.sizeof(L.PlanOpts)
     assert opts.nesterov == 1 and abs(opts.eps - 1e-7) < 1e-12 and abs(opts.rms_scale - 0.2) < 1e-7
-    assert opts.tile == -1 and opts.form == 0 and opts.precision == 0
+    assert opts.tile == -1 and opts.form == 0 and opts.precision == 0 and opts.lanes == 0
+    assert ctypes.sizeof(L.PlanInfo) == 64
 
 
 def _host(shapes, dtype="bf16", **kw):
@@ -125,10 +126,12 @@ def test_forced_forms_and_cost_model():
     assert r.matrix_choice(0)["form"] == "direct"
 
 
-def _set_key(entries):
+def _set_key(entries, forced_lanes=0):
     """Key of a matrix set in the tune cache: FNV-1a (64-bit) of
-    "m,n,path,count,form,tile;" per canonical shape key, keys in (path, m, n) order."""
+    "m,n,path,count,form,tile;" per canonical shape key, keys in (path, m, n)
+    order, then "lanes=<forced lane count>"."""
     text = "".join(f"{m},{n},{p},{c},{f},{t};" for (p, m, n, c, f, t) in sorted(entries))
+    text += f"lanes={forced_lanes}"
     h = 1469598103934665603
     for b in text.encode():
         h = ((h ^ b) * 1099511628211) % (1 << 64)
@@ -149,16 +152,54 @@ def test_tune_cache_set_line_gives_every_direct_shape_one_tile_plan(tmp_path):
     path.write_text(shape_lines + f"muon-tune-v2 host set={key} tile=2 us=5\n")
     p = _host(shapes, cache_path=str(path))
     assert [p.matrix_choice(i)["tile"] for i in range(5)] == [2] * 5
-    # -1 keeps the per-shape choices; other sets, bad keys and bad tiles are ignored
+    assert p.info()["n_lanes"] == 1
+    path.write_text(shape_lines + f"muon-tune-v2 host set={key} tile=-1 lanes=2 us=5\n")
+    q = _host(shapes, cache_path=str(path))
+    assert [q.matrix_choice(i)["tile"] for i in range(5)] == [0, 0, 0, 0, 1]
+    assert q.info()["n_lanes"] == 2 and {q.matrix_choice(i)["lane"] for i in range(5)} == {0, 1}
+    # -1 keeps the per-shape choices; other sets, bad keys, tiles and lane counts are ignored
     for line in (f"set={key} tile=-1 us=5", f"set={other} tile=2 us=5", f"set={key[:-1]} tile=2 us=5",
-                 f"set={key.upper()} tile=2 us=5", f"set={key} tile=9 us=5", f"set={key} us=5"):
+                 f"set={key.upper()} tile=2 us=5", f"set={key} tile=9 us=5", f"set={key} us=5",
+                 f"set={key} tile=2 lanes=5 us=5", f"set={key} tile=2 lanes=0 us=5"):
         path.write_text(shape_lines + f"muon-tune-v2 host {line}\n")
         q = _host(shapes, cache_path=str(path))
         assert q.serialize() == per_shape.serialize(), line
-    # a forced tile plan ignores the set line
-    path.write_text(shape_lines + f"muon-tune-v2 host set={key} tile=2 us=5\n")
+    # a forced tile plan takes only the lane count of its own set line
+    path.write_text(shape_lines + f"muon-tune-v2 host set={key} tile=2 lanes=2 us=5\n")
     f = _host(shapes, cache_path=str(path), tile=1)
-    assert [f.matrix_choice(i)["tile"] for i in range(5)] == [1] * 5
+    assert [f.matrix_choice(i)["tile"] for i in range(5)] == [1] * 5 and f.info()["n_lanes"] == 1
+    fkey = _set_key([(1, 1024, 1024, 2, 1, 1), (1, 1024, 3072, 2, 1, 1), (1, 1024, 4096, 1, 1, 1)])
+    path.write_text(shape_lines + f"muon-tune-v2 host set={fkey} tile=2 lanes=4 us=5\n")
+    f = _host(shapes, cache_path=str(path), tile=1)
+    assert [f.matrix_choice(i)["tile"] for i in range(5)] == [1] * 5 and f.info()["n_lanes"] == 4
+    # forced lanes: the set line (keyed with the forced count) gives only the tile plan
+    lkey = _set_key([(1, 1024, 1024, 2, 1, 0), (1, 1024, 3072, 2, 1, 0), (1, 1024, 4096, 1, 1, 1)], 2)
+    path.write_text(shape_lines + f"muon-tune-v2 host set={lkey} tile=2 lanes=4 us=5\n")
+    g = _host(shapes, cache_path=str(path), lanes=2)
+    assert [g.matrix_choice(i)["tile"] for i in range(5)] == [2] * 5 and g.info()["n_lanes"] == 2
+
+
+def test_lanes_cut_each_chunk_into_runs_of_equal_work():
+    wl = WL.workload(2)
+    for lanes in (1, 2, 3, 4):
+        p = _host(wl.shapes, lanes=lanes)
+        assert p.info()["n_lanes"] == lanes
+        ch = [p.matrix_choice(i) for i in range(len(wl.shapes))]
+        # lanes follow the group order: sorting by (group, index) gives non-decreasing lanes
+        order = sorted(range(len(ch)), key=lambda i: (ch[i]["group"], i))
+        got = [ch[i]["lane"] for i in order]
+        assert got == sorted(got) and set(got) == set(range(lanes))
+        work = [0.0] * lanes
+        for i, (r, c) in enumerate(wl.shapes):
+            m, n = min(r, c), max(r, c)
+            work[ch[i]["lane"]] += n * m * (m + 1) + m * m * (m + 1) + 2.0 * m * m * n
+        # no lane exceeds its share by more than one matrix's work
+        biggest = max(2.0 * min(s) ** 2 * max(s) * 2 for s in wl.shapes)
+        assert max(work) <= sum(work) / lanes + biggest
+        # the plan text names every lane
+        assert f"lanes={lanes}".encode() in p.serialize()
+    with pytest.raises(M.MuonError):
+        _host(wl.shapes, lanes=5)
 
 
 def test_tune_cache_is_read_and_bad_lines_ignored(tmp_path):

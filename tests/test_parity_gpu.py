@@ -202,3 +202,51 @@ def test_bf16_gram_every_tile_plan(M, tile):
     assert all(plan.matrix_choice(i)["form"] == "gram" for i in range(len(shapes)))
     for T in (5, 1):
         run_and_compare(plan, Ws, Gs, Bs, WL.BF16, ns_steps=T)
+
+
+def _mixed_lane_state():
+    from gpu_util import make_state
+    sb = [(300, 700), (700, 300), (129, 1000), (520, 520), (200, 1500), (64, 2048)]
+    sf = [(256, 512), (96, 96)]
+    Wb, Gb, Bb = make_state(sb, WL.BF16, seed=81, buf_scale=0.01)
+    Wf, Gf, Bf = make_state(sf, WL.F32, seed=82, buf_scale=0.01)
+    return sb + sf, ["bf16"] * len(sb) + ["f32"] * len(sf), Wb + Wf, Gb + Gf, Bb + Bf
+
+
+@pytest.mark.parametrize("lanes,chunked", [(2, False), (3, False), (4, False), (2, True)])
+def test_lanes_give_bitwise_the_one_lane_result(M, lanes, chunked):
+    """NS lanes change only which stream a launch goes to: three consecutive
+    steps (bf16 direct and Gram, fp32 matrices, one or several workspace chunks)
+    leave parameters and momenta bitwise equal to the one-lane plan's."""
+    import torch
+    from gpu_util import device_state
+    shapes, dts, Ws, Gs, Bs = _mixed_lane_state()
+    cap = 0
+    if chunked:
+        cap = _plan(M, shapes, dts).info()["workspace_bytes"] // 2
+    outs = []
+    for L in (1, lanes):
+        plan = _plan(M, shapes, dts, lanes=L, workspace_cap=cap)
+        info = plan.info()
+        assert info["n_lanes"] == L and (info["n_chunks"] >= 2) == chunked
+        P, G, B = device_state(Ws, Gs, Bs)
+        for _ in range(3):
+            plan.step(P, G, B)
+        torch.cuda.synchronize()
+        assert plan.flags() == 0
+        outs.append([p.view(torch.int16).cpu().numpy().copy() if p.dtype == torch.bfloat16
+                     else p.cpu().numpy().copy() for p in P] + [b.cpu().numpy().copy() for b in B])
+        plan.close()
+    for i, (a, b) in enumerate(zip(*outs)):
+        assert np.array_equal(a, b), i
+
+
+def test_lanes_match_oracle(M):
+    from gpu_util import run_and_compare
+    shapes, dts, Ws, Gs, Bs = _mixed_lane_state()
+    plan = _plan(M, shapes, dts, lanes=4)
+    assert len({plan.matrix_choice(i)["lane"] for i in range(len(shapes))}) >= 3
+    bf = [i for i, d in enumerate(dts) if d == "bf16"]
+    f32 = [i for i, d in enumerate(dts) if d == "f32"]
+    run_and_compare(plan, Ws, Gs, Bs, WL.BF16, check=bf)
+    run_and_compare(plan, Ws, Gs, Bs, WL.F32, check=f32)
