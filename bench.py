@@ -11,6 +11,7 @@ Prints one JSON line.  `value` is the NS throughput of the whole step:
 algorithmic (symmetric-aware) NS flops per step / measured step time.
 """
 import argparse
+import re
 import json
 import os
 import sys
@@ -83,13 +84,14 @@ COPY_BYTES = 1 << 30   # bytes read and written by the calibration copy
 
 
 def demangled(label):
-    """rocprofv3's name of a kernel instance label such as k_nt<128,128,bf16>."""
+    """Pattern of rocprofv3's name of a kernel instance label such as
+    k_nt<128,128,bf16> (the template also carries the block's wave grid)."""
     base, _, args = label.partition("<")
     args = args.rstrip(">").split(",") if args else []
     conv = {"bf16": "unsigned short", "f32": "float"}
     if base == "k_nt":
-        return f"k_nt<{args[0]}, {args[1]}, {conv[args[2]]}>"
-    return base
+        return re.compile(rf"k_nt<{args[0]}, {args[1]}, \d+, \d+, {conv[args[2]]}>")
+    return re.compile(re.escape(base))
 
 
 def counter_rows(dirpath, counter):
@@ -113,11 +115,11 @@ def write_traffic(args, wl):
     for key, d, counter in (("fetch", args.traffic_from[0], "FETCH_SIZE"),
                             ("write", args.traffic_from[1], "WRITE_SIZE")):
         rows = counter_rows(d, counter)
-        kern = [v for n, v in rows if name in n]
+        kern = [v for n, v in rows if name.search(n)]
         copy = [v for n, v in rows if "elementwise_kernel" in n]
         copy = [v for v in copy if v * 1024 > COPY_BYTES / 2]
         if not kern or not copy:
-            raise SystemExit(f"{counter}: no rows for {name} or for the calibration copy in {d}")
+            raise SystemExit(f"{counter}: no rows for {name.pattern} or for the calibration copy in {d}")
         factor = COPY_BYTES / (statistics.median(copy) * 1024)
         entry[f"{key}_bytes_per_launch"] = statistics.mean(kern) * 1024 * factor
         entry[f"{key}_copy_factor"] = factor
@@ -188,6 +190,21 @@ def cpu_baseline(wl, ns_flops_per_step):
                       f"fp64 numpy, input generation excluded"}
 
 
+def union_ms(spans):
+    """Total length of the union of [start, end) intervals."""
+    total, cur_s, cur_e = 0.0, None, None
+    for a, b in sorted(spans):
+        if cur_e is None or a > cur_e:
+            if cur_e is not None:
+                total += cur_e - cur_s
+            cur_s, cur_e = a, b
+        else:
+            cur_e = max(cur_e, b)
+    if cur_e is not None:
+        total += cur_e - cur_s
+    return total
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -256,13 +273,15 @@ def main():
     p = lambda q: step_ms[min(len(step_ms) - 1, int(q * len(step_ms)))]
 
     # per-kernel HIP-event times (the library records them on the step's stream)
-    kt = []
+    kt, intervals = [], []
     if not args.no_kernel_times:
         plan.set_profiling(True)
         plan.kernel_times(reset=True)
         for _ in range(args.steps):
             step()
-        kt = plan.kernel_times(reset=True)
+        kt = plan.kernel_times(reset=False)
+        intervals = plan.launch_intervals()
+        plan.kernel_times(reset=True)
         plan.set_profiling(False)
     ns_flops = info["ns_flops_min"]
     bf16 = wl.dtype == "bf16"
@@ -286,13 +305,19 @@ def main():
         avg_ms = dom["total_ms"] / dom["launches"]
         fpl = dom["flops"] / dom["launches"]
         ach = fpl / (avg_ms * 1e-3) / 1e12
+        # with NS lanes launches of this kernel overlap: the union of their
+        # intervals is the time the kernel kept the GPU busy
+        busy_ms = union_ms([(iv["start_ms"], iv["end_ms"]) for iv in intervals if iv["kernel"] == name])
         roofline = {"bound": "mfma", "kernel": name, "stages": sorted(set(dom["stages"])),
                     "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
                     "frac": round(ach / peak, 4),
                     "traffic": traffic_for(name, wl.name, dom["launches"] / args.steps),
                     "avg_launch_us": round(avg_ms * 1e3, 2), "flops_per_launch": fpl,
                     "launches_per_step": dom["launches"] / args.steps,
-                    "share_of_step": round(dom["total_ms"] / args.steps / ms, 4)}
+                    "share_of_step": round(dom["total_ms"] / args.steps / ms, 4),
+                    "lanes": info["n_lanes"],
+                    "busy_ms_per_step": round(busy_ms / args.steps, 4),
+                    "achieved_busy": round(dom["flops"] / (busy_ms * 1e-3) / 1e12, 2) if busy_ms else None}
     ew = {}
     for n, d in ew_kern.items():
         avg_ms = d["total_ms"] / d["launches"]

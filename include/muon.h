@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define MUON_ABI_VERSION 3
+#define MUON_ABI_VERSION 4
 
 typedef enum muon_status {
   MUON_OK = 0,
@@ -134,6 +134,14 @@ typedef struct muon_kernel_time {
   double bytes;         /* summed algorithmic HBM bytes of those launches */
 } muon_kernel_time;
 
+/* One profiled launch: its hipEvent pair as times from the first launch
+ * recorded since profiling was enabled or the totals were last reset. */
+typedef struct muon_launch_interval {
+  char name[32];        /* stage */
+  char kernel[32];      /* kernel instance */
+  double start_ms, end_ms;
+} muon_launch_interval;
+
 /* Fills *opts with the defaults listed above.  NULL: EINVAL. */
 int muon_plan_opts_default(muon_plan_opts* opts);
 
@@ -218,11 +226,17 @@ int muon_plan_matrix_choice(const muon_plan* plan, int i, int32_t* form, int32_t
  * muon_plan_get_kernel_times synchronizes,
  * folds the recorded pairs into per-(stage, kernel) totals, sorted by stage then
  * kernel name, and writes up to max entries to out (host array), the count to
- * *n_out.  reset != 0 clears the totals after.
+ * *n_out.  reset != 0 clears the totals (and the intervals) after.
+ * muon_plan_get_launch_intervals writes, in launch order, up to max of the
+ * launches folded so far (by muon_plan_get_kernel_times) to out and their
+ * count to *n_out: with NS lanes, the union of a kernel's intervals is the time
+ * it kept the GPU busy.
  */
 int muon_plan_set_profiling(muon_plan* plan, int enable);
 int muon_plan_get_kernel_times(muon_plan* plan, muon_kernel_time* out, int max, int* n_out,
                                int reset);
+int muon_plan_get_launch_intervals(const muon_plan* plan, muon_launch_interval* out, int max,
+                                   int* n_out);
 
 /* Thread-local text of the last error on this thread ("" if none).  Never NULL. */
 const char* muon_last_error(void);

@@ -202,6 +202,14 @@ class MuonPlan:
     def set_profiling(self, enable=True):
         L.check(L.lib().muon_plan_set_profiling(self._h, 1 if enable else 0))
 
+    def launch_intervals(self, max_n=1 << 16):
+        """Folded launches (call after kernel_times(reset=False)), in launch order."""
+        arr = (L.LaunchInterval * max_n)()
+        n = ctypes.c_int()
+        L.check(L.lib().muon_plan_get_launch_intervals(self._h, arr, max_n, ctypes.byref(n)))
+        return [{"name": arr[k].name.decode(), "kernel": arr[k].kernel.decode(),
+                 "start_ms": arr[k].start_ms, "end_ms": arr[k].end_ms} for k in range(n.value)]
+
     def kernel_times(self, reset=True):
         arr = (L.KernelTime * 64)()
         n = ctypes.c_int()

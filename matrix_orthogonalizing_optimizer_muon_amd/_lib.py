@@ -48,6 +48,11 @@ class KernelTime(ctypes.Structure):
                 ("bytes", ctypes.c_double)]
 
 
+class LaunchInterval(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 32), ("kernel", ctypes.c_char * 32),
+                ("start_ms", ctypes.c_double), ("end_ms", ctypes.c_double)]
+
+
 _PP = ctypes.POINTER(ctypes.c_void_p)
 _FP = ctypes.POINTER(ctypes.c_float)
 
@@ -80,6 +85,8 @@ PROTOTYPES = {
     "muon_plan_get_kernel_times": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(KernelTime),
                                                   ctypes.c_int, ctypes.POINTER(ctypes.c_int),
                                                   ctypes.c_int]),
+    "muon_plan_get_launch_intervals": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(LaunchInterval),
+                                                      ctypes.c_int, ctypes.POINTER(ctypes.c_int)]),
 }
 
 _lib = None

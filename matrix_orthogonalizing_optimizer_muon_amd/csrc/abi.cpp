@@ -128,6 +128,8 @@ struct muon_plan {
   std::vector<float*> capture;
   bool profiling = false;
   std::vector<ProfRec> recs;
+  hipEvent_t prof_epoch = nullptr;              // first recorded event since enable / reset
+  std::vector<muon_launch_interval> intervals;  // folded launches, in launch order
   std::vector<hipEvent_t> ev_pool;
   std::map<std::pair<int, std::string>, Totals> tot;   // (stage, kernel) -> totals
 };
@@ -166,6 +168,8 @@ void free_plan_memory(muon_plan* p) {
     (void)hipEventDestroy(r.b);
   }
   for (hipEvent_t e : p->ev_pool) (void)hipEventDestroy(e);
+  if (p->prof_epoch) (void)hipEventDestroy(p->prof_epoch);
+  p->prof_epoch = nullptr;
   for (hipEvent_t e : p->lane_join) (void)hipEventDestroy(e);
   if (p->lane_fork) (void)hipEventDestroy(p->lane_fork);
   for (hipStream_t st : p->lane_streams) (void)hipStreamDestroy(st);
@@ -1011,7 +1015,16 @@ int muon_plan_matrix_choice(const muon_plan* p, int i, int32_t* form, int32_t* t
 
 int muon_plan_set_profiling(muon_plan* p, int enable) {
   if (!p) return fail(MUON_EINVAL, "plan is NULL");
+  if (enable && !p->profiling) p->intervals.clear();
   p->profiling = enable != 0;
+  return MUON_OK;
+}
+
+int muon_plan_get_launch_intervals(const muon_plan* p, muon_launch_interval* out, int max, int* n_out) {
+  if (!p || !n_out || (max > 0 && !out)) return fail(MUON_EINVAL, "NULL argument");
+  const int n = std::min<int>((int)p->intervals.size(), std::max(max, 0));
+  for (int i = 0; i < n; ++i) out[i] = p->intervals[i];
+  *n_out = n;
   return MUON_OK;
 }
 
@@ -1021,6 +1034,21 @@ int muon_plan_get_kernel_times(muon_plan* p, muon_kernel_time* out, int max, int
     HIP_TRY(hipEventSynchronize(r.b));
     float ms = 0;
     HIP_TRY(hipEventElapsedTime(&ms, r.a, r.b));
+    if (!p->prof_epoch) {
+      // the first pair after a reset: its start event becomes the time origin
+      p->prof_epoch = r.a;
+      r.a = pool_event(p);
+      if (!r.a) return fail(MUON_EHIP, "hipEventCreate failed");
+    }
+    float t0 = 0;
+    HIP_TRY(hipEventElapsedTime(&t0, p->prof_epoch, r.b));
+    muon_launch_interval iv;
+    std::memset(&iv, 0, sizeof iv);
+    std::strncpy(iv.name, kKindNames[r.kind], sizeof(iv.name) - 1);
+    std::strncpy(iv.kernel, r.kern, sizeof(iv.kernel) - 1);
+    iv.end_ms = t0;
+    iv.start_ms = t0 - ms;
+    p->intervals.push_back(iv);
     Totals& t = p->tot[{r.kind, std::string(r.kern)}];
     t.launches++;
     t.ms += ms;
@@ -1046,7 +1074,12 @@ int muon_plan_get_kernel_times(muon_plan* p, muon_kernel_time* out, int max, int
     ++k;
   }
   *n_out = std::min(k, std::max(max, 0));
-  if (reset) p->tot.clear();
+  if (reset) {
+    p->tot.clear();
+    p->intervals.clear();
+    if (p->prof_epoch) p->ev_pool.push_back(p->prof_epoch);
+    p->prof_epoch = nullptr;
+  }
   return MUON_OK;
 }
 

@@ -28,7 +28,7 @@ def test_every_declared_function_is_exported_and_bound():
         assert hasattr(lib, n), n
         assert n in L.PROTOTYPES, f"{n} has no ctypes prototype"
     assert set(L.PROTOTYPES) == set(names)
-    assert lib.muon_abi_version() == 3
+    assert lib.muon_abi_version() == 4
 
 
 def test_struct_sizes_match_header_layout():
@@ -227,3 +227,14 @@ def test_tune_cache_is_read_and_bad_lines_ignored(tmp_path):
     # a forced form or tile never takes a cached choice that violates it
     p4 = _host([(512, 16384)], cache_path=str(path), form="direct")
     assert p4.matrix_choice(0)["form"] == "direct"
+
+
+def test_bench_busy_time_is_the_union_of_intervals():
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("bench_mod", os.path.join(ROOT, "bench.py"))
+    b = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(b)
+    assert b.union_ms([]) == 0.0
+    assert b.union_ms([(0.0, 1.0), (0.5, 2.0), (3.0, 4.0), (3.5, 3.6)]) == pytest.approx(3.0)
+    assert b.union_ms([(2.0, 3.0), (0.0, 1.0)]) == pytest.approx(2.0)
+    assert b.union_ms([(0.0, 5.0), (1.0, 2.0)]) == pytest.approx(5.0)
