@@ -36,6 +36,10 @@ def parse():
     ap.add_argument("--form", default="auto", choices=["auto", "direct", "gram"])
     ap.add_argument("--tile", type=int, default=None, help="force a tile plan (0..4)")
     ap.add_argument("--lanes", type=int, default=None, help="force the NS lane count (1..4)")
+    ap.add_argument("--owners", type=int, default=1,
+                    help="assign the workload's matrices to this many owners (makespan-balanced) "
+                         "and time one owner's share")
+    ap.add_argument("--owner-rank", type=int, default=0, help="the owner whose share is timed")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run 2 steps and a 1 GiB device copy (for rocprofv3 --pmc passes), print nothing")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -190,6 +194,29 @@ def cpu_baseline(wl, ns_flops_per_step):
                       f"fp64 numpy, input generation excluded"}
 
 
+def owner_share(args, wl, MU):
+    """The matrices one owner gets when the workload is balanced over
+    args.owners owners by estimated step time (plan costs, muon_assign_owners)."""
+    import dataclasses
+    if not 0 <= args.owner_rank < args.owners:
+        raise SystemExit("--owner-rank must be in [0, --owners)")
+    full = MU.MuonPlan(wl.shapes, wl.dtype, tune=args.tune, cache_path=args.cache, form=args.form,
+                       tile=args.tile, lanes=args.lanes)
+    costs = [full.matrix_cost(i) for i in range(wl.n_matrices)]
+    full.close()
+    owner, span, optimal = MU.assign_owners(costs, args.owners)
+    idx = [i for i, o in enumerate(owner) if o == args.owner_rank]
+    if not idx:
+        raise SystemExit(f"owner {args.owner_rank} of {args.owners} gets no matrix")
+    share = dataclasses.replace(wl, shapes=tuple(wl.shapes[i] for i in idx),
+                                name=f"{wl.name}, owner {args.owner_rank} of {args.owners}")
+    info = {"owners": args.owners, "rank": args.owner_rank, "matrices": len(idx),
+            "est_share_us": round(sum(costs[i] for i in idx), 1), "est_makespan_us": round(span, 1),
+            "est_lower_bound_us": round(max(max(costs), sum(costs) / args.owners), 1),
+            "optimal": optimal}
+    return share, info
+
+
 def union_ms(spans):
     """Total length of the union of [start, end) intervals."""
     total, cur_s, cur_e = 0.0, None, None
@@ -221,6 +248,9 @@ def main():
 
     torch.cuda.init()
     os.makedirs(os.path.dirname(args.cache), exist_ok=True)
+    owner_info = None
+    if args.owners > 1:
+        wl, owner_info = owner_share(args, wl, MU)
     t0 = time.perf_counter()
     plan = MU.MuonPlan(wl.shapes, wl.dtype, tune=args.tune, cache_path=args.cache, form=args.form,
                        tile=args.tile, lanes=args.lanes)
@@ -332,6 +362,7 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if bf16 else "f32",
         "data": "synthetic",
         "config": {"workload": wl.name, "matrices": wl.n_matrices, "elements": wl.n_elements,
+                   **({"owner": owner_info} if owner_info else {}),
                    "ns_steps": h.ns_steps, "coeffs": list(h.coeffs), "lr": h.lr, "beta": h.beta,
                    "wd": h.wd, "parallelism": "single GPU"},
         "step_ms_p10_p50_p90": [round(p(0.1), 4), round(p(0.5), 4), round(p(0.9), 4)],

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define MUON_ABI_VERSION 4
+#define MUON_ABI_VERSION 5
 
 typedef enum muon_status {
   MUON_OK = 0,
@@ -240,6 +240,33 @@ int muon_plan_get_launch_intervals(const muon_plan* plan, muon_launch_interval* 
 
 /* Thread-local text of the last error on this thread ("" if none).  Never NULL. */
 const char* muon_last_error(void);
+
+/*
+ * Estimated step time of matrix i in microseconds (*us): the NS time per
+ * matrix that its shape measured when the plan was tuned (the cost model's
+ * estimate otherwise) plus its elementwise bytes at 5 TB/s.  This is the cost
+ * muon_assign_owners balances.  EINVAL: NULL plan or us, i out of range.
+ */
+int muon_plan_matrix_cost(const muon_plan* plan, int i, double* us);
+
+/*
+ * Owner assignment (DMuon announcement (wjxwpt.net), improvement 3
+ * "computation-aware load balancing"): every item (matrix) goes to exactly
+ * one of n_owners owners so that the largest per-owner total cost (the
+ * makespan) is minimal.  Exact depth-first branch and bound seeded with the
+ * LPT schedule (largest item first, to the least-loaded owner); when the
+ * search exceeds node_limit nodes (<= 0: 2,000,000) the best schedule found is
+ * improved by moves and swaps off the most loaded owner and returned as not
+ * proven optimal.  Host-only: no device is used.
+ *   costs      host array of n finite, non-negative costs (any unit)
+ *   owner      host array of n, receives each item's owner in [0, n_owners)
+ *   makespan   nullable; receives the schedule's makespan
+ *   optimal    nullable; receives 1 if the makespan is proven minimal, else 0
+ * EINVAL: n < 0, n_owners < 1, NULL costs or owner with n > 0, a negative or
+ * non-finite cost.  Deterministic: equal inputs give equal assignments.
+ */
+int muon_assign_owners(const double* costs, int n, int n_owners, int64_t node_limit,
+                       int32_t* owner, double* makespan, int32_t* optimal);
 
 /* MUON_ABI_VERSION of the library. */
 int muon_abi_version(void);

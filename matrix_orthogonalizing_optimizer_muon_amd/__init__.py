@@ -14,7 +14,7 @@ import ctypes
 from . import _lib as L
 from ._lib import MuonError  # noqa: F401
 
-__all__ = ["MuonPlan", "MuonError", "library_path"]
+__all__ = ["MuonPlan", "MuonError", "library_path", "assign_owners"]
 
 
 def library_path():
@@ -202,6 +202,12 @@ class MuonPlan:
     def set_profiling(self, enable=True):
         L.check(L.lib().muon_plan_set_profiling(self._h, 1 if enable else 0))
 
+    def matrix_cost(self, i):
+        """Estimated step time of matrix i in microseconds (owner-assignment input)."""
+        us = ctypes.c_double()
+        L.check(L.lib().muon_plan_matrix_cost(self._h, int(i), ctypes.byref(us)))
+        return us.value
+
     def launch_intervals(self, max_n=1 << 16):
         """Folded launches (call after kernel_times(reset=False)), in launch order."""
         arr = (L.LaunchInterval * max_n)()
@@ -218,3 +224,17 @@ class MuonPlan:
                  "launches": arr[k].launches,
                  "total_ms": arr[k].total_ms, "flops": arr[k].flops, "bytes": arr[k].bytes}
                 for k in range(n.value)]
+
+
+def assign_owners(costs, n_owners, node_limit=0):
+    """Makespan-minimizing assignment of items to owners (muon_assign_owners).
+
+    Returns (owner list, makespan, proven optimal)."""
+    n = len(costs)
+    arr = (ctypes.c_double * max(n, 1))(*[float(c) for c in costs])
+    out = (ctypes.c_int32 * max(n, 1))()
+    span = ctypes.c_double()
+    opt = ctypes.c_int32()
+    L.check(L.lib().muon_assign_owners(arr, n, int(n_owners), int(node_limit), out,
+                                       ctypes.byref(span), ctypes.byref(opt)))
+    return [out[i] for i in range(n)], span.value, bool(opt.value)

@@ -12,6 +12,7 @@
 
 #include "muon.h"
 #include "kernels.hpp"
+#include "assign.hpp"
 #include "plan.hpp"
 
 using namespace muon;
@@ -1010,6 +1011,27 @@ int muon_plan_matrix_choice(const muon_plan* p, int i, int32_t* form, int32_t* t
   if (group) *group = M.group;
   if (chunk) *chunk = M.chunk;
   if (lane) *lane = M.lane;
+  return MUON_OK;
+}
+
+int muon_plan_matrix_cost(const muon_plan* p, int i, double* us) {
+  if (!p || !us || i < 0 || i >= (int)p->host.mats.size()) return fail(MUON_EINVAL, "bad plan, index or pointer");
+  *us = p->host.mats[i].cost_us;
+  return MUON_OK;
+}
+
+int muon_assign_owners(const double* costs, int n, int n_owners, int64_t node_limit, int32_t* owner,
+                       double* makespan, int32_t* optimal) {
+  g_err.clear();
+  if (n < 0 || n_owners < 1) return fail(MUON_EINVAL, "n < 0 or n_owners < 1");
+  if (n > 0 && (!costs || !owner)) return fail(MUON_EINVAL, "NULL costs or owner");
+  std::vector<double> c(costs ? costs : nullptr, costs ? costs + n : nullptr);
+  for (int i = 0; i < n; ++i)
+    if (!std::isfinite(c[i]) || c[i] < 0) return fail(MUON_EINVAL, "cost " + std::to_string(i) + " is negative or not finite");
+  const AssignResult r = assign_owners(c, n_owners, node_limit > 0 ? node_limit : 2000000);
+  for (int i = 0; i < n; ++i) owner[i] = r.owner[i];
+  if (makespan) *makespan = r.makespan;
+  if (optimal) *optimal = r.optimal ? 1 : 0;
   return MUON_OK;
 }
 

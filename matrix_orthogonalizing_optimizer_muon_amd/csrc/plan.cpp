@@ -263,11 +263,22 @@ std::string build_plan(const std::vector<int64_t>& rows, const std::vector<int64
     g.tile = kv.first.path ? it->second.tile : 0;
     g.members = kv.second;
     const int32_t gi = (int32_t)P.groups.size();
+    // estimated step time of one member: the NS time its shape measured when
+    // timed (else the cost model at the group's count) plus its elementwise
+    // bytes at 5 TB/s
+    const double ns_us = it->second.timed && it->second.us > 0
+                             ? it->second.us
+                             : model_cost_us(kv.first, g.form, g.tile, (int)g.members.size());
     for (int32_t i : g.members) {
       MatPlan& M = P.mats[i];
       M.form = g.form;
       M.tile = g.tile;
       M.group = gi;
+      {
+        const double e = (double)M.rows * M.cols, pes = M.dtype ? 2 : 4, es = M.path ? 2 : 4;
+        const double ew = e * (pes + 8 + es + (M.path ? es : 0) + 2 * pes + (M.path ? 0 : 4));
+        M.cost_us = ns_us + ew / 5e12 * 1e6;
+      }
       padded_dims(kv.first, g.form, g.tile, &M.m_pad, &M.n_pad);
       M.ws_bytes = layout(kv.first, g.form, g.tile, M.off, M.has);
       M.ew_tiles = (M.m_pad / kEw) * (M.n_pad / kEw);

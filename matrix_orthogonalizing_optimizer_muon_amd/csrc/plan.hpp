@@ -88,6 +88,7 @@ struct MatPlan {
   bool has[kPlanBufs] = {false};  // buffer present
   uint64_t ws_bytes = 0;
   int64_t ew_tiles = 0;           // 64 x 64 tiles of the padded canonical extent
+  double cost_us = 0;             // estimated step time (owner assignment input)
 };
 
 struct GroupPlan {

@@ -1,0 +1,112 @@
+"""Owner assignment (host only): the brute-force definition in the oracle is
+pinned by closed forms, and the library's solver (through the C ABI) is
+checked against it on tiny instances and against its guarantees on large ones."""
+import math
+import random
+
+import pytest
+
+import matrix_orthogonalizing_optimizer_muon_amd as M
+from matrix_orthogonalizing_optimizer_muon_amd import _lib as L
+from oracle import assign_oracle as A
+import workloads as WL
+
+
+# ---- pins of the brute-force oracle ----------------------------------------
+
+def test_oracle_closed_forms():
+    costs = [5.0, 3.0, 2.0, 7.0]
+    assert A.best_makespan(costs, 1)[0] == sum(costs)          # one owner: everything
+    assert A.best_makespan(costs, 4)[0] == max(costs)          # an owner per item
+    assert A.best_makespan(costs, 6)[0] == max(costs)
+    assert A.best_makespan([2.0] * 7, 3)[0] == 2.0 * math.ceil(7 / 3)   # equal items
+    assert A.best_makespan([], 3)[0] == 0.0
+    # the classic case where largest-first greedy is not optimal: {3,3} {2,2,2}
+    assert A.best_makespan([3.0, 3.0, 2.0, 2.0, 2.0], 2)[0] == 6.0
+    span, owner = A.best_makespan([4.0, 1.0, 1.0, 2.0], 2)
+    assert span == 4.0 and A.makespan([4.0, 1.0, 1.0, 2.0], owner, 2) == 4.0
+
+
+def test_oracle_makespan_definition():
+    assert A.makespan([1.0, 2.0, 3.0], [0, 1, 0], 2) == 4.0
+    assert A.makespan([1.0, 2.0, 3.0], [1, 1, 1], 3) == 6.0
+
+
+# ---- the library's solver ----------------------------------------------------
+
+def _check_valid(costs, owner, k, span):
+    assert len(owner) == len(costs) and all(0 <= o < k for o in owner)
+    assert span == pytest.approx(A.makespan(costs, owner, k), rel=1e-12, abs=0.0)
+
+
+def test_solver_is_exact_on_tiny_instances():
+    rng = random.Random(7)
+    for trial in range(120):
+        n = rng.randint(0, 8)
+        k = rng.randint(1, 3)
+        if rng.random() < 0.3:   # repeated shapes (equal costs), as in real matrix sets
+            costs = [float(rng.choice([1, 2, 3, 5])) for _ in range(n)]
+        else:
+            costs = [rng.uniform(0.0, 10.0) for _ in range(n)]
+        owner, span, optimal = M.assign_owners(costs, k)
+        want, _ = A.best_makespan(costs, k)
+        assert optimal, (costs, k)
+        assert span == pytest.approx(want, rel=1e-12, abs=1e-12), (costs, k)
+        _check_valid(costs, owner, k, span)
+
+
+def test_solver_beats_greedy_on_the_classic_case():
+    owner, span, optimal = M.assign_owners([3.0, 3.0, 2.0, 2.0, 2.0], 2)
+    assert optimal and span == 6.0
+
+
+def test_budget_exhausted_keeps_the_greedy_guarantee():
+    # with a one-node budget the result is the LPT schedule improved by local moves:
+    # never worse than LPT's bound (4/3 - 1/(3k)) * optimum
+    rng = random.Random(11)
+    for trial in range(60):
+        n = rng.randint(5, 8)
+        k = rng.randint(2, 3)
+        costs = [rng.uniform(1.0, 10.0) for _ in range(n)]
+        owner, span, optimal = M.assign_owners(costs, k, node_limit=1)
+        want, _ = A.best_makespan(costs, k)
+        assert span <= (4.0 / 3.0 - 1.0 / (3 * k)) * want * (1 + 1e-12)
+        _check_valid(costs, owner, k, span)
+
+
+def test_large_matrix_sets_are_balanced():
+    # every workload's matrices over 8 owners, model costs from host-only plans
+    for cfg in (2, 3, 4, 5):
+        wl = WL.workload(cfg)
+        plan = M.MuonPlan(wl.shapes, wl.dtype, host_only=True, tune="off")
+        costs = [plan.matrix_cost(i) for i in range(len(wl.shapes))]
+        assert all(c > 0 for c in costs)
+        owner, span, optimal = M.assign_owners(costs, 8)
+        _check_valid(costs, owner, 8, span)
+        lower = max(max(costs), sum(costs) / 8)
+        assert span >= lower * (1 - 1e-12)
+        # many similar items: within 5% of the lower bound (or the largest item)
+        assert span <= 1.05 * lower, (cfg, span, lower)
+        # deterministic
+        assert M.assign_owners(costs, 8) == (owner, span, optimal)
+
+
+def test_matrix_cost_grows_with_the_matrix():
+    plan = M.MuonPlan([(512, 512), (1024, 1024), (1024, 4096)], "bf16", host_only=True, tune="off")
+    c = [plan.matrix_cost(i) for i in range(3)]
+    assert c[0] < c[1] < c[2]
+
+
+def test_assign_argument_errors():
+    with pytest.raises(M.MuonError):
+        M.assign_owners([1.0, 2.0], 0)
+    with pytest.raises(M.MuonError):
+        M.assign_owners([1.0, -2.0], 2)
+    with pytest.raises(M.MuonError):
+        M.assign_owners([1.0, float("nan")], 2)
+    with pytest.raises(M.MuonError):
+        M.assign_owners([1.0, float("inf")], 2)
+    assert M.assign_owners([], 3) == ([], 0.0, True)
+    lib = L.lib()
+    assert lib.muon_assign_owners(None, 2, 2, 0, None, None, None) == L.MUON_EINVAL
+    assert lib.muon_assign_owners(None, -1, 2, 0, None, None, None) == L.MUON_EINVAL
