@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define MUON_ABI_VERSION 5
+#define MUON_ABI_VERSION 6
 
 typedef enum muon_status {
   MUON_OK = 0,
@@ -240,6 +240,27 @@ int muon_plan_get_launch_intervals(const muon_plan* plan, muon_launch_interval* 
 
 /* Thread-local text of the last error on this thread ("" if none).  Never NULL. */
 const char* muon_last_error(void);
+
+/*
+ * Newton-Schulz orthogonalization alone ("DeepSpeed now supports Muon"
+ * (setupai.cc), technical deep dive: the orthogonalization Muon applies to
+ * the update; here without momentum, scale or weight decay): for every matrix
+ * i of the plan, out_i = NS_T(M_i / (||M_i||_F + eps)) with the plan's form,
+ * tile plan and precision, in the stored orientation (a tall matrix is
+ * iterated transposed and transposed back).
+ *   inputs   host array of n device pointers, rows x cols row-major in the
+ *            matrix's plan dtype; read only
+ *   outputs  host array of n device pointers, rows x cols row-major fp32
+ *   coeffs   host, 3*ns_steps floats (a_k, b_k, c_k), one triple per step;
+ *            NULL: the quintic (3.4445, -4.7750, 2.0315) at every step
+ * ns_steps = 0 gives the normalized input.  Asynchronous on stream; it uses
+ * the plan's workspace, so it must not overlap a muon_step or another call on
+ * the same plan.  A non-finite norm sets the flag muon_plan_get_flags reads.
+ * EINVAL (NULL array or pointer, ns_steps outside [0, 64], non-finite
+ * coefficient), ESTATE (host-only plan), EHIP (launch error).
+ */
+int muon_orthogonalize(muon_plan* plan, const void* const* inputs, float* const* outputs,
+                       int ns_steps, const float* coeffs, void* stream);
 
 /*
  * Estimated step time of matrix i in microseconds (*us): the NS time per

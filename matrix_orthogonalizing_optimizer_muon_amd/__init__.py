@@ -156,6 +156,25 @@ class MuonPlan:
             carr = (ctypes.c_float * 3)(*[float(x) for x in coeffs])
         L.check(lib.muon_step(self._h, P, G, M, lr, beta, wd, int(ns_steps), carr, s))
 
+    def orthogonalize(self, inputs, outputs, ns_steps=5, coeffs=None, stream=None):
+        """NS orthogonalization alone (muon_orthogonalize): outputs[i] (fp32, the
+        input's shape) = NS_T(inputs[i] / (||inputs[i]||_F + eps)).  coeffs: None
+        (quintic), (a, b, c) for every step, or a list of ns_steps triples."""
+        dev = self._check_tensors("inputs", inputs, self.dtypes)
+        self._check_tensors("outputs", outputs, [L.MUON_F32] * len(self.shapes))
+        for i, (a, b) in enumerate(zip(inputs, outputs)):
+            if a.data_ptr() == b.data_ptr():
+                raise ValueError(f"matrix {i}: output aliases input")
+        sched = None
+        if coeffs is not None:
+            rows = coeffs if len(coeffs) and isinstance(coeffs[0], (list, tuple)) else [coeffs] * ns_steps
+            if len(rows) != ns_steps or any(len(r) != 3 for r in rows):
+                raise ValueError("coeffs must be (a, b, c) or one (a, b, c) per NS step")
+            flat = [float(x) for r in rows for x in r]
+            sched = (ctypes.c_float * max(len(flat), 1))(*flat)
+        L.check(L.lib().muon_orthogonalize(self._h, self._ptrs(inputs), self._ptrs(outputs),
+                                           int(ns_steps), sched, self._stream(stream, dev)))
+
     def set_update_capture(self, dst):
         """dst: list of fp32 tensors (or None entries) shaped like the params, or None."""
         if dst is None:

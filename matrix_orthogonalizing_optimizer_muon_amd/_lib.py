@@ -87,6 +87,8 @@ PROTOTYPES = {
                                                   ctypes.c_int]),
     "muon_plan_get_launch_intervals": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(LaunchInterval),
                                                       ctypes.c_int, ctypes.POINTER(ctypes.c_int)]),
+    "muon_orthogonalize": (ctypes.c_int, [ctypes.c_void_p, _PP, _PP, ctypes.c_int,
+                                          ctypes.POINTER(ctypes.c_float), ctypes.c_void_p]),
     "muon_plan_matrix_cost": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int,
                                              ctypes.POINTER(ctypes.c_double)]),
     "muon_assign_owners": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double), ctypes.c_int, ctypes.c_int,

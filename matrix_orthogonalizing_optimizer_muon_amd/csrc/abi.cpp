@@ -78,6 +78,7 @@ struct ChunkDev {
   double bytes_mom = 0, bytes_apply = 0;
   bool all_fused = false;     // every matrix's update is applied by its last NS product
   double bytes_apply_unfused = 0;   // k_ew_apply bytes when fused matrices are skipped
+  double bytes_load = 0, bytes_store = 0;   // orthogonalization alone: input -> D (and D^T), X_T -> out
   std::vector<SetDev> sets;
   int n_lanes = 1;
 };
@@ -239,6 +240,8 @@ int materialize(muon_plan* p) {
       const double e = (double)M.rows * M.cols, pes = M.dtype ? 2 : 4, es = M.path ? 2 : 4;
       C.bytes_mom += e * (pes + 8 + es + (M.has[bX0T] ? es : 0));
       C.bytes_apply += e * (4 + 2 * pes);
+      C.bytes_load += e * (pes + es + (M.has[bX0T] ? es : 0));
+      C.bytes_store += e * (4 + 4);
     }
     C.total_tiles = tb;
     C.all_fused = true;
@@ -540,8 +543,11 @@ int enqueue_chunk_ns(muon_plan* p, const ChunkDev& C, int T, const float* sched,
 
 bool aligned16(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; }
 
+// Per-matrix pointers of a chunk to the device (skipped when unchanged).
+// momenta NULL: no momentum buffers (orthogonalization alone); use_capture 0:
+// no update capture.
 int upload_dyn(muon_plan* p, ChunkDev& C, void* const* params, const void* const* grads,
-               float* const* momenta, hipStream_t s) {
+               float* const* momenta, bool use_capture, hipStream_t s) {
   const size_t nm = C.mats.size();
   std::vector<EwDyn> d(nm);
   for (size_t k = 0; k < nm; ++k) {
@@ -551,8 +557,8 @@ int upload_dyn(muon_plan* p, ChunkDev& C, void* const* params, const void* const
     std::memset(&e, 0, sizeof e);
     e.w = params[i];
     e.g = grads[i];
-    e.buf = momenta[i];
-    e.upd = p->capture[i];
+    e.buf = momenta ? momenta[i] : nullptr;
+    e.upd = use_capture ? p->capture[i] : nullptr;
     e.vec = (M.cols % 8 == 0 && aligned16(e.w) && aligned16(e.g) && aligned16(e.buf) &&
              (!e.upd || aligned16(e.upd))) ? 1 : 0;
   }
@@ -583,11 +589,11 @@ int step_impl(muon_plan* p, void* const* params, const void* const* grads, float
   hipStream_t s = static_cast<hipStream_t>(stream);
   int rc;
   for (ChunkDev& C : p->chunks) {
-    if ((rc = upload_dyn(p, C, params, grads, momenta, s))) return rc;
+    if ((rc = upload_dyn(p, C, params, grads, momenta, true, s))) return rc;
     const int nm = (int)C.mats.size();
     if ((rc = run(p, kEwMom, "k_ew_momentum", 0, C.bytes_mom, s, [&] {
            return launch_ew_momentum(C.ew, C.dyn, C.prefix, nm, C.total_tiles, C.partials, beta,
-                                     p->host.opts.nesterov, p->grid_cap, s);
+                                     p->host.opts.nesterov, 0, p->grid_cap, s);
          }))) return rc;
     if ((rc = run(p, kNorm, "k_norm", 0, 0, s, [&] {
            return launch_norm(C.ew, nm, C.partials, p->rscale, p->flags, p->host.opts.eps, s);
@@ -597,7 +603,42 @@ int step_impl(muon_plan* p, void* const* params, const void* const* grads, float
     if (T >= 1 && C.all_fused) continue;
     if ((rc = run(p, kEwApply, "k_ew_apply", 0, T >= 1 ? C.bytes_apply_unfused : C.bytes_apply, s, [&] {
            return launch_ew_apply(C.ew, C.dyn, C.prefix, nm, C.total_tiles, p->rscale, lr, wd,
-                                  T == 0 ? 1 : 0, T >= 1 ? 1 : 0, p->grid_cap, s);
+                                  T == 0 ? 1 : 0, T >= 1 ? 1 : 0, 0, p->grid_cap, s);
+         }))) return rc;
+  }
+  return MUON_OK;
+}
+
+// Orthogonalization alone: X0 = M / (||M||_F + eps), T NS steps, X_T to out.
+int ortho_impl(muon_plan* p, const void* const* inputs, float* const* outputs, int T,
+               const float* sched, void* stream) {
+  if (!p) return fail(MUON_EINVAL, "plan is NULL");
+  if (p->host.opts.host_only) return fail(MUON_ESTATE, "muon_orthogonalize on a host-only plan");
+  if (!inputs || !outputs) return fail(MUON_EINVAL, "NULL pointer array");
+  if (T < 0 || T > 64) return fail(MUON_EINVAL, "ns_steps must be in [0, 64]");
+  for (int k = 0; k < 3 * T; ++k)
+    if (!std::isfinite(sched[k])) return fail(MUON_EINVAL, "non-finite NS coefficient");
+  const size_t n = p->host.mats.size();
+  for (size_t i = 0; i < n; ++i)
+    if (!inputs[i] || !outputs[i]) return fail(MUON_EINVAL, "NULL matrix pointer at index " + std::to_string(i));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  std::vector<void*> outs(outputs, outputs + n);
+  int rc;
+  for (ChunkDev& C : p->chunks) {
+    if ((rc = upload_dyn(p, C, outs.data(), inputs, nullptr, false, s))) return rc;
+    const int nm = (int)C.mats.size();
+    if ((rc = run(p, kEwMom, "k_ew_momentum", 0, C.bytes_load, s, [&] {
+           return launch_ew_momentum(C.ew, C.dyn, C.prefix, nm, C.total_tiles, C.partials, 0.f, 1, 1,
+                                     p->grid_cap, s);
+         }))) return rc;
+    if ((rc = run(p, kNorm, "k_norm", 0, 0, s, [&] {
+           return launch_norm(C.ew, nm, C.partials, p->rscale, p->flags, p->host.opts.eps, s);
+         }))) return rc;
+    // no parameters: the last NS product writes X_T (fp32) to the workspace
+    if ((rc = enqueue_chunk_ns(p, C, T, sched, nullptr, 0.f, 0.f, s))) return rc;
+    if ((rc = run(p, kEwApply, "k_ew_apply", 0, C.bytes_store, s, [&] {
+           return launch_ew_apply(C.ew, C.dyn, C.prefix, nm, C.total_tiles, p->rscale, 0.f, 0.f,
+                                  T == 0 ? 1 : 0, 0, 1, p->grid_cap, s);
          }))) return rc;
   }
   return MUON_OK;
@@ -957,6 +998,15 @@ int muon_step_schedule(muon_plan* p, void* const* params, const void* const* gra
                        const float* coeffs, void* stream) {
   if (ns_steps > 0 && !coeffs) return fail(MUON_EINVAL, "coeffs is NULL");
   return step_impl(p, params, grads, momenta, lr, beta, wd, ns_steps, coeffs ? coeffs : kQuintic, stream);
+}
+
+int muon_orthogonalize(muon_plan* p, const void* const* inputs, float* const* outputs, int ns_steps,
+                       const float* coeffs, void* stream) {
+  if (ns_steps < 0 || ns_steps > 64) return fail(MUON_EINVAL, "ns_steps must be in [0, 64]");
+  std::vector<float> sched(3 * (size_t)ns_steps);
+  for (int k = 0; k < ns_steps; ++k)
+    std::memcpy(&sched[3 * k], coeffs ? coeffs + 3 * k : kQuintic, 3 * sizeof(float));
+  return ortho_impl(p, inputs, outputs, ns_steps, sched.data(), stream);
 }
 
 int muon_plan_set_update_capture(muon_plan* p, float* const* dst) {

@@ -112,7 +112,7 @@ __device__ __forceinline__ int find_mat(const int64_t* prefix, int nmats, int64_
 __global__ __launch_bounds__(256) void k_ew_momentum(
     const EwMat* __restrict__ mats, const EwDyn* __restrict__ dyn,
     const int64_t* __restrict__ prefix, int nmats, int64_t total,
-    float* __restrict__ partials, float beta, int nesterov) {
+    float* __restrict__ partials, float beta, int nesterov, int load_only) {
   __shared__ float tT[kEwTile][kEwTile + 1];
   __shared__ float red[4];
   const int tid = threadIdx.x;
@@ -126,7 +126,18 @@ __global__ __launch_bounds__(256) void k_ew_momentum(
     const int64_t sr0 = M.trans ? j0 : i0, sc0 = M.trans ? i0 : j0;
     const int64_t sr = sr0 + r;
     float dv[16];
-    if (D.vec && sr0 + kEwTile <= M.rows && sc0 + kEwTile <= M.cols) {
+    if (load_only) {
+      // d = the input itself (orthogonalization alone: no momentum buffer)
+      if (D.vec && sr0 + kEwTile <= M.rows && sc0 + kEwTile <= M.cols) {
+        load16_vec(D.g, M.pdtype, sr * M.cols + sc0 + c0, dv);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int64_t sc = sc0 + c0 + e;
+          dv[e] = (sr < M.rows && sc < M.cols) ? load1(D.g, M.pdtype, sr * M.cols + sc) : 0.f;
+        }
+      }
+    } else if (D.vec && sr0 + kEwTile <= M.rows && sc0 + kEwTile <= M.cols) {
       const int64_t off = sr * M.cols + sc0 + c0;
       float g[16], b[16];
       load16_vec(D.g, M.pdtype, off, g);
@@ -206,7 +217,8 @@ __global__ __launch_bounds__(256) void k_norm(const EwMat* __restrict__ mats,
 __global__ __launch_bounds__(256) void k_ew_apply(
     const EwMat* __restrict__ mats, const EwDyn* __restrict__ dyn,
     const int64_t* __restrict__ prefix, int nmats, int64_t total,
-    const float* __restrict__ rscale, float lr, float wd, int src_is_d, int skip_fused) {
+    const float* __restrict__ rscale, float lr, float wd, int src_is_d, int skip_fused,
+    int store_x) {
   __shared__ float tT[kEwTile][kEwTile + 1];
   const int tid = threadIdx.x;
   const int r = tid >> 2, c0 = (tid & 3) * 16;
@@ -240,6 +252,19 @@ __global__ __launch_bounds__(256) void k_ew_apply(
       sc0 = i0 + c0;
     }
     const float s = M.s;
+    if (store_x) {
+      // orthogonalization alone: the NS output itself, fp32, stored orientation
+#pragma unroll
+      for (int e = 0; e < 16; ++e) x[e] *= sx;
+      if (D.vec && sr < M.rows && sc0 + 16 <= M.cols) {
+        store16_vec(D.w, kF32, sr * M.cols + sc0, x);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (sr < M.rows && sc0 + e < M.cols) static_cast<float*>(D.w)[sr * M.cols + sc0 + e] = x[e];
+      }
+      continue;
+    }
     if (D.vec && sr < M.rows && sc0 + 16 <= M.cols) {
       const int64_t off = sr * M.cols + sc0;
       float w[16], u[16];
@@ -898,11 +923,11 @@ hipError_t launch_nt_cfg(int out_dt, const GemmParams& p, hipStream_t s) {
 
 hipError_t launch_ew_momentum(const EwMat* mats, const EwDyn* dyn, const int64_t* tile_prefix,
                               int nmats, int64_t total_tiles, float* partials, float beta,
-                              int nesterov, int grid_cap, hipStream_t s) {
+                              int nesterov, int load_only, int grid_cap, hipStream_t s) {
   if (total_tiles <= 0) return hipSuccess;
   const int64_t grid = total_tiles < grid_cap ? total_tiles : grid_cap;
   hipLaunchKernelGGL(k_ew_momentum, dim3((unsigned)grid), dim3(256), 0, s, mats, dyn, tile_prefix,
-                     nmats, total_tiles, partials, beta, nesterov);
+                     nmats, total_tiles, partials, beta, nesterov, load_only);
   return hipGetLastError();
 }
 
@@ -915,11 +940,12 @@ hipError_t launch_norm(const EwMat* mats, int nmats, const float* partials, floa
 
 hipError_t launch_ew_apply(const EwMat* mats, const EwDyn* dyn, const int64_t* tile_prefix,
                            int nmats, int64_t total_tiles, const float* rscale, float lr,
-                           float wd, int src_is_d, int skip_fused, int grid_cap, hipStream_t s) {
+                           float wd, int src_is_d, int skip_fused, int store_x, int grid_cap,
+                           hipStream_t s) {
   if (total_tiles <= 0) return hipSuccess;
   const int64_t grid = total_tiles < grid_cap ? total_tiles : grid_cap;
   hipLaunchKernelGGL(k_ew_apply, dim3((unsigned)grid), dim3(256), 0, s, mats, dyn, tile_prefix,
-                     nmats, total_tiles, rscale, lr, wd, src_is_d, skip_fused);
+                     nmats, total_tiles, rscale, lr, wd, src_is_d, skip_fused, store_x);
   return hipGetLastError();
 }
 

@@ -130,13 +130,14 @@ constexpr TileCfg kNtCfgs[kNumNtCfgs] = {{128, 128}, {256, 256}, {256, 128}, {12
 // Launchers (kernels.hip).  All return hipError_t of the launch.
 hipError_t launch_ew_momentum(const EwMat* mats, const EwDyn* dyn, const int64_t* tile_prefix,
                               int nmats, int64_t total_tiles, float* partials, float beta,
-                              int nesterov, int grid_cap, hipStream_t s);
+                              int nesterov, int load_only, int grid_cap, hipStream_t s);
 hipError_t launch_norm(const EwMat* mats, int nmats, const float* partials, float* rscale,
                        uint32_t* flags, float eps, hipStream_t s);
 // skip_fused != 0: matrices whose update the last NS product applied are skipped.
 hipError_t launch_ew_apply(const EwMat* mats, const EwDyn* dyn, const int64_t* tile_prefix,
                            int nmats, int64_t total_tiles, const float* rscale, float lr,
-                           float wd, int src_is_d, int skip_fused, int grid_cap, hipStream_t s);
+                           float wd, int src_is_d, int skip_fused, int store_x, int grid_cap,
+                           hipStream_t s);
 // kShapeApply runs the NN kernel, the other shapes the NT kernel.
 hipError_t launch_gemm(int tile_cfg, int in_dtype, int out_dtype, const GemmParams& p,
                        hipStream_t s);

@@ -121,6 +121,19 @@ def ns_gram(X0: np.ndarray, ns_steps: int, coeffs=QUINTIC) -> np.ndarray:
     return out.T.copy() if tall else out
 
 
+def orthogonalize_ref(M, ns_steps: int = 5, coeffs=QUINTIC, eps: float = 1e-7,
+                      form: str = "direct") -> np.ndarray:
+    """The orthogonalization Muon applies to its update, on its own: M scaled to
+    unit Frobenius norm (plus eps), then ns_steps Newton-Schulz steps.
+    "DeepSpeed now supports Muon" (setupai.cc), technical deep dive."""
+    X0, _ = frobenius_normalize(M, eps)
+    if form == "direct":
+        return ns_direct(X0, ns_steps, coeffs)
+    if form == "gram":
+        return ns_gram(X0, ns_steps, coeffs)
+    raise ValueError(form)
+
+
 def rms_scale(rows: int, cols: int, base: float = 0.2) -> float:
     """Update scale chosen by RMS matching: an exact polar factor of a full-rank
     rows x cols matrix has RMS 1/sqrt(max(rows, cols)), so s*X has RMS `base`."""

@@ -28,7 +28,7 @@ def test_every_declared_function_is_exported_and_bound():
         assert hasattr(lib, n), n
         assert n in L.PROTOTYPES, f"{n} has no ctypes prototype"
     assert set(L.PROTOTYPES) == set(names)
-    assert lib.muon_abi_version() == 5
+    assert lib.muon_abi_version() == 6
 
 
 def test_struct_sizes_match_header_layout():
@@ -238,3 +238,14 @@ def test_bench_busy_time_is_the_union_of_intervals():
     assert b.union_ms([(0.0, 1.0), (0.5, 2.0), (3.0, 4.0), (3.5, 3.6)]) == pytest.approx(3.0)
     assert b.union_ms([(2.0, 3.0), (0.0, 1.0)]) == pytest.approx(2.0)
     assert b.union_ms([(0.0, 5.0), (1.0, 2.0)]) == pytest.approx(5.0)
+
+
+def test_orthogonalize_marshalling_and_host_only_refusal():
+    p = _host([(16, 32), (32, 16)])
+    lib = L.lib()
+    ins = (ctypes.c_void_p * 2)(16, 32)
+    outs = (ctypes.c_void_p * 2)(64, 128)
+    sched = (ctypes.c_float * 3)(1.5, -0.5, 0.0)
+    assert lib.muon_orthogonalize(p._h, ins, outs, 1, sched, None) == L.MUON_ESTATE
+    assert lib.muon_orthogonalize(None, ins, outs, 1, sched, None) == L.MUON_EINVAL
+    assert lib.muon_orthogonalize(p._h, ins, outs, 65, None, None) == L.MUON_EINVAL

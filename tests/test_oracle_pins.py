@@ -246,3 +246,23 @@ def test_multi_step_driver_carries_state():
     r2 = O.muon_step_ref(r1["W_new_stored"], g2, O.round_to_f32(r1["buf_new"]))
     assert np.array_equal(last[0]["U"], r2["U"])
     assert np.array_equal(bufs2[0], O.round_to_f32(r2["buf_new"]))
+
+
+@pytest.mark.parametrize("shape", [(6, 9), (9, 6), (20, 20), (1, 7)])
+@pytest.mark.parametrize("T", [0, 1, 5])
+def test_orthogonalize_equals_svd_of_the_normalized_input(shape, T):
+    """orthogonalize_ref(M) = U phi^T(S / (||M||_F + eps)) V^T, from numpy's SVD of
+    M itself (the normalization written out by hand here, not the oracle's)."""
+    M = _gauss(shape, 31 + T) * 3.0
+    U, S, Vt = np.linalg.svd(M, full_matrices=False)
+    nu = np.sqrt(np.sum(S ** 2))          # ||M||_F from the singular values
+    want = (U * _phi_scalar(S / (nu + 1e-7), O.coeff_schedule(O.QUINTIC, T))) @ Vt
+    assert _rel(O.orthogonalize_ref(M, T), want) < 1e-12
+    assert _rel(O.orthogonalize_ref(M, T, form="gram"), want) < 1e-11
+    # a different eps and a cubic schedule
+    want2 = (U * _phi_scalar(S / (nu + 0.5), O.coeff_schedule((1.5, -0.5, 0.0), T))) @ Vt
+    assert _rel(O.orthogonalize_ref(M, T, (1.5, -0.5, 0.0), eps=0.5), want2) < 1e-12
+
+
+def test_orthogonalize_of_zero_is_zero():
+    assert np.all(O.orthogonalize_ref(np.zeros((4, 6)), 5) == 0.0)
