@@ -36,6 +36,9 @@ def parse():
     ap.add_argument("--form", default="auto", choices=["auto", "direct", "gram"])
     ap.add_argument("--tile", type=int, default=None, help="force a tile plan (0..4)")
     ap.add_argument("--lanes", type=int, default=None, help="force the NS lane count (1..4)")
+    ap.add_argument("--adamw", action="store_true",
+                    help="time the fused AdamW step over the non-matrix parameters of the "
+                         "workload-2 model (vocab 32000 embedding and classifier, norms)")
     ap.add_argument("--owners", type=int, default=1,
                     help="assign the workload's matrices to this many owners (makespan-balanced) "
                          "and time one owner's share")
@@ -194,6 +197,53 @@ def cpu_baseline(wl, ns_flops_per_step):
                       f"fp64 numpy, input generation excluded"}
 
 
+ADAMW_VOCAB, ADAMW_D, ADAMW_LAYERS = 32000, 1024, 4
+
+
+def bench_adamw(args, torch, MU):
+    """The AdamW half of the hybrid on the workload-2 model's non-matrix
+    parameters (bf16 params and grads, fp32 moments): one fused launch per step."""
+    numels = [ADAMW_VOCAB * ADAMW_D, ADAMW_VOCAB * ADAMW_D] + [ADAMW_D] * (2 * ADAMW_LAYERS + 1)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(99)
+    P = [(torch.randn(n, device="cuda", generator=gen) * 0.02).to(torch.bfloat16) for n in numels]
+    G = [(torch.randn(n, device="cuda", generator=gen) * 0.02).to(torch.bfloat16) for n in numels]
+    Mo = [torch.zeros(n, device="cuda") for n in numels]
+    Vo = [torch.zeros(n, device="cuda") for n in numels]
+    plan = MU.AdamWPlan(numels, "bf16")
+    t = [0]
+
+    def step():
+        t[0] += 1
+        plan.step(P, G, Mo, Vo, lr=2e-2, beta1=0.9, beta2=0.95, eps=1e-8, wd=0.01, step=t[0])
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    elems = sum(numels)
+    nbytes = elems * (2 + 2 + 4 + 4 + 2 + 4 + 4)   # p, g, m, v in; p, m, v out
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "fused AdamW step GB/s (% of MI355X 8 TB/s HBM)", "value": round(gbs, 1),
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"non-matrix parameters of the 4-layer d={ADAMW_D} transformer: "
+                               f"{ADAMW_VOCAB}x{ADAMW_D} embedding and classifier, "
+                               f"{2 * ADAMW_LAYERS + 1} norm vectors",
+                   "tensors": len(numels), "elements": elems, "bytes_per_step": nbytes},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}}))
+    plan.close()
+
+
 def owner_share(args, wl, MU):
     """The matrices one owner gets when the workload is balanced over
     args.owners owners by estimated step time (plan costs, muon_assign_owners)."""
@@ -247,6 +297,9 @@ def main():
     import matrix_orthogonalizing_optimizer_muon_amd as MU
 
     torch.cuda.init()
+    if args.adamw:
+        bench_adamw(args, torch, MU)
+        return
     os.makedirs(os.path.dirname(args.cache), exist_ok=True)
     owner_info = None
     if args.owners > 1:

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define MUON_ABI_VERSION 6
+#define MUON_ABI_VERSION 7
 
 typedef enum muon_status {
   MUON_OK = 0,
@@ -288,6 +288,37 @@ int muon_plan_matrix_cost(const muon_plan* plan, int i, double* us);
  */
 int muon_assign_owners(const double* costs, int n, int n_owners, int64_t node_limit,
                        int32_t* owner, double* makespan, int32_t* optimal);
+
+/*
+ * Fused multi-tensor AdamW for the parameters that do not go to Muon
+ * ("DeepSpeed now supports Muon" (setupai.cc), technical deep dive: the
+ * usual hybrid runs Muon on the weight matrices and AdamW on embeddings,
+ * biases and the final classifier).  The pages do not write AdamW out; this is
+ * AdamW with decoupled weight decay as published (Loshchilov and Hutter), per
+ * element, t = step >= 1:
+ *   m <- beta1 m + (1 - beta1) g;  v <- beta2 v + (1 - beta2) g^2
+ *   p <- p (1 - lr wd) - lr / (1 - beta1^t) * m / (sqrt(v) / sqrt(1 - beta2^t) + eps)
+ * in fp32 arithmetic; p stored back in its dtype (bf16: round to nearest even).
+ * The hyperparameters are doubles: 1 - beta, the bias corrections and
+ * 1 - lr wd are formed in double on the host before rounding to fp32.
+ *
+ * muon_adamw_plan_create: n tensors of numels[i] >= 1 elements with params and
+ * grads of dtypes[i] (MUON_F32 or MUON_BF16); moments are fp32.  Needs a
+ * current HIP device (gfx950); owns a small device table.  EINVAL (NULL, n <= 0),
+ * EUNSUPPORTED (dtype, numel < 1), ENOMEM, EHIP.
+ *
+ * muon_adamw_step: host arrays of n caller-owned device pointers (contiguous,
+ * numels[i] elements each); params, exp_avg and exp_avg_sq updated in place,
+ * grads read only.  One launch on stream, asynchronous.  EINVAL (NULL pointer,
+ * step < 1, beta outside [0, 1), eps < 0, non-finite lr, wd or eps), EHIP.
+ */
+typedef struct muon_adamw_plan muon_adamw_plan;
+int muon_adamw_plan_create(const int64_t* numels, const int32_t* dtypes, int n,
+                           muon_adamw_plan** out);
+int muon_adamw_step(muon_adamw_plan* plan, void* const* params, const void* const* grads,
+                    float* const* exp_avg, float* const* exp_avg_sq, double lr, double beta1,
+                    double beta2, double eps, double wd, int64_t step, void* stream);
+int muon_adamw_plan_destroy(muon_adamw_plan* plan);
 
 /* MUON_ABI_VERSION of the library. */
 int muon_abi_version(void);

@@ -14,7 +14,7 @@ import ctypes
 from . import _lib as L
 from ._lib import MuonError  # noqa: F401
 
-__all__ = ["MuonPlan", "MuonError", "library_path", "assign_owners"]
+__all__ = ["MuonPlan", "AdamWPlan", "MuonError", "library_path", "assign_owners"]
 
 
 def library_path():
@@ -257,3 +257,52 @@ def assign_owners(costs, n_owners, node_limit=0):
     L.check(L.lib().muon_assign_owners(arr, n, int(n_owners), int(node_limit), out,
                                        ctypes.byref(span), ctypes.byref(opt)))
     return [out[i] for i in range(n)], span.value, bool(opt.value)
+
+
+class AdamWPlan:
+    """Fused multi-tensor AdamW over a fixed list of tensors (muon_adamw_*): the
+    non-matrix half of the Muon + AdamW hybrid."""
+
+    def __init__(self, numels, dtypes):
+        numels = [int(x) for x in numels]
+        codes = [_dtype_code(d) for d in dtypes] if isinstance(dtypes, (list, tuple)) \
+            else [_dtype_code(dtypes)] * len(numels)
+        if len(codes) != len(numels):
+            raise ValueError("one dtype per tensor")
+        self.numels, self.dtypes = numels, codes
+        n = len(numels)
+        ne = (ctypes.c_int64 * max(n, 1))(*numels)
+        dt = (ctypes.c_int32 * max(n, 1))(*codes)
+        h = ctypes.c_void_p()
+        L.check(L.lib().muon_adamw_plan_create(ne, dt, n, ctypes.byref(h)))
+        self._h = h
+
+    def close(self):
+        if getattr(self, "_h", None):
+            L.lib().muon_adamw_plan_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def step(self, params, grads, exp_avg, exp_avg_sq, *, lr, beta1=0.9, beta2=0.999, eps=1e-8,
+             wd=0.01, step=1, stream=None):
+        import torch
+        n = len(self.numels)
+        for name, ts, want in (("params", params, self.dtypes), ("grads", grads, self.dtypes),
+                               ("exp_avg", exp_avg, [L.MUON_F32] * n),
+                               ("exp_avg_sq", exp_avg_sq, [L.MUON_F32] * n)):
+            if len(ts) != n:
+                raise ValueError(f"{name}: {len(ts)} tensors, plan has {n}")
+            for i, (t, d) in enumerate(zip(ts, want)):
+                tdt = torch.float32 if d == L.MUON_F32 else torch.bfloat16
+                if not t.is_cuda or t.dtype != tdt or t.numel() != self.numels[i] or not t.is_contiguous():
+                    raise ValueError(f"{name}[{i}] must be a contiguous CUDA {tdt} of {self.numels[i]} elements")
+        ptr = MuonPlan._ptrs
+        dev = params[0].device if n else torch.device("cuda")
+        L.check(L.lib().muon_adamw_step(self._h, ptr(params), ptr(grads), ptr(exp_avg), ptr(exp_avg_sq),
+                                        float(lr), float(beta1), float(beta2), float(eps), float(wd),
+                                        int(step), MuonPlan._stream(stream, dev)))

@@ -89,6 +89,13 @@ PROTOTYPES = {
                                                       ctypes.c_int, ctypes.POINTER(ctypes.c_int)]),
     "muon_orthogonalize": (ctypes.c_int, [ctypes.c_void_p, _PP, _PP, ctypes.c_int,
                                           ctypes.POINTER(ctypes.c_float), ctypes.c_void_p]),
+    "muon_adamw_plan_create": (ctypes.c_int, [ctypes.POINTER(ctypes.c_int64),
+                                              ctypes.POINTER(ctypes.c_int32), ctypes.c_int,
+                                              ctypes.POINTER(ctypes.c_void_p)]),
+    "muon_adamw_step": (ctypes.c_int, [ctypes.c_void_p, _PP, _PP, _PP, _PP, ctypes.c_double,
+                                       ctypes.c_double, ctypes.c_double, ctypes.c_double,
+                                       ctypes.c_double, ctypes.c_int64, ctypes.c_void_p]),
+    "muon_adamw_plan_destroy": (ctypes.c_int, [ctypes.c_void_p]),
     "muon_plan_matrix_cost": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int,
                                              ctypes.POINTER(ctypes.c_double)]),
     "muon_assign_owners": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double), ctypes.c_int, ctypes.c_int,

@@ -1009,6 +1009,142 @@ int muon_orthogonalize(muon_plan* p, const void* const* inputs, float* const* ou
   return ortho_impl(p, inputs, outputs, ns_steps, sched.data(), stream);
 }
 
+}  // extern "C" (reopened below)
+
+struct muon_adamw_plan {
+  int device = -1;
+  int grid_cap = 2048;
+  std::vector<int64_t> numels;
+  std::vector<int32_t> dtypes;
+  std::vector<int64_t> prefix;    // first chunk of each tensor
+  int64_t total_chunks = 0;
+  muon::AdamTensor* dev_tensors = nullptr;
+  int64_t* dev_prefix = nullptr;
+  muon::AdamTensor* pinned = nullptr;
+  std::vector<muon::AdamTensor> last;
+  bool valid = false, pending = false;
+  hipEvent_t upload_ev = nullptr;
+};
+
+namespace {
+void free_adamw(muon_adamw_plan* a) {
+  if (!a) return;
+  (void)hipDeviceSynchronize();
+  if (a->upload_ev) (void)hipEventDestroy(a->upload_ev);
+  if (a->dev_tensors) (void)hipFree(a->dev_tensors);
+  if (a->dev_prefix) (void)hipFree(a->dev_prefix);
+  if (a->pinned) (void)hipHostFree(a->pinned);
+}
+}  // namespace
+
+extern "C" {
+
+int muon_adamw_plan_create(const int64_t* numels, const int32_t* dtypes, int n, muon_adamw_plan** out) {
+  g_err.clear();
+  if (!out) return fail(MUON_EINVAL, "out is NULL");
+  *out = nullptr;
+  if (!numels || !dtypes || n <= 0) return fail(MUON_EINVAL, "NULL arrays or n <= 0");
+  for (int i = 0; i < n; ++i) {
+    if (dtypes[i] != MUON_F32 && dtypes[i] != MUON_BF16)
+      return fail(MUON_EUNSUPPORTED, "unsupported dtype at index " + std::to_string(i));
+    if (numels[i] < 1) return fail(MUON_EUNSUPPORTED, "empty tensor at index " + std::to_string(i));
+  }
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(MUON_EUNSUPPORTED, "no HIP device");
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return fail(MUON_EHIP, "hipGetDeviceProperties failed");
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(MUON_EUNSUPPORTED, std::string("device is ") + prop.gcnArchName + ", not gfx950");
+  muon_adamw_plan* a = new muon_adamw_plan;
+  a->device = dev;
+  a->grid_cap = prop.multiProcessorCount * 8;
+  a->numels.assign(numels, numels + n);
+  a->dtypes.assign(dtypes, dtypes + n);
+  a->prefix.resize(n);
+  for (int i = 0; i < n; ++i) {
+    a->prefix[i] = a->total_chunks;
+    a->total_chunks += (numels[i] + kAdamChunk - 1) / kAdamChunk;
+  }
+  auto bad = [&](const char* what) {
+    free_adamw(a);
+    delete a;
+    return fail(MUON_ENOMEM, what);
+  };
+  if (hipMalloc(&a->dev_tensors, n * sizeof(AdamTensor)) != hipSuccess) return bad("hipMalloc (AdamW table)");
+  if (hipMalloc(&a->dev_prefix, n * sizeof(int64_t)) != hipSuccess) return bad("hipMalloc (AdamW prefix)");
+  if (hipHostMalloc(&a->pinned, n * sizeof(AdamTensor), hipHostMallocDefault) != hipSuccess)
+    return bad("hipHostMalloc (AdamW table)");
+  if (hipMemcpy(a->dev_prefix, a->prefix.data(), n * sizeof(int64_t), hipMemcpyHostToDevice) != hipSuccess ||
+      hipEventCreateWithFlags(&a->upload_ev, hipEventDisableTiming) != hipSuccess) {
+    free_adamw(a);
+    delete a;
+    return fail(MUON_EHIP, "AdamW plan setup failed");
+  }
+  *out = a;
+  return MUON_OK;
+}
+
+int muon_adamw_step(muon_adamw_plan* a, void* const* params, const void* const* grads,
+                    float* const* exp_avg, float* const* exp_avg_sq, double lr, double beta1,
+                    double beta2, double eps, double wd, int64_t step, void* stream) {
+  g_err.clear();
+  if (!a) return fail(MUON_EINVAL, "plan is NULL");
+  if (!params || !grads || !exp_avg || !exp_avg_sq) return fail(MUON_EINVAL, "NULL pointer array");
+  if (step < 1) return fail(MUON_EINVAL, "step must be >= 1");
+  if (!(beta1 >= 0.0 && beta1 < 1.0) || !(beta2 >= 0.0 && beta2 < 1.0))
+    return fail(MUON_EINVAL, "beta1 and beta2 must be in [0, 1)");
+  if (!std::isfinite(lr) || !std::isfinite(wd) || !std::isfinite(eps) || eps < 0.0)
+    return fail(MUON_EINVAL, "non-finite lr or wd, or eps not finite and >= 0");
+  const size_t n = a->numels.size();
+  std::vector<AdamTensor> t(n);
+  for (size_t i = 0; i < n; ++i) {
+    if (!params[i] || !grads[i] || !exp_avg[i] || !exp_avg_sq[i])
+      return fail(MUON_EINVAL, "NULL tensor pointer at index " + std::to_string(i));
+    AdamTensor& e = t[i];
+    std::memset(&e, 0, sizeof e);
+    e.p = params[i];
+    e.g = grads[i];
+    e.m = exp_avg[i];
+    e.v = exp_avg_sq[i];
+    e.n = a->numels[i];
+    e.chunk_begin = a->prefix[i];
+    e.pdtype = a->dtypes[i];
+    e.vec = (aligned16(e.p) && aligned16(e.g) && aligned16(e.m) && aligned16(e.v)) ? 1 : 0;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!a->valid || std::memcmp(t.data(), a->last.data(), n * sizeof(AdamTensor)) != 0) {
+    if (a->pending) HIP_TRY(hipEventSynchronize(a->upload_ev));
+    std::memcpy(a->pinned, t.data(), n * sizeof(AdamTensor));
+    HIP_TRY(hipMemcpyAsync(a->dev_tensors, a->pinned, n * sizeof(AdamTensor), hipMemcpyHostToDevice, s));
+    HIP_TRY(hipEventRecord(a->upload_ev, s));
+    a->pending = true;
+    a->last = t;
+    a->valid = true;
+  }
+  // bias corrections in double on the host
+  const double bc1 = 1.0 - std::pow(beta1, (double)step);
+  const double bc2 = 1.0 - std::pow(beta2, (double)step);
+  AdamScalars sc;
+  sc.beta1 = (float)beta1;
+  sc.beta2 = (float)beta2;
+  sc.eps = (float)eps;
+  sc.omb1 = (float)(1.0 - beta1);
+  sc.omb2 = (float)(1.0 - beta2);
+  sc.decay = (float)(1.0 - lr * wd);
+  sc.step_size = (float)(lr / bc1);
+  sc.inv_bc2_sqrt = (float)(1.0 / std::sqrt(bc2));
+  const hipError_t e = launch_adamw(a->dev_tensors, a->dev_prefix, (int)n, a->total_chunks, sc, a->grid_cap, s);
+  if (e != hipSuccess) return fail(MUON_EHIP, std::string("adamw launch: ") + hipGetErrorString(e));
+  return MUON_OK;
+}
+
+int muon_adamw_plan_destroy(muon_adamw_plan* a) {
+  if (!a) return MUON_OK;
+  free_adamw(a);
+  delete a;
+  return MUON_OK;
+}
+
 int muon_plan_set_update_capture(muon_plan* p, float* const* dst) {
   if (!p) return fail(MUON_EINVAL, "plan is NULL");
   for (size_t i = 0; i < p->capture.size(); ++i) p->capture[i] = dst ? dst[i] : nullptr;

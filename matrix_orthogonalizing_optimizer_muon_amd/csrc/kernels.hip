@@ -25,6 +25,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+#define GLOBAL_AS __attribute__((address_space(1)))
 
 // ---------------------------------------------------------------- conversions
 
@@ -212,6 +213,99 @@ __global__ __launch_bounds__(256) void k_norm(const EwMat* __restrict__ mats,
   }
 }
 
+// ------------------------------------------------------------ elementwise: AdamW
+//
+// "DeepSpeed now supports Muon" (setupai.cc), technical deep dive: the usual
+// hybrid runs Muon on the weight matrices and AdamW on the other parameters
+// (embeddings, biases, the final classifier).  AdamW with decoupled weight
+// decay, per element, t the step count:
+//   m <- b1 m + (1 - b1) g;  v <- b2 v + (1 - b2) g^2
+//   p <- p (1 - lr wd) - lr / (1 - b1^t) * m / (sqrt(v) / sqrt(1 - b2^t) + eps)
+// Block: 256 threads x 8 consecutive elements = one 2048-element chunk.
+__device__ __forceinline__ void adam8(float* p, const float* g, float* m, float* v,
+                                      const AdamScalars& c) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    m[e] = c.beta1 * m[e] + c.omb1 * g[e];
+    v[e] = c.beta2 * v[e] + c.omb2 * (g[e] * g[e]);
+    const float denom = sqrtf(v[e]) * c.inv_bc2_sqrt + c.eps;
+    p[e] = p[e] * c.decay - c.step_size * (m[e] / denom);
+  }
+}
+
+__global__ __launch_bounds__(256) void k_adamw(const AdamTensor* __restrict__ ts,
+                                               const int64_t* __restrict__ prefix, int nt,
+                                               int64_t total, AdamScalars c) {
+  typedef float f32x4_t __attribute__((ext_vector_type(4)));
+  for (int64_t ch = blockIdx.x; ch < total; ch += gridDim.x) {
+    const int ti = find_mat(prefix, nt, ch);
+    const AdamTensor& T = ts[ti];
+    const int64_t off = (ch - T.chunk_begin) * kAdamChunk + (int64_t)threadIdx.x * 8;
+    if (off >= T.n) continue;
+    float p[8], g[8], m[8], v[8];
+    if (T.vec && off + 8 <= T.n) {
+      if (T.pdtype == kBF16) {
+        const u32x4_t qp = *(GLOBAL_AS const u32x4_t*)(static_cast<const uint16_t*>(T.p) + off);
+        const u32x4_t qg = *(GLOBAL_AS const u32x4_t*)(static_cast<const uint16_t*>(T.g) + off);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          p[2 * e] = bf16_to_f32(qp[e] & 0xffffu);
+          p[2 * e + 1] = bf16_to_f32(qp[e] >> 16);
+          g[2 * e] = bf16_to_f32(qg[e] & 0xffffu);
+          g[2 * e + 1] = bf16_to_f32(qg[e] >> 16);
+        }
+      } else {
+        const GLOBAL_AS f32x4_t* sp = (const GLOBAL_AS f32x4_t*)(static_cast<const float*>(T.p) + off);
+        const GLOBAL_AS f32x4_t* sg = (const GLOBAL_AS f32x4_t*)(static_cast<const float*>(T.g) + off);
+        const f32x4_t a = sp[0], b = sp[1], x = sg[0], y = sg[1];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          p[e] = a[e]; p[4 + e] = b[e]; g[e] = x[e]; g[4 + e] = y[e];
+        }
+      }
+      GLOBAL_AS f32x4_t* sm = (GLOBAL_AS f32x4_t*)(T.m + off);
+      GLOBAL_AS f32x4_t* sv = (GLOBAL_AS f32x4_t*)(T.v + off);
+      const f32x4_t m0 = sm[0], m1 = sm[1], v0 = sv[0], v1 = sv[1];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        m[e] = m0[e]; m[4 + e] = m1[e]; v[e] = v0[e]; v[4 + e] = v1[e];
+      }
+      adam8(p, g, m, v, c);
+      sm[0] = f32x4_t{m[0], m[1], m[2], m[3]};
+      sm[1] = f32x4_t{m[4], m[5], m[6], m[7]};
+      sv[0] = f32x4_t{v[0], v[1], v[2], v[3]};
+      sv[1] = f32x4_t{v[4], v[5], v[6], v[7]};
+      if (T.pdtype == kBF16) {
+        *(GLOBAL_AS u32x4_t*)(static_cast<uint16_t*>(T.p) + off) =
+            u32x4_t{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                    pack_bf16x2(p[6], p[7])};
+      } else {
+        GLOBAL_AS f32x4_t* dp = (GLOBAL_AS f32x4_t*)(static_cast<float*>(T.p) + off);
+        dp[0] = f32x4_t{p[0], p[1], p[2], p[3]};
+        dp[1] = f32x4_t{p[4], p[5], p[6], p[7]};
+      }
+    } else {
+      const int cnt = (int)(T.n - off < 8 ? T.n - off : 8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const bool in = e < cnt;
+        p[e] = in ? load1(T.p, T.pdtype, off + e) : 0.f;
+        g[e] = in ? load1(T.g, T.pdtype, off + e) : 0.f;
+        m[e] = in ? T.m[off + e] : 0.f;
+        v[e] = in ? T.v[off + e] : 0.f;
+      }
+      adam8(p, g, m, v, c);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (e < cnt) {
+          store1(T.p, T.pdtype, off + e, p[e]);
+          T.m[off + e] = m[e];
+          T.v[off + e] = v[e];
+        }
+    }
+  }
+}
+
 // ------------------------------------------------------------ elementwise: apply
 
 __global__ __launch_bounds__(256) void k_ew_apply(
@@ -359,7 +453,6 @@ __device__ __forceinline__ uint32_t half16(const u32x4_t& v, int e) {
 }
 __device__ __forceinline__ uint32_t word32(const u32x4_t& v, int e) { return v[e]; }
 
-#define GLOBAL_AS __attribute__((address_space(1)))
 typedef GLOBAL_AS const u32x4_t gu32x4_c;
 
 template <int BM, int BN, bool NN, int ES>
@@ -928,6 +1021,15 @@ hipError_t launch_ew_momentum(const EwMat* mats, const EwDyn* dyn, const int64_t
   const int64_t grid = total_tiles < grid_cap ? total_tiles : grid_cap;
   hipLaunchKernelGGL(k_ew_momentum, dim3((unsigned)grid), dim3(256), 0, s, mats, dyn, tile_prefix,
                      nmats, total_tiles, partials, beta, nesterov, load_only);
+  return hipGetLastError();
+}
+
+hipError_t launch_adamw(const AdamTensor* tensors, const int64_t* chunk_prefix, int ntensors,
+                        int64_t total_chunks, AdamScalars sc, int grid_cap, hipStream_t s) {
+  if (total_chunks <= 0) return hipSuccess;
+  const int64_t grid = total_chunks < grid_cap ? total_chunks : grid_cap;
+  hipLaunchKernelGGL(k_adamw, dim3((unsigned)grid), dim3(256), 0, s, tensors, chunk_prefix, ntensors,
+                     total_chunks, sc);
   return hipGetLastError();
 }
 

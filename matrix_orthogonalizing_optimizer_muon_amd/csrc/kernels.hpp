@@ -39,6 +39,29 @@ struct EwMat {
   int32_t fused;             // 1: the last NS product applies the update (bf16 NT path)
 };
 
+// One tensor of a fused AdamW step: caller pointers and its place in the
+// launch's chunk sequence (kAdamChunk elements per chunk).
+constexpr int kAdamChunk = 2048;
+struct AdamTensor {
+  void* p;             // params (pdtype), n elements
+  const void* g;       // grads (pdtype)
+  float* m;            // first moment (fp32)
+  float* v;            // second moment (fp32)
+  int64_t n;
+  int64_t chunk_begin; // first chunk of this tensor in the launch
+  int32_t pdtype;
+  int32_t vec;         // 1: all four pointers 16-byte aligned
+};
+
+// Per step scalars of AdamW (host-computed bias corrections).
+struct AdamScalars {
+  float beta1, beta2, eps;
+  float omb1, omb2;    // 1 - beta1, 1 - beta2 (computed in double: 1 - 0.999f would be off by 1e-5)
+  float decay;         // 1 - lr * wd
+  float step_size;     // lr / (1 - beta1^t)
+  float inv_bc2_sqrt;  // 1 / sqrt(1 - beta2^t)
+};
+
 // Per matrix, caller pointers of the current step (uploaded when they change).
 struct EwDyn {
   void* w;           // params (pdtype), rows x cols
@@ -133,6 +156,9 @@ hipError_t launch_ew_momentum(const EwMat* mats, const EwDyn* dyn, const int64_t
                               int nesterov, int load_only, int grid_cap, hipStream_t s);
 hipError_t launch_norm(const EwMat* mats, int nmats, const float* partials, float* rscale,
                        uint32_t* flags, float eps, hipStream_t s);
+// Fused AdamW over a list of tensors (chunk_prefix[i] = tensors[i].chunk_begin).
+hipError_t launch_adamw(const AdamTensor* tensors, const int64_t* chunk_prefix, int ntensors,
+                        int64_t total_chunks, AdamScalars sc, int grid_cap, hipStream_t s);
 // skip_fused != 0: matrices whose update the last NS product applied are skipped.
 hipError_t launch_ew_apply(const EwMat* mats, const EwDyn* dyn, const int64_t* tile_prefix,
                            int nmats, int64_t total_tiles, const float* rscale, float lr,

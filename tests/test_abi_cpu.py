@@ -28,7 +28,7 @@ def test_every_declared_function_is_exported_and_bound():
         assert hasattr(lib, n), n
         assert n in L.PROTOTYPES, f"{n} has no ctypes prototype"
     assert set(L.PROTOTYPES) == set(names)
-    assert lib.muon_abi_version() == 6
+    assert lib.muon_abi_version() == 7
 
 
 def test_struct_sizes_match_header_layout():
@@ -249,3 +249,17 @@ def test_orthogonalize_marshalling_and_host_only_refusal():
     assert lib.muon_orthogonalize(p._h, ins, outs, 1, sched, None) == L.MUON_ESTATE
     assert lib.muon_orthogonalize(None, ins, outs, 1, sched, None) == L.MUON_EINVAL
     assert lib.muon_orthogonalize(p._h, ins, outs, 65, None, None) == L.MUON_EINVAL
+
+
+def test_adamw_entry_points_refuse_bad_arguments_without_a_device():
+    lib = L.lib()
+    out = ctypes.c_void_p()
+    ne = (ctypes.c_int64 * 2)(10, 20)
+    dt = (ctypes.c_int32 * 2)(L.MUON_F32, L.MUON_BF16)
+    assert lib.muon_adamw_plan_create(None, dt, 2, ctypes.byref(out)) == L.MUON_EINVAL
+    assert lib.muon_adamw_plan_create(ne, dt, 0, ctypes.byref(out)) == L.MUON_EINVAL
+    bad = (ctypes.c_int32 * 2)(L.MUON_F32, 9)
+    assert lib.muon_adamw_plan_create(ne, bad, 2, ctypes.byref(out)) == L.MUON_EUNSUPPORTED
+    arr = (ctypes.c_void_p * 1)(16)
+    assert lib.muon_adamw_step(None, arr, arr, arr, arr, 1e-3, 0.9, 0.999, 1e-8, 0.0, 1, None) == L.MUON_EINVAL
+    assert lib.muon_adamw_plan_destroy(None) == L.MUON_OK
