@@ -963,7 +963,8 @@ int muon_plan_create(const muon_matrix_desc* descs, int n, const muon_plan_opts*
   p->device = dev;
   if (!po.host_only) {
     hipDeviceProp_t prop;
-    if (hipGetDeviceProperties(&prop, dev) == hipSuccess) p->grid_cap = prop.multiProcessorCount * 8;
+    // elementwise launches: up to 32 blocks per CU in flight (grid-stride beyond)
+    if (hipGetDeviceProperties(&prop, dev) == hipSuccess) p->grid_cap = prop.multiProcessorCount * 32;
     const int rc = materialize(p);
     if (rc) {
       const std::string keep = g_err;
@@ -1057,7 +1058,7 @@ int muon_adamw_plan_create(const int64_t* numels, const int32_t* dtypes, int n, 
     return fail(MUON_EUNSUPPORTED, std::string("device is ") + prop.gcnArchName + ", not gfx950");
   muon_adamw_plan* a = new muon_adamw_plan;
   a->device = dev;
-  a->grid_cap = prop.multiProcessorCount * 8;
+  a->grid_cap = prop.multiProcessorCount * 32;
   a->numels.assign(numels, numels + n);
   a->dtypes.assign(dtypes, dtypes + n);
   a->prefix.resize(n);

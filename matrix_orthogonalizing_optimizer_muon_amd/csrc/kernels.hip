@@ -45,38 +45,51 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
 }
 
-// 16 consecutive elements of dtype dt starting at element offset off (16-byte aligned).
+// 16-byte global accesses and 16 consecutive elements of dtype dt starting at
+// element offset off (16-byte aligned).  (Nontemporal variants of these were
+// measured slower for every elementwise kernel here.)
+__device__ __forceinline__ u32x4_t ld_u4(const void* p) {
+  return *(const GLOBAL_AS u32x4_t*)p;
+}
+
+__device__ __forceinline__ void st_u4(void* p, u32x4_t v) {
+  *(GLOBAL_AS u32x4_t*)p = v;
+}
+
 __device__ __forceinline__ void load16_vec(const void* base, int dt, int64_t off, float* v) {
   if (dt == kBF16) {
-    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + off);
-    uint4 a = p[0], b = p[1];
-    uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    const uint16_t* p = static_cast<const uint16_t*>(base) + off;
+    const u32x4_t a = ld_u4(p), b = ld_u4(p + 8);
+    const uint32_t w[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       v[2 * e] = bf16_to_f32(w[e] & 0xffffu);
       v[2 * e + 1] = bf16_to_f32(w[e] >> 16);
     }
   } else {
-    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + off);
+    const float* p = static_cast<const float*>(base) + off;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      float4 t = p[q];
-      v[4 * q] = t.x; v[4 * q + 1] = t.y; v[4 * q + 2] = t.z; v[4 * q + 3] = t.w;
+      const u32x4_t t = ld_u4(p + 4 * q);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[4 * q + e] = __uint_as_float(t[e]);
     }
   }
 }
 
 __device__ __forceinline__ void store16_vec(void* base, int dt, int64_t off, const float* v) {
   if (dt == kBF16) {
-    uint4* p = reinterpret_cast<uint4*>(static_cast<uint16_t*>(base) + off);
-    p[0] = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
-                      pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
-    p[1] = make_uint4(pack_bf16x2(v[8], v[9]), pack_bf16x2(v[10], v[11]),
-                      pack_bf16x2(v[12], v[13]), pack_bf16x2(v[14], v[15]));
+    uint16_t* p = static_cast<uint16_t*>(base) + off;
+    st_u4(p, u32x4_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                         pack_bf16x2(v[6], v[7])});
+    st_u4(p + 8, u32x4_t{pack_bf16x2(v[8], v[9]), pack_bf16x2(v[10], v[11]),
+                             pack_bf16x2(v[12], v[13]), pack_bf16x2(v[14], v[15])});
   } else {
-    float4* p = reinterpret_cast<float4*>(static_cast<float*>(base) + off);
+    float* p = static_cast<float*>(base) + off;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) p[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+    for (int q = 0; q < 4; ++q)
+      st_u4(p + 4 * q, u32x4_t{__float_as_uint(v[4 * q]), __float_as_uint(v[4 * q + 1]),
+                                   __float_as_uint(v[4 * q + 2]), __float_as_uint(v[4 * q + 3])});
   }
 }
 
@@ -236,7 +249,6 @@ __device__ __forceinline__ void adam8(float* p, const float* g, float* m, float*
 __global__ __launch_bounds__(256) void k_adamw(const AdamTensor* __restrict__ ts,
                                                const int64_t* __restrict__ prefix, int nt,
                                                int64_t total, AdamScalars c) {
-  typedef float f32x4_t __attribute__((ext_vector_type(4)));
   for (int64_t ch = blockIdx.x; ch < total; ch += gridDim.x) {
     const int ti = find_mat(prefix, nt, ch);
     const AdamTensor& T = ts[ti];
@@ -245,8 +257,8 @@ __global__ __launch_bounds__(256) void k_adamw(const AdamTensor* __restrict__ ts
     float p[8], g[8], m[8], v[8];
     if (T.vec && off + 8 <= T.n) {
       if (T.pdtype == kBF16) {
-        const u32x4_t qp = *(GLOBAL_AS const u32x4_t*)(static_cast<const uint16_t*>(T.p) + off);
-        const u32x4_t qg = *(GLOBAL_AS const u32x4_t*)(static_cast<const uint16_t*>(T.g) + off);
+        const u32x4_t qp = ld_u4(static_cast<const uint16_t*>(T.p) + off);
+        const u32x4_t qg = ld_u4(static_cast<const uint16_t*>(T.g) + off);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           p[2 * e] = bf16_to_f32(qp[e] & 0xffffu);
@@ -255,34 +267,39 @@ __global__ __launch_bounds__(256) void k_adamw(const AdamTensor* __restrict__ ts
           g[2 * e + 1] = bf16_to_f32(qg[e] >> 16);
         }
       } else {
-        const GLOBAL_AS f32x4_t* sp = (const GLOBAL_AS f32x4_t*)(static_cast<const float*>(T.p) + off);
-        const GLOBAL_AS f32x4_t* sg = (const GLOBAL_AS f32x4_t*)(static_cast<const float*>(T.g) + off);
-        const f32x4_t a = sp[0], b = sp[1], x = sg[0], y = sg[1];
+        const float* sp = static_cast<const float*>(T.p) + off;
+        const float* sg = static_cast<const float*>(T.g) + off;
+        const u32x4_t a0 = ld_u4(sp), a1 = ld_u4(sp + 4);
+        const u32x4_t b0 = ld_u4(sg), b1 = ld_u4(sg + 4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          p[e] = a[e]; p[4 + e] = b[e]; g[e] = x[e]; g[4 + e] = y[e];
+          p[e] = __uint_as_float(a0[e]); p[4 + e] = __uint_as_float(a1[e]);
+          g[e] = __uint_as_float(b0[e]); g[4 + e] = __uint_as_float(b1[e]);
         }
       }
-      GLOBAL_AS f32x4_t* sm = (GLOBAL_AS f32x4_t*)(T.m + off);
-      GLOBAL_AS f32x4_t* sv = (GLOBAL_AS f32x4_t*)(T.v + off);
-      const f32x4_t m0 = sm[0], m1 = sm[1], v0 = sv[0], v1 = sv[1];
+      const u32x4_t m0 = ld_u4(T.m + off), m1 = ld_u4(T.m + off + 4);
+      const u32x4_t v0 = ld_u4(T.v + off), v1 = ld_u4(T.v + off + 4);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        m[e] = m0[e]; m[4 + e] = m1[e]; v[e] = v0[e]; v[4 + e] = v1[e];
+        m[e] = __uint_as_float(m0[e]); m[4 + e] = __uint_as_float(m1[e]);
+        v[e] = __uint_as_float(v0[e]); v[4 + e] = __uint_as_float(v1[e]);
       }
       adam8(p, g, m, v, c);
-      sm[0] = f32x4_t{m[0], m[1], m[2], m[3]};
-      sm[1] = f32x4_t{m[4], m[5], m[6], m[7]};
-      sv[0] = f32x4_t{v[0], v[1], v[2], v[3]};
-      sv[1] = f32x4_t{v[4], v[5], v[6], v[7]};
+      auto u4 = [](const float* x) {
+        return u32x4_t{__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])};
+      };
+      st_u4(T.m + off, u4(m));
+      st_u4(T.m + off + 4, u4(m + 4));
+      st_u4(T.v + off, u4(v));
+      st_u4(T.v + off + 4, u4(v + 4));
       if (T.pdtype == kBF16) {
-        *(GLOBAL_AS u32x4_t*)(static_cast<uint16_t*>(T.p) + off) =
-            u32x4_t{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
-                    pack_bf16x2(p[6], p[7])};
+        st_u4(static_cast<uint16_t*>(T.p) + off,
+                    u32x4_t{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                            pack_bf16x2(p[6], p[7])});
       } else {
-        GLOBAL_AS f32x4_t* dp = (GLOBAL_AS f32x4_t*)(static_cast<float*>(T.p) + off);
-        dp[0] = f32x4_t{p[0], p[1], p[2], p[3]};
-        dp[1] = f32x4_t{p[4], p[5], p[6], p[7]};
+        float* dp = static_cast<float*>(T.p) + off;
+        st_u4(dp, u4(p));
+        st_u4(dp + 4, u4(p + 4));
       }
     } else {
       const int cnt = (int)(T.n - off < 8 ? T.n - off : 8);
