@@ -92,12 +92,14 @@ COPY_BYTES = 1 << 30   # bytes read and written by the calibration copy
 
 def demangled(label):
     """Pattern of rocprofv3's name of a kernel instance label such as
-    k_nt<128,128,bf16> (the template also carries the block's wave grid)."""
+    k_nt<128,128,bf16> or k_nt<256,256,bf16,qt> (the template also carries the
+    block's wave grid and the k-major read flag)."""
     base, _, args = label.partition("<")
     args = args.rstrip(">").split(",") if args else []
     conv = {"bf16": "unsigned short", "f32": "float"}
     if base == "k_nt":
-        return re.compile(rf"k_nt<{args[0]}, {args[1]}, \d+, \d+, {conv[args[2]]}>")
+        qt = "true" if len(args) > 3 and args[3] == "qt" else "false"
+        return re.compile(rf"k_nt<{args[0]}, {args[1]}, \d+, \d+, {conv[args[2]]}, {qt}>")
     return re.compile(re.escape(base))
 
 

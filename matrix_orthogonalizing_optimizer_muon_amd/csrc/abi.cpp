@@ -47,10 +47,10 @@ struct SetDev {
   int lane = 0;
   int nmats = 0;
   NsMat* mats = nullptr;
-  Items nt_sym[kNumNtCfgs], nt_full[kNumNtCfgs], old_sym, old_full;
+  Items nt_sym[kNumNtCfgs], nt_full[2 * kNumNtCfgs], old_sym, old_full;   // nt_full: full_list(cfg, qt)
   // algorithmic (symmetric-aware) flops of each launch: per NT configuration
-  // on the bf16 path, index 0 for the fp32 kernel
-  double fl_gram[kNumNtCfgs] = {0}, fl_square[kNumNtCfgs] = {0}, fl_apply[kNumNtCfgs] = {0};
+  // (and read mode for B X) on the bf16 path, index 0 for the fp32 kernel
+  double fl_gram[kNumNtCfgs] = {0}, fl_square[kNumNtCfgs] = {0}, fl_apply[2 * kNumNtCfgs] = {0};
 };
 
 static_assert(kNumNtCfgs == kNtTiles && sizeof(kNtTileShapes) / sizeof(kNtTileShapes[0]) == kNtTiles,
@@ -83,12 +83,15 @@ struct ChunkDev {
   int n_lanes = 1;
 };
 
-// Kernel symbol labels for the profiling records (one per template instance).
-const char* nt_name(int cfg, int odt) {
-  static const char* names[kNumNtCfgs][2] = {
-      {"k_nt<128,128,f32>", "k_nt<128,128,bf16>"}, {"k_nt<256,256,f32>", "k_nt<256,256,bf16>"},
-      {"k_nt<256,128,f32>", "k_nt<256,128,bf16>"}, {"k_nt<128,256,f32>", "k_nt<128,256,bf16>"}};
-  return names[cfg][odt == kBF16 ? 1 : 0];
+// Kernel symbol labels for the profiling records (one per template instance;
+// ",qt": the instance that reads Q k-major).
+const char* nt_name(int cfg, int odt, int qt = 0) {
+  static const char* names[2][kNumNtCfgs][2] = {
+      {{"k_nt<128,128,f32>", "k_nt<128,128,bf16>"}, {"k_nt<256,256,f32>", "k_nt<256,256,bf16>"},
+       {"k_nt<256,128,f32>", "k_nt<256,128,bf16>"}, {"k_nt<128,256,f32>", "k_nt<128,256,bf16>"}},
+      {{"k_nt<128,128,f32,qt>", "k_nt<128,128,bf16,qt>"}, {"k_nt<256,256,f32,qt>", "k_nt<256,256,bf16,qt>"},
+       {"k_nt<256,128,f32,qt>", "k_nt<256,128,bf16,qt>"}, {"k_nt<128,256,f32,qt>", "k_nt<128,256,bf16,qt>"}}};
+  return names[qt ? 1 : 0][cfg][odt == kBF16 ? 1 : 0];
 }
 const char* rs_name(bool nn, int idt, int odt) {
   if (idt == kF32) return nn ? "k_gemm<f32,f32,NN>" : "k_gemm<f32,f32,NT>";
@@ -288,8 +291,8 @@ int materialize(muon_plan* p) {
       for (int c = 0; c < kNumNtCfgs; ++c) {
         D.fl_gram[c] = S.fl_gram[c];
         D.fl_square[c] = S.fl_square[c];
-        D.fl_apply[c] = S.fl_apply[c];
       }
+      for (int c = 0; c < 2 * kNumNtCfgs; ++c) D.fl_apply[c] = S.fl_apply[c];
       if ((rc = dev_alloc(p, &D.mats, nsm.size() * sizeof(NsMat)))) return rc;
       HIP_TRY(hipMemcpy(D.mats, nsm.data(), nsm.size() * sizeof(NsMat), hipMemcpyHostToDevice));
       auto upload = [&](const std::vector<ItemHost>& v, Items* out) -> int {
@@ -303,8 +306,9 @@ int materialize(muon_plan* p) {
         return MUON_OK;
       };
       for (int c = 0; c < kNumNtCfgs; ++c)
-        if ((rc = upload(S.nt_sym[c], &D.nt_sym[c])) || (rc = upload(S.nt_full[c], &D.nt_full[c])))
-          return rc;
+        if ((rc = upload(S.nt_sym[c], &D.nt_sym[c]))) return rc;
+      for (int c = 0; c < 2 * kNumNtCfgs; ++c)
+        if ((rc = upload(S.nt_full[c], &D.nt_full[c]))) return rc;
       if ((rc = upload(S.old_sym, &D.old_sym)) || (rc = upload(S.old_full, &D.old_full))) return rc;
       C.sets.push_back(D);
     }
@@ -426,12 +430,15 @@ int enqueue_ns(muon_plan* p, const SetDev& S, int T, const float* sched, const E
           if ((rc = run(p, kNsComb, nt_name(cfg, kBF16), S.fl_square[cfg], 0, s, [&] { return launch_gemm_nt(cfg, kBF16, g2, s); }))) return rc;
         }
         const int odt = last ? kF32 : kBF16;
-        for (int cfg = 0; cfg < kNumNtCfgs; ++cfg) {
-          if (!S.nt_full[cfg].n) continue;
-          GemmParams g3 = gp(S, S.nt_full[cfg], false, kShapeApplyT, kB, srcT, -1, dst, -1, dstT, 1.f,
-                             0.f, 0.f, k == 0 ? 1 : 0, rs);
+        for (int fi = 0; fi < 2 * kNumNtCfgs; ++fi) {
+          if (!S.nt_full[fi].n) continue;
+          const int cfg = fi % kNumNtCfgs, qt = fi / kNumNtCfgs;
+          // qt: B X reads X itself k-major and no transposed copy is written
+          GemmParams g3 = gp(S, S.nt_full[fi], false, kShapeApplyT, kB, qt ? src : srcT, -1, dst, -1,
+                             qt ? -1 : dstT, 1.f, 0.f, 0.f, k == 0 ? 1 : 0, rs);
+          g3.qt = qt;
           if (last && dyn) fuse_update(&g3, dyn, lr, wd);
-          if ((rc = run(p, kNsApply, nt_name(cfg, odt), S.fl_apply[cfg], 0, s, [&] { return launch_gemm_nt(cfg, odt, g3, s); }))) return rc;
+          if ((rc = run(p, kNsApply, nt_name(cfg, odt, qt), S.fl_apply[fi], 0, s, [&] { return launch_gemm_nt(cfg, odt, g3, s); }))) return rc;
         }
       }
       return MUON_OK;
@@ -467,11 +474,14 @@ int enqueue_ns(muon_plan* p, const SetDev& S, int T, const float* sched, const E
         if ((rc = run(p, kGramSquare, rs_name(false, kF32, kF32), fl_square, 0, s, [&] { return launch_gemm(0, kF32, kF32, ga, s); }))) return rc;
       }
     }
-    for (int cfg = 0; cfg < kNumNtCfgs; ++cfg) {
-      if (!S.nt_full[cfg].n) continue;
-      GemmParams gf = gp(S, S.nt_full[cfg], false, kShapeApplyT, kQH, kX0T, -1, kXT, -1, -1, 1.f, 0.f, 0.f, 1, rs);
+    for (int fi = 0; fi < 2 * kNumNtCfgs; ++fi) {
+      if (!S.nt_full[fi].n) continue;
+      const int cfg = fi % kNumNtCfgs, qt = fi / kNumNtCfgs;
+      GemmParams gf = gp(S, S.nt_full[fi], false, kShapeApplyT, kQH, qt ? kX0 : kX0T, -1, kXT, -1, -1,
+                         1.f, 0.f, 0.f, 1, rs);
+      gf.qt = qt;
       if (dyn) fuse_update(&gf, dyn, lr, wd);
-      if ((rc = run(p, kGramFinal, nt_name(cfg, kF32), S.fl_apply[cfg], 0, s, [&] { return launch_gemm_nt(cfg, kF32, gf, s); }))) return rc;
+      if ((rc = run(p, kGramFinal, nt_name(cfg, kF32, qt), S.fl_apply[fi], 0, s, [&] { return launch_gemm_nt(cfg, kF32, gf, s); }))) return rc;
     }
     return MUON_OK;
   }

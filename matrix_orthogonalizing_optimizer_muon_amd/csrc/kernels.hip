@@ -977,7 +977,7 @@ __device__ __forceinline__ void nt_epilogue(const nt::f32x16_t (&acc)[BM / 32 / 
   }
 }
 
-template <int BM, int BN, int WGM, int WGN, typename TO>
+template <int BM, int BN, int WGM, int WGN, typename TO, bool QT>
 __global__ __launch_bounds__(64 * WGM * WGN) void k_nt(const GemmParams p) {
   extern __shared__ __attribute__((aligned(1024))) char nt_smem[];
   using G = nt::Geom<BM, BN, 64, 2, WGM, WGN>;
@@ -990,8 +990,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_nt(const GemmParams p) {
     K = n_pad; ldp = ldq = n_pad; ldo = m_pad; Mr = Nr = nmp->m; p_rows = q_rows = m_pad;
   } else if (p.shape == kShapeSquare) {
     K = m_pad; ldp = ldq = m_pad; ldo = m_pad; Mr = Nr = nmp->m; p_rows = q_rows = m_pad;
-  } else {
+  } else if (!QT) {
     K = m_pad; ldp = ldq = m_pad; ldo = n_pad; Mr = nmp->m; Nr = nmp->n; p_rows = m_pad; q_rows = n_pad;
+  } else {
+    // Q = X itself, m_pad rows (k) of n_pad
+    K = m_pad; ldp = m_pad; ldq = n_pad; ldo = n_pad; Mr = nmp->m; Nr = nmp->n; p_rows = m_pad;
+    q_rows = m_pad;
   }
   const void* Pg = nmp->buf[p.p_id];
   const void* Qg = nmp->buf[p.q_id];
@@ -999,18 +1003,18 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_nt(const GemmParams p) {
   const __amdgpu_buffer_rsrc_t Qr = nt::make_rsrc(Qg, q_rows * (uint32_t)ldq * 2u);
   const int m0 = it.tm * BM, n0 = it.tn * BN;
   nt::f32x16_t acc[G::MT][G::NT];
-  nt::mainloop<BM, BN, 64, 2, WGM, WGN>(acc, (MUON_LDS char*)nt_smem, Pr, Qr, (uint32_t)ldp,
-                                        (uint32_t)ldq, (uint32_t)m0, (uint32_t)n0, K);
+  nt::mainloop<BM, BN, 64, 2, WGM, WGN, QT>(acc, (MUON_LDS char*)nt_smem, Pr, Qr, (uint32_t)ldp,
+                                            (uint32_t)ldq, (uint32_t)m0, (uint32_t)n0, K);
 
   nt_epilogue<BM, BN, WGM, WGN, TO>(acc, (MUON_LDS float*)nt_smem, p, nmp, m0, n0, ldo, Mr, Nr);
 }
 
-template <int BM, int BN, int WGM, int WGN, typename TO>
+template <int BM, int BN, int WGM, int WGN, typename TO, bool QT>
 hipError_t launch_nt_t(const GemmParams& p, hipStream_t s) {
-  using G = nt::Geom<BM, BN, 64, 2, WGM, WGN>;
+  using G = nt::Geom<BM, BN, 64, 2, WGM, WGN, QT>;
   constexpr int smem = G::LDS;
   static bool attr_done = false;
-  auto kern = &k_nt<BM, BN, WGM, WGN, TO>;
+  auto kern = &k_nt<BM, BN, WGM, WGN, TO, QT>;
   if (!attr_done) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, smem);
@@ -1024,8 +1028,14 @@ hipError_t launch_nt_t(const GemmParams& p, hipStream_t s) {
 
 template <int BM, int BN, int WGM, int WGN>
 hipError_t launch_nt_cfg(int out_dt, const GemmParams& p, hipStream_t s) {
-  if (out_dt == kBF16) return launch_nt_t<BM, BN, WGM, WGN, uint16_t>(p, s);
-  if (out_dt == kF32) return launch_nt_t<BM, BN, WGM, WGN, float>(p, s);
+  if (p.qt) {
+    if (p.shape != kShapeApplyT) return hipErrorInvalidValue;
+    if (out_dt == kBF16) return launch_nt_t<BM, BN, WGM, WGN, uint16_t, true>(p, s);
+    if (out_dt == kF32) return launch_nt_t<BM, BN, WGM, WGN, float, true>(p, s);
+    return hipErrorInvalidValue;
+  }
+  if (out_dt == kBF16) return launch_nt_t<BM, BN, WGM, WGN, uint16_t, false>(p, s);
+  if (out_dt == kF32) return launch_nt_t<BM, BN, WGM, WGN, float, false>(p, s);
   return hipErrorInvalidValue;
 }
 

@@ -136,6 +136,9 @@ struct GemmParams {
   int32_t fuse;
   const EwDyn* dyn;
   float lr, wd;
+  // NT kernel, kShapeApplyT: 1 = Q is X itself (m_pad x n_pad, read k-major
+  // with LDS transpose reads) instead of X^T
+  int32_t qt;
 };
 
 // Kernel configurations (the planner's tile choices).

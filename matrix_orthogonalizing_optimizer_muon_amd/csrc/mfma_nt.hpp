@@ -12,6 +12,12 @@
 // chunk) hit 16 distinct 16-byte bank groups.  A lane's MFMA fragment is the
 // 16 bytes of chunk (2*kg + lane/32) of row (lane % 32) of a 32-row slab.
 //
+// With QT the second operand is stored the other way, Q[k][j] (k-major, j
+// contiguous): acc(i, j) += sum_k P[i][k] * Q[k][j].  Its k-tile is copied as
+// BK rows of BN elements and the MFMA B fragments are read with the gfx950
+// LDS transpose read (ds_read_b64_tr_b16), so no transposed copy of Q has to
+// exist in memory.
+//
 // The buffer descriptors carry the byte size of each operand, so an access
 // outside it reads zeros instead of faulting; the callers still only issue
 // in-bounds tiles (every extent is padded to the tile size).
@@ -44,7 +50,7 @@ constexpr int kWaitVmLgkm0 = 0x0070;   // vmcnt(0) lgkmcnt(0)
 
 // BM x BN output tile, BK bf16 per k-tile (32 or 64), S LDS stages, a WGM x WGN
 // grid of waves (each owns a (BM/WGM) x (BN/WGN) tile).
-template <int BM, int BN, int BK, int S, int WGM = 2, int WGN = 2>
+template <int BM, int BN, int BK, int S, int WGM = 2, int WGN = 2, bool QT = false>
 struct Geom {
   static constexpr int NW = WGM * WGN;                 // waves per block
   static constexpr int THREADS = 64 * NW;
@@ -59,10 +65,19 @@ struct Geom {
   static constexpr int LDS = S * STAGE;
   static constexpr int RPI = 1024 / ROWB;              // rows per wave copy instruction
   static constexpr int RPR = NW * RPI;                 // rows per round of all waves
-  static constexpr int PR = BM / RPR, QR = BN / RPR;   // copy rounds per operand
+  // Q tile: BN rows of BK (NT) or, with QT, BK rows of BN elements
+  static constexpr int QROWB = QT ? BN * 2 : ROWB;     // bytes per Q tile row
+  static constexpr int QCPR = QROWB / 16;
+  static constexpr int QRPI = 1024 / QROWB;
+  static constexpr int QRPR = NW * QRPI;
+  static constexpr int QROWS = QT ? BK : BN;
+  static constexpr bool QT_ = QT;
+  static constexpr int NDS = MT + (QT ? 2 : 1) * NT;   // LDS fragment reads per k-group
+  static constexpr int PR = BM / RPR, QR = QROWS / QRPR;   // copy rounds per operand
   static constexpr int NI = PR + QR;                   // copy instructions per wave per tile
   static_assert(BK == 32 || BK == 64, "k-tile");
-  static_assert(WM % 32 == 0 && WN % 32 == 0 && BM % RPR == 0 && BN % RPR == 0, "tile edges");
+  static_assert(WM % 32 == 0 && WN % 32 == 0 && BM % RPR == 0 && QROWS % QRPR == 0, "tile edges");
+  static_assert(!QT || (QCPR >= 16 && QRPI >= 1), "k-major Q tiles need rows of >= 256 bytes");
   static_assert(S >= 2 && LDS <= 160 * 1024, "LDS budget");
   static_assert((S - 1) * NI <= 63, "vmcnt range");
 };
@@ -74,6 +89,13 @@ __device__ __forceinline__ int swz(int r) {
   return (r / (256 / ROWB)) % (ROWB / 16);
 }
 
+// LDS slot of 16-byte chunk c of row k of a k-major Q tile: c ^ swzt(k).  A
+// transpose read by 16 lanes covers rows k..k+3 (k a multiple of 4) at two
+// adjacent chunks; the pattern puts those 4 pairs on 4 distinct 32-byte bank
+// groups of a 128-byte window, and the pairs of the next 16 lanes (the next
+// two chunks, same rows) on the rest of the 256-byte window.
+__device__ __forceinline__ int swzt(int k) { return 4 * (k & 3) + 2 * ((k >> 1) & 1); }
+
 // Global -> LDS copies of one operand.  Wave w copies the contiguous run of
 // tile rows [w * NR * RPI, (w+1) * NR * RPI): copy u writes LDS bytes
 // [(w*NR + u) KiB, +1 KiB), i.e. RPI whole rows, lane l into row l / CPR,
@@ -81,9 +103,14 @@ __device__ __forceinline__ int swz(int r) {
 // (the LDS base) changes every fourth copy; the 12-bit immediate supplies the
 // 1 KiB steps in between.  The immediate also advances the global address, so
 // the scalar offset takes it back out.
-template <class G, int NR>
+template <class G, int NR, bool T = false>
 struct Copier {
-  static_assert(NR % 2 == 0 || G::ROWB == 64, "the swizzle phase must follow the copy index");
+  // geometry of the copied tile: the P / NT layout, or the k-major Q tile
+  static constexpr int RPI = T ? G::QRPI : G::RPI;
+  static constexpr int CPR = T ? G::QCPR : G::CPR;
+  static constexpr int ROWB = T ? G::QROWB : G::ROWB;
+  static_assert(T || NR % 2 == 0 || G::ROWB == 64, "the swizzle phase must follow the copy index");
+  static_assert(!T || RPI == 2 || RPI == 4, "k-major rows per copy");
   __amdgpu_buffer_rsrc_t rsrc;
   uint32_t voff[2];   // per-lane offsets for even / odd copies (swizzle phase)
   uint32_t soff;      // bytes to the wave's first row (row-block origin added per call)
@@ -93,11 +120,11 @@ struct Copier {
     rsrc = r;
 #pragma unroll
     for (int par = 0; par < 2; ++par) {
-      const int row = (w * NR + par) * G::RPI + lane / G::CPR;   // any copy of this parity
-      const int chunk = (lane % G::CPR) ^ swz<G::ROWB>(row);
-      voff[par] = (uint32_t)(lane / G::CPR) * ld_bytes + (uint32_t)chunk * 16u;
+      const int row = (w * NR + par) * RPI + lane / CPR;   // any copy of this parity
+      const int chunk = (lane % CPR) ^ (T ? swzt(row) : swz<ROWB>(row));
+      voff[par] = (uint32_t)(lane / CPR) * ld_bytes + (uint32_t)chunk * 16u;
     }
-    step = (uint32_t)G::RPI * ld_bytes;
+    step = (uint32_t)RPI * ld_bytes;
     soff = (uint32_t)(w * NR) * step;
   }
 
@@ -127,16 +154,53 @@ struct Frags {
 // Fragments of k-group kg (16 k values) of the stage at `st`: lane l reads
 // chunk (2 kg + l / 32) of row (l % 32) of every 32-row slab of its wave tile.
 template <class G>
+__device__ __forceinline__ void load_frags_qt(u32x4_t (&b)[G::NT], const MUON_LDS char* stq, int kg,
+                                              int lane, int wx);
+
+template <class G>
 __device__ __forceinline__ void load_frags(Frags<G>& f, const MUON_LDS char* st, int kg, int lane,
                                            int wy, int wx) {
   const int lr = lane & 31, hi = lane >> 5;
   const int q = ((kg * 2 + hi) ^ swz<G::ROWB>(lr)) * 16;
   const MUON_LDS char* pa = st + (wy * G::WM + lr) * G::ROWB + q;
-  const MUON_LDS char* qa = st + G::PB + (wx * G::WN + lr) * G::ROWB + q;
 #pragma unroll
   for (int i = 0; i < G::MT; ++i) f.a[i] = *(const MUON_LDS u32x4_t*)(pa + i * 32 * G::ROWB);
+  if constexpr (G::QT_) {
+    load_frags_qt<G>(f.b, st + G::PB, kg, lane, wx);
+  } else {
+    const MUON_LDS char* qa = st + G::PB + (wx * G::WN + lr) * G::ROWB + q;
 #pragma unroll
-  for (int j = 0; j < G::NT; ++j) f.b[j] = *(const MUON_LDS u32x4_t*)(qa + j * 32 * G::ROWB);
+    for (int j = 0; j < G::NT; ++j) f.b[j] = *(const MUON_LDS u32x4_t*)(qa + j * 32 * G::ROWB);
+  }
+}
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// B fragments of k-group kg from a k-major Q tile (G::QT).  A 32x32x16 B
+// fragment is lane l: Q[k0 + 8 (l / 32) + 0..7][j0 + l % 32].  The transpose
+// read gives lane i of each 16-lane group element (i % 4) of the 8 bytes that
+// lane 4e + i / 4 addresses, for e = 0..3; so lane s of group g addresses row
+// k0 + 8 (g / 2) + s / 4 (then 4 rows further for the second read), columns
+// j0 + 16 (g % 2) + 4 (s % 4) .. + 3, and receives its column's 4 + 4 k values.
+template <class G>
+__device__ __forceinline__ void load_frags_qt(u32x4_t (&b)[G::NT], const MUON_LDS char* stq, int kg,
+                                              int lane, int wx) {
+  const int g = lane >> 4, sl = lane & 15;
+  const int k = kg * 16 + 8 * (g >> 1) + (sl >> 2);
+  const int off = ((g & 1) * 16 + 4 * (sl & 3)) * 2;       // byte offset of the lane's 4 columns
+  const int sw = swzt(k);                                   // = swzt(k + 4)
+#pragma unroll
+  for (int j = 0; j < G::NT; ++j) {
+    const int byte = (wx * G::WN + j * 32) * 2 + off;
+    const int a = (((byte >> 4) ^ sw) << 4) + (byte & 15);
+    const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (MUON_LDS s16x4_t*)(stq + k * G::QROWB + a));
+    const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (MUON_LDS s16x4_t*)(stq + (k + 4) * G::QROWB + a));
+    const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
+    b[j] = u32x4_t{l2[0], l2[1], h2[0], h2[1]};
+  }
 }
 
 template <class G>
@@ -185,12 +249,12 @@ __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "
 // last group's MFMAs and the reads of group 0 of tile kt+1.  Copies past the
 // last tile re-read the last tile (in bounds, never consumed) so the steady
 // state has no branches and always S-1 tiles in flight.
-template <int BM, int BN, int BK, int S, int WGM = 2, int WGN = 2>
+template <int BM, int BN, int BK, int S, int WGM = 2, int WGN = 2, bool QT = false>
 __device__ __forceinline__ void mainloop(
     f32x16_t (&acc)[BM / 32 / WGM][BN / 32 / WGN],
     MUON_LDS char* lds, __amdgpu_buffer_rsrc_t P, __amdgpu_buffer_rsrc_t Q, uint32_t ldp,
     uint32_t ldq, uint32_t m0, uint32_t n0, int K) {
-  using G = Geom<BM, BN, BK, S, WGM, WGN>;
+  using G = Geom<BM, BN, BK, S, WGM, WGN, QT>;
   static_assert(G::KG % 2 == 0, "the last group's fragments are in f1");
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -202,45 +266,50 @@ __device__ __forceinline__ void mainloop(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
   Copier<G, G::PR> cp;
-  Copier<G, G::QR> cq;
+  Copier<G, G::QR, QT> cq;
   cp.init(P, ldp * 2u, lane, w);
   cq.init(Q, ldq * 2u, lane, w);
-  const uint32_t sp = m0 * ldp * 2u, sq = n0 * ldq * 2u;
+  // k-tile byte steps: along a P row; along a Q row (NT) or down BK Q rows (QT)
+  const uint32_t sp = m0 * ldp * 2u, sq = QT ? n0 * 2u : n0 * ldq * 2u;
+  const uint32_t kq = QT ? (uint32_t)BK * ldq * 2u : (uint32_t)G::ROWB;
   const int nk = K / BK;
-  const uint32_t klast = (uint32_t)(nk - 1) * G::ROWB;
+  const uint32_t klast = (uint32_t)(nk - 1) * G::ROWB, klast_q = (uint32_t)(nk - 1) * kq;
 #pragma unroll
   for (int t = 0; t < S; ++t) {
     const uint32_t kb = t < nk ? (uint32_t)t * G::ROWB : klast;
+    const uint32_t kbq = t < nk ? (uint32_t)t * kq : klast_q;
     cp.issue(lds + t * G::STAGE, sp + kb, w);
-    cq.issue(lds + t * G::STAGE + G::PB, sq + kb, w);
+    cq.issue(lds + t * G::STAGE + G::PB, sq + kbq, w);
   }
   __builtin_amdgcn_s_waitcnt(waitcnt_vm((S - 1) * G::NI));   // tile 0 landed
   block_barrier();
   Frags<G> f0, f1;
   load_frags<G>(f0, lds, 0, lane, wy, wx);
   int stage = 0;
-  uint32_t knext = (uint32_t)S * G::ROWB;
+  uint32_t knext = (uint32_t)S * G::ROWB, knext_q = (uint32_t)S * kq;
   for (int kt = 0; kt < nk; ++kt) {
     const MUON_LDS char* st = lds + stage * G::STAGE;
 #pragma unroll
     for (int g = 0; g + 1 < G::KG; ++g) {
       if (g & 1) { load_frags<G>(f0, st, g + 1, lane, wy, wx); mfma_group<G>(acc, f1); }
       else       { load_frags<G>(f1, st, g + 1, lane, wy, wx); mfma_group<G>(acc, f0); }
-      interleave_hint<G, 0, G::MT + G::NT>();
+      interleave_hint<G, 0, G::NDS>();
     }
     // tile kt+1 landed (S-2 later tiles may stay in flight), own reads done
     constexpr int kWait = waitcnt_vm((S - 2) * G::NI) & ~0xF00;
     __builtin_amdgcn_s_waitcnt(kWait);
     block_barrier();
     const uint32_t kb = knext <= klast ? knext : klast;
+    const uint32_t kbq = knext_q <= klast_q ? knext_q : klast_q;
     knext += G::ROWB;
+    knext_q += kq;
     MUON_LDS char* dst = lds + stage * G::STAGE;
     cp.issue(dst, sp + kb, w);
-    cq.issue(dst + G::PB, sq + kb, w);
+    cq.issue(dst + G::PB, sq + kbq, w);
     stage = stage + 1 == S ? 0 : stage + 1;
     load_frags<G>(f0, lds + stage * G::STAGE, 0, lane, wy, wx);
     mfma_group<G>(acc, f1);
-    interleave_hint<G, G::NI, G::MT + G::NT>();
+    interleave_hint<G, G::NI, G::NDS>();
   }
   __builtin_amdgcn_s_waitcnt(kWaitVmLgkm0);   // no copy outlives the loop
 }

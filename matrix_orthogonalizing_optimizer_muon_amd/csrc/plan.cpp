@@ -19,8 +19,9 @@ constexpr int kXcds = 8;          // MI355X: 8 XCDs, workgroups dealt round-robi
 constexpr int kCus = 256;
 constexpr double kLaunchUs = 4.0; // per-launch cost used by the model
 
-// Tile plans: (sym config, apply config).
-constexpr TilePlan kTilePlans[5] = {{0, 0}, {0, 1}, {1, 1}, {0, 2}, {0, 3}};
+// Tile plans: (sym config, apply config, k-major reads of X in B X).
+constexpr TilePlan kTilePlans[8] = {{0, 0, 0}, {0, 1, 0}, {1, 1, 0}, {0, 2, 0}, {0, 3, 0},
+                                    {0, 0, 1}, {0, 1, 1}, {1, 1, 1}};
 
 uint64_t align_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
 int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
@@ -35,17 +36,17 @@ uint64_t layout(const ShapeKey& k, int32_t form, int32_t tile, uint64_t* off, bo
   uint64_t sizes[kPlanBufs] = {0};
   sizes[bX0] = es * mn;
   sizes[bXT] = 4 * mn;
+  // transposed copies of X only where B X reads them (not with k-major reads)
+  const bool copies = k.path && !tile_plan(tile).qt;
   if (form == kFormDirect) {
     sizes[bX1] = es * mn;
     sizes[bA] = es * mm;
     sizes[bB] = es * mm;
-    if (k.path) sizes[bX0T] = sizes[bX1T] = 2 * mn;
+    if (copies) sizes[bX0T] = sizes[bX1T] = 2 * mn;
   } else {
     sizes[bA] = sizes[bH] = sizes[bQX] = sizes[bQY] = sizes[bT1] = 4 * mm;
-    if (k.path) {
-      sizes[bQH] = 2 * mm;
-      sizes[bX0T] = 2 * mn;
-    }
+    if (k.path) sizes[bQH] = 2 * mm;
+    if (copies) sizes[bX0T] = 2 * mn;
   }
   uint64_t cur = 0;
   for (int b = 0; b < kPlanBufs; ++b) {
@@ -178,7 +179,7 @@ std::vector<std::pair<int32_t, int32_t>> candidates(const ShapeKey& k, int32_t f
     for (int t = 0; t < num_tile_plans(); ++t)
       if (want(t)) out.push_back({kFormDirect, t});
   if (gram)
-    for (int t : {0, 1, 2})
+    for (int t : {0, 1, 2, 5, 6, 7})
       if (want(t)) out.push_back({kFormGram, t});
   return out;
 }
@@ -203,7 +204,10 @@ double model_cost_us(const ShapeKey& k, int32_t form, int32_t tile, int count) {
   const TileShape s = nt_cfg_shape(tp.sym), a = nt_cfg_shape(tp.apply);
   const double st = sym_tiles(mp64, s.bm) * c, ft = (mp / a.bm) * (np / a.bn) * c;
   const double g = launch_us(st, 2.0 * s.bm * s.bn * np, nt_rate(tp.sym), nt_blocks_per_cu(tp.sym));
-  const double ap = launch_us(ft, 2.0 * a.bm * a.bn * mp, nt_rate(tp.apply), nt_blocks_per_cu(tp.apply));
+  // k-major reads: about 10% slower main loop, no X'^T stores; the model
+  // rates them slightly behind the transposed copies (timing decides)
+  const double ap = launch_us(ft, 2.0 * a.bm * a.bn * mp, nt_rate(tp.apply), nt_blocks_per_cu(tp.apply)) *
+                    (tp.qt ? 1.02 : 1.0);
   if (form == kFormDirect) {
     const double sq = launch_us(st, 2.0 * s.bm * s.bn * mp, nt_rate(tp.sym), nt_blocks_per_cu(tp.sym));
     us = T * (g + sq + ap);
@@ -276,7 +280,8 @@ std::string build_plan(const std::vector<int64_t>& rows, const std::vector<int64
       M.group = gi;
       {
         const double e = (double)M.rows * M.cols, pes = M.dtype ? 2 : 4, es = M.path ? 2 : 4;
-        const double ew = e * (pes + 8 + es + (M.path ? es : 0) + 2 * pes + (M.path ? 0 : 4));
+        const bool dt = M.path && !tile_plan(g.tile).qt;   // D^T written by the momentum kernel
+        const double ew = e * (pes + 8 + es + (dt ? es : 0) + 2 * pes + (M.path ? 0 : 4));
         M.cost_us = ns_us + ew / 5e12 * 1e6;
       }
       padded_dims(kv.first, g.form, g.tile, &M.m_pad, &M.n_pad);
@@ -352,10 +357,10 @@ std::string build_plan(const std::vector<int64_t>& rows, const std::vector<int64
         const TilePlan tp = tile_plan(M.tile);
         const TileShape s = nt_cfg_shape(tp.sym), a = nt_cfg_shape(tp.apply);
         add_sym(S->nt_sym[tp.sym], slot, M.m_pad, s.bm);
-        add_full(S->nt_full[tp.apply], slot, M.m_pad, M.n_pad, a);
+        add_full(S->nt_full[full_list(tp.apply, tp.qt)], slot, M.m_pad, M.n_pad, a);
         S->fl_gram[tp.sym] += fg;
         S->fl_square[tp.sym] += fs;
-        S->fl_apply[tp.apply] += fa;
+        S->fl_apply[full_list(tp.apply, tp.qt)] += fa;
         const double st = sym_tiles(M.m_pad, s.bm);
         S->flops_gram_issued += st * 2.0 * s.bm * s.bn * np;
         S->flops_apply_issued += (mp / a.bm) * (np / a.bn) * 2.0 * a.bm * a.bn * mp;
@@ -383,10 +388,8 @@ std::string build_plan(const std::vector<int64_t>& rows, const std::vector<int64
       auto kn = [&](const ItemHost& it) { return P.mats[S.mats[it.slot]].n_pad; };
       auto km = [&](const ItemHost& it) { return P.mats[S.mats[it.slot]].m_pad; };
       std::vector<std::vector<ItemHost>*> sym{&S.old_sym}, full{&S.old_full};
-      for (int c = 0; c < kNtTiles; ++c) {
-        sym.push_back(&S.nt_sym[c]);
-        full.push_back(&S.nt_full[c]);
-      }
+      for (int c = 0; c < kNtTiles; ++c) sym.push_back(&S.nt_sym[c]);
+      for (int c = 0; c < 2 * kNtTiles; ++c) full.push_back(&S.nt_full[c]);
       for (std::vector<ItemHost>* v : sym) {
         std::stable_sort(v->begin(), v->end(),
                          [&](const ItemHost& x, const ItemHost& y) { return kn(x) > kn(y); });
@@ -405,7 +408,7 @@ std::string build_plan(const std::vector<int64_t>& rows, const std::vector<int64
 
 std::string serialize_plan(const PlanHost& p) {
   std::ostringstream o;
-  o << "muon-plan v3\n";
+  o << "muon-plan v4\n";
   o << "opts nesterov=" << p.opts.nesterov << " eps=" << std::hexfloat << p.opts.eps
     << " rms=" << p.opts.rms_scale << std::defaultfloat << " precision=" << p.opts.precision
     << " form=" << p.opts.form << " tile=" << p.opts.tile << " cap=" << p.opts.workspace_cap
@@ -429,7 +432,8 @@ std::string serialize_plan(const PlanHost& p) {
       << " lanes=" << C.n_lanes << "\n";
     for (const LaunchSetPlan& S : C.sets) {
       o << " set path=" << S.path << " form=" << S.form << " lane=" << S.lane << " mats=" << S.mats.size() << " items=";
-      for (int c = 0; c < kNtTiles; ++c) o << S.nt_sym[c].size() << "/" << S.nt_full[c].size() << ",";
+      for (int c = 0; c < kNtTiles; ++c)
+        o << S.nt_sym[c].size() << "/" << S.nt_full[c].size() << "/" << S.nt_full[c + kNtTiles].size() << ",";
       o << S.old_sym.size() << "/" << S.old_full.size() << " order=";
       uint64_t h = 1469598103934665603ull;
       auto mix = [&](int32_t v) { for (int b = 0; b < 4; ++b) { h ^= (uint8_t)(v >> (8 * b)); h *= 1099511628211ull; } };
@@ -437,6 +441,7 @@ std::string serialize_plan(const PlanHost& p) {
       for (int c = 0; c < kNtTiles; ++c) {
         lists.push_back(&S.nt_sym[c]);
         lists.push_back(&S.nt_full[c]);
+        lists.push_back(&S.nt_full[c + kNtTiles]);
       }
       lists.push_back(&S.old_sym);
       lists.push_back(&S.old_full);

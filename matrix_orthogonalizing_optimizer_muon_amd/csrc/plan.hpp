@@ -36,9 +36,15 @@ constexpr TileShape kNtTileShapes[kNtTiles] = {{128, 128}, {256, 256}, {256, 128
 TileShape nt_cfg_shape(int cfg);
 
 // A tile plan: the NT kernel configuration of the symmetric m x m products
-// (X X^T, A A; square tiles) and of the m x n product B X.  The fp32 path runs
+// (X X^T, A A; square tiles), that of the m x n product B X, and how B X
+// reads X: from a transposed copy X^T kept beside X (qt = 0: the epilogue of
+// every B X also writes X'^T), or k-major from X itself with LDS transpose
+// reads (qt = 1: no transposed copies; slower main loop).  The fp32 path runs
 // the 128 x 128 register-staged kernel and has the single plan 0.
-struct TilePlan { int32_t sym, apply; };
+struct TilePlan { int32_t sym, apply, qt; };
+
+// Work-item list of the m x n product for NT configuration cfg and read mode qt.
+constexpr int full_list(int cfg, int qt) { return cfg + kNtTiles * qt; }
 int num_tile_plans();
 TilePlan tile_plan(int t);
 
@@ -109,12 +115,12 @@ struct LaunchSetPlan {
   int32_t lane = 0;                        // NS lane (stream) the set's launches go to
   std::vector<int32_t> mats;               // matrix indices, in slot order
   std::vector<ItemHost> nt_sym[kNtTiles];  // upper-triangle m x m tiles per NT configuration
-  std::vector<ItemHost> nt_full[kNtTiles]; // m x n tiles per NT configuration
+  std::vector<ItemHost> nt_full[2 * kNtTiles]; // m x n tiles per (NT configuration, read mode)
   std::vector<ItemHost> old_sym;           // upper-triangle 128-tiles (fp32 kernel)
   std::vector<ItemHost> old_full;          // m x n 128-tiles (fp32 kernel)
   // symmetric-aware algorithmic flops of one product over the matrices of each
   // NT configuration's launch (bf16 path) or of the whole set (fp32 path: index 0)
-  double fl_gram[kNtTiles] = {0}, fl_square[kNtTiles] = {0}, fl_apply[kNtTiles] = {0};
+  double fl_gram[kNtTiles] = {0}, fl_square[kNtTiles] = {0}, fl_apply[2 * kNtTiles] = {0};
   double flops_gram_min = 0;       // one X X^T over the set
   double flops_square_min = 0;     // one symmetric m x m product over the set
   double flops_apply_min = 0;      // one (m x m)(m x n) product over the set

@@ -28,7 +28,7 @@ def test_every_declared_function_is_exported_and_bound():
         assert hasattr(lib, n), n
         assert n in L.PROTOTYPES, f"{n} has no ctypes prototype"
     assert set(L.PROTOTYPES) == set(names)
-    assert lib.muon_abi_version() == 7
+    assert lib.muon_abi_version() == 8
 
 
 def test_struct_sizes_match_header_layout():
@@ -208,7 +208,7 @@ def test_tune_cache_is_read_and_bad_lines_ignored(tmp_path):
         "garbage line\n"
         "muon-tune-v2 host m=512 n=16384 path=1 form=2 tile=1 us=400\n"
         "muon-tune-v2 host m=1024 n=1024 path=1 form=9 tile=0 us=1\n"
-        "muon-tune-v2 host m=2048 n=2048 path=1 form=1 tile=7 us=1\n"
+        "muon-tune-v2 host m=2048 n=2048 path=1 form=1 tile=8 us=1\n"
         "muon-tune-v1 host m=256 n=256 path=1 form=2 tile=0 us_direct=1 us_gram=1\n"
         "muon-tune-v2 otherdev m=64 n=64 path=1 form=2 tile=0 us=1\n")
     shapes = [(512, 16384), (1024, 1024), (64, 64), (2048, 2048), (256, 256)]
