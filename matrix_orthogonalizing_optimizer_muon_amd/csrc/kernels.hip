@@ -710,12 +710,21 @@ __device__ __forceinline__ void st_bf16x4(void* base, int64_t off, const float* 
       u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
 }
 
+// Pipeline of each NT configuration: k-tile (elements) and LDS stages.  One
+// setting serves all four: k-tiles of 32 with three or four stages were
+// measured slower on the 128x128 tile.
+template <int BM, int BN, int WGM, int WGN>
+struct NtPipe {
+  static constexpr int BK = 64, S = 2;
+};
+
 // Rows of the output tile staged in LDS at a time: the largest power of two
 // whose fp32 slab (row pitch BN + 4 floats) fits the mainloop's LDS.
 template <int BM, int BN, int WGM, int WGN>
 constexpr int slab_rows() {
   int sh = BM;
-  while (sh > 8 && sh * (BN + 4) * 4 > nt::Geom<BM, BN, 64, 2, WGM, WGN>::LDS) sh /= 2;
+  using P = NtPipe<BM, BN, WGM, WGN>;
+  while (sh > 8 && sh * (BN + 4) * 4 > nt::Geom<BM, BN, P::BK, P::S, WGM, WGN>::LDS) sh /= 2;
   return sh;
 }
 
@@ -832,7 +841,8 @@ __device__ __forceinline__ void nt_epilogue(const nt::f32x16_t (&acc)[BM / 32 / 
                                             MUON_LDS float* C, const GemmParams& p,
                                             const NsMat* nmp, int m0, int n0, int ldo, int Mr,
                                             int Nr) {
-  using G = nt::Geom<BM, BN, 64, 2, WGM, WGN>;
+  using PP = NtPipe<BM, BN, WGM, WGN>;
+  using G = nt::Geom<BM, BN, PP::BK, PP::S, WGM, WGN>;
   constexpr int NT = G::THREADS;
   constexpr int SH = slab_rows<BM, BN, WGM, WGN>();
   constexpr int PITCH = BN + 4;
@@ -980,7 +990,8 @@ __device__ __forceinline__ void nt_epilogue(const nt::f32x16_t (&acc)[BM / 32 / 
 template <int BM, int BN, int WGM, int WGN, typename TO, bool QT>
 __global__ __launch_bounds__(64 * WGM * WGN) void k_nt(const GemmParams p) {
   extern __shared__ __attribute__((aligned(1024))) char nt_smem[];
-  using G = nt::Geom<BM, BN, 64, 2, WGM, WGN>;
+  using PP = NtPipe<BM, BN, WGM, WGN>;
+  using G = nt::Geom<BM, BN, PP::BK, PP::S, WGM, WGN>;
   const WorkItem it = p.items[blockIdx.x];
   const NsMat* nmp = p.mats + it.slot;
   const int m_pad = nmp->m_pad, n_pad = nmp->n_pad;
@@ -1003,7 +1014,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_nt(const GemmParams p) {
   const __amdgpu_buffer_rsrc_t Qr = nt::make_rsrc(Qg, q_rows * (uint32_t)ldq * 2u);
   const int m0 = it.tm * BM, n0 = it.tn * BN;
   nt::f32x16_t acc[G::MT][G::NT];
-  nt::mainloop<BM, BN, 64, 2, WGM, WGN, QT>(acc, (MUON_LDS char*)nt_smem, Pr, Qr, (uint32_t)ldp,
+  nt::mainloop<BM, BN, PP::BK, PP::S, WGM, WGN, QT>(acc, (MUON_LDS char*)nt_smem, Pr, Qr, (uint32_t)ldp,
                                             (uint32_t)ldq, (uint32_t)m0, (uint32_t)n0, K);
 
   nt_epilogue<BM, BN, WGM, WGN, TO>(acc, (MUON_LDS float*)nt_smem, p, nmp, m0, n0, ldo, Mr, Nr);
@@ -1011,7 +1022,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_nt(const GemmParams p) {
 
 template <int BM, int BN, int WGM, int WGN, typename TO, bool QT>
 hipError_t launch_nt_t(const GemmParams& p, hipStream_t s) {
-  using G = nt::Geom<BM, BN, 64, 2, WGM, WGN, QT>;
+  using PP = NtPipe<BM, BN, WGM, WGN>;
+  using G = nt::Geom<BM, BN, PP::BK, PP::S, WGM, WGN, QT>;
   constexpr int smem = G::LDS;
   static bool attr_done = false;
   auto kern = &k_nt<BM, BN, WGM, WGN, TO, QT>;
