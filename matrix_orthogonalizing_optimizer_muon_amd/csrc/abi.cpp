@@ -75,12 +75,19 @@ struct ChunkDev {
   bool upload_pending = false;
   float* partials = nullptr;
   int64_t total_tiles = 0;
-  double bytes_mom = 0, bytes_apply = 0;
+  double bytes_apply = 0;
   bool all_fused = false;     // every matrix's update is applied by its last NS product
   double bytes_apply_unfused = 0;   // k_ew_apply bytes when fused matrices are skipped
-  double bytes_load = 0, bytes_store = 0;   // orthogonalization alone: input -> D (and D^T), X_T -> out
+  double bytes_store = 0;   // orthogonalization alone: X_T -> out
   std::vector<SetDev> sets;
   int n_lanes = 1;
+  // lane l's matrices: mats[lane_first[l] .. lane_first[l + 1]) (contiguous in
+  // chunk order); tile_first[k]: first elementwise tile of mats[k] (k = nm: the
+  // total); per-matrix bytes of the momentum kernel and of the input load
+  // (orthogonalization alone: input -> D, and D^T when kept)
+  std::vector<int> lane_first;
+  std::vector<int64_t> tile_first;
+  std::vector<double> mat_bytes_mom, mat_bytes_load;
 };
 
 // Kernel symbol labels for the profiling records (one per template instance;
@@ -125,11 +132,11 @@ struct muon_plan {
   std::vector<void*> dev_allocs;
   std::vector<void*> host_allocs;
   std::vector<ChunkDev> chunks;
-  // NS lanes 1 .. lanes-1: a stream each (default priority, non-blocking) and
-  // the events that fork them from and join them into the caller's stream
+  // NS lanes 1 .. lanes-1: a stream each (default priority, non-blocking);
+  // lane_front[l]: lane l's front is done (lane l+1 starts on it); lane_join:
+  // lanes 1.. joined back into the caller's stream
   std::vector<hipStream_t> lane_streams;
-  std::vector<hipEvent_t> lane_join;
-  hipEvent_t lane_fork = nullptr;
+  std::vector<hipEvent_t> lane_front, lane_join;
   std::vector<float*> capture;
   bool profiling = false;
   std::vector<ProfRec> recs;
@@ -176,10 +183,10 @@ void free_plan_memory(muon_plan* p) {
   if (p->prof_epoch) (void)hipEventDestroy(p->prof_epoch);
   p->prof_epoch = nullptr;
   for (hipEvent_t e : p->lane_join) (void)hipEventDestroy(e);
-  if (p->lane_fork) (void)hipEventDestroy(p->lane_fork);
+  for (hipEvent_t e : p->lane_front) (void)hipEventDestroy(e);
   for (hipStream_t st : p->lane_streams) (void)hipStreamDestroy(st);
   p->lane_join.clear();
-  p->lane_fork = nullptr;
+  p->lane_front.clear();
   p->lane_streams.clear();
   for (void* v : p->dev_allocs) (void)hipFree(v);
   for (void* v : p->host_allocs) (void)hipHostFree(v);
@@ -239,13 +246,15 @@ int materialize(muon_plan* p) {
       E.s = M.s;
       E.fused = M.path ? 1 : 0;
       prefix[k] = tb;
+      C.tile_first.push_back(tb);
       tb += M.ew_tiles;
       const double e = (double)M.rows * M.cols, pes = M.dtype ? 2 : 4, es = M.path ? 2 : 4;
-      C.bytes_mom += e * (pes + 8 + es + (M.has[bX0T] ? es : 0));
+      C.mat_bytes_mom.push_back(e * (pes + 8 + es + (M.has[bX0T] ? es : 0)));
+      C.mat_bytes_load.push_back(e * (pes + es + (M.has[bX0T] ? es : 0)));
       C.bytes_apply += e * (4 + 2 * pes);
-      C.bytes_load += e * (pes + es + (M.has[bX0T] ? es : 0));
       C.bytes_store += e * (4 + 4);
     }
+    C.tile_first.push_back(tb);
     C.total_tiles = tb;
     C.all_fused = true;
     for (size_t k = 0; k < nm; ++k) {
@@ -265,6 +274,14 @@ int materialize(muon_plan* p) {
     HIP_TRY(hipMemcpy(C.prefix, prefix.data(), nm * sizeof(int64_t), hipMemcpyHostToDevice));
     HIP_TRY(hipEventCreateWithFlags(&C.upload_ev, hipEventDisableTiming));
     C.n_lanes = CP.n_lanes;
+    if (C.n_lanes > H.lanes) return fail(MUON_EINVAL, "plan: chunk lane count above the plan's");
+    C.lane_first.assign(C.n_lanes + 1, (int)nm);
+    for (size_t k = nm; k-- > 0;) {
+      const int l = H.mats[C.mats[k]].lane;
+      if (l < 0 || l >= C.n_lanes || (k + 1 < nm && l > H.mats[C.mats[k + 1]].lane))
+        return fail(MUON_EINVAL, "plan: lanes are not contiguous runs of the chunk");
+      for (int q = 0; q <= l; ++q) C.lane_first[q] = (int)k;
+    }
     for (const LaunchSetPlan& S : CP.sets) {
       SetDev D;
       D.path = S.path;
@@ -313,16 +330,15 @@ int materialize(muon_plan* p) {
       C.sets.push_back(D);
     }
   }
-  if (H.lanes > 1) {
-    HIP_TRY(hipEventCreateWithFlags(&p->lane_fork, hipEventDisableTiming));
-    for (int l = 1; l < H.lanes; ++l) {
-      hipStream_t st = nullptr;
-      hipEvent_t ev = nullptr;
-      HIP_TRY(hipStreamCreateWithFlags(&st, hipStreamNonBlocking));
-      p->lane_streams.push_back(st);
-      HIP_TRY(hipEventCreateWithFlags(&ev, hipEventDisableTiming));
-      p->lane_join.push_back(ev);
-    }
+  for (int l = 1; l < H.lanes; ++l) {
+    hipStream_t st = nullptr;
+    hipEvent_t ev = nullptr, ef = nullptr;
+    HIP_TRY(hipStreamCreateWithFlags(&st, hipStreamNonBlocking));
+    p->lane_streams.push_back(st);
+    HIP_TRY(hipEventCreateWithFlags(&ev, hipEventDisableTiming));
+    p->lane_join.push_back(ev);
+    HIP_TRY(hipEventCreateWithFlags(&ef, hipEventDisableTiming));
+    p->lane_front.push_back(ef);
   }
   return MUON_OK;
 }
@@ -527,28 +543,57 @@ int enqueue_ns(muon_plan* p, const SetDev& S, int T, const float* sched, const E
   return MUON_OK;
 }
 
-// The NS stages of a chunk: with one lane all sets go to s; with more, lanes
-// 1.. run on their own streams, forked from s before and joined into s after.
-int enqueue_chunk_ns(muon_plan* p, const ChunkDev& C, int T, const float* sched, const EwDyn* dyn,
-                     float lr, float wd, hipStream_t s) {
+// A chunk's front and NS stages.  front(a, b, stream) enqueues the front
+// (momentum or input load, then k_norm) of the chunk's matrices [a, b).  With
+// one lane (or T = 0) everything goes to s.  With more, lane l runs on its own
+// stream (lane 0 on s): its front starts when lane l-1's front is done, then
+// its NS launch sets follow, so each lane's HBM-bound front runs beside the
+// MFMA-bound NS of the lanes before it.  Lanes 1.. are joined back into s.
+template <class Front>
+int enqueue_chunk(muon_plan* p, const ChunkDev& C, int T, const float* sched, const EwDyn* dyn,
+                  float lr, float wd, hipStream_t s, Front&& front) {
   int rc;
-  const int L = std::min<int>(C.n_lanes, (int)p->lane_streams.size() + 1);
-  if (T <= 0 || L <= 1) {
+  const int L = T > 0 ? C.n_lanes : 1;
+  if (L > (int)p->lane_streams.size() + 1) return fail(MUON_EINVAL, "plan: lane without a stream");
+  if (L <= 1) {
+    if ((rc = front(0, (int)C.mats.size(), s))) return rc;
     for (const SetDev& S : C.sets)
       if ((rc = enqueue_ns(p, S, T, sched, dyn, lr, wd, s))) return rc;
     return MUON_OK;
   }
-  HIP_TRY(hipEventRecord(p->lane_fork, s));
-  for (int l = 1; l < L; ++l) HIP_TRY(hipStreamWaitEvent(p->lane_streams[l - 1], p->lane_fork, 0));
-  for (const SetDev& S : C.sets) {
-    hipStream_t ls = S.lane == 0 ? s : p->lane_streams[S.lane - 1];
-    if ((rc = enqueue_ns(p, S, T, sched, dyn, lr, wd, ls))) return rc;
+  for (int l = 0; l < L; ++l) {
+    hipStream_t ls = l == 0 ? s : p->lane_streams[l - 1];
+    if (l > 0) HIP_TRY(hipStreamWaitEvent(ls, p->lane_front[l - 1], 0));
+    if ((rc = front(C.lane_first[l], C.lane_first[l + 1], ls))) return rc;
+    if (l + 1 < L) HIP_TRY(hipEventRecord(p->lane_front[l], ls));
+    for (const SetDev& S : C.sets)
+      if (S.lane == l && (rc = enqueue_ns(p, S, T, sched, dyn, lr, wd, ls))) return rc;
   }
   for (int l = 1; l < L; ++l) {
     HIP_TRY(hipEventRecord(p->lane_join[l - 1], p->lane_streams[l - 1]));
     HIP_TRY(hipStreamWaitEvent(s, p->lane_join[l - 1], 0));
   }
   return MUON_OK;
+}
+
+// Front of matrices [a, b) of a chunk: k_ew_momentum (load_only: d is the
+// input itself) over their tiles, then k_norm over them.
+int enqueue_front(muon_plan* p, const ChunkDev& C, int a, int b, float beta, int load_only,
+                  hipStream_t s) {
+  if (a >= b) return MUON_OK;
+  double bytes = 0;
+  for (int k = a; k < b; ++k) bytes += load_only ? C.mat_bytes_load[k] : C.mat_bytes_mom[k];
+  const int nm = (int)C.mats.size();
+  const int64_t t0 = C.tile_first[a], t1 = C.tile_first[b];
+  const int nesterov = load_only ? 1 : p->host.opts.nesterov;
+  int rc;
+  if ((rc = run(p, kEwMom, "k_ew_momentum", 0, bytes, s, [&] {
+         return launch_ew_momentum(C.ew, C.dyn, C.prefix, nm, t0, t1, C.partials, beta, nesterov,
+                                   load_only, p->grid_cap, s);
+       }))) return rc;
+  return run(p, kNorm, "k_norm", 0, 0, s, [&] {
+    return launch_norm(C.ew + a, b - a, C.partials, p->rscale, p->flags, p->host.opts.eps, s);
+  });
 }
 
 bool aligned16(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; }
@@ -601,14 +646,9 @@ int step_impl(muon_plan* p, void* const* params, const void* const* grads, float
   for (ChunkDev& C : p->chunks) {
     if ((rc = upload_dyn(p, C, params, grads, momenta, true, s))) return rc;
     const int nm = (int)C.mats.size();
-    if ((rc = run(p, kEwMom, "k_ew_momentum", 0, C.bytes_mom, s, [&] {
-           return launch_ew_momentum(C.ew, C.dyn, C.prefix, nm, C.total_tiles, C.partials, beta,
-                                     p->host.opts.nesterov, 0, p->grid_cap, s);
+    if ((rc = enqueue_chunk(p, C, T, sched, C.dyn, lr, wd, s, [&](int a, int b, hipStream_t ls) {
+           return enqueue_front(p, C, a, b, beta, 0, ls);
          }))) return rc;
-    if ((rc = run(p, kNorm, "k_norm", 0, 0, s, [&] {
-           return launch_norm(C.ew, nm, C.partials, p->rscale, p->flags, p->host.opts.eps, s);
-         }))) return rc;
-    if ((rc = enqueue_chunk_ns(p, C, T, sched, C.dyn, lr, wd, s))) return rc;
     // with T >= 1 the last NS product of every bf16-path matrix applied its update
     if (T >= 1 && C.all_fused) continue;
     if ((rc = run(p, kEwApply, "k_ew_apply", 0, T >= 1 ? C.bytes_apply_unfused : C.bytes_apply, s, [&] {
@@ -637,15 +677,10 @@ int ortho_impl(muon_plan* p, const void* const* inputs, float* const* outputs, i
   for (ChunkDev& C : p->chunks) {
     if ((rc = upload_dyn(p, C, outs.data(), inputs, nullptr, false, s))) return rc;
     const int nm = (int)C.mats.size();
-    if ((rc = run(p, kEwMom, "k_ew_momentum", 0, C.bytes_load, s, [&] {
-           return launch_ew_momentum(C.ew, C.dyn, C.prefix, nm, C.total_tiles, C.partials, 0.f, 1, 1,
-                                     p->grid_cap, s);
-         }))) return rc;
-    if ((rc = run(p, kNorm, "k_norm", 0, 0, s, [&] {
-           return launch_norm(C.ew, nm, C.partials, p->rscale, p->flags, p->host.opts.eps, s);
-         }))) return rc;
     // no parameters: the last NS product writes X_T (fp32) to the workspace
-    if ((rc = enqueue_chunk_ns(p, C, T, sched, nullptr, 0.f, 0.f, s))) return rc;
+    if ((rc = enqueue_chunk(p, C, T, sched, nullptr, 0.f, 0.f, s, [&](int a, int b, hipStream_t ls) {
+           return enqueue_front(p, C, a, b, 0.f, 1, ls);
+         }))) return rc;
     if ((rc = run(p, kEwApply, "k_ew_apply", 0, C.bytes_store, s, [&] {
            return launch_ew_apply(C.ew, C.dyn, C.prefix, nm, C.total_tiles, p->rscale, 0.f, 0.f,
                                   T == 0 ? 1 : 0, 0, 1, p->grid_cap, s);
@@ -658,13 +693,47 @@ const float kQuintic[3] = {3.4445f, -4.7750f, 2.0315f};
 
 // Times the NS stages (T = 5) of a host plan on bounded synthetic operands:
 // every workspace byte 0x3C (bf16 and fp32 ~0.0115), X0 scaled to unit
-// Frobenius norm.  4 runs over all chunks, best of the last 3, in ms.
-int time_ns(PlanHost&& H, float* best_ms) {
+// Frobenius norm.  with_front: each chunk's fronts run too, lane-staggered as
+// in a step (the momentum kernel on synthetic gradients and momenta, also
+// 0x3C bytes, then k_norm), so the timing sees fronts overlapping NS.  4 runs
+// over all chunks, best of the last 3, in ms.
+int time_ns(PlanHost&& H, bool with_front, float* best_ms) {
   muon_plan tp;
   tp.host = std::move(H);
   int rc = materialize(&tp);
   if (rc) { free_plan_memory(&tp); return rc; }
   const size_t n = tp.host.mats.size();
+  // front operands: per chunk, each matrix's gradient (its parameter dtype)
+  // then its fp32 momentum, 256-byte aligned; chunks run one after another
+  // and share the memory
+  std::vector<void*> grads(n, nullptr);
+  std::vector<float*> moms(n, nullptr);
+  if (with_front) {
+    auto gbytes = [](const MatPlan& M) {
+      return ((size_t)M.rows * (size_t)M.cols * (M.dtype ? 2 : 4) + 255) / 256 * 256;
+    };
+    auto mbytes = [](const MatPlan& M) { return ((size_t)M.rows * (size_t)M.cols * 4 + 255) / 256 * 256; };
+    std::vector<size_t> at(n, 0);
+    size_t most = 0;
+    for (const ChunkDev& C : tp.chunks) {
+      size_t off = 0;
+      for (int i : C.mats) {
+        at[i] = off;
+        off += gbytes(tp.host.mats[i]) + mbytes(tp.host.mats[i]);
+      }
+      most = std::max(most, off);
+    }
+    char* fm = nullptr;
+    if ((rc = dev_alloc(&tp, &fm, most))) { free_plan_memory(&tp); return rc; }
+    if (hipMemset(fm, 0x3C, most) != hipSuccess) {
+      free_plan_memory(&tp);
+      return fail(MUON_EHIP, "tuning setup failed");
+    }
+    for (size_t i = 0; i < n; ++i) {
+      grads[i] = fm + at[i];
+      moms[i] = reinterpret_cast<float*>(fm + at[i] + gbytes(tp.host.mats[i]));
+    }
+  }
   std::vector<float> r(n);
   for (size_t i = 0; i < n; ++i) {
     const MatPlan& M = tp.host.mats[i];
@@ -691,8 +760,23 @@ int time_ns(PlanHost&& H, float* best_ms) {
   float best = 1e30f;
   for (int rep = 0; rep < 4; ++rep) {
     (void)hipEventRecord(e0, s);
-    for (const ChunkDev& C : tp.chunks)
-      if ((rc = enqueue_chunk_ns(&tp, C, 5, sched, nullptr, 0.f, 0.f, s))) { cleanup(); return rc; }
+    for (ChunkDev& C : tp.chunks) {
+      if (with_front) {
+        // the parameters are never touched (no update is applied here)
+        rc = upload_dyn(&tp, C, grads.data(), grads.data(), moms.data(), false, s);
+        if (!rc)
+          rc = enqueue_chunk(&tp, C, 5, sched, nullptr, 0.f, 0.f, s, [&](int a, int b, hipStream_t ls) {
+            return enqueue_front(&tp, C, a, b, 0.95f, 0, ls);
+          });
+      } else {
+        rc = enqueue_chunk(&tp, C, 5, sched, nullptr, 0.f, 0.f, s,
+                           [](int, int, hipStream_t) { return (int)MUON_OK; });
+      }
+      if (rc) {
+        cleanup();
+        return rc;
+      }
+    }
     (void)hipEventRecord(e1, s);
     if (hipEventSynchronize(e1) != hipSuccess) { cleanup(); return fail(MUON_EHIP, "tuning sync failed"); }
     float ms = 0;
@@ -731,7 +815,7 @@ int time_shape(const ShapeKey& k, const PlanOptions& base, int count,
     std::string err = build_plan(rows, cols, dts, o, ch, &H);
     if (!err.empty()) return fail(MUON_ENOMEM, "tuning: " + err);
     float ms = 0;
-    const int rc = time_ns(std::move(H), &ms);
+    const int rc = time_ns(std::move(H), false, &ms);
     if (rc) return rc;
     const double us = ms * 1000.0 / batch;
     if (!have || us < 0.97 * best_us) {
@@ -773,7 +857,7 @@ int refine_set(const std::vector<int64_t>& rows, const std::vector<int64_t>& col
       if (!same) tiles.push_back(t);
     }
   std::vector<int> lanes{std::max(po.lanes, 1)};
-  if (lanes_free) lanes = {1, 2, 4};
+  if (lanes_free) lanes = {1, 2, 3, 4};
   bool have = false;
   float best = 0;
   for (int t : tiles)
@@ -784,7 +868,7 @@ int refine_set(const std::vector<int64_t>& rows, const std::vector<int64_t>& col
       const std::string err = build_plan(rows, cols, dts, o, with_tile(t), &H);
       if (!err.empty()) return fail(MUON_ENOMEM, "tuning: " + err);
       float ms = 0;
-      const int rc = time_ns(std::move(H), &ms);
+      const int rc = time_ns(std::move(H), true, &ms);
       if (rc) return rc;
       if (!have || ms < 0.985f * best) {
         best = ms;

@@ -125,13 +125,13 @@ __device__ __forceinline__ int find_mat(const int64_t* prefix, int nmats, int64_
 // 16 consecutive columns from c0 = (tid % 4) * 16.
 __global__ __launch_bounds__(256) void k_ew_momentum(
     const EwMat* __restrict__ mats, const EwDyn* __restrict__ dyn,
-    const int64_t* __restrict__ prefix, int nmats, int64_t total,
+    const int64_t* __restrict__ prefix, int nmats, int64_t t_begin, int64_t t_end,
     float* __restrict__ partials, float beta, int nesterov, int load_only) {
   __shared__ float tT[kEwTile][kEwTile + 1];
   __shared__ float red[4];
   const int tid = threadIdx.x;
   const int r = tid >> 2, c0 = (tid & 3) * 16;
-  for (int64_t t = blockIdx.x; t < total; t += gridDim.x) {
+  for (int64_t t = t_begin + blockIdx.x; t < t_end; t += gridDim.x) {
     const int mi = find_mat(prefix, nmats, t);
     const EwMat& M = mats[mi];
     const EwDyn& D = dyn[mi];
@@ -1054,12 +1054,13 @@ hipError_t launch_nt_cfg(int out_dt, const GemmParams& p, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_ew_momentum(const EwMat* mats, const EwDyn* dyn, const int64_t* tile_prefix,
-                              int nmats, int64_t total_tiles, float* partials, float beta,
-                              int nesterov, int load_only, int grid_cap, hipStream_t s) {
-  if (total_tiles <= 0) return hipSuccess;
-  const int64_t grid = total_tiles < grid_cap ? total_tiles : grid_cap;
+                              int nmats, int64_t tile_begin, int64_t tile_end, float* partials,
+                              float beta, int nesterov, int load_only, int grid_cap, hipStream_t s) {
+  const int64_t n = tile_end - tile_begin;
+  if (n <= 0) return hipSuccess;
+  const int64_t grid = n < grid_cap ? n : grid_cap;
   hipLaunchKernelGGL(k_ew_momentum, dim3((unsigned)grid), dim3(256), 0, s, mats, dyn, tile_prefix,
-                     nmats, total_tiles, partials, beta, nesterov, load_only);
+                     nmats, tile_begin, tile_end, partials, beta, nesterov, load_only);
   return hipGetLastError();
 }
 

@@ -154,9 +154,11 @@ enum NtCfg : int32_t { kNt128 = 0, kNt256 = 1, kNt256x128 = 2, kNt128x256 = 3, k
 constexpr TileCfg kNtCfgs[kNumNtCfgs] = {{128, 128}, {256, 256}, {256, 128}, {128, 256}};
 
 // Launchers (kernels.hip).  All return hipError_t of the launch.
+// Tiles [tile_begin, tile_end) of the chunk (mats, tile_prefix: the whole chunk).
 hipError_t launch_ew_momentum(const EwMat* mats, const EwDyn* dyn, const int64_t* tile_prefix,
-                              int nmats, int64_t total_tiles, float* partials, float beta,
-                              int nesterov, int load_only, int grid_cap, hipStream_t s);
+                              int nmats, int64_t tile_begin, int64_t tile_end, float* partials,
+                              float beta, int nesterov, int load_only, int grid_cap, hipStream_t s);
+// One block per matrix of mats[0 .. nmats).
 hipError_t launch_norm(const EwMat* mats, int nmats, const float* partials, float* rscale,
                        uint32_t* flags, float eps, hipStream_t s);
 // Fused AdamW over a list of tensors (chunk_prefix[i] = tensors[i].chunk_begin).

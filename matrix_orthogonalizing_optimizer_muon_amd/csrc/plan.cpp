@@ -470,7 +470,7 @@ TuneCache read_cache(const std::string& path, const std::string& device_tag) {
   while (std::getline(f, line)) {
     std::istringstream is(line);
     std::string magic, tag;
-    if (!(is >> magic >> tag) || magic != "muon-tune-v2" || tag != device_tag) continue;
+    if (!(is >> magic >> tag) || magic != "muon-tune-v3" || tag != device_tag) continue;
     ShapeKey k{-1, -1, -1};
     ShapeChoice c;
     c.form = -1;
@@ -523,7 +523,7 @@ bool write_cache(const std::string& path, const std::string& device_tag, const T
     while (std::getline(f, line)) {
       std::istringstream is(line);
       std::string magic, tag;
-      if ((is >> magic >> tag) && magic == "muon-tune-v2" && tag == device_tag) continue;
+      if ((is >> magic >> tag) && magic == "muon-tune-v3" && tag == device_tag) continue;
       if (!line.empty()) keep.push_back(line);
     }
   }
@@ -534,13 +534,13 @@ bool write_cache(const std::string& path, const std::string& device_tag, const T
     for (const std::string& l : keep) f << l << "\n";
     char buf[256];
     for (const auto& kv : entries.shapes) {
-      snprintf(buf, sizeof buf, "muon-tune-v2 %s m=%lld n=%lld path=%d form=%d tile=%d us=%.3f\n",
+      snprintf(buf, sizeof buf, "muon-tune-v3 %s m=%lld n=%lld path=%d form=%d tile=%d us=%.3f\n",
                device_tag.c_str(), (long long)kv.first.m, (long long)kv.first.n, kv.first.path,
                kv.second.form, kv.second.tile, kv.second.us);
       f << buf;
     }
     for (const auto& kv : entries.sets) {
-      snprintf(buf, sizeof buf, "muon-tune-v2 %s set=%s tile=%d lanes=%d us=%.3f\n",
+      snprintf(buf, sizeof buf, "muon-tune-v3 %s set=%s tile=%d lanes=%d us=%.3f\n",
                device_tag.c_str(), kv.first.c_str(), kv.second.tile, kv.second.lanes, kv.second.us);
       f << buf;
     }
