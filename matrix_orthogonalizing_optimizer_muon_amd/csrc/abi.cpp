@@ -543,11 +543,12 @@ int enqueue_ns(muon_plan* p, const SetDev& S, int T, const float* sched, const E
   return MUON_OK;
 }
 
-// A chunk's front and NS stages.  front(a, b, stream) enqueues the front
-// (momentum or input load, then k_norm) of the chunk's matrices [a, b).  With
-// one lane (or T = 0) everything goes to s.  With more, lane l runs on its own
-// stream (lane 0 on s): its front starts when lane l-1's front is done, then
-// its NS launch sets follow, so each lane's HBM-bound front runs beside the
+// A chunk's front and NS stages.  front(a, b, stream, ev) enqueues the front
+// (momentum or input load, then k_norm) of the chunk's matrices [a, b) and,
+// when ev is set, records it once the HBM-heavy part is done.  With one lane
+// (or T = 0) everything goes to s.  With more, lane l runs on its own stream
+// (lane 0 on s): its front starts when lane l-1's momentum is done, then its
+// NS launch sets follow, so each lane's HBM-bound front runs beside the
 // MFMA-bound NS of the lanes before it.  Lanes 1.. are joined back into s.
 template <class Front>
 int enqueue_chunk(muon_plan* p, const ChunkDev& C, int T, const float* sched, const EwDyn* dyn,
@@ -556,7 +557,7 @@ int enqueue_chunk(muon_plan* p, const ChunkDev& C, int T, const float* sched, co
   const int L = T > 0 ? C.n_lanes : 1;
   if (L > (int)p->lane_streams.size() + 1) return fail(MUON_EINVAL, "plan: lane without a stream");
   if (L <= 1) {
-    if ((rc = front(0, (int)C.mats.size(), s))) return rc;
+    if ((rc = front(0, (int)C.mats.size(), s, nullptr))) return rc;
     for (const SetDev& S : C.sets)
       if ((rc = enqueue_ns(p, S, T, sched, dyn, lr, wd, s))) return rc;
     return MUON_OK;
@@ -564,8 +565,8 @@ int enqueue_chunk(muon_plan* p, const ChunkDev& C, int T, const float* sched, co
   for (int l = 0; l < L; ++l) {
     hipStream_t ls = l == 0 ? s : p->lane_streams[l - 1];
     if (l > 0) HIP_TRY(hipStreamWaitEvent(ls, p->lane_front[l - 1], 0));
-    if ((rc = front(C.lane_first[l], C.lane_first[l + 1], ls))) return rc;
-    if (l + 1 < L) HIP_TRY(hipEventRecord(p->lane_front[l], ls));
+    if ((rc = front(C.lane_first[l], C.lane_first[l + 1], ls, l + 1 < L ? p->lane_front[l] : nullptr)))
+      return rc;
     for (const SetDev& S : C.sets)
       if (S.lane == l && (rc = enqueue_ns(p, S, T, sched, dyn, lr, wd, ls))) return rc;
   }
@@ -577,10 +578,14 @@ int enqueue_chunk(muon_plan* p, const ChunkDev& C, int T, const float* sched, co
 }
 
 // Front of matrices [a, b) of a chunk: k_ew_momentum (load_only: d is the
-// input itself) over their tiles, then k_norm over them.
+// input itself) over their tiles, then k_norm over them; ev (if set) is
+// recorded between the two.
 int enqueue_front(muon_plan* p, const ChunkDev& C, int a, int b, float beta, int load_only,
-                  hipStream_t s) {
-  if (a >= b) return MUON_OK;
+                  hipStream_t s, hipEvent_t ev) {
+  if (a >= b) {
+    if (ev) HIP_TRY(hipEventRecord(ev, s));
+    return MUON_OK;
+  }
   double bytes = 0;
   for (int k = a; k < b; ++k) bytes += load_only ? C.mat_bytes_load[k] : C.mat_bytes_mom[k];
   const int nm = (int)C.mats.size();
@@ -591,6 +596,7 @@ int enqueue_front(muon_plan* p, const ChunkDev& C, int a, int b, float beta, int
          return launch_ew_momentum(C.ew, C.dyn, C.prefix, nm, t0, t1, C.partials, beta, nesterov,
                                    load_only, p->grid_cap, s);
        }))) return rc;
+  if (ev) HIP_TRY(hipEventRecord(ev, s));
   return run(p, kNorm, "k_norm", 0, 0, s, [&] {
     return launch_norm(C.ew + a, b - a, C.partials, p->rscale, p->flags, p->host.opts.eps, s);
   });
@@ -646,8 +652,8 @@ int step_impl(muon_plan* p, void* const* params, const void* const* grads, float
   for (ChunkDev& C : p->chunks) {
     if ((rc = upload_dyn(p, C, params, grads, momenta, true, s))) return rc;
     const int nm = (int)C.mats.size();
-    if ((rc = enqueue_chunk(p, C, T, sched, C.dyn, lr, wd, s, [&](int a, int b, hipStream_t ls) {
-           return enqueue_front(p, C, a, b, beta, 0, ls);
+    if ((rc = enqueue_chunk(p, C, T, sched, C.dyn, lr, wd, s, [&](int a, int b, hipStream_t ls, hipEvent_t ev) {
+           return enqueue_front(p, C, a, b, beta, 0, ls, ev);
          }))) return rc;
     // with T >= 1 the last NS product of every bf16-path matrix applied its update
     if (T >= 1 && C.all_fused) continue;
@@ -678,8 +684,8 @@ int ortho_impl(muon_plan* p, const void* const* inputs, float* const* outputs, i
     if ((rc = upload_dyn(p, C, outs.data(), inputs, nullptr, false, s))) return rc;
     const int nm = (int)C.mats.size();
     // no parameters: the last NS product writes X_T (fp32) to the workspace
-    if ((rc = enqueue_chunk(p, C, T, sched, nullptr, 0.f, 0.f, s, [&](int a, int b, hipStream_t ls) {
-           return enqueue_front(p, C, a, b, 0.f, 1, ls);
+    if ((rc = enqueue_chunk(p, C, T, sched, nullptr, 0.f, 0.f, s, [&](int a, int b, hipStream_t ls, hipEvent_t ev) {
+           return enqueue_front(p, C, a, b, 0.f, 1, ls, ev);
          }))) return rc;
     if ((rc = run(p, kEwApply, "k_ew_apply", 0, C.bytes_store, s, [&] {
            return launch_ew_apply(C.ew, C.dyn, C.prefix, nm, C.total_tiles, p->rscale, 0.f, 0.f,
@@ -765,12 +771,15 @@ int time_ns(PlanHost&& H, bool with_front, float* best_ms) {
         // the parameters are never touched (no update is applied here)
         rc = upload_dyn(&tp, C, grads.data(), grads.data(), moms.data(), false, s);
         if (!rc)
-          rc = enqueue_chunk(&tp, C, 5, sched, nullptr, 0.f, 0.f, s, [&](int a, int b, hipStream_t ls) {
-            return enqueue_front(&tp, C, a, b, 0.95f, 0, ls);
+          rc = enqueue_chunk(&tp, C, 5, sched, nullptr, 0.f, 0.f, s, [&](int a, int b, hipStream_t ls, hipEvent_t ev) {
+            return enqueue_front(&tp, C, a, b, 0.95f, 0, ls, ev);
           });
       } else {
         rc = enqueue_chunk(&tp, C, 5, sched, nullptr, 0.f, 0.f, s,
-                           [](int, int, hipStream_t) { return (int)MUON_OK; });
+                           [](int, int, hipStream_t ls, hipEvent_t ev) {
+                             if (ev) HIP_TRY(hipEventRecord(ev, ls));
+                             return (int)MUON_OK;
+                           });
       }
       if (rc) {
         cleanup();

@@ -33,17 +33,16 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }
 
-// Round to nearest, ties to even; NaN stays NaN.
-__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
+// fp32 -> bf16 by gfx950's v_cvt_pk_bf16_f32 (two values per instruction):
+// round to nearest, ties to even; NaN stays NaN.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
+
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) { return pack_bf16x2(f, 0.f) & 0xffffu; }
 
 // 16-byte global accesses and 16 consecutive elements of dtype dt starting at
 // element offset off (16-byte aligned).  (Nontemporal variants of these were
@@ -832,7 +831,7 @@ __device__ __forceinline__ void apply_update8(const UpdCtx& c, int64_t row, int6
 // Epilogue of the NT kernel through LDS, in slabs of SH rows:
 //  1. each wave writes its accumulators of the slab's rows into an fp32 tile;
 //  2. row pass: every thread takes 8 consecutive columns of a row, applies
-//     out = s (alpha acc + beta Cin) + gamma [i == j] (0 outside the real
+//     out = (s alpha) acc + (s beta) Cin + gamma [i == j] (0 outside the real
 //     extents) and stores 16-byte runs of the output (Cin read the same way);
 //  3. column pass (transposed copy or mirrored tile only): every thread takes 8
 //     consecutive rows of one column and stores them as a 16-byte run.
@@ -854,7 +853,11 @@ __device__ __forceinline__ void nt_epilogue(const nt::f32x16_t (&acc)[BM / 32 / 
     const float rr = p.rscale[nmp->mat];
     sc = p.scale_pow == 2 ? rr * rr : rr;
   }
-  const float alpha = p.alpha, beta = p.beta, gamma = p.gamma;
+  const float gamma = p.gamma;
+  const float as = p.alpha * sc, bs = p.beta * sc;
+  // only tiles that reach past the real extents, or that the diagonal crosses
+  // when gamma is added there, need the per-element checks
+  const bool edge = m0 + BM > Mr || n0 + BN > Nr || (gamma != 0.f && m0 < n0 + BN && n0 < m0 + BM);
   void* Out = nmp->buf[p.o_id];
   void* OutT = p.ot_id >= 0 ? nmp->buf[p.ot_id] : nullptr;
   const void* Cin = p.c_id >= 0 ? nmp->buf[p.c_id] : nullptr;
@@ -921,12 +924,16 @@ __device__ __forceinline__ void nt_epilogue(const nt::f32x16_t (&acc)[BM / 32 / 
       for (int e = 0; e < 8; ++e) v[e] = src[e];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        float x = alpha * v[e];
-        if (Cin) x += beta * bf16_to_f32((e & 1) ? (craw[t][e >> 1] >> 16) : (craw[t][e >> 1] & 0xffffu));
-        x *= sc;
-        if (i == j + e) x += gamma;
-        if (i >= Mr || j + e >= Nr) x = 0.f;
+        float x = as * v[e];
+        if (Cin) x = fmaf(bs, bf16_to_f32((e & 1) ? (craw[t][e >> 1] >> 16) : (craw[t][e >> 1] & 0xffffu)), x);
         v[e] = x;
+      }
+      if (edge) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          if (i == j + e) v[e] += gamma;
+          if (i >= Mr || j + e >= Nr) v[e] = 0.f;
+        }
       }
       if (!fuse) {
         st8<TO>(Out, (int64_t)i * ldo + j, v);
