@@ -846,7 +846,7 @@ __device__ __forceinline__ void nt_epilogue(const nt::f32x16_t (&acc)[BM / 32 / 
   constexpr int SH = slab_rows<BM, BN, WGM, WGN>();
   constexpr int PITCH = BN + 4;
   constexpr int TPR = BN / 8, RPP = NT / TPR;
-  static_assert(SH % 8 == 0 && SH * PITCH * 4 <= G::LDS && NT % TPR == 0, "slab");
+  static_assert(SH % 32 == 0 && PITCH % 4 == 0 && SH * PITCH * 4 <= G::LDS && NT % TPR == 0, "slab");
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wy = w / WGN, wx = w % WGN;
   float sc = 1.0f;
   if (p.scale_pow) {
@@ -877,20 +877,23 @@ __device__ __forceinline__ void nt_epilogue(const nt::f32x16_t (&acc)[BM / 32 / 
   __syncthreads();   // every wave is done with the main loop's LDS
 #pragma unroll 1
   for (int s0 = 0; s0 < BM; s0 += SH) {
+    // lane l holds row l % 32 of each MFMA tile, 4 consecutive columns per
+    // register group: one 16-byte LDS write each (rows 16 bytes apart in bank
+    // terms, so any 16 lanes cover all banks)
 #pragma unroll
-    for (int a = 0; a < G::MT; ++a)
+    for (int a = 0; a < G::MT; ++a) {
+      const int rbase = wy * G::WM + a * 32;   // 32-row MFMA tile, uniform per wave
+      if (rbase < s0 || rbase >= s0 + SH) continue;
+      const int r = rbase - s0 + (lane & 31);
 #pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const int rbase = wy * G::WM + a * 32 + rg * 8;   // 8-row group, uniform per wave
-        if (rbase < s0 || rbase >= s0 + SH) continue;
-        const int r = rbase - s0 + (lane >> 5) * 4;
+      for (int b = 0; b < G::NT; ++b)
 #pragma unroll
-        for (int b = 0; b < G::NT; ++b) {
-          const int c = wx * G::WN + b * 32 + (lane & 31);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) C[(r + q) * PITCH + c] = acc[a][b][rg * 4 + q];
+        for (int g = 0; g < 4; ++g) {
+          const int c = wx * G::WN + b * 32 + g * 8 + (lane >> 5) * 4;
+          *(MUON_LDS nt::f32x4_t*)(C + r * PITCH + c) =
+              nt::f32x4_t{acc[a][b][4 * g], acc[a][b][4 * g + 1], acc[a][b][4 * g + 2], acc[a][b][4 * g + 3]};
         }
-      }
+    }
     __syncthreads();
     // row pass: this thread's SH / RPP rows, 8 columns each; Cin for all of
     // them (or, for an update applied here, the bf16 W rows) is requested

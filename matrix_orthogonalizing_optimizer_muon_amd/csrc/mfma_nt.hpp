@@ -30,6 +30,7 @@ namespace nt {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 #define MUON_LDS __attribute__((address_space(3)))
 
@@ -203,14 +204,17 @@ __device__ __forceinline__ void load_frags_qt(u32x4_t (&b)[G::NT], const MUON_LD
   }
 }
 
+// The fragments go into the MFMA as (Q, P), so it accumulates the transposed
+// 32 x 32 tile and acc[i][j] comes out row-major friendly: lane l holds row
+// l % 32 of tile (i, j), columns 8 g + 4 (l / 32) + 0..3 in registers 4 g + 0..3.
 template <class G>
 __device__ __forceinline__ void mfma_group(f32x16_t (&acc)[G::MT][G::NT], const Frags<G>& f) {
 #pragma unroll
   for (int i = 0; i < G::MT; ++i)
 #pragma unroll
     for (int j = 0; j < G::NT; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, f.a[i]),
-                                                         __builtin_bit_cast(bf16x8_t, f.b[j]),
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, f.b[j]),
+                                                         __builtin_bit_cast(bf16x8_t, f.a[i]),
                                                          acc[i][j], 0, 0, 0);
 }
 
