@@ -69,7 +69,8 @@ def source_digest():
 def traffic_for(kernel, workload, launches_per_step):
     """HBM bytes per launch of `kernel` from a committed counter summary
     (profiles/traffic.json, written from two rocprofv3 --pmc passes), or None
-    when none matches this kernel, workload and kernel-source digest."""
+    when none matches this kernel, workload, kernel-source digest and launches
+    per step (the plan's lane count sets how much one launch covers)."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -80,7 +81,8 @@ def traffic_for(kernel, workload, launches_per_step):
         return None
     digest = source_digest()
     for r in rec.get("entries", []):
-        if r.get("kernel") == kernel and r.get("workload") == workload and r.get("source") == digest:
+        if (r.get("kernel") == kernel and r.get("workload") == workload and r.get("source") == digest
+                and abs(r.get("launches_per_step", -1) - launches_per_step) < 1e-6):
             return {"fetch_bytes": r["fetch_bytes_per_launch"], "write_bytes": r["write_bytes_per_launch"],
                     "bytes": r["fetch_bytes_per_launch"] + r["write_bytes_per_launch"],
                     "copy_factor": r.get("copy_factor"), "source": digest}
@@ -117,7 +119,9 @@ def counter_rows(dirpath, counter):
 
 def write_traffic(args, wl):
     """Per-launch HBM bytes of one kernel from FETCH_SIZE / WRITE_SIZE (KiB per
-    dispatch), each scaled so that the calibration copy reads as COPY_BYTES."""
+    dispatch), each scaled so that the calibration copy reads as COPY_BYTES.
+    The passes ran --traffic-probe with the same --warmup (warmup + 2 steps, the
+    plan from the tune cache), which gives the launches per step."""
     import statistics
     name = demangled(args.kernel)
     entry = {"kernel": args.kernel, "workload": wl.name, "source": source_digest()}
@@ -133,6 +137,10 @@ def write_traffic(args, wl):
         entry[f"{key}_bytes_per_launch"] = statistics.mean(kern) * 1024 * factor
         entry[f"{key}_copy_factor"] = factor
         entry[f"{key}_dispatches"] = len(kern)
+    if entry["fetch_dispatches"] != entry["write_dispatches"] or entry["fetch_dispatches"] % (args.warmup + 2):
+        raise SystemExit(f"dispatch counts {entry['fetch_dispatches']} / {entry['write_dispatches']} "
+                         f"do not fit {args.warmup} + 2 steps")
+    entry["launches_per_step"] = entry["fetch_dispatches"] / (args.warmup + 2)
     entry["copy_factor"] = [entry["fetch_copy_factor"], entry["write_copy_factor"]]
     path = os.path.join(ROOT, "profiles", "traffic.json")
     rec = {"entries": []}

@@ -359,16 +359,22 @@ int run(muon_plan* p, int kind, const char* kern, double flops, double bytes, hi
         F&& launch) {
   hipEvent_t a = nullptr, b = nullptr;
   if (p->profiling) {
+    // the launch's dispatch start and end go into a and b
     a = pool_event(p);
     b = pool_event(p);
     if (!a || !b) return fail(MUON_EHIP, "hipEventCreate failed");
-    HIP_TRY(hipEventRecord(a, s));
+    set_launch_events(a, b);
   }
   const hipError_t e = launch();
+  const bool did = launched();
+  if (p->profiling) set_launch_events(nullptr, nullptr);
   if (e != hipSuccess)
     return fail(MUON_EHIP, std::string(kKindNames[kind]) + " launch: " + hipGetErrorString(e));
   if (p->profiling) {
-    HIP_TRY(hipEventRecord(b, s));
+    if (!did) {   // nothing to launch: an empty interval
+      HIP_TRY(hipEventRecord(a, s));
+      HIP_TRY(hipEventRecord(b, s));
+    }
     p->recs.push_back({kind, kern, flops, bytes, a, b});
   }
   return MUON_OK;

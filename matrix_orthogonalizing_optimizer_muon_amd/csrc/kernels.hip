@@ -12,6 +12,7 @@
 //                 item 1).  LDS-staged 128-byte k-tiles, double buffered.
 //  k_ew_apply     decoupled weight decay plus the RMS-matched orthogonal step
 //                 (same deep-dive section), transposing back through LDS.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -20,6 +21,20 @@
 
 namespace muon {
 namespace {
+
+// profiling events of the next launch on this thread (see set_launch_events)
+thread_local hipEvent_t t_ev_start = nullptr, t_ev_stop = nullptr;
+thread_local bool t_launched = false;
+
+template <typename F, typename... Args>
+void launch_kernel(F kernel, dim3 grid, dim3 block, uint32_t smem, hipStream_t s, Args... args) {
+  if (t_ev_start)
+    hipExtLaunchKernelGGL(kernel, grid, block, smem, s, t_ev_start, t_ev_stop, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, smem, s, args...);
+  t_ev_start = t_ev_stop = nullptr;
+  t_launched = true;
+}
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
@@ -673,7 +688,7 @@ hipError_t launch_gemm_t(const GemmParams& p, hipStream_t s) {
     attr_done = true;
   }
   if (p.n_items <= 0) return hipSuccess;
-  hipLaunchKernelGGL(kern, dim3(p.n_items), dim3(256), smem, s, p);
+  launch_kernel(kern, dim3(p.n_items), dim3(256), smem, s, p);
   return hipGetLastError();
 }
 
@@ -1044,7 +1059,7 @@ hipError_t launch_nt_t(const GemmParams& p, hipStream_t s) {
     attr_done = true;
   }
   if (p.n_items <= 0) return hipSuccess;
-  hipLaunchKernelGGL(kern, dim3(p.n_items), dim3(G::THREADS), smem, s, p);
+  launch_kernel(kern, dim3(p.n_items), dim3(G::THREADS), smem, s, p);
   return hipGetLastError();
 }
 
@@ -1069,7 +1084,7 @@ hipError_t launch_ew_momentum(const EwMat* mats, const EwDyn* dyn, const int64_t
   const int64_t n = tile_end - tile_begin;
   if (n <= 0) return hipSuccess;
   const int64_t grid = n < grid_cap ? n : grid_cap;
-  hipLaunchKernelGGL(k_ew_momentum, dim3((unsigned)grid), dim3(256), 0, s, mats, dyn, tile_prefix,
+  launch_kernel(k_ew_momentum, dim3((unsigned)grid), dim3(256), 0, s, mats, dyn, tile_prefix,
                      nmats, tile_begin, tile_end, partials, beta, nesterov, load_only);
   return hipGetLastError();
 }
@@ -1078,7 +1093,7 @@ hipError_t launch_adamw(const AdamTensor* tensors, const int64_t* chunk_prefix, 
                         int64_t total_chunks, AdamScalars sc, int grid_cap, hipStream_t s) {
   if (total_chunks <= 0) return hipSuccess;
   const int64_t grid = total_chunks < grid_cap ? total_chunks : grid_cap;
-  hipLaunchKernelGGL(k_adamw, dim3((unsigned)grid), dim3(256), 0, s, tensors, chunk_prefix, ntensors,
+  launch_kernel(k_adamw, dim3((unsigned)grid), dim3(256), 0, s, tensors, chunk_prefix, ntensors,
                      total_chunks, sc);
   return hipGetLastError();
 }
@@ -1086,7 +1101,7 @@ hipError_t launch_adamw(const AdamTensor* tensors, const int64_t* chunk_prefix, 
 hipError_t launch_norm(const EwMat* mats, int nmats, const float* partials, float* rscale,
                        uint32_t* flags, float eps, hipStream_t s) {
   if (nmats <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_norm, dim3(nmats), dim3(256), 0, s, mats, partials, rscale, flags, eps);
+  launch_kernel(k_norm, dim3(nmats), dim3(256), 0, s, mats, partials, rscale, flags, eps);
   return hipGetLastError();
 }
 
@@ -1096,7 +1111,7 @@ hipError_t launch_ew_apply(const EwMat* mats, const EwDyn* dyn, const int64_t* t
                            hipStream_t s) {
   if (total_tiles <= 0) return hipSuccess;
   const int64_t grid = total_tiles < grid_cap ? total_tiles : grid_cap;
-  hipLaunchKernelGGL(k_ew_apply, dim3((unsigned)grid), dim3(256), 0, s, mats, dyn, tile_prefix,
+  launch_kernel(k_ew_apply, dim3((unsigned)grid), dim3(256), 0, s, mats, dyn, tile_prefix,
                      nmats, total_tiles, rscale, lr, wd, src_is_d, skip_fused, store_x);
   return hipGetLastError();
 }
@@ -1121,5 +1136,13 @@ hipError_t launch_gemm_nt(int nt_cfg, int out_dtype, const GemmParams& p, hipStr
     default: return hipErrorInvalidValue;
   }
 }
+
+void set_launch_events(hipEvent_t start, hipEvent_t stop) {
+  t_ev_start = start;
+  t_ev_stop = stop;
+  t_launched = false;
+}
+
+bool launched() { return t_launched; }
 
 }  // namespace muon

@@ -176,4 +176,11 @@ hipError_t launch_gemm(int tile_cfg, int in_dtype, int out_dtype, const GemmPara
 // out_dtype: kF32 or kBF16; Cin (c_id) and out^T (ot_id) are bf16.
 hipError_t launch_gemm_nt(int nt_cfg, int out_dtype, const GemmParams& p, hipStream_t s);
 
+// Profiling: the next kernel launched by any launcher above on this thread
+// records its dispatch start and end in these events (hipExtLaunchKernel), the
+// times a kernel-trace profiler reports even when streams overlap.  launched()
+// says whether a kernel has been launched since the events were set.
+void set_launch_events(hipEvent_t start, hipEvent_t stop);
+bool launched();
+
 }  // namespace muon
