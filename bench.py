@@ -277,21 +277,6 @@ def owner_share(args, wl, MU):
     return share, info
 
 
-def union_ms(spans):
-    """Total length of the union of [start, end) intervals."""
-    total, cur_s, cur_e = 0.0, None, None
-    for a, b in sorted(spans):
-        if cur_e is None or a > cur_e:
-            if cur_e is not None:
-                total += cur_e - cur_s
-            cur_s, cur_e = a, b
-        else:
-            cur_e = max(cur_e, b)
-    if cur_e is not None:
-        total += cur_e - cur_s
-    return total
-
-
 def main():
     args = parse()
     if args.gpus != 1:
@@ -365,15 +350,17 @@ def main():
     step_ms = sorted(a.elapsed_time(b) for a, b in per)
     p = lambda q: step_ms[min(len(step_ms) - 1, int(q * len(step_ms)))]
 
-    # per-kernel HIP-event times (the library records them on the step's stream)
-    kt, intervals = [], []
+    # per-kernel dispatch times over as many steps again, after the timed
+    # region: while profiling the library records each kernel's dispatch start
+    # and end and runs the NS lanes one after another, so each time is the
+    # kernel's own
+    kt = []
     if not args.no_kernel_times:
         plan.set_profiling(True)
         plan.kernel_times(reset=True)
         for _ in range(args.steps):
             step()
         kt = plan.kernel_times(reset=False)
-        intervals = plan.launch_intervals()
         plan.kernel_times(reset=True)
         plan.set_profiling(False)
     ns_flops = info["ns_flops_min"]
@@ -398,9 +385,6 @@ def main():
         avg_ms = dom["total_ms"] / dom["launches"]
         fpl = dom["flops"] / dom["launches"]
         ach = fpl / (avg_ms * 1e-3) / 1e12
-        # with NS lanes launches of this kernel overlap: the union of their
-        # intervals is the time the kernel kept the GPU busy
-        busy_ms = union_ms([(iv["start_ms"], iv["end_ms"]) for iv in intervals if iv["kernel"] == name])
         roofline = {"bound": "mfma", "kernel": name, "stages": sorted(set(dom["stages"])),
                     "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
                     "frac": round(ach / peak, 4),
@@ -408,9 +392,7 @@ def main():
                     "avg_launch_us": round(avg_ms * 1e3, 2), "flops_per_launch": fpl,
                     "launches_per_step": dom["launches"] / args.steps,
                     "share_of_step": round(dom["total_ms"] / args.steps / ms, 4),
-                    "lanes": info["n_lanes"],
-                    "busy_ms_per_step": round(busy_ms / args.steps, 4),
-                    "achieved_busy": round(dom["flops"] / (busy_ms * 1e-3) / 1e12, 2) if busy_ms else None}
+                    "lanes": info["n_lanes"]}
     ew = {}
     for n, d in ew_kern.items():
         avg_ms = d["total_ms"] / d["launches"]

@@ -131,13 +131,13 @@ typedef struct muon_kernel_time {
   char name[32];        /* stage, e.g. "ns_apply", "ew_momentum" */
   char kernel[32];      /* kernel instance, e.g. "k_nt<256,256,bf16>" */
   int64_t launches;     /* launches timed */
-  double total_ms;      /* summed hipEvent time of those launches */
+  double total_ms;      /* summed dispatch time (hipEvent pairs) of those launches */
   double flops;         /* summed algorithmic flops of those launches (0 for elementwise) */
   double bytes;         /* summed algorithmic HBM bytes of those launches */
 } muon_kernel_time;
 
-/* One profiled launch: its hipEvent pair as times from the first launch
- * recorded since profiling was enabled or the totals were last reset. */
+/* One profiled launch: its dispatch start and end as times from the first
+ * launch recorded since profiling was enabled or the totals were last reset. */
 typedef struct muon_launch_interval {
   char name[32];        /* stage */
   char kernel[32];      /* kernel instance */
@@ -222,17 +222,18 @@ int muon_plan_matrix_choice(const muon_plan* plan, int i, int32_t* form, int32_t
                             int32_t* group, int32_t* chunk, int32_t* lane);
 
 /*
- * Profiling: while enabled, muon_step records a hipEvent pair around each
- * kernel launch on the stream it is launched on (the step's stream or an NS
- * lane's; concurrent lanes share the GPU, so their pairs overlap in time).
+ * Profiling: while enabled, muon_step (and muon_orthogonalize) record each
+ * kernel's dispatch start and end in a hipEvent pair (hipExtLaunchKernel), and
+ * run the NS lanes one after another on the step's stream, so every recorded
+ * time is one kernel's alone (the events also hold the few microseconds of the
+ * dispatch itself).  Timing with profiling off is therefore not comparable.
  * muon_plan_get_kernel_times synchronizes,
  * folds the recorded pairs into per-(stage, kernel) totals, sorted by stage then
  * kernel name, and writes up to max entries to out (host array), the count to
  * *n_out.  reset != 0 clears the totals (and the intervals) after.
  * muon_plan_get_launch_intervals writes, in launch order, up to max of the
  * launches folded so far (by muon_plan_get_kernel_times) to out and their
- * count to *n_out: with NS lanes, the union of a kernel's intervals is the time
- * it kept the GPU busy.
+ * count to *n_out.
  */
 int muon_plan_set_profiling(muon_plan* plan, int enable);
 int muon_plan_get_kernel_times(muon_plan* plan, muon_kernel_time* out, int max, int* n_out,

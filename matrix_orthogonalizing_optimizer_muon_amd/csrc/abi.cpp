@@ -556,6 +556,8 @@ int enqueue_ns(muon_plan* p, const SetDev& S, int T, const float* sched, const E
 // (lane 0 on s): its front starts when lane l-1's momentum is done, then its
 // NS launch sets follow, so each lane's HBM-bound front runs beside the
 // MFMA-bound NS of the lanes before it.  Lanes 1.. are joined back into s.
+// While profiling, the same launches run lane after lane on s, so each
+// recorded dispatch time is the kernel's own, not shared with another lane.
 template <class Front>
 int enqueue_chunk(muon_plan* p, const ChunkDev& C, int T, const float* sched, const EwDyn* dyn,
                   float lr, float wd, hipStream_t s, Front&& front) {
@@ -568,15 +570,17 @@ int enqueue_chunk(muon_plan* p, const ChunkDev& C, int T, const float* sched, co
       if ((rc = enqueue_ns(p, S, T, sched, dyn, lr, wd, s))) return rc;
     return MUON_OK;
   }
+  const bool serial = p->profiling;
   for (int l = 0; l < L; ++l) {
-    hipStream_t ls = l == 0 ? s : p->lane_streams[l - 1];
-    if (l > 0) HIP_TRY(hipStreamWaitEvent(ls, p->lane_front[l - 1], 0));
-    if ((rc = front(C.lane_first[l], C.lane_first[l + 1], ls, l + 1 < L ? p->lane_front[l] : nullptr)))
+    hipStream_t ls = (l == 0 || serial) ? s : p->lane_streams[l - 1];
+    if (l > 0 && !serial) HIP_TRY(hipStreamWaitEvent(ls, p->lane_front[l - 1], 0));
+    if ((rc = front(C.lane_first[l], C.lane_first[l + 1], ls,
+                    (l + 1 < L && !serial) ? p->lane_front[l] : nullptr)))
       return rc;
     for (const SetDev& S : C.sets)
       if (S.lane == l && (rc = enqueue_ns(p, S, T, sched, dyn, lr, wd, ls))) return rc;
   }
-  for (int l = 1; l < L; ++l) {
+  for (int l = 1; l < L && !serial; ++l) {
     HIP_TRY(hipEventRecord(p->lane_join[l - 1], p->lane_streams[l - 1]));
     HIP_TRY(hipStreamWaitEvent(s, p->lane_join[l - 1], 0));
   }

@@ -229,17 +229,6 @@ def test_tune_cache_is_read_and_bad_lines_ignored(tmp_path):
     assert p4.matrix_choice(0)["form"] == "direct"
 
 
-def test_bench_busy_time_is_the_union_of_intervals():
-    import importlib.util
-    spec = importlib.util.spec_from_file_location("bench_mod", os.path.join(ROOT, "bench.py"))
-    b = importlib.util.module_from_spec(spec)
-    spec.loader.exec_module(b)
-    assert b.union_ms([]) == 0.0
-    assert b.union_ms([(0.0, 1.0), (0.5, 2.0), (3.0, 4.0), (3.5, 3.6)]) == pytest.approx(3.0)
-    assert b.union_ms([(2.0, 3.0), (0.0, 1.0)]) == pytest.approx(2.0)
-    assert b.union_ms([(0.0, 5.0), (1.0, 2.0)]) == pytest.approx(5.0)
-
-
 def test_orthogonalize_marshalling_and_host_only_refusal():
     p = _host([(16, 32), (32, 16)])
     lib = L.lib()
