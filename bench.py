@@ -398,7 +398,8 @@ def main():
         avg_ms = d["total_ms"] / d["launches"]
         gbs = d["bytes"] / d["launches"] / (avg_ms * 1e-3) / 1e9
         ew[n] = {"GB/s": round(gbs, 1), "frac_of_hbm": round(gbs / PEAK_HBM_GBS, 4),
-                 "avg_launch_us": round(avg_ms * 1e3, 2), "bytes_per_launch": d["bytes"] / d["launches"]}
+                 "avg_launch_us": round(avg_ms * 1e3, 2), "bytes_per_launch": d["bytes"] / d["launches"],
+                 "traffic": traffic_for(n, wl.name, d["launches"] / args.steps)}
     value = ns_flops / (ms * 1e-3) / 1e12
     out = {
         "metric": "Muon optimizer-step ms + NS TFLOP/s (% of MI355X bf16 MFMA peak)",
