@@ -213,11 +213,14 @@ def _mixed_lane_state():
     return sb + sf, ["bf16"] * len(sb) + ["f32"] * len(sf), Wb + Wf, Gb + Gf, Bb + Bf
 
 
-@pytest.mark.parametrize("lanes,chunked", [(2, False), (3, False), (4, False), (2, True)])
-def test_lanes_give_bitwise_the_one_lane_result(M, lanes, chunked):
+@pytest.mark.parametrize("lanes,chunked,profiled", [(2, False, False), (3, False, False),
+                                                     (4, False, False), (2, True, False),
+                                                     (3, False, True)])
+def test_lanes_give_bitwise_the_one_lane_result(M, lanes, chunked, profiled):
     """NS lanes change only which stream a launch goes to: three consecutive
     steps (bf16 direct and Gram, fp32 matrices, one or several workspace chunks)
-    leave parameters and momenta bitwise equal to the one-lane plan's."""
+    leave parameters and momenta bitwise equal to the one-lane plan's; so does
+    profiling, which runs the lanes one after another with dispatch events."""
     import torch
     from gpu_util import device_state
     shapes, dts, Ws, Gs, Bs = _mixed_lane_state()
@@ -230,9 +233,21 @@ def test_lanes_give_bitwise_the_one_lane_result(M, lanes, chunked):
         info = plan.info()
         assert info["n_lanes"] == L and (info["n_chunks"] >= 2) == chunked
         P, G, B = device_state(Ws, Gs, Bs)
+        if profiled and L > 1:
+            plan.set_profiling(True)
         for _ in range(3):
             plan.step(P, G, B)
         torch.cuda.synchronize()
+        if profiled and L > 1:
+            kt = plan.kernel_times(reset=False)
+            iv = plan.launch_intervals()
+            plan.set_profiling(False)
+            # every launch recorded, with a dispatch interval of positive length;
+            # serial lanes: no two intervals overlap
+            assert sum(k["launches"] for k in kt) == len(iv) > 0
+            assert all(0 <= x["start_ms"] < x["end_ms"] for x in iv)
+            spans = sorted((x["start_ms"], x["end_ms"]) for x in iv)
+            assert all(b[0] >= a[1] - 5e-3 for a, b in zip(spans, spans[1:]))
         assert plan.flags() == 0
         outs.append([p.view(torch.int16).cpu().numpy().copy() if p.dtype == torch.bfloat16
                      else p.cpu().numpy().copy() for p in P] + [b.cpu().numpy().copy() for b in B])
