@@ -727,19 +727,32 @@ __device__ __forceinline__ void st_bf16x4(void* base, int64_t off, const float* 
 // Pipeline of each NT configuration: k-tile (elements) and LDS stages.  One
 // setting serves all four: k-tiles of 32 with three or four stages were
 // measured slower on the 128x128 tile.
+// LDS_CAP: the LDS a block may take without lowering the blocks per CU its
+// registers allow (two 128x128 blocks per CU, one of any other).
 template <int BM, int BN, int WGM, int WGN>
 struct NtPipe {
   static constexpr int BK = 64, S = 2;
+  static constexpr int LDS_CAP = (BM == 128 && BN == 128) ? 80 * 1024 : 160 * 1024;
 };
 
 // Rows of the output tile staged in LDS at a time: the largest power of two
-// whose fp32 slab (row pitch BN + 4 floats) fits the mainloop's LDS.
+// whose fp32 slab (row pitch BN + 4 floats) fits the block's LDS budget.
 template <int BM, int BN, int WGM, int WGN>
 constexpr int slab_rows() {
   int sh = BM;
-  using P = NtPipe<BM, BN, WGM, WGN>;
-  while (sh > 8 && sh * (BN + 4) * 4 > nt::Geom<BM, BN, P::BK, P::S, WGM, WGN>::LDS) sh /= 2;
+  while (sh > 8 && sh * (BN + 4) * 4 > NtPipe<BM, BN, WGM, WGN>::LDS_CAP) sh /= 2;
   return sh;
+}
+
+// Dynamic LDS of a block: the main loop's stages or the epilogue slab,
+// whichever is larger (the two never live at once).
+template <int BM, int BN, int WGM, int WGN>
+constexpr int nt_lds() {
+  using P = NtPipe<BM, BN, WGM, WGN>;
+  constexpr int stages = nt::Geom<BM, BN, P::BK, P::S, WGM, WGN>::LDS;
+  constexpr int slab = slab_rows<BM, BN, WGM, WGN>() * (BN + 4) * 4;
+  static_assert(stages <= P::LDS_CAP && slab <= P::LDS_CAP, "LDS budget");
+  return stages > slab ? stages : slab;
 }
 
 __device__ __forceinline__ void ld8_bf16(const void* base, int64_t off, float* v) {
@@ -861,7 +874,8 @@ __device__ __forceinline__ void nt_epilogue(const nt::f32x16_t (&acc)[BM / 32 / 
   constexpr int SH = slab_rows<BM, BN, WGM, WGN>();
   constexpr int PITCH = BN + 4;
   constexpr int TPR = BN / 8, RPP = NT / TPR;
-  static_assert(SH % 32 == 0 && PITCH % 4 == 0 && SH * PITCH * 4 <= G::LDS && NT % TPR == 0, "slab");
+  static_assert(SH % 32 == 0 && PITCH % 4 == 0 && SH * PITCH * 4 <= nt_lds<BM, BN, WGM, WGN>() &&
+                NT % TPR == 0, "slab");
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wy = w / WGN, wx = w % WGN;
   float sc = 1.0f;
   if (p.scale_pow) {
@@ -1049,7 +1063,8 @@ template <int BM, int BN, int WGM, int WGN, typename TO, bool QT>
 hipError_t launch_nt_t(const GemmParams& p, hipStream_t s) {
   using PP = NtPipe<BM, BN, WGM, WGN>;
   using G = nt::Geom<BM, BN, PP::BK, PP::S, WGM, WGN, QT>;
-  constexpr int smem = G::LDS;
+  static_assert(G::LDS == nt::Geom<BM, BN, PP::BK, PP::S, WGM, WGN>::LDS, "k-major Q tile, same bytes");
+  constexpr int smem = nt_lds<BM, BN, WGM, WGN>();
   static bool attr_done = false;
   auto kern = &k_nt<BM, BN, WGM, WGN, TO, QT>;
   if (!attr_done) {
