@@ -77,14 +77,19 @@ def test_ns_steps_zero_and_schedule(M):
     run_and_compare(plan, Ws, Gs, Bs, WL.F32, ns_steps=3, coeffs=sched)
 
 
-def test_c2_three_steps_all_matrices(M):
-    """The transformer-block workload as the bench runs it: 16 bf16 matrices, 3 steps,
-    fresh gradients each step, momentum and weights carried over."""
+@pytest.mark.parametrize("tune", ["off", "once"])
+def test_c2_three_steps_all_matrices(M, tune, tmp_path):
+    """The transformer-block workload: 16 bf16 matrices, 3 steps, fresh
+    gradients each step, momentum and weights carried over; with the cost
+    model's plan and with the plan bench.py times (shapes and the whole set
+    timed once into a fresh cache: tile plan, NS lanes, staggered fronts)."""
     import torch
     from gpu_util import to_device, to_f64, rel
     from oracle import muon_oracle as O
     wl = WL.workload(2)
-    plan = _plan(M, wl.shapes, "bf16")
+    plan = _plan(M, wl.shapes, "bf16", tune=tune, cache_path=str(tmp_path / "tune.txt"))
+    print("c2 plan", tune, plan.info()["n_lanes"], "lanes,",
+          sorted({(plan.matrix_choice(i)["form"], plan.matrix_choice(i)["tile"]) for i in range(wl.n_matrices)}))
     P = [to_device(WL.draw(wl, i, 0, WL.KIND_W)) for i in range(wl.n_matrices)]
     B = [torch.zeros(s, dtype=torch.float32, device="cuda") for s in wl.shapes]
     cap = [torch.empty(s, dtype=torch.float32, device="cuda") for s in wl.shapes]
