@@ -385,10 +385,14 @@ def main():
         avg_ms = dom["total_ms"] / dom["launches"]
         fpl = dom["flops"] / dom["launches"]
         ach = fpl / (avg_ms * 1e-3) / 1e12
+        tr = traffic_for(name, wl.name, dom["launches"] / args.steps)
         roofline = {"bound": "mfma", "kernel": name, "stages": sorted(set(dom["stages"])),
                     "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
                     "frac": round(ach / peak, 4),
-                    "traffic": traffic_for(name, wl.name, dom["launches"] / args.steps),
+                    # measured HBM bytes per launch (fetch + write), null when
+                    # no counter record matches these kernel sources and plan
+                    "traffic": tr["bytes"] if tr else None,
+                    "traffic_detail": tr,
                     "avg_launch_us": round(avg_ms * 1e3, 2), "flops_per_launch": fpl,
                     "launches_per_step": dom["launches"] / args.steps,
                     "share_of_step": round(dom["total_ms"] / args.steps / ms, 4),
