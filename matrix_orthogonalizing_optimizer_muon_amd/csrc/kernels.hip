@@ -744,15 +744,21 @@ constexpr int slab_rows() {
   return sh;
 }
 
-// Dynamic LDS of a block: the main loop's stages or the epilogue slab,
-// whichever is larger (the two never live at once).
+// Row pitch (elements) of the bf16 epilogue tile.
+template <int BN>
+constexpr int bf16_pitch() { return BN + 8; }
+
+// Dynamic LDS of a block: the main loop's stages, the fp32 epilogue slab or the
+// whole output tile in bf16, whichever is largest (they never live at once).
 template <int BM, int BN, int WGM, int WGN>
 constexpr int nt_lds() {
   using P = NtPipe<BM, BN, WGM, WGN>;
   constexpr int stages = nt::Geom<BM, BN, P::BK, P::S, WGM, WGN>::LDS;
   constexpr int slab = slab_rows<BM, BN, WGM, WGN>() * (BN + 4) * 4;
-  static_assert(stages <= P::LDS_CAP && slab <= P::LDS_CAP, "LDS budget");
-  return stages > slab ? stages : slab;
+  constexpr int tile16 = BM * bf16_pitch<BN>() * 2;
+  static_assert(stages <= P::LDS_CAP && slab <= P::LDS_CAP && tile16 <= P::LDS_CAP, "LDS budget");
+  constexpr int m = stages > slab ? stages : slab;
+  return m > tile16 ? m : tile16;
 }
 
 __device__ __forceinline__ void ld8_bf16(const void* base, int64_t off, float* v) {
@@ -856,7 +862,10 @@ __device__ __forceinline__ void apply_update8(const UpdCtx& c, int64_t row, int6
   }
 }
 
-// Epilogue of the NT kernel through LDS, in slabs of SH rows:
+// Epilogue of the NT kernel.  With only a bf16 row-major output to write (no
+// Cin, transposed copy, mirrored tile or update) the values are finished in
+// registers and the whole tile goes through LDS once, as bf16.  Otherwise it
+// goes through LDS in fp32 slabs of SH rows:
 //  1. each wave writes its accumulators of the slab's rows into an fp32 tile;
 //  2. row pass: every thread takes 8 consecutive columns of a row, applies
 //     out = (s alpha) acc + (s beta) Cin + gamma [i == j] (0 outside the real
@@ -903,6 +912,45 @@ __device__ __forceinline__ void nt_epilogue(const nt::f32x16_t (&acc)[BM / 32 / 
   // the update's W runs are loaded ahead when they are aligned bf16 runs
   const bool wvec = fuse && uc.pdtype == kBF16 && uc.vec;
   const bool wrow = wvec && !ftrans, wcol = wvec && ftrans;
+  if constexpr (sizeof(TO) == 2) {
+    if (!colpass && !fuse && !Cin) {
+      // only the bf16 row-major output: each lane finishes its values in
+      // registers (4 consecutive columns of a row per register group) and
+      // stages them as bf16 for the whole tile; then 16-byte row runs out
+      constexpr int PB = bf16_pitch<BN>();
+      constexpr int TPR = BN / 8, RPP = NT / TPR;
+      MUON_LDS uint16_t* Cb = reinterpret_cast<MUON_LDS uint16_t*>(C);
+      __syncthreads();   // every wave is done with the main loop's LDS
+#pragma unroll
+      for (int a = 0; a < G::MT; ++a) {
+        const int r = wy * G::WM + a * 32 + (lane & 31), i = m0 + r;
+#pragma unroll
+        for (int b = 0; b < G::NT; ++b)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int c = wx * G::WN + b * 32 + g * 8 + (lane >> 5) * 4, j = n0 + c;
+            float v[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v[q] = as * acc[a][b][4 * g + q];
+            if (edge) {
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                if (i == j + q) v[q] += gamma;
+                if (i >= Mr || j + q >= Nr) v[q] = 0.f;
+              }
+            }
+            *(MUON_LDS u32x2_t*)(Cb + r * PB + c) = u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+          }
+      }
+      __syncthreads();
+      const int cc = (tid % TPR) * 8;
+#pragma unroll 4
+      for (int r = tid / TPR; r < BM; r += RPP)
+        *(GLOBAL_AS u32x4_t*)(static_cast<uint16_t*>(Out) + (int64_t)(m0 + r) * ldo + n0 + cc) =
+            *(const MUON_LDS u32x4_t*)(Cb + r * PB + cc);
+      return;
+    }
+  }
   __syncthreads();   // every wave is done with the main loop's LDS
 #pragma unroll 1
   for (int s0 = 0; s0 < BM; s0 += SH) {
