@@ -59,52 +59,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ uint32_t f32_to_bf16(float f) { return pack_bf16x2(f, 0.f) & 0xffffu; }
 
-// 16-byte global accesses and 16 consecutive elements of dtype dt starting at
-// element offset off (16-byte aligned).  (Nontemporal variants of these were
-// measured slower for every elementwise kernel here.)
+// 16-byte global accesses.  (Nontemporal variants were measured slower for
+// every elementwise kernel here.)
 __device__ __forceinline__ u32x4_t ld_u4(const void* p) {
   return *(const GLOBAL_AS u32x4_t*)p;
 }
 
 __device__ __forceinline__ void st_u4(void* p, u32x4_t v) {
   *(GLOBAL_AS u32x4_t*)p = v;
-}
-
-__device__ __forceinline__ void load16_vec(const void* base, int dt, int64_t off, float* v) {
-  if (dt == kBF16) {
-    const uint16_t* p = static_cast<const uint16_t*>(base) + off;
-    const u32x4_t a = ld_u4(p), b = ld_u4(p + 8);
-    const uint32_t w[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      v[2 * e] = bf16_to_f32(w[e] & 0xffffu);
-      v[2 * e + 1] = bf16_to_f32(w[e] >> 16);
-    }
-  } else {
-    const float* p = static_cast<const float*>(base) + off;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const u32x4_t t = ld_u4(p + 4 * q);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[4 * q + e] = __uint_as_float(t[e]);
-    }
-  }
-}
-
-__device__ __forceinline__ void store16_vec(void* base, int dt, int64_t off, const float* v) {
-  if (dt == kBF16) {
-    uint16_t* p = static_cast<uint16_t*>(base) + off;
-    st_u4(p, u32x4_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
-                         pack_bf16x2(v[6], v[7])});
-    st_u4(p + 8, u32x4_t{pack_bf16x2(v[8], v[9]), pack_bf16x2(v[10], v[11]),
-                             pack_bf16x2(v[12], v[13]), pack_bf16x2(v[14], v[15])});
-  } else {
-    float* p = static_cast<float*>(base) + off;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      st_u4(p + 4 * q, u32x4_t{__float_as_uint(v[4 * q]), __float_as_uint(v[4 * q + 1]),
-                                   __float_as_uint(v[4 * q + 2]), __float_as_uint(v[4 * q + 3])});
-  }
 }
 
 __device__ __forceinline__ float load1(const void* base, int dt, int64_t off) {
@@ -135,8 +97,38 @@ __device__ __forceinline__ int find_mat(const int64_t* prefix, int nmats, int64_
 
 // ------------------------------------------------------------ elementwise: momentum
 
-// Thread layout on a 64 x 64 block (stored orientation): row r = tid / 4,
-// 16 consecutive columns from c0 = (tid % 4) * 16.
+// Four consecutive elements of dtype dt at element offset off (a multiple of
+// 4 on a 16-byte aligned base): one 8-byte (bf16) or 16-byte (fp32) access.
+__device__ __forceinline__ void load4_vec(const void* base, int dt, int64_t off, float* v) {
+  if (dt == kBF16) {
+    const u32x2_t a = *(const GLOBAL_AS u32x2_t*)(static_cast<const uint16_t*>(base) + off);
+    v[0] = bf16_to_f32(a[0] & 0xffffu);
+    v[1] = bf16_to_f32(a[0] >> 16);
+    v[2] = bf16_to_f32(a[1] & 0xffffu);
+    v[3] = bf16_to_f32(a[1] >> 16);
+  } else {
+    const u32x4_t t = ld_u4(static_cast<const float*>(base) + off);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = __uint_as_float(t[e]);
+  }
+}
+
+__device__ __forceinline__ void store4_vec(void* base, int dt, int64_t off, const float* v) {
+  if (dt == kBF16) {
+    *(GLOBAL_AS u32x2_t*)(static_cast<uint16_t*>(base) + off) =
+        u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+  } else {
+    st_u4(static_cast<float*>(base) + off, u32x4_t{__float_as_uint(v[0]), __float_as_uint(v[1]),
+                                                   __float_as_uint(v[2]), __float_as_uint(v[3])});
+  }
+}
+
+// Thread layout on a 64 x 64 tile (stored orientation): 16 lanes span one
+// 64-element row segment, 4 consecutive columns each, so every wave-wide
+// access covers four whole row segments (128 contiguous bytes of bf16, 256 of
+// fp32).  Thread tid holds rows rq + 16 k (rq = tid / 16, k = 0..3) at
+// columns cq .. cq + 3 (cq = 4 (tid % 16)).  The same layout makes the LDS
+// transpose below free of bank conflicts (row pitch 65 floats).
 __global__ __launch_bounds__(256) void k_ew_momentum(
     const EwMat* __restrict__ mats, const EwDyn* __restrict__ dyn,
     const int64_t* __restrict__ prefix, int nmats, int64_t t_begin, int64_t t_end,
@@ -144,7 +136,7 @@ __global__ __launch_bounds__(256) void k_ew_momentum(
   __shared__ float tT[kEwTile][kEwTile + 1];
   __shared__ float red[4];
   const int tid = threadIdx.x;
-  const int r = tid >> 2, c0 = (tid & 3) * 16;
+  const int rq = tid >> 4, cq = (tid & 15) * 4;
   for (int64_t t = t_begin + blockIdx.x; t < t_end; t += gridDim.x) {
     const int mi = find_mat(prefix, nmats, t);
     const EwMat& M = mats[mi];
@@ -152,64 +144,89 @@ __global__ __launch_bounds__(256) void k_ew_momentum(
     const int64_t lt = t - M.tile_begin;
     const int64_t i0 = (lt / M.tiles_j) * kEwTile, j0 = (lt % M.tiles_j) * kEwTile;
     const int64_t sr0 = M.trans ? j0 : i0, sc0 = M.trans ? i0 : j0;
-    const int64_t sr = sr0 + r;
-    float dv[16];
+    const bool full = D.vec && sr0 + kEwTile <= M.rows && sc0 + kEwTile <= M.cols;
+    float dv[4][4];
     if (load_only) {
       // d = the input itself (orthogonalization alone: no momentum buffer)
-      if (D.vec && sr0 + kEwTile <= M.rows && sc0 + kEwTile <= M.cols) {
-        load16_vec(D.g, M.pdtype, sr * M.cols + sc0 + c0, dv);
-      } else {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int64_t sc = sc0 + c0 + e;
-          dv[e] = (sr < M.rows && sc < M.cols) ? load1(D.g, M.pdtype, sr * M.cols + sc) : 0.f;
+      for (int k = 0; k < 4; ++k) {
+        const int64_t sr = sr0 + rq + 16 * k;
+        if (full) {
+          load4_vec(D.g, M.pdtype, sr * M.cols + sc0 + cq, dv[k]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int64_t sc = sc0 + cq + e;
+            dv[k][e] = (sr < M.rows && sc < M.cols) ? load1(D.g, M.pdtype, sr * M.cols + sc) : 0.f;
+          }
         }
       }
-    } else if (D.vec && sr0 + kEwTile <= M.rows && sc0 + kEwTile <= M.cols) {
-      const int64_t off = sr * M.cols + sc0 + c0;
-      float g[16], b[16];
-      load16_vec(D.g, M.pdtype, off, g);
-      load16_vec(D.buf, kF32, off, b);
+    } else if (full) {
+      float g[4][4], b[4][4];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        b[e] = beta * b[e] + g[e];
-        dv[e] = nesterov ? g[e] + beta * b[e] : b[e];
+      for (int k = 0; k < 4; ++k) {
+        const int64_t off = (sr0 + rq + 16 * k) * M.cols + sc0 + cq;
+        load4_vec(D.g, M.pdtype, off, g[k]);
+        load4_vec(D.buf, kF32, off, b[k]);
       }
-      store16_vec(D.buf, kF32, off, b);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          b[k][e] = beta * b[k][e] + g[k][e];
+          dv[k][e] = nesterov ? g[k][e] + beta * b[k][e] : b[k][e];
+        }
+        store4_vec(D.buf, kF32, (sr0 + rq + 16 * k) * M.cols + sc0 + cq, b[k]);
+      }
     } else {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int64_t sc = sc0 + c0 + e;
-        dv[e] = 0.f;
-        if (sr < M.rows && sc < M.cols) {
-          const int64_t off = sr * M.cols + sc;
-          const float g = load1(D.g, M.pdtype, off);
-          const float b = beta * D.buf[off] + g;
-          D.buf[off] = b;
-          dv[e] = nesterov ? g + beta * b : b;
+      for (int k = 0; k < 4; ++k) {
+        const int64_t sr = sr0 + rq + 16 * k;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int64_t sc = sc0 + cq + e;
+          dv[k][e] = 0.f;
+          if (sr < M.rows && sc < M.cols) {
+            const int64_t off = sr * M.cols + sc;
+            const float g = load1(D.g, M.pdtype, off);
+            const float b = beta * D.buf[off] + g;
+            D.buf[off] = b;
+            dv[k][e] = nesterov ? g + beta * b : b;
+          }
         }
       }
     }
     float ss = 0.f;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) ss += dv[e] * dv[e];
-    // dv is row r of the tile in stored orientation: canonical row i0 + r of
-    // D (stored = canonical) or canonical column j0 + r, i.e. row j0 + r of
-    // D^T (tall matrices).  That orientation is stored directly; the other
-    // one, when the NS path uses it, goes through an LDS transpose.
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ss += dv[k][e] * dv[k][e];
+    // dv[k] is row rq + 16 k of the tile in stored orientation: canonical row
+    // i0 + rq + 16 k of D (stored = canonical) or canonical column j0 + rq +
+    // 16 k, i.e. a row of D^T (tall matrices).  That orientation is stored
+    // directly; the other one, when the NS path uses it, goes through an LDS
+    // transpose.
     void* direct = M.trans ? M.dt : M.d;
     void* other = M.trans ? M.d : M.dt;
     const int64_t ld_dir = M.trans ? M.ldt : M.ldd, ld_oth = M.trans ? M.ldd : M.ldt;
-    const int64_t r0_dir = M.trans ? j0 : i0, c0_dir = M.trans ? i0 : j0;
-    if (direct) store16_vec(direct, M.ddtype, (r0_dir + r) * ld_dir + c0_dir + c0, dv);
+    if (direct) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        store4_vec(direct, M.ddtype, (sr0 + rq + 16 * k) * ld_dir + sc0 + cq, dv[k]);
+    }
     if (other) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) tT[c0 + e][r] = dv[e];
-      __syncthreads();
-      float o[16];
+      for (int k = 0; k < 4; ++k)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) o[e] = tT[r][c0 + e];
-      store16_vec(other, M.ddtype, (c0_dir + r) * ld_oth + r0_dir + c0, o);
+        for (int e = 0; e < 4; ++e) tT[cq + e][rq + 16 * k] = dv[k][e];
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        float o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = tT[rq + 16 * k][cq + e];
+        store4_vec(other, M.ddtype, (sc0 + rq + 16 * k) * ld_oth + sr0 + cq, o);
+      }
     }
     ss = wave_sum(ss);
     if ((tid & 63) == 0) red[tid >> 6] = ss;
@@ -339,6 +356,7 @@ __global__ __launch_bounds__(256) void k_adamw(const AdamTensor* __restrict__ ts
 
 // ------------------------------------------------------------ elementwise: apply
 
+// Same thread layout as k_ew_momentum (rows rq + 16 k, columns cq .. cq + 3).
 __global__ __launch_bounds__(256) void k_ew_apply(
     const EwMat* __restrict__ mats, const EwDyn* __restrict__ dyn,
     const int64_t* __restrict__ prefix, int nmats, int64_t total,
@@ -346,7 +364,7 @@ __global__ __launch_bounds__(256) void k_ew_apply(
     int store_x) {
   __shared__ float tT[kEwTile][kEwTile + 1];
   const int tid = threadIdx.x;
-  const int r = tid >> 2, c0 = (tid & 3) * 16;
+  const int rq = tid >> 4, cq = (tid & 15) * 4;
   for (int64_t t = blockIdx.x; t < total; t += gridDim.x) {
     const int mi = find_mat(prefix, nmats, t);
     const EwMat& M = mats[mi];
@@ -358,59 +376,70 @@ __global__ __launch_bounds__(256) void k_ew_apply(
     const float sx = src_is_d ? rscale[M.mat] : 1.0f;
     const void* src = src_is_d ? M.d : static_cast<const void*>(M.xt);
     const int sdt = src_is_d ? M.ddtype : kF32;
-    float x[16];
-    int64_t sr, sc0;
+    float x[4][4];
+    int64_t sr0, sc0;   // the tile's origin in stored orientation
     if (!M.trans) {
-      load16_vec(src, sdt, (i0 + r) * M.ldd + j0 + c0, x);
-      sr = i0 + r;
-      sc0 = j0 + c0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) load4_vec(src, sdt, (i0 + rq + 16 * k) * M.ldd + j0 + cq, x[k]);
+      sr0 = i0;
+      sc0 = j0;
     } else {
-      float o[16];
-      load16_vec(src, sdt, (i0 + r) * M.ldd + j0 + c0, o);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) tT[r][c0 + e] = o[e];
+      for (int k = 0; k < 4; ++k) {
+        float o[4];
+        load4_vec(src, sdt, (i0 + rq + 16 * k) * M.ldd + j0 + cq, o);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) tT[rq + 16 * k][cq + e] = o[e];
+      }
       __syncthreads();
 #pragma unroll
-      for (int e = 0; e < 16; ++e) x[e] = tT[c0 + e][r];
+      for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[k][e] = tT[cq + e][rq + 16 * k];
       __syncthreads();
-      sr = j0 + r;
-      sc0 = i0 + c0;
+      sr0 = j0;
+      sc0 = i0;
     }
     const float s = M.s;
-    if (store_x) {
-      // orthogonalization alone: the NS output itself, fp32, stored orientation
+    const int64_t sc = sc0 + cq;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) x[e] *= sx;
-      if (D.vec && sr < M.rows && sc0 + 16 <= M.cols) {
-        store16_vec(D.w, kF32, sr * M.cols + sc0, x);
+    for (int k = 0; k < 4; ++k) {
+      const int64_t sr = sr0 + rq + 16 * k;
+      const bool vec = D.vec && sr < M.rows && sc + 4 <= M.cols;
+      if (store_x) {
+        // orthogonalization alone: the NS output itself, fp32, stored orientation
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[k][e] *= sx;
+        if (vec) {
+          store4_vec(D.w, kF32, sr * M.cols + sc, x[k]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (sr < M.rows && sc + e < M.cols) static_cast<float*>(D.w)[sr * M.cols + sc + e] = x[k][e];
+        }
+        continue;
+      }
+      if (vec) {
+        const int64_t off = sr * M.cols + sc;
+        float w[4], u[4];
+        load4_vec(D.w, M.pdtype, off, w);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          u[e] = -lr * (wd * w[e] + s * (sx * x[k][e]));
+          w[e] = w[e] + u[e];
+        }
+        store4_vec(D.w, M.pdtype, off, w);
+        if (D.upd) store4_vec(D.upd, kF32, off, u);
       } else {
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-          if (sr < M.rows && sc0 + e < M.cols) static_cast<float*>(D.w)[sr * M.cols + sc0 + e] = x[e];
-      }
-      continue;
-    }
-    if (D.vec && sr < M.rows && sc0 + 16 <= M.cols) {
-      const int64_t off = sr * M.cols + sc0;
-      float w[16], u[16];
-      load16_vec(D.w, M.pdtype, off, w);
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        u[e] = -lr * (wd * w[e] + s * (sx * x[e]));
-        w[e] = w[e] + u[e];
-      }
-      store16_vec(D.w, M.pdtype, off, w);
-      if (D.upd) store16_vec(D.upd, kF32, off, u);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int64_t sc = sc0 + e;
-        if (sr < M.rows && sc < M.cols) {
-          const int64_t off = sr * M.cols + sc;
-          const float w = load1(D.w, M.pdtype, off);
-          const float u = -lr * (wd * w + s * (sx * x[e]));
-          store1(D.w, M.pdtype, off, w + u);
-          if (D.upd) D.upd[off] = u;
+        for (int e = 0; e < 4; ++e) {
+          if (sr < M.rows && sc + e < M.cols) {
+            const int64_t off = sr * M.cols + sc + e;
+            const float w = load1(D.w, M.pdtype, off);
+            const float u = -lr * (wd * w + s * (sx * x[k][e]));
+            store1(D.w, M.pdtype, off, w + u);
+            if (D.upd) D.upd[off] = u;
+          }
         }
       }
     }
