@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--cache", default=os.path.join(os.path.expanduser("~"), ".cache", "muon_mi355x",
                                                     "tune.txt"))
     ap.add_argument("--no-kernel-times", action="store_true")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the measured ceilings (dense bf16 MFMA loop, 1 GiB HBM copy)")
     return ap.parse_args()
 
 
@@ -363,6 +365,22 @@ def main():
         kt = plan.kernel_times(reset=False)
         plan.kernel_times(reset=True)
         plan.set_profiling(False)
+    # measured ceilings of this device, after the timed region: a dense bf16
+    # MFMA loop without memory traffic, and a 1 GiB device-to-device copy
+    ceil = None
+    if not args.no_ceilings:
+        mfma_tf, _ = MU.probe_mfma_bf16(iters=100000)              # about 17 ms
+        mfma_sus, _ = MU.probe_mfma_bf16(iters=1000000)            # about 170 ms
+        a = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+        b = torch.empty_like(a)
+        copy_gbs = MU.probe_hbm_copy(b, a, reps=10)
+        del a, b
+        ceil = {"mfma_bf16_tflops": round(mfma_tf, 1), "mfma_bf16_tflops_sustained": round(mfma_sus, 1),
+                "hbm_copy_gbs": round(copy_gbs, 1),
+                "how": "muon_probe_mfma_bf16 (2 blocks of 4 waves per CU, 4 independent "
+                       "32x32x16 bf16 MFMA chains per wave, no memory traffic; 1e5 and 1e6 "
+                       "rounds) and muon_probe_hbm_copy (1 GiB copy, read + written bytes, "
+                       "best of 8 launch variants)"}
     ns_flops = info["ns_flops_min"]
     bf16 = wl.dtype == "bf16"
     peak = PEAK_BF16_TFLOPS if bf16 else PEAK_FP32_TFLOPS
@@ -397,6 +415,8 @@ def main():
                     "launches_per_step": dom["launches"] / args.steps,
                     "share_of_step": round(dom["total_ms"] / args.steps / ms, 4),
                     "lanes": info["n_lanes"]}
+        if ceil and bf16:
+            roofline["frac_of_measured_mfma"] = round(ach / ceil["mfma_bf16_tflops"], 4)
     ew = {}
     for n, d in ew_kern.items():
         avg_ms = d["total_ms"] / d["launches"]
@@ -404,6 +424,8 @@ def main():
         ew[n] = {"GB/s": round(gbs, 1), "frac_of_hbm": round(gbs / PEAK_HBM_GBS, 4),
                  "avg_launch_us": round(avg_ms * 1e3, 2), "bytes_per_launch": d["bytes"] / d["launches"],
                  "traffic": traffic_for(n, wl.name, d["launches"] / args.steps)}
+        if ceil:
+            ew[n]["frac_of_measured_copy"] = round(gbs / ceil["hbm_copy_gbs"], 4)
     value = ns_flops / (ms * 1e-3) / 1e12
     out = {
         "metric": "Muon optimizer-step ms + NS TFLOP/s (% of MI355X bf16 MFMA peak)",
@@ -422,7 +444,7 @@ def main():
         "ns_kernel_ms_per_step_serial": round(ns_ms, 4) if kt else None,
         "ns_tflops_kernels_serial": round(ns_flops / (ns_ms * 1e-3) / 1e12, 2) if ns_ms else None,
         "step_frac_of_peak": round(value / peak, 4),
-        "elementwise": ew, "roofline": roofline,
+        "elementwise": ew, "roofline": roofline, "ceilings": ceil,
         "kernels": [{"stage": k["name"], "kernel": k["kernel"],
                      "launches_per_step": k["launches"] / args.steps,
                      "ms_per_step": round(k["total_ms"] / args.steps, 4)} for k in kt],

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define MUON_ABI_VERSION 8
+#define MUON_ABI_VERSION 9
 
 typedef enum muon_status {
   MUON_OK = 0,
@@ -322,6 +322,35 @@ int muon_adamw_step(muon_adamw_plan* plan, void* const* params, const void* cons
                     float* const* exp_avg, float* const* exp_avg_sq, double lr, double beta1,
                     double beta2, double eps, double wd, int64_t step, void* stream);
 int muon_adamw_plan_destroy(muon_adamw_plan* plan);
+
+/*
+ * Ceiling probes (measurement only; not part of a step).  They give the rates
+ * this part sustains when nothing else limits them, so a kernel's figure can be
+ * read against a measured ceiling beside the published peak (dense bf16 MFMA
+ * about 2.5 PFLOP/s, HBM3E 8 TB/s).  Both need a current HIP device, run on a
+ * stream of their own (default priority) and return when done: one warm-up
+ * launch, then the timed launch(es) between two events.
+ *
+ * muon_probe_mfma_bf16: 2 blocks of 4 waves per compute unit; every wave runs
+ * iters rounds of 4 independent v_mfma_f32_32x32x16_bf16 accumulations on
+ * register operands (no memory traffic; 32768 flop each).  tflops receives
+ * flop / time / 1e12, flops (nullable) the flop count of the timed launch.
+ * Allocates and frees a small output buffer (one float per thread).
+ * EINVAL: iters outside [1, 2^24], NULL tflops.  EHIP: device or launch error.
+ *
+ * muon_probe_hbm_copy: copies `bytes` from src to dst (caller-owned device
+ * buffers, 16-byte aligned, non-overlapping; bytes a non-zero multiple of 16)
+ * with 16-byte accesses, for each of eight launch variants (grid-stride over
+ * 4, 8 or 16 blocks of 256 threads per compute unit, or one block per
+ * contiguous 16 KiB run; plain or nontemporal loads and stores): one warm-up
+ * copy, then reps timed copies.  gbs receives the
+ * best variant's 2 * bytes * reps / time / 1e9 (read plus written bytes).  Use
+ * buffers well above the 256 MB last-level cache to measure HBM.
+ * EINVAL: NULL pointer, size or alignment, overlap, reps outside [1, 1000].
+ * EHIP: launch error.
+ */
+int muon_probe_mfma_bf16(int iters, double* tflops, double* flops);
+int muon_probe_hbm_copy(void* dst, const void* src, uint64_t bytes, int reps, double* gbs);
 
 /* MUON_ABI_VERSION of the library. */
 int muon_abi_version(void);

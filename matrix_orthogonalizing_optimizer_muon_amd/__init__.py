@@ -14,7 +14,8 @@ import ctypes
 from . import _lib as L
 from ._lib import MuonError  # noqa: F401
 
-__all__ = ["MuonPlan", "AdamWPlan", "MuonError", "library_path", "assign_owners"]
+__all__ = ["MuonPlan", "AdamWPlan", "MuonError", "library_path", "assign_owners",
+           "probe_mfma_bf16", "probe_hbm_copy"]
 
 
 def library_path():
@@ -257,6 +258,30 @@ def assign_owners(costs, n_owners, node_limit=0):
     L.check(L.lib().muon_assign_owners(arr, n, int(n_owners), int(node_limit), out,
                                        ctypes.byref(span), ctypes.byref(opt)))
     return [out[i] for i in range(n)], span.value, bool(opt.value)
+
+
+def probe_mfma_bf16(iters=20000):
+    """Measured dense bf16 MFMA rate of the current device (muon_probe_mfma_bf16).
+
+    Returns (TFLOP/s, flop count of the timed launch)."""
+    tf = ctypes.c_double()
+    fl = ctypes.c_double()
+    L.check(L.lib().muon_probe_mfma_bf16(int(iters), ctypes.byref(tf), ctypes.byref(fl)))
+    return tf.value, fl.value
+
+
+def probe_hbm_copy(dst, src, reps=10):
+    """Measured copy rate (read plus written GB/s) between two equal-sized,
+    contiguous device tensors (muon_probe_hbm_copy); dst receives src's bytes."""
+    if not (dst.is_cuda and src.is_cuda and dst.is_contiguous() and src.is_contiguous()):
+        raise ValueError("dst and src must be contiguous device tensors")
+    nb = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nb:
+        raise ValueError("dst and src must hold the same number of bytes")
+    gbs = ctypes.c_double()
+    L.check(L.lib().muon_probe_hbm_copy(ctypes.c_void_p(dst.data_ptr()), ctypes.c_void_p(src.data_ptr()),
+                                        nb, int(reps), ctypes.byref(gbs)))
+    return gbs.value
 
 
 class AdamWPlan:

@@ -96,6 +96,10 @@ PROTOTYPES = {
                                        ctypes.c_double, ctypes.c_double, ctypes.c_double,
                                        ctypes.c_double, ctypes.c_int64, ctypes.c_void_p]),
     "muon_adamw_plan_destroy": (ctypes.c_int, [ctypes.c_void_p]),
+    "muon_probe_mfma_bf16": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_double),
+                                            ctypes.POINTER(ctypes.c_double)]),
+    "muon_probe_hbm_copy": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64,
+                                           ctypes.c_int, ctypes.POINTER(ctypes.c_double)]),
     "muon_plan_matrix_cost": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int,
                                              ctypes.POINTER(ctypes.c_double)]),
     "muon_assign_owners": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double), ctypes.c_int, ctypes.c_int,

@@ -43,8 +43,8 @@ def build(verbose: bool = False) -> str:
     hipcc = _hipcc()
     with tempfile.TemporaryDirectory(prefix="muon_build_") as tmp:
         objs = []
-        for src, kind in (("kernels.hip", "hip"), ("abi.cpp", "hip"), ("plan.cpp", "host"),
-                          ("assign.cpp", "host")):
+        for src, kind in (("kernels.hip", "hip"), ("probe.hip", "hip"), ("abi.cpp", "hip"),
+                          ("plan.cpp", "host"), ("assign.cpp", "host")):
             obj = os.path.join(tmp, src + ".o")
             path = os.path.join(CSRC, src)
             if kind == "hip":

@@ -12,6 +12,7 @@
 
 #include "muon.h"
 #include "kernels.hpp"
+#include "probe.hpp"
 #include "assign.hpp"
 #include "plan.hpp"
 
@@ -905,6 +906,95 @@ int refine_set(const std::vector<int64_t>& rows, const std::vector<int64_t>& col
 extern "C" {
 
 int muon_abi_version(void) { return MUON_ABI_VERSION; }
+
+// ---------------------------------------------------------------- ceiling probes
+
+namespace {
+
+// Stream, events and device buffers of one probe run, released on every path.
+struct ProbeRun {
+  hipStream_t s = nullptr;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  float* out = nullptr;
+  ~ProbeRun() {
+    if (s) (void)hipStreamSynchronize(s);
+    if (out) (void)hipFree(out);
+    if (e0) (void)hipEventDestroy(e0);
+    if (e1) (void)hipEventDestroy(e1);
+    if (s) (void)hipStreamDestroy(s);
+  }
+  int init() {
+    HIP_TRY(hipStreamCreateWithFlags(&s, hipStreamNonBlocking));
+    HIP_TRY(hipEventCreate(&e0));
+    HIP_TRY(hipEventCreate(&e1));
+    return MUON_OK;
+  }
+  int elapsed(double* ms) {
+    HIP_TRY(hipEventSynchronize(e1));
+    float f = 0.f;
+    HIP_TRY(hipEventElapsedTime(&f, e0, e1));
+    *ms = f;
+    return MUON_OK;
+  }
+};
+
+int device_cus(int* cus) {
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  HIP_TRY(hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev));
+  if (*cus < 1) return fail(MUON_EHIP, "no compute units reported");
+  return MUON_OK;
+}
+
+}  // namespace
+
+int muon_probe_mfma_bf16(int iters, double* tflops, double* flops) {
+  if (iters < 1 || iters > (1 << 24) || !tflops) return fail(MUON_EINVAL, "iters out of [1, 2^24] or NULL tflops");
+  int cus = 0, rc;
+  if ((rc = device_cus(&cus))) return rc;
+  const int blocks = 2 * cus;   // 8 waves per CU, two per SIMD
+  ProbeRun r;
+  if ((rc = r.init())) return rc;
+  HIP_TRY(hipMalloc(&r.out, (size_t)blocks * 256 * sizeof(float)));
+  HIP_TRY(launch_probe_mfma(blocks, iters, r.out, r.s));   // warm-up: clocks settle
+  HIP_TRY(hipEventRecord(r.e0, r.s));
+  HIP_TRY(launch_probe_mfma(blocks, iters, r.out, r.s));
+  HIP_TRY(hipEventRecord(r.e1, r.s));
+  double ms = 0;
+  if ((rc = r.elapsed(&ms))) return rc;
+  const double fl = (double)blocks * 4 * (double)iters * kProbeChains * (2.0 * 32 * 32 * 16);
+  if (flops) *flops = fl;
+  *tflops = ms > 0 ? fl / (ms * 1e-3) / 1e12 : 0.0;
+  return MUON_OK;
+}
+
+int muon_probe_hbm_copy(void* dst, const void* src, uint64_t bytes, int reps, double* gbs) {
+  if (!dst || !src || !gbs) return fail(MUON_EINVAL, "NULL pointer");
+  if (bytes == 0 || bytes % 16 || !aligned16(dst) || !aligned16(src))
+    return fail(MUON_EINVAL, "bytes must be a non-zero multiple of 16 and both buffers 16-byte aligned");
+  if (reps < 1 || reps > 1000) return fail(MUON_EINVAL, "reps out of [1, 1000]");
+  const uintptr_t d = reinterpret_cast<uintptr_t>(dst), q = reinterpret_cast<uintptr_t>(src);
+  if (d < q + bytes && q < d + bytes) return fail(MUON_EINVAL, "source and destination overlap");
+  int cus = 0, rc;
+  if ((rc = device_cus(&cus))) return rc;
+  const int64_t n16 = (int64_t)(bytes / 16);
+  ProbeRun r;
+  if ((rc = r.init())) return rc;
+  double best = 0.0;
+  for (int nontemporal = 0; nontemporal < 2; ++nontemporal)
+    for (int per_cu : {4, 8, 16, 0}) {
+      const int blocks = per_cu * cus;   // 0: a block per 16 KiB run
+      HIP_TRY(launch_probe_copy(src, dst, n16, blocks, nontemporal != 0, r.s));   // warm-up
+      HIP_TRY(hipEventRecord(r.e0, r.s));
+      for (int k = 0; k < reps; ++k) HIP_TRY(launch_probe_copy(src, dst, n16, blocks, nontemporal != 0, r.s));
+      HIP_TRY(hipEventRecord(r.e1, r.s));
+      double ms = 0;
+      if ((rc = r.elapsed(&ms))) return rc;
+      if (ms > 0) best = std::max(best, 2.0 * (double)bytes * reps / (ms * 1e-3) / 1e9);
+    }
+  *gbs = best;
+  return MUON_OK;
+}
 
 const char* muon_last_error(void) { return g_err.c_str(); }
 

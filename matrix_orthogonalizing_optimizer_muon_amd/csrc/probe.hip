@@ -1,0 +1,116 @@
+// Ceiling probes (declared in probe.hpp): the rates this part sustains for
+// dense bf16 MFMA work and for streaming HBM copies when nothing else limits
+// them.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "probe.hpp"
+
+namespace muon {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+namespace {
+
+__global__ __launch_bounds__(256) void k_probe_mfma(int iters, float* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  bf16x8_t a, b;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    a[e] = (__bf16)(0.001f * (float)(lane + e));
+    b[e] = (__bf16)(0.002f * (float)(lane - e));
+  }
+  f32x16_t acc[kProbeChains];
+#pragma unroll
+  for (int c = 0; c < kProbeChains; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[c][r] = 0.f;
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int c = 0; c < kProbeChains; ++c)
+      acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
+  }
+  float sum = 0.f;
+#pragma unroll
+  for (int c = 0; c < kProbeChains; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sum += acc[c][r];
+  out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = sum;
+}
+
+template <bool NTMP>
+__device__ __forceinline__ u32x4_t probe_ld(const u32x4_t* p) {
+  if constexpr (NTMP) return __builtin_nontemporal_load(p);
+  return *p;
+}
+
+template <bool NTMP>
+__device__ __forceinline__ void probe_st(u32x4_t* p, u32x4_t v) {
+  if constexpr (NTMP) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
+
+// NTMP: nontemporal loads and stores (streaming cache policy)
+template <bool NTMP>
+__global__ __launch_bounds__(256) void k_probe_copy(const u32x4_t* __restrict__ src,
+                                                    u32x4_t* __restrict__ dst, int64_t n16) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const u32x4_t v0 = probe_ld<NTMP>(src + i), v1 = probe_ld<NTMP>(src + i + stride);
+    const u32x4_t v2 = probe_ld<NTMP>(src + i + 2 * stride), v3 = probe_ld<NTMP>(src + i + 3 * stride);
+    probe_st<NTMP>(dst + i, v0);
+    probe_st<NTMP>(dst + i + stride, v1);
+    probe_st<NTMP>(dst + i + 2 * stride, v2);
+    probe_st<NTMP>(dst + i + 3 * stride, v3);
+  }
+  for (; i < n16; i += stride) probe_st<NTMP>(dst + i, probe_ld<NTMP>(src + i));
+}
+
+// One contiguous 16 KiB run per block (256 threads x 4 words), as many blocks
+// as runs.
+template <bool NTMP>
+__global__ __launch_bounds__(256) void k_probe_copy_runs(const u32x4_t* __restrict__ src,
+                                                         u32x4_t* __restrict__ dst, int64_t n16) {
+  const int64_t base = (int64_t)blockIdx.x * 1024 + threadIdx.x;
+  u32x4_t v[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    if (base + u * 256 < n16) v[u] = probe_ld<NTMP>(src + base + u * 256);
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    if (base + u * 256 < n16) probe_st<NTMP>(dst + base + u * 256, v[u]);
+}
+
+}  // namespace
+
+hipError_t launch_probe_mfma(int blocks, int iters, float* out, hipStream_t s) {
+  hipLaunchKernelGGL(k_probe_mfma, dim3((unsigned)blocks), dim3(256), 0, s, iters, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_probe_copy(const void* src, void* dst, int64_t n16, int blocks, bool nontemporal,
+                             hipStream_t s) {
+  if (blocks <= 0) {
+    const int64_t runs = (n16 + 1023) / 1024;
+    if (runs > 0x7fffffff) return hipErrorInvalidValue;
+    if (nontemporal)
+      hipLaunchKernelGGL(k_probe_copy_runs<true>, dim3((unsigned)runs), dim3(256), 0, s,
+                         static_cast<const u32x4_t*>(src), static_cast<u32x4_t*>(dst), n16);
+    else
+      hipLaunchKernelGGL(k_probe_copy_runs<false>, dim3((unsigned)runs), dim3(256), 0, s,
+                         static_cast<const u32x4_t*>(src), static_cast<u32x4_t*>(dst), n16);
+    return hipGetLastError();
+  }
+  if (nontemporal)
+    hipLaunchKernelGGL(k_probe_copy<true>, dim3((unsigned)blocks), dim3(256), 0, s,
+                       static_cast<const u32x4_t*>(src), static_cast<u32x4_t*>(dst), n16);
+  else
+    hipLaunchKernelGGL(k_probe_copy<false>, dim3((unsigned)blocks), dim3(256), 0, s,
+                       static_cast<const u32x4_t*>(src), static_cast<u32x4_t*>(dst), n16);
+  return hipGetLastError();
+}
+
+}  // namespace muon

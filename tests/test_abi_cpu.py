@@ -28,7 +28,7 @@ def test_every_declared_function_is_exported_and_bound():
         assert hasattr(lib, n), n
         assert n in L.PROTOTYPES, f"{n} has no ctypes prototype"
     assert set(L.PROTOTYPES) == set(names)
-    assert lib.muon_abi_version() == 8
+    assert lib.muon_abi_version() == 9
 
 
 def test_struct_sizes_match_header_layout():
@@ -252,3 +252,19 @@ def test_adamw_entry_points_refuse_bad_arguments_without_a_device():
     arr = (ctypes.c_void_p * 1)(16)
     assert lib.muon_adamw_step(None, arr, arr, arr, arr, 1e-3, 0.9, 0.999, 1e-8, 0.0, 1, None) == L.MUON_EINVAL
     assert lib.muon_adamw_plan_destroy(None) == L.MUON_OK
+
+
+def test_probes_refuse_bad_arguments_without_a_device():
+    lib = L.lib()
+    tf, fl, gbs = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
+    assert lib.muon_probe_mfma_bf16(0, ctypes.byref(tf), ctypes.byref(fl)) == L.MUON_EINVAL
+    assert lib.muon_probe_mfma_bf16((1 << 24) + 1, ctypes.byref(tf), None) == L.MUON_EINVAL
+    assert lib.muon_probe_mfma_bf16(10, None, None) == L.MUON_EINVAL
+    a, b = ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 24)   # never dereferenced
+    assert lib.muon_probe_hbm_copy(None, b, 1024, 1, ctypes.byref(gbs)) == L.MUON_EINVAL
+    assert lib.muon_probe_hbm_copy(a, b, 1000, 1, ctypes.byref(gbs)) == L.MUON_EINVAL      # not 16 | bytes
+    assert lib.muon_probe_hbm_copy(a, b, 0, 1, ctypes.byref(gbs)) == L.MUON_EINVAL
+    assert lib.muon_probe_hbm_copy(ctypes.c_void_p((1 << 20) + 8), b, 1024, 1, ctypes.byref(gbs)) == L.MUON_EINVAL
+    assert lib.muon_probe_hbm_copy(a, ctypes.c_void_p((1 << 20) + 512), 1024, 1, ctypes.byref(gbs)) == L.MUON_EINVAL
+    assert lib.muon_probe_hbm_copy(a, b, 1024, 0, ctypes.byref(gbs)) == L.MUON_EINVAL
+    assert lib.muon_probe_hbm_copy(a, b, 1024, 1, None) == L.MUON_EINVAL

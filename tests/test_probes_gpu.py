@@ -1,0 +1,40 @@
+"""Ceiling probes through the C ABI: the dense bf16 MFMA loop and the HBM copy
+give rates inside what the part can physically reach (published dense bf16
+peak about 2.5 PFLOP/s, HBM3E 8 TB/s), and the copy probe copies."""
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+PEAK_BF16_TFLOPS = 2516.6   # 256 CUs x 2.4 GHz x 4096 dense bf16 flop per clock
+PEAK_HBM_GBS = 8000.0
+
+
+@pytest.fixture(scope="module")
+def M():
+    import matrix_orthogonalizing_optimizer_muon_amd as mod
+    return mod
+
+
+def test_mfma_probe_rate_is_physical(M):
+    tflops, flops = M.probe_mfma_bf16(iters=4000)
+    print(f"mfma probe: {tflops:.1f} TFLOP/s", flush=True)
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert flops == 2 * cus * 4 * 4000 * 4 * 32768
+    assert 0.2 * PEAK_BF16_TFLOPS < tflops <= 1.02 * PEAK_BF16_TFLOPS
+
+
+def test_hbm_copy_probe_copies_and_rate_is_physical(M):
+    import torch
+    n = (1 << 30) // 4 + 4   # 1 GiB + 16 bytes: the grid-stride tail runs too
+    src = torch.arange(n, dtype=torch.int32, device="cuda")
+    dst = torch.zeros(n, dtype=torch.int32, device="cuda")
+    gbs = M.probe_hbm_copy(dst, src, reps=3)
+    torch.cuda.synchronize()
+    print(f"copy probe: {gbs:.0f} GB/s", flush=True)
+    assert torch.equal(dst, src)
+    assert 0.1 * PEAK_HBM_GBS < gbs <= 1.05 * PEAK_HBM_GBS
+    with pytest.raises(ValueError):
+        M.probe_hbm_copy(dst[:-4], src)
+    with pytest.raises(M.MuonError):
+        M.probe_hbm_copy(dst[4:], dst[:-4])   # overlapping buffers
