@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--cache", default=os.path.join(os.path.expanduser("~"), ".cache", "muon_mi355x",
                                                     "tune.txt"))
     ap.add_argument("--no-kernel-times", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="run the steps on a side stream with graph replay (muon_plan_set_graph)")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the measured ceilings (dense bf16 MFMA loop, 1 GiB HBM copy)")
     return ap.parse_args()
@@ -312,6 +314,10 @@ def main():
         choices.setdefault(f"{min(r, c)}x{max(r, c)}", f"{ch['form']}/tile{ch['tile']}")
     P, G, B = make_inputs(wl, torch)
     h = wl.hyper
+    if args.graph:
+        # graph capture needs a stream other than the null stream
+        torch.cuda.set_stream(torch.cuda.Stream())
+        plan.set_graph(True)
     stream = torch.cuda.current_stream()
 
     def step():
@@ -451,7 +457,7 @@ def main():
         "plan": {"choices": choices, "groups": info["n_groups"], "chunks": info["n_chunks"], "gram": info["n_gram"],
                  "lanes": info["n_lanes"],
                  "workspace_gb": round(info["workspace_bytes"] / 1e9, 3),
-                 "create_s": round(plan_s, 3), "hash": info["plan_hash"]},
+                 "create_s": round(plan_s, 3), "hash": info["plan_hash"], "graph_replay": args.graph},
         "wall_s_timed": round(wall, 3),
         "cpu_baseline": None,
     }

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define MUON_ABI_VERSION 9
+#define MUON_ABI_VERSION 10
 
 typedef enum muon_status {
   MUON_OK = 0,
@@ -322,6 +322,26 @@ int muon_adamw_step(muon_adamw_plan* plan, void* const* params, const void* cons
                     float* const* exp_avg, float* const* exp_avg_sq, double lr, double beta1,
                     double beta2, double eps, double wd, int64_t step, void* stream);
 int muon_adamw_plan_destroy(muon_adamw_plan* plan);
+
+/*
+ * Graph replay of muon_step / muon_step_schedule (enable != 0), for callers
+ * whose step is bound by launch overhead (few or small matrices) and whose
+ * arguments repeat from step to step.  The first step with a given set of
+ * arguments (the params, grads and momenta pointers, the update capture
+ * buffers, lr, beta, wd, ns_steps and the coefficients) runs as usual; the
+ * next step with the same arguments is captured into a HIP graph (stream
+ * capture, thread-local mode) and launched; later steps with the same
+ * arguments launch that graph again.  Any other argument set starts over
+ * (eager, then a new capture); the tensors' contents may change freely.  With
+ * lr or a coefficient changing every step, nothing is ever replayed.  The
+ * graph holds kernel launches and the lanes' event dependencies only (no
+ * memory set or copy nodes); a changed pointer table is uploaded before the
+ * graph launches.  Needs a stream other than the null stream (EINVAL on
+ * muon_step otherwise); profiling steps always run eagerly.  enable = 0
+ * waits for the device and releases the graph.  EINVAL (NULL plan), ESTATE
+ * (host-only plan).
+ */
+int muon_plan_set_graph(muon_plan* plan, int enable);
 
 /*
  * Ceiling probes (measurement only; not part of a step).  They give the rates

@@ -219,6 +219,11 @@ class MuonPlan:
         return {"form": {1: "direct", 2: "gram"}[f.value], "tile": t.value, "group": g.value,
                 "chunk": c.value, "lane": ln.value}
 
+    def set_graph(self, enable=True):
+        """Graph replay of repeated steps (muon_plan_set_graph); steps must then
+        run on a stream other than the null stream."""
+        L.check(L.lib().muon_plan_set_graph(self._h, 1 if enable else 0))
+
     def set_profiling(self, enable=True):
         L.check(L.lib().muon_plan_set_profiling(self._h, 1 if enable else 0))
 

@@ -82,6 +82,7 @@ PROTOTYPES = {
                                                ctypes.POINTER(ctypes.c_int32),
                                                ctypes.POINTER(ctypes.c_int32)]),
     "muon_plan_set_profiling": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int]),
+    "muon_plan_set_graph": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int]),
     "muon_plan_get_kernel_times": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(KernelTime),
                                                   ctypes.c_int, ctypes.POINTER(ctypes.c_int),
                                                   ctypes.c_int]),

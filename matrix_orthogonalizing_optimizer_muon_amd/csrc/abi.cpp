@@ -145,6 +145,12 @@ struct muon_plan {
   std::vector<muon_launch_interval> intervals;  // folded launches, in launch order
   std::vector<hipEvent_t> ev_pool;
   std::map<std::pair<int, std::string>, Totals> tot;   // (stage, kernel) -> totals
+  // graph replay of muon_step (muon_plan_set_graph): the instantiated graph of
+  // the step whose arguments give graph_key; pending_key: the arguments of the
+  // last eager step, captured if the next step repeats them
+  bool graph_on = false;
+  hipGraphExec_t graph_exec = nullptr;
+  std::string graph_key, pending_key;
 };
 
 namespace {
@@ -171,9 +177,16 @@ int host_alloc(muon_plan* p, T** ptr, size_t bytes) {
   return MUON_OK;
 }
 
+void drop_graph(muon_plan* p) {
+  if (p->graph_exec) (void)hipGraphExecDestroy(p->graph_exec);
+  p->graph_exec = nullptr;
+  p->graph_key.clear();
+}
+
 void free_plan_memory(muon_plan* p) {
   if (!p) return;
   if (!p->host.opts.host_only) (void)hipDeviceSynchronize();
+  drop_graph(p);
   for (ChunkDev& c : p->chunks)
     if (c.upload_ev) (void)hipEventDestroy(c.upload_ev);
   for (ProfRec& r : p->recs) {
@@ -660,19 +673,69 @@ int step_impl(muon_plan* p, void* const* params, const void* const* grads, float
     if (!params[i] || !grads[i] || !momenta[i]) return fail(MUON_EINVAL, "NULL matrix pointer at index " + std::to_string(i));
   hipStream_t s = static_cast<hipStream_t>(stream);
   int rc;
-  for (ChunkDev& C : p->chunks) {
+  // every chunk's per-matrix pointers first (uploaded only when they changed;
+  // each chunk has its own table), then the kernels
+  for (ChunkDev& C : p->chunks)
     if ((rc = upload_dyn(p, C, params, grads, momenta, true, s))) return rc;
-    const int nm = (int)C.mats.size();
-    if ((rc = enqueue_chunk(p, C, T, sched, C.dyn, lr, wd, s, [&](int a, int b, hipStream_t ls, hipEvent_t ev) {
-           return enqueue_front(p, C, a, b, beta, 0, ls, ev);
-         }))) return rc;
-    // with T >= 1 the last NS product of every bf16-path matrix applied its update
-    if (T >= 1 && C.all_fused) continue;
-    if ((rc = run(p, kEwApply, "k_ew_apply", 0, T >= 1 ? C.bytes_apply_unfused : C.bytes_apply, s, [&] {
-           return launch_ew_apply(C.ew, C.dyn, C.prefix, nm, C.total_tiles, p->rscale, lr, wd,
-                                  T == 0 ? 1 : 0, T >= 1 ? 1 : 0, 0, p->grid_cap, s);
-         }))) return rc;
+  auto enqueue = [&]() -> int {
+    for (ChunkDev& C : p->chunks) {
+      const int nm = (int)C.mats.size();
+      int r;
+      if ((r = enqueue_chunk(p, C, T, sched, C.dyn, lr, wd, s, [&](int a, int b, hipStream_t ls, hipEvent_t ev) {
+             return enqueue_front(p, C, a, b, beta, 0, ls, ev);
+           }))) return r;
+      // with T >= 1 the last NS product of every bf16-path matrix applied its update
+      if (T >= 1 && C.all_fused) continue;
+      if ((r = run(p, kEwApply, "k_ew_apply", 0, T >= 1 ? C.bytes_apply_unfused : C.bytes_apply, s, [&] {
+             return launch_ew_apply(C.ew, C.dyn, C.prefix, nm, C.total_tiles, p->rscale, lr, wd,
+                                    T == 0 ? 1 : 0, T >= 1 ? 1 : 0, 0, p->grid_cap, s);
+           }))) return r;
+    }
+    return MUON_OK;
+  };
+  if (!p->graph_on || p->profiling) return enqueue();
+  if (!s) return fail(MUON_EINVAL, "graph replay needs a stream other than the null stream");
+  // the step's launches depend on the pointers (through the uploaded tables,
+  // which the key pins), the update capture buffers and the scalars
+  std::string key;
+  const size_t n_ptr = p->host.mats.size();
+  auto put = [&key](const void* v, size_t bytes) { key.append(static_cast<const char*>(v), bytes); };
+  put(params, n_ptr * sizeof(void*));
+  put(grads, n_ptr * sizeof(void*));
+  put(momenta, n_ptr * sizeof(void*));
+  if (!p->capture.empty()) put(p->capture.data(), p->capture.size() * sizeof(float*));
+  const float sc[3] = {lr, beta, wd};
+  put(sc, sizeof sc);
+  put(&T, sizeof T);
+  put(sched, 3 * (size_t)T * sizeof(float));
+  if (p->graph_exec && key == p->graph_key) {
+    HIP_TRY(hipGraphLaunch(p->graph_exec, s));
+    return MUON_OK;
   }
+  if (key != p->pending_key) {
+    // first step with these arguments: eager; the next one like it is captured
+    p->pending_key = key;
+    return enqueue();
+  }
+  if (p->graph_exec) HIP_TRY(hipDeviceSynchronize());   // the old graph may still run
+  drop_graph(p);
+  HIP_TRY(hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal));
+  rc = enqueue();
+  hipGraph_t g = nullptr;
+  const hipError_t e = hipStreamEndCapture(s, &g);
+  if (rc || e != hipSuccess || !g) {
+    if (g) (void)hipGraphDestroy(g);
+    if (rc) return rc;
+    return fail(MUON_EHIP, std::string("hipStreamEndCapture: ") + hipGetErrorString(e));
+  }
+  const hipError_t ie = hipGraphInstantiate(&p->graph_exec, g, nullptr, nullptr, 0);
+  (void)hipGraphDestroy(g);
+  if (ie != hipSuccess) {
+    p->graph_exec = nullptr;
+    return fail(MUON_EHIP, std::string("hipGraphInstantiate: ") + hipGetErrorString(ie));
+  }
+  p->graph_key = key;
+  HIP_TRY(hipGraphLaunch(p->graph_exec, s));
   return MUON_OK;
 }
 
@@ -1422,6 +1485,18 @@ int muon_assign_owners(const double* costs, int n, int n_owners, int64_t node_li
   for (int i = 0; i < n; ++i) owner[i] = r.owner[i];
   if (makespan) *makespan = r.makespan;
   if (optimal) *optimal = r.optimal ? 1 : 0;
+  return MUON_OK;
+}
+
+int muon_plan_set_graph(muon_plan* p, int enable) {
+  if (!p) return fail(MUON_EINVAL, "plan is NULL");
+  if (p->host.opts.host_only) return fail(MUON_ESTATE, "graph replay on a host-only plan");
+  if (!enable) {
+    if (p->graph_exec) HIP_TRY(hipDeviceSynchronize());
+    drop_graph(p);
+    p->pending_key.clear();
+  }
+  p->graph_on = enable != 0;
   return MUON_OK;
 }
 

@@ -28,7 +28,7 @@ def test_every_declared_function_is_exported_and_bound():
         assert hasattr(lib, n), n
         assert n in L.PROTOTYPES, f"{n} has no ctypes prototype"
     assert set(L.PROTOTYPES) == set(names)
-    assert lib.muon_abi_version() == 9
+    assert lib.muon_abi_version() == 10
 
 
 def test_struct_sizes_match_header_layout():
@@ -268,3 +268,11 @@ def test_probes_refuse_bad_arguments_without_a_device():
     assert lib.muon_probe_hbm_copy(a, ctypes.c_void_p((1 << 20) + 512), 1024, 1, ctypes.byref(gbs)) == L.MUON_EINVAL
     assert lib.muon_probe_hbm_copy(a, b, 1024, 0, ctypes.byref(gbs)) == L.MUON_EINVAL
     assert lib.muon_probe_hbm_copy(a, b, 1024, 1, None) == L.MUON_EINVAL
+
+
+def test_graph_toggle_refuses_null_and_host_only_plans():
+    lib = L.lib()
+    assert lib.muon_plan_set_graph(None, 1) == L.MUON_EINVAL
+    p = _host([(64, 128)])
+    with pytest.raises(M.MuonError):
+        p.set_graph(True)
