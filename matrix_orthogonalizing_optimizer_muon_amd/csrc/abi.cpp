@@ -49,6 +49,7 @@ struct SetDev {
   int nmats = 0;
   NsMat* mats = nullptr;
   Items nt_sym[kNumNtCfgs], nt_full[2 * kNumNtCfgs], old_sym, old_full;   // nt_full: full_list(cfg, qt)
+  int old_cfg = 0;   // fp32 kernel configuration of old_sym / old_full (kTileCfgs index)
   // algorithmic (symmetric-aware) flops of each launch: per NT configuration
   // (and read mode for B X) on the bf16 path, index 0 for the fp32 kernel
   double fl_gram[kNumNtCfgs] = {0}, fl_square[kNumNtCfgs] = {0}, fl_apply[2 * kNumNtCfgs] = {0};
@@ -302,6 +303,10 @@ int materialize(muon_plan* p) {
       D.form = S.form;
       D.lane = S.lane;
       D.nmats = (int)S.mats.size();
+      D.old_cfg = -1;
+      for (int c = 0; c < kNumTileCfgs; ++c)
+        if (kTileCfgs[c].bm == S.old_edge && kTileCfgs[c].bn == S.old_edge) D.old_cfg = c;
+      if (D.old_cfg < 0) return fail(MUON_EINVAL, "plan: no fp32 kernel for the set's tile edge");
       std::vector<NsMat> nsm(S.mats.size());
       for (size_t k = 0; k < S.mats.size(); ++k) {
         const MatPlan& M = H.mats[S.mats[k]];
@@ -495,19 +500,19 @@ int enqueue_ns(muon_plan* p, const SetDev& S, int T, const float* sched, const E
       // H = a I + b A + c A^2 (at k = 0 this is Q_1 itself)
       GemmParams gh = gp(S, S.old_sym, true, kShapeSquare, kA, kA, kA, hbuf, (k == 0 && last) ? kQH : -1,
                          -1, c, b, a, 0, rs);
-      if ((rc = run(p, kGramSquare, rs_name(false, kF32, kF32), fl_square, 0, s, [&] { return launch_gemm(0, kF32, kF32, gh, s); }))) return rc;
+      if ((rc = run(p, kGramSquare, rs_name(false, kF32, kF32), fl_square, 0, s, [&] { return launch_gemm(S.old_cfg, kF32, kF32, gh, s); }))) return rc;
       if (k > 0) {
         const int nxt = cur == kQX ? kQY : kQX;
         GemmParams gq = gp(S, S.old_sym, true, kShapeSquare, kH, cur, -1, nxt, last ? kQH : -1, -1, 1.f,
                            0.f, 0.f, 0, rs);
-        if ((rc = run(p, kGramSquare, rs_name(false, kF32, kF32), fl_square, 0, s, [&] { return launch_gemm(0, kF32, kF32, gq, s); }))) return rc;
+        if ((rc = run(p, kGramSquare, rs_name(false, kF32, kF32), fl_square, 0, s, [&] { return launch_gemm(S.old_cfg, kF32, kF32, gq, s); }))) return rc;
         cur = nxt;
       }
       if (!last) {
         GemmParams gt = gp(S, S.old_sym, true, kShapeSquare, hbuf, kA, -1, kT1, -1, -1, 1.f, 0.f, 0.f, 0, rs);
-        if ((rc = run(p, kGramSquare, rs_name(false, kF32, kF32), fl_square, 0, s, [&] { return launch_gemm(0, kF32, kF32, gt, s); }))) return rc;
+        if ((rc = run(p, kGramSquare, rs_name(false, kF32, kF32), fl_square, 0, s, [&] { return launch_gemm(S.old_cfg, kF32, kF32, gt, s); }))) return rc;
         GemmParams ga = gp(S, S.old_sym, true, kShapeSquare, kT1, hbuf, -1, kA, -1, -1, 1.f, 0.f, 0.f, 0, rs);
-        if ((rc = run(p, kGramSquare, rs_name(false, kF32, kF32), fl_square, 0, s, [&] { return launch_gemm(0, kF32, kF32, ga, s); }))) return rc;
+        if ((rc = run(p, kGramSquare, rs_name(false, kF32, kF32), fl_square, 0, s, [&] { return launch_gemm(S.old_cfg, kF32, kF32, ga, s); }))) return rc;
       }
     }
     for (int fi = 0; fi < 2 * kNumNtCfgs; ++fi) {
@@ -528,38 +533,38 @@ int enqueue_ns(muon_plan* p, const SetDev& S, int T, const float* sched, const E
       const int src = (k % 2 == 0) ? kX0 : kX1;
       const int dst = (k == T - 1) ? kXT : (src == kX0 ? kX1 : kX0);
       GemmParams g1 = gp(S, S.old_sym, true, kShapeGram, src, src, -1, kA, -1, -1, 1.f, 0.f, 0.f, k == 0 ? 2 : 0, rs);
-      if ((rc = run(p, kNsSyrk, rs_name(false, kF32, kF32), S.fl_gram[0], 0, s, [&] { return launch_gemm(0, kF32, kF32, g1, s); }))) return rc;
+      if ((rc = run(p, kNsSyrk, rs_name(false, kF32, kF32), S.fl_gram[0], 0, s, [&] { return launch_gemm(S.old_cfg, kF32, kF32, g1, s); }))) return rc;
       GemmParams g2 = gp(S, S.old_sym, true, kShapeSquare, kA, kA, kA, kB, -1, -1, c, b, 0.f, 0, rs);
-      if ((rc = run(p, kNsComb, rs_name(false, kF32, kF32), S.fl_square[0], 0, s, [&] { return launch_gemm(0, kF32, kF32, g2, s); }))) return rc;
+      if ((rc = run(p, kNsComb, rs_name(false, kF32, kF32), S.fl_square[0], 0, s, [&] { return launch_gemm(S.old_cfg, kF32, kF32, g2, s); }))) return rc;
       GemmParams g3 = gp(S, S.old_full, false, kShapeApply, kB, src, src, dst, -1, -1, 1.f, a, 0.f, k == 0 ? 1 : 0, rs);
-      if ((rc = run(p, kNsApply, rs_name(true, kF32, kF32), S.fl_apply[0], 0, s, [&] { return launch_gemm(0, kF32, kF32, g3, s); }))) return rc;
+      if ((rc = run(p, kNsApply, rs_name(true, kF32, kF32), S.fl_apply[0], 0, s, [&] { return launch_gemm(S.old_cfg, kF32, kF32, g3, s); }))) return rc;
     }
     return MUON_OK;
   }
   GemmParams g0 = gp(S, S.old_sym, true, kShapeGram, kX0, kX0, -1, kA, -1, -1, 1.f, 0.f, 0.f, 2, rs);
-  if ((rc = run(p, kGramXxt, rs_name(false, kF32, kF32), S.fl_gram[0], 0, s, [&] { return launch_gemm(0, kF32, kF32, g0, s); }))) return rc;
+  if ((rc = run(p, kGramXxt, rs_name(false, kF32, kF32), S.fl_gram[0], 0, s, [&] { return launch_gemm(S.old_cfg, kF32, kF32, g0, s); }))) return rc;
   int cur = kQX;
   for (int k = 0; k < T; ++k) {
     const float a = sched[3 * k], b = sched[3 * k + 1], c = sched[3 * k + 2];
     const bool last = k == T - 1;
     const int hbuf = (k == 0) ? kQX : kH;
     GemmParams gh = gp(S, S.old_sym, true, kShapeSquare, kA, kA, kA, hbuf, -1, -1, c, b, a, 0, rs);
-    if ((rc = run(p, kGramSquare, rs_name(false, kF32, kF32), S.fl_square[0], 0, s, [&] { return launch_gemm(0, kF32, kF32, gh, s); }))) return rc;
+    if ((rc = run(p, kGramSquare, rs_name(false, kF32, kF32), S.fl_square[0], 0, s, [&] { return launch_gemm(S.old_cfg, kF32, kF32, gh, s); }))) return rc;
     if (k > 0) {
       const int nxt = cur == kQX ? kQY : kQX;
       GemmParams gq = gp(S, S.old_sym, true, kShapeSquare, kH, cur, -1, nxt, -1, -1, 1.f, 0.f, 0.f, 0, rs);
-      if ((rc = run(p, kGramSquare, rs_name(false, kF32, kF32), S.fl_square[0], 0, s, [&] { return launch_gemm(0, kF32, kF32, gq, s); }))) return rc;
+      if ((rc = run(p, kGramSquare, rs_name(false, kF32, kF32), S.fl_square[0], 0, s, [&] { return launch_gemm(S.old_cfg, kF32, kF32, gq, s); }))) return rc;
       cur = nxt;
     }
     if (!last) {
       GemmParams gt = gp(S, S.old_sym, true, kShapeSquare, hbuf, kA, -1, kT1, -1, -1, 1.f, 0.f, 0.f, 0, rs);
-      if ((rc = run(p, kGramSquare, rs_name(false, kF32, kF32), S.fl_square[0], 0, s, [&] { return launch_gemm(0, kF32, kF32, gt, s); }))) return rc;
+      if ((rc = run(p, kGramSquare, rs_name(false, kF32, kF32), S.fl_square[0], 0, s, [&] { return launch_gemm(S.old_cfg, kF32, kF32, gt, s); }))) return rc;
       GemmParams ga = gp(S, S.old_sym, true, kShapeSquare, kT1, hbuf, -1, kA, -1, -1, 1.f, 0.f, 0.f, 0, rs);
-      if ((rc = run(p, kGramSquare, rs_name(false, kF32, kF32), S.fl_square[0], 0, s, [&] { return launch_gemm(0, kF32, kF32, ga, s); }))) return rc;
+      if ((rc = run(p, kGramSquare, rs_name(false, kF32, kF32), S.fl_square[0], 0, s, [&] { return launch_gemm(S.old_cfg, kF32, kF32, ga, s); }))) return rc;
     }
   }
   GemmParams gf = gp(S, S.old_full, false, kShapeApply, cur, kX0, -1, kXT, -1, -1, 1.f, 0.f, 0.f, 1, rs);
-  if ((rc = run(p, kGramFinal, rs_name(true, kF32, kF32), S.fl_apply[0], 0, s, [&] { return launch_gemm(0, kF32, kF32, gf, s); }))) return rc;
+  if ((rc = run(p, kGramFinal, rs_name(true, kF32, kF32), S.fl_apply[0], 0, s, [&] { return launch_gemm(S.old_cfg, kF32, kF32, gf, s); }))) return rc;
   return MUON_OK;
 }
 

@@ -579,13 +579,17 @@ __device__ __forceinline__ void gemm_lstore(const u32x4_t (&pr)[BM / 32], const 
         uint32_t w[G::QCH / 2];
 #pragma unroll
         for (int h = 0; h < G::QCH / 2; ++h) w[h] = half16(qr[2 * h], e) | (half16(qr[2 * h + 1], e) << 16);
-        if constexpr (G::QCH == 4) {
+        if constexpr (G::QCH == 2) {
+          *reinterpret_cast<uint32_t*>(dst) = w[0];
+        } else if constexpr (G::QCH == 4) {
           *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{w[0], w[1]};
         } else {
 #pragma unroll
           for (int h = 0; h < G::QCH / 8; ++h)
             *reinterpret_cast<u32x4_t*>(dst + 16 * h) = u32x4_t{w[4 * h], w[4 * h + 1], w[4 * h + 2], w[4 * h + 3]};
         }
+      } else if constexpr (G::QCH == 2) {
+        *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{word32(qr[0], e), word32(qr[1], e)};
       } else {
 #pragma unroll
         for (int h = 0; h < G::QCH / 4; ++h)
@@ -1212,6 +1216,8 @@ hipError_t launch_gemm(int tile_cfg, int in_dtype, int out_dtype, const GemmPara
                        hipStream_t s) {
   switch (tile_cfg) {
     case 0: return launch_gemm_cfg<128, 128>(in_dtype, out_dtype, p, s);
+    // 64 x 64 tiles: four times the blocks for products too small to fill the CUs
+    case 1: return launch_gemm_cfg<64, 64>(in_dtype, out_dtype, p, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -145,8 +145,8 @@ struct GemmParams {
 struct TileCfg {
   int32_t bm, bn;  // output tile (rows, cols); k-tile is always 128 bytes
 };
-constexpr int kNumTileCfgs = 1;
-constexpr TileCfg kTileCfgs[kNumTileCfgs] = {{128, 128}};
+constexpr int kNumTileCfgs = 2;
+constexpr TileCfg kTileCfgs[kNumTileCfgs] = {{128, 128}, {64, 64}};
 
 // Tile configurations of the bf16 NT kernel (mfma_nt.hpp): output tile BM x BN,
 // 64-element k-tiles, two LDS stages.

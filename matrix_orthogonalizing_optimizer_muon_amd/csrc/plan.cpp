@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdio>
 #include <fstream>
+#include <map>
 #include <sstream>
 
 namespace muon {
@@ -333,6 +334,12 @@ std::string build_plan(const std::vector<int64_t>& rows, const std::vector<int64
       M.lane = total > 0 ? std::min<int32_t>(lanes - 1, (int32_t)(mid * lanes / total)) : 0;
       C.n_lanes = std::max(C.n_lanes, M.lane + 1);
     }
+    // fp32-path sets: 128-tiles of their m x n products, which sets the tile edge
+    std::map<std::pair<int32_t, int32_t>, int64_t> fp32_tiles;   // (form, lane) -> tiles
+    for (int32_t i : C.mats) {
+      const MatPlan& M = P.mats[i];
+      if (!M.path) fp32_tiles[{M.form, M.lane}] += (M.m_pad / kOld) * (M.n_pad / kOld);
+    }
     for (int32_t i : C.mats) {
       const MatPlan& M = P.mats[i];
       LaunchSetPlan* S = nullptr;
@@ -344,6 +351,7 @@ std::string build_plan(const std::vector<int64_t>& rows, const std::vector<int64
         S->path = M.path;
         S->form = M.form;
         S->lane = M.lane;
+        if (!M.path && fp32_tiles[{M.form, M.lane}] < kCus) S->old_edge = kOld / 2;
       }
       const int32_t slot = (int32_t)S->mats.size();
       S->mats.push_back(i);
@@ -371,16 +379,18 @@ std::string build_plan(const std::vector<int64_t>& rows, const std::vector<int64
           S->flops_square_issued_fp32 += sym_tiles(M.m_pad, kOld) * old_tf * mp;
         }
       } else {
-        add_sym(S->old_sym, slot, M.m_pad, kOld);
-        add_full(S->old_full, slot, M.m_pad, M.n_pad, TileShape{kOld, kOld});
+        const int e = S->old_edge;
+        const double etf = 2.0 * e * e;
+        add_sym(S->old_sym, slot, M.m_pad, e);
+        add_full(S->old_full, slot, M.m_pad, M.n_pad, TileShape{e, e});
         S->fl_gram[0] += fg;
         S->fl_square[0] += fs;
         S->fl_apply[0] += fa;
-        const double st = sym_tiles(M.m_pad, kOld);
-        S->flops_gram_issued += st * old_tf * np;
-        S->flops_apply_issued += (mp / kOld) * (np / kOld) * old_tf * mp;
-        if (M.form == kFormDirect) S->flops_square_issued += st * old_tf * mp;
-        else S->flops_square_issued_fp32 += st * old_tf * mp;
+        const double st = sym_tiles(M.m_pad, e);
+        S->flops_gram_issued += st * etf * np;
+        S->flops_apply_issued += (mp / e) * (np / e) * etf * mp;
+        if (M.form == kFormDirect) S->flops_square_issued += st * etf * mp;
+        else S->flops_square_issued_fp32 += st * etf * mp;
       }
     }
     for (LaunchSetPlan& S : C.sets) {
@@ -431,7 +441,8 @@ std::string serialize_plan(const PlanHost& p) {
     o << "chunk " << c << " mats=" << C.mats.size() << " ws=" << C.ws_bytes << " ew_tiles=" << C.ew_tiles
       << " lanes=" << C.n_lanes << "\n";
     for (const LaunchSetPlan& S : C.sets) {
-      o << " set path=" << S.path << " form=" << S.form << " lane=" << S.lane << " mats=" << S.mats.size() << " items=";
+      o << " set path=" << S.path << " form=" << S.form << " lane=" << S.lane << " mats=" << S.mats.size()
+        << " edge=" << S.old_edge << " items=";
       for (int c = 0; c < kNtTiles; ++c)
         o << S.nt_sym[c].size() << "/" << S.nt_full[c].size() << "/" << S.nt_full[c + kNtTiles].size() << ",";
       o << S.old_sym.size() << "/" << S.old_full.size() << " order=";

@@ -116,8 +116,12 @@ struct LaunchSetPlan {
   std::vector<int32_t> mats;               // matrix indices, in slot order
   std::vector<ItemHost> nt_sym[kNtTiles];  // upper-triangle m x m tiles per NT configuration
   std::vector<ItemHost> nt_full[2 * kNtTiles]; // m x n tiles per (NT configuration, read mode)
-  std::vector<ItemHost> old_sym;           // upper-triangle 128-tiles (fp32 kernel)
-  std::vector<ItemHost> old_full;          // m x n 128-tiles (fp32 kernel)
+  std::vector<ItemHost> old_sym;           // upper-triangle tiles of the fp32 kernel (edge old_edge)
+  std::vector<ItemHost> old_full;          // m x n tiles of the fp32 kernel
+  // tile edge of the fp32 kernel in this set: 128, or 64 on the fp32 path when
+  // the set's m x n products have fewer 128-tiles than the GPU has CUs (the
+  // bf16 Gram iterates keep 128)
+  int32_t old_edge = 128;
   // symmetric-aware algorithmic flops of one product over the matrices of each
   // NT configuration's launch (bf16 path) or of the whole set (fp32 path: index 0)
   double fl_gram[kNtTiles] = {0}, fl_square[kNtTiles] = {0}, fl_apply[2 * kNtTiles] = {0};

@@ -270,3 +270,23 @@ def test_lanes_match_oracle(M):
     f32 = [i for i, d in enumerate(dts) if d == "f32"]
     run_and_compare(plan, Ws, Gs, Bs, WL.BF16, check=bf)
     run_and_compare(plan, Ws, Gs, Bs, WL.F32, check=f32)
+
+
+@pytest.mark.parametrize("shapes,edge", [
+    ([(256, 512), (100, 300), (300, 100)], 64),   # few 128-tiles: 64 x 64 fp32 tiles
+    ([(512, 512)] * 15 + [(512, 1000)], 128),     # 256 128-tiles of m x n: 128 x 128
+])
+def test_fp32_tile_edge_matches_oracle(M, shapes, edge):
+    """The fp32 kernel's tile edge follows the set's size (64 when its m x n
+    products have fewer 128-tiles than the GPU has CUs); both edges meet the
+    fp32 bar, direct form over T = 5 and 2, Gram form over T = 5."""
+    from gpu_util import make_state, run_and_compare
+    Ws, Gs, Bs = make_state(shapes, WL.F32, seed=120 + edge, buf_scale=0.01)
+    plan = _plan(M, shapes, "f32", form="direct")
+    assert f"edge={edge} ".encode() in plan.serialize()
+    check = [0, 1, 2, len(shapes) - 1]
+    for T in (5, 2):
+        run_and_compare(plan, Ws, Gs, Bs, WL.F32, ns_steps=T, check=check)
+    gram = _plan(M, shapes, "f32", form="gram")
+    assert f"edge={edge} ".encode() in gram.serialize()
+    run_and_compare(gram, Ws, Gs, Bs, WL.F32, ns_steps=5, check=check)
