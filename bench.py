@@ -34,7 +34,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--tune", default="once", choices=["off", "once", "force"])
     ap.add_argument("--form", default="auto", choices=["auto", "direct", "gram"])
-    ap.add_argument("--tile", type=int, default=None, help="force a tile plan (0..7)")
+    ap.add_argument("--tile", type=int, default=None, help="force a tile plan (0..9)")
     ap.add_argument("--lanes", type=int, default=None, help="force the NS lane count (1..4)")
     ap.add_argument("--adamw", action="store_true",
                     help="time the fused AdamW step over the non-matrix parameters of the "

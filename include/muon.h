@@ -89,12 +89,14 @@ typedef struct muon_plan_opts {
   int32_t precision;            /* muon_precision, default AUTO */
   int32_t form;                 /* muon_form, default AUTO */
   int32_t tile;                 /* tile plan of the bf16 NS kernels, -1 (default): chosen per
-                                   shape; 0..7 force one plan for every bf16 matrix (the
+                                   shape; 0..9 force one plan for every bf16 matrix (the
                                    symmetric and the m x n products' output tiles:
                                    0: 128/128x128, 1: 128/256x256, 2: 256/256x256,
                                    3: 128/256x128, 4: 128/128x256; 5, 6, 7: plans 0, 1, 2
                                    with the m x n product reading X k-major, so no
-                                   transposed copy of X is kept).  Ignored on the fp32 path */
+                                   transposed copy of X is kept; 8: 64/256x256 and
+                                   9: 64/128x128, both k-major).  Ignored on the fp32
+                                   path */
   int32_t tune;                 /* muon_tune, default ONCE (OFF when no cache path is known) */
   int32_t host_only;            /* 1: plan on the host only - no device, no workspace, no
                                    timing; muon_step refuses such a plan (planner tests) */

@@ -60,7 +60,8 @@ static_assert(kNumNtCfgs == kNtTiles && sizeof(kNtTileShapes) / sizeof(kNtTileSh
 static_assert(kNtCfgs[0].bm == kNtTileShapes[0].bm && kNtCfgs[0].bn == kNtTileShapes[0].bn &&
               kNtCfgs[1].bm == kNtTileShapes[1].bm && kNtCfgs[1].bn == kNtTileShapes[1].bn &&
               kNtCfgs[2].bm == kNtTileShapes[2].bm && kNtCfgs[2].bn == kNtTileShapes[2].bn &&
-              kNtCfgs[3].bm == kNtTileShapes[3].bm && kNtCfgs[3].bn == kNtTileShapes[3].bn,
+              kNtCfgs[3].bm == kNtTileShapes[3].bm && kNtCfgs[3].bn == kNtTileShapes[3].bn &&
+              kNtCfgs[4].bm == kNtTileShapes[4].bm && kNtCfgs[4].bn == kNtTileShapes[4].bn,
               "planner and kernel tile tables agree");
 static_assert((int)kPlanBufs == (int)kNumBufs && (int)bX0T == (int)kX0T && (int)bX1T == (int)kX1T &&
               (int)bQH == (int)kQH, "buffer ids agree");
@@ -97,9 +98,11 @@ struct ChunkDev {
 const char* nt_name(int cfg, int odt, int qt = 0) {
   static const char* names[2][kNumNtCfgs][2] = {
       {{"k_nt<128,128,f32>", "k_nt<128,128,bf16>"}, {"k_nt<256,256,f32>", "k_nt<256,256,bf16>"},
-       {"k_nt<256,128,f32>", "k_nt<256,128,bf16>"}, {"k_nt<128,256,f32>", "k_nt<128,256,bf16>"}},
+       {"k_nt<256,128,f32>", "k_nt<256,128,bf16>"}, {"k_nt<128,256,f32>", "k_nt<128,256,bf16>"},
+       {"k_nt<64,64,f32>", "k_nt<64,64,bf16>"}},
       {{"k_nt<128,128,f32,qt>", "k_nt<128,128,bf16,qt>"}, {"k_nt<256,256,f32,qt>", "k_nt<256,256,bf16,qt>"},
-       {"k_nt<256,128,f32,qt>", "k_nt<256,128,bf16,qt>"}, {"k_nt<128,256,f32,qt>", "k_nt<128,256,bf16,qt>"}}};
+       {"k_nt<256,128,f32,qt>", "k_nt<256,128,bf16,qt>"}, {"k_nt<128,256,f32,qt>", "k_nt<128,256,bf16,qt>"},
+       {"k_nt<64,64,f32,qt>", "k_nt<64,64,bf16,qt>"}}};
   return names[qt ? 1 : 0][cfg][odt == kBF16 ? 1 : 0];
 }
 const char* rs_name(bool nn, int idt, int odt) {

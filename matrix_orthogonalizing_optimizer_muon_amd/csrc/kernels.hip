@@ -765,7 +765,9 @@ __device__ __forceinline__ void st_bf16x4(void* base, int64_t off, const float* 
 template <int BM, int BN, int WGM, int WGN>
 struct NtPipe {
   static constexpr int BK = 64, S = 2;
-  static constexpr int LDS_CAP = (BM == 128 && BN == 128) ? 80 * 1024 : 160 * 1024;
+  static constexpr int LDS_CAP = (BM == 64 && BN == 64)     ? 32 * 1024
+                                 : (BM == 128 && BN == 128) ? 80 * 1024
+                                                            : 160 * 1024;
 };
 
 // Rows of the output tile staged in LDS at a time: the largest power of two
@@ -1163,8 +1165,10 @@ template <int BM, int BN, int WGM, int WGN>
 hipError_t launch_nt_cfg(int out_dt, const GemmParams& p, hipStream_t s) {
   if (p.qt) {
     if (p.shape != kShapeApplyT) return hipErrorInvalidValue;
-    if (out_dt == kBF16) return launch_nt_t<BM, BN, WGM, WGN, uint16_t, true>(p, s);
-    if (out_dt == kF32) return launch_nt_t<BM, BN, WGM, WGN, float, true>(p, s);
+    if constexpr (BN >= 128) {   // k-major Q tiles need rows of >= 256 bytes
+      if (out_dt == kBF16) return launch_nt_t<BM, BN, WGM, WGN, uint16_t, true>(p, s);
+      if (out_dt == kF32) return launch_nt_t<BM, BN, WGM, WGN, float, true>(p, s);
+    }
     return hipErrorInvalidValue;
   }
   if (out_dt == kBF16) return launch_nt_t<BM, BN, WGM, WGN, uint16_t, false>(p, s);
@@ -1231,6 +1235,9 @@ hipError_t launch_gemm_nt(int nt_cfg, int out_dtype, const GemmParams& p, hipStr
     case kNt256: return launch_nt_cfg<256, 256, 2, 4>(out_dtype, p, s);
     case kNt256x128: return launch_nt_cfg<256, 128, 2, 2>(out_dtype, p, s);
     case kNt128x256: return launch_nt_cfg<128, 256, 2, 2>(out_dtype, p, s);
+    // 64 x 64 (4 waves of 32 x 32, 32 KiB of LDS): four times the blocks of
+    // 128 x 128 for m x m products too small to fill the CUs
+    case kNt64: return launch_nt_cfg<64, 64, 2, 2>(out_dtype, p, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -150,8 +150,8 @@ constexpr TileCfg kTileCfgs[kNumTileCfgs] = {{128, 128}, {64, 64}};
 
 // Tile configurations of the bf16 NT kernel (mfma_nt.hpp): output tile BM x BN,
 // 64-element k-tiles, two LDS stages.
-enum NtCfg : int32_t { kNt128 = 0, kNt256 = 1, kNt256x128 = 2, kNt128x256 = 3, kNumNtCfgs = 4 };
-constexpr TileCfg kNtCfgs[kNumNtCfgs] = {{128, 128}, {256, 256}, {256, 128}, {128, 256}};
+enum NtCfg : int32_t { kNt128 = 0, kNt256 = 1, kNt256x128 = 2, kNt128x256 = 3, kNt64 = 4, kNumNtCfgs = 5 };
+constexpr TileCfg kNtCfgs[kNumNtCfgs] = {{128, 128}, {256, 256}, {256, 128}, {128, 256}, {64, 64}};
 
 // Launchers (kernels.hip).  All return hipError_t of the launch.
 // Tiles [tile_begin, tile_end) of the chunk (mats, tile_prefix: the whole chunk).

@@ -21,8 +21,10 @@ constexpr int kCus = 256;
 constexpr double kLaunchUs = 4.0; // per-launch cost used by the model
 
 // Tile plans: (sym config, apply config, k-major reads of X in B X).
-constexpr TilePlan kTilePlans[8] = {{0, 0, 0}, {0, 1, 0}, {1, 1, 0}, {0, 2, 0}, {0, 3, 0},
-                                    {0, 0, 1}, {0, 1, 1}, {1, 1, 1}};
+// Plans 8 and 9 are plans 6 and 5 with 64 x 64 tiles (config 4) for the
+// symmetric products.
+constexpr TilePlan kTilePlans[10] = {{0, 0, 0}, {0, 1, 0}, {1, 1, 0}, {0, 2, 0}, {0, 3, 0},
+                                     {0, 0, 1}, {0, 1, 1}, {1, 1, 1}, {4, 1, 1}, {4, 0, 1}};
 
 uint64_t align_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
 int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
@@ -104,10 +106,11 @@ double nt_rate(int cfg) {
   switch (cfg) {
     case 1: return 4.6e12;
     case 2: case 3: return 3.4e12;
+    case 4: return 0.8e12;
     default: return 1.8e12;
   }
 }
-int nt_blocks_per_cu(int cfg) { return cfg == 0 ? 2 : 1; }
+int nt_blocks_per_cu(int cfg) { return cfg == 0 ? 2 : cfg == 4 ? 4 : 1; }
 constexpr double kOldRateBf16 = 0.9e12;   // fp32-kernel blocks, bf16 operands
 constexpr double kOldRateF32 = 0.25e12;   // fp32-kernel blocks, fp32 operands (per block, 2 per CU)
 
@@ -121,7 +124,7 @@ double launch_us(double tiles, double flops_per_tile, double rate, int per_cu) {
 }  // namespace
 
 TileShape nt_cfg_shape(int cfg) {
-  if (cfg < 0 || cfg >= 4) cfg = 0;
+  if (cfg < 0 || cfg >= kNtTiles) cfg = 0;
   return kNtTileShapes[cfg];
 }
 
@@ -180,7 +183,7 @@ std::vector<std::pair<int32_t, int32_t>> candidates(const ShapeKey& k, int32_t f
     for (int t = 0; t < num_tile_plans(); ++t)
       if (want(t)) out.push_back({kFormDirect, t});
   if (gram)
-    for (int t : {0, 1, 2, 5, 6, 7})
+    for (int t : {0, 1, 2, 5, 6, 7, 8, 9})
       if (want(t)) out.push_back({kFormGram, t});
   return out;
 }
@@ -481,7 +484,7 @@ TuneCache read_cache(const std::string& path, const std::string& device_tag) {
   while (std::getline(f, line)) {
     std::istringstream is(line);
     std::string magic, tag;
-    if (!(is >> magic >> tag) || magic != "muon-tune-v3" || tag != device_tag) continue;
+    if (!(is >> magic >> tag) || magic != "muon-tune-v4" || tag != device_tag) continue;
     ShapeKey k{-1, -1, -1};
     ShapeChoice c;
     c.form = -1;
@@ -534,7 +537,7 @@ bool write_cache(const std::string& path, const std::string& device_tag, const T
     while (std::getline(f, line)) {
       std::istringstream is(line);
       std::string magic, tag;
-      if ((is >> magic >> tag) && magic == "muon-tune-v3" && tag == device_tag) continue;
+      if ((is >> magic >> tag) && magic == "muon-tune-v4" && tag == device_tag) continue;
       if (!line.empty()) keep.push_back(line);
     }
   }
@@ -545,13 +548,13 @@ bool write_cache(const std::string& path, const std::string& device_tag, const T
     for (const std::string& l : keep) f << l << "\n";
     char buf[256];
     for (const auto& kv : entries.shapes) {
-      snprintf(buf, sizeof buf, "muon-tune-v3 %s m=%lld n=%lld path=%d form=%d tile=%d us=%.3f\n",
+      snprintf(buf, sizeof buf, "muon-tune-v4 %s m=%lld n=%lld path=%d form=%d tile=%d us=%.3f\n",
                device_tag.c_str(), (long long)kv.first.m, (long long)kv.first.n, kv.first.path,
                kv.second.form, kv.second.tile, kv.second.us);
       f << buf;
     }
     for (const auto& kv : entries.sets) {
-      snprintf(buf, sizeof buf, "muon-tune-v3 %s set=%s tile=%d lanes=%d us=%.3f\n",
+      snprintf(buf, sizeof buf, "muon-tune-v4 %s set=%s tile=%d lanes=%d us=%.3f\n",
                device_tag.c_str(), kv.first.c_str(), kv.second.tile, kv.second.lanes, kv.second.us);
       f << buf;
     }

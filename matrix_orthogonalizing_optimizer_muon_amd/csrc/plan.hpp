@@ -31,8 +31,8 @@ enum PlanBuf : int32_t {
 // Output tiles of the bf16 NT kernel configurations (kernels.hpp NtCfg; abi.cpp
 // checks at compile time that the two tables agree).
 struct TileShape { int32_t bm, bn; };
-constexpr int kNtTiles = 4;
-constexpr TileShape kNtTileShapes[kNtTiles] = {{128, 128}, {256, 256}, {256, 128}, {128, 256}};
+constexpr int kNtTiles = 5;
+constexpr TileShape kNtTileShapes[kNtTiles] = {{128, 128}, {256, 256}, {256, 128}, {128, 256}, {64, 64}};
 TileShape nt_cfg_shape(int cfg);
 
 // A tile plan: the NT kernel configuration of the symmetric m x m products

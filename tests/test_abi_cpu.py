@@ -140,41 +140,41 @@ def _set_key(entries, forced_lanes=0):
 
 def test_tune_cache_set_line_gives_every_direct_shape_one_tile_plan(tmp_path):
     shapes = [(3072, 1024), (1024, 3072), (1024, 1024), (1024, 1024), (4096, 1024)]
-    shape_lines = ("muon-tune-v3 host m=1024 n=1024 path=1 form=1 tile=0 us=1\n"
-                   "muon-tune-v3 host m=1024 n=3072 path=1 form=1 tile=0 us=1\n"
-                   "muon-tune-v3 host m=1024 n=4096 path=1 form=1 tile=1 us=1\n")
+    shape_lines = ("muon-tune-v4 host m=1024 n=1024 path=1 form=1 tile=0 us=1\n"
+                   "muon-tune-v4 host m=1024 n=3072 path=1 form=1 tile=0 us=1\n"
+                   "muon-tune-v4 host m=1024 n=4096 path=1 form=1 tile=1 us=1\n")
     key = _set_key([(1, 1024, 1024, 2, 1, 0), (1, 1024, 3072, 2, 1, 0), (1, 1024, 4096, 1, 1, 1)])
     other = _set_key([(1, 1024, 1024, 2, 1, 0)])
     path = tmp_path / "tune.txt"
     path.write_text(shape_lines)
     per_shape = _host(shapes, cache_path=str(path))
     assert [per_shape.matrix_choice(i)["tile"] for i in range(5)] == [0, 0, 0, 0, 1]
-    path.write_text(shape_lines + f"muon-tune-v3 host set={key} tile=2 us=5\n")
+    path.write_text(shape_lines + f"muon-tune-v4 host set={key} tile=2 us=5\n")
     p = _host(shapes, cache_path=str(path))
     assert [p.matrix_choice(i)["tile"] for i in range(5)] == [2] * 5
     assert p.info()["n_lanes"] == 1
-    path.write_text(shape_lines + f"muon-tune-v3 host set={key} tile=-1 lanes=2 us=5\n")
+    path.write_text(shape_lines + f"muon-tune-v4 host set={key} tile=-1 lanes=2 us=5\n")
     q = _host(shapes, cache_path=str(path))
     assert [q.matrix_choice(i)["tile"] for i in range(5)] == [0, 0, 0, 0, 1]
     assert q.info()["n_lanes"] == 2 and {q.matrix_choice(i)["lane"] for i in range(5)} == {0, 1}
     # -1 keeps the per-shape choices; other sets, bad keys, tiles and lane counts are ignored
     for line in (f"set={key} tile=-1 us=5", f"set={other} tile=2 us=5", f"set={key[:-1]} tile=2 us=5",
-                 f"set={key.upper()} tile=2 us=5", f"set={key} tile=9 us=5", f"set={key} us=5",
+                 f"set={key.upper()} tile=2 us=5", f"set={key} tile=10 us=5", f"set={key} us=5",
                  f"set={key} tile=2 lanes=5 us=5", f"set={key} tile=2 lanes=0 us=5"):
-        path.write_text(shape_lines + f"muon-tune-v3 host {line}\n")
+        path.write_text(shape_lines + f"muon-tune-v4 host {line}\n")
         q = _host(shapes, cache_path=str(path))
         assert q.serialize() == per_shape.serialize(), line
     # a forced tile plan takes only the lane count of its own set line
-    path.write_text(shape_lines + f"muon-tune-v3 host set={key} tile=2 lanes=2 us=5\n")
+    path.write_text(shape_lines + f"muon-tune-v4 host set={key} tile=2 lanes=2 us=5\n")
     f = _host(shapes, cache_path=str(path), tile=1)
     assert [f.matrix_choice(i)["tile"] for i in range(5)] == [1] * 5 and f.info()["n_lanes"] == 1
     fkey = _set_key([(1, 1024, 1024, 2, 1, 1), (1, 1024, 3072, 2, 1, 1), (1, 1024, 4096, 1, 1, 1)])
-    path.write_text(shape_lines + f"muon-tune-v3 host set={fkey} tile=2 lanes=4 us=5\n")
+    path.write_text(shape_lines + f"muon-tune-v4 host set={fkey} tile=2 lanes=4 us=5\n")
     f = _host(shapes, cache_path=str(path), tile=1)
     assert [f.matrix_choice(i)["tile"] for i in range(5)] == [1] * 5 and f.info()["n_lanes"] == 4
     # forced lanes: the set line (keyed with the forced count) gives only the tile plan
     lkey = _set_key([(1, 1024, 1024, 2, 1, 0), (1, 1024, 3072, 2, 1, 0), (1, 1024, 4096, 1, 1, 1)], 2)
-    path.write_text(shape_lines + f"muon-tune-v3 host set={lkey} tile=2 lanes=4 us=5\n")
+    path.write_text(shape_lines + f"muon-tune-v4 host set={lkey} tile=2 lanes=4 us=5\n")
     g = _host(shapes, cache_path=str(path), lanes=2)
     assert [g.matrix_choice(i)["tile"] for i in range(5)] == [2] * 5 and g.info()["n_lanes"] == 2
 
@@ -206,11 +206,11 @@ def test_tune_cache_is_read_and_bad_lines_ignored(tmp_path):
     path = tmp_path / "tune.txt"
     path.write_text(
         "garbage line\n"
-        "muon-tune-v3 host m=512 n=16384 path=1 form=2 tile=1 us=400\n"
-        "muon-tune-v3 host m=1024 n=1024 path=1 form=9 tile=0 us=1\n"
-        "muon-tune-v3 host m=2048 n=2048 path=1 form=1 tile=8 us=1\n"
+        "muon-tune-v4 host m=512 n=16384 path=1 form=2 tile=1 us=400\n"
+        "muon-tune-v4 host m=1024 n=1024 path=1 form=9 tile=0 us=1\n"
+        "muon-tune-v4 host m=2048 n=2048 path=1 form=1 tile=10 us=1\n"
         "muon-tune-v1 host m=256 n=256 path=1 form=2 tile=0 us_direct=1 us_gram=1\n"
-        "muon-tune-v3 otherdev m=64 n=64 path=1 form=2 tile=0 us=1\n")
+        "muon-tune-v4 otherdev m=64 n=64 path=1 form=2 tile=0 us=1\n")
     shapes = [(512, 16384), (1024, 1024), (64, 64), (2048, 2048), (256, 256)]
     p = _host(shapes, cache_path=str(path))
     model = _host(shapes, tune="off")

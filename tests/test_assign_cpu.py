@@ -85,8 +85,10 @@ def test_large_matrix_sets_are_balanced():
         _check_valid(costs, owner, 8, span)
         lower = max(max(costs), sum(costs) / 8)
         assert span >= lower * (1 - 1e-12)
-        # many similar items: within 5% of the lower bound (or the largest item)
-        assert span <= 1.05 * lower, (cfg, span, lower)
+        # many similar items: within 5% of the lower bound, unless the schedule is
+        # proven optimal (the 16 transformer-block matrices come in 3-4 costs over
+        # 8 owners: two per owner, and the bound itself may be out of reach)
+        assert span <= 1.05 * lower or optimal, (cfg, span, lower)
         # deterministic
         assert M.assign_owners(costs, 8) == (owner, span, optimal)
 

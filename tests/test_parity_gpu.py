@@ -185,7 +185,7 @@ def test_plan_errors_and_host_checks(M):
         plan.step([good[0].clone()], good, mom, ns_steps=-1)
 
 
-@pytest.mark.parametrize("tile", [0, 1, 2, 3, 4, 5, 6, 7])
+@pytest.mark.parametrize("tile", [0, 1, 2, 3, 4, 5, 6, 7, 8, 9])
 def test_bf16_direct_every_tile_plan(M, tile):
     """Each NT tile plan (symmetric / m x n output tiles), ragged and tall shapes
     in one batched plan, T = 5, 1 and 2."""
@@ -198,7 +198,7 @@ def test_bf16_direct_every_tile_plan(M, tile):
         run_and_compare(plan, Ws, Gs, Bs, WL.BF16, ns_steps=T)
 
 
-@pytest.mark.parametrize("tile", [0, 1, 2, 5, 6, 7])
+@pytest.mark.parametrize("tile", [0, 1, 2, 5, 6, 7, 8, 9])
 def test_bf16_gram_every_tile_plan(M, tile):
     from gpu_util import make_state, run_and_compare
     shapes = [(200, 1500), (1500, 200), (256, 4096)]
