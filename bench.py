@@ -315,7 +315,9 @@ def main():
     P, G, B = make_inputs(wl, torch)
     h = wl.hyper
     if args.graph:
-        # graph capture needs a stream other than the null stream
+        # graph capture needs a stream other than the null stream; the inputs
+        # were made on the default stream, so let that work finish first
+        torch.cuda.synchronize()
         torch.cuda.set_stream(torch.cuda.Stream())
         plan.set_graph(True)
     stream = torch.cuda.current_stream()
