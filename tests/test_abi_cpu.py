@@ -276,3 +276,48 @@ def test_graph_toggle_refuses_null_and_host_only_plans():
     p = _host([(64, 128)])
     with pytest.raises(M.MuonError):
         p.set_graph(True)
+
+
+_PLAN_DIGESTS = r"""
+import hashlib, sys
+import matrix_orthogonalizing_optimizer_muon_amd as M
+import workloads as WL
+cache = sys.argv[1]
+for cfg in (1, 2, 3, 4, 5):
+    wl = WL.workload(cfg)
+    p = M.MuonPlan(wl.shapes, wl.dtype, host_only=True, cache_path=cache)
+    print(cfg, hashlib.sha256(p.serialize()).hexdigest(), flush=True)
+"""
+
+
+def test_plans_are_byte_identical_across_runs_and_processes(tmp_path):
+    """The plan is a function of (shapes, options, cache): 100 creations in this
+    process and two fresh processes reading the same cache file give the same
+    bytes for every workload's matrix set."""
+    import hashlib
+    import subprocess
+    import sys
+    cache = tmp_path / "tune.txt"
+    cache.write_text("muon-tune-v4 host m=1024 n=4096 path=1 form=1 tile=6 us=1\n"
+                     "muon-tune-v4 host m=512 n=16384 path=1 form=2 tile=8 us=1\n")
+    here = {}
+    for cfg in (1, 2, 3, 4, 5):
+        wl = WL.workload(cfg)
+        here[cfg] = hashlib.sha256(
+            M.MuonPlan(wl.shapes, wl.dtype, host_only=True, cache_path=str(cache)).serialize()).hexdigest()
+    wl2 = WL.workload(2)
+    for _ in range(100):
+        p = M.MuonPlan(wl2.shapes, wl2.dtype, host_only=True, cache_path=str(cache))
+        assert hashlib.sha256(p.serialize()).hexdigest() == here[2]
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, PYTHONPATH=root + os.pathsep + os.environ.get("PYTHONPATH", ""))
+    for _ in range(2):
+        out = subprocess.run([sys.executable, "-c", _PLAN_DIGESTS, str(cache)], capture_output=True,
+                             text=True, env=env, cwd=root, timeout=300)
+        assert out.returncode == 0, out.stderr
+        got = {int(a): b for a, b in (line.split() for line in out.stdout.split("\n") if line.strip())}
+        assert got == here
+    # the cached choices were taken
+    p = M.MuonPlan(wl2.shapes, wl2.dtype, host_only=True, cache_path=str(cache))
+    assert {p.matrix_choice(i)["tile"] for i in range(len(wl2.shapes))
+            if max(wl2.shapes[i]) == 4096 and min(wl2.shapes[i]) == 1024} == {6}
