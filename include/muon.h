@@ -339,7 +339,9 @@ int muon_adamw_plan_destroy(muon_adamw_plan* plan);
  * graph holds kernel launches and the lanes' event dependencies only (no
  * memory set or copy nodes); a changed pointer table is uploaded before the
  * graph launches.  Needs a stream other than the null stream (EINVAL on
- * muon_step otherwise); profiling steps always run eagerly.  enable = 0
+ * muon_step otherwise); profiling steps always run eagerly, and so do steps
+ * enqueued while the caller is capturing the stream into a graph of its own
+ * (the launches then go into the caller's graph).  enable = 0
  * waits for the device and releases the graph.  EINVAL (NULL plan), ESTATE
  * (host-only plan).
  */

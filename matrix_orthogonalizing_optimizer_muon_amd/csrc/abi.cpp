@@ -703,6 +703,9 @@ int step_impl(muon_plan* p, void* const* params, const void* const* grads, float
   };
   if (!p->graph_on || p->profiling) return enqueue();
   if (!s) return fail(MUON_EINVAL, "graph replay needs a stream other than the null stream");
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  HIP_TRY(hipStreamIsCapturing(s, &cs));
+  if (cs != hipStreamCaptureStatusNone) return enqueue();   // the caller captures the step itself
   // the step's launches depend on the pointers (through the uploaded tables,
   // which the key pins), the update capture buffers and the scalars
   std::string key;

@@ -84,3 +84,50 @@ def test_graph_mode_refuses_the_null_stream(M):
     plan.step(P, G, B, stream=0)           # eager again on the null stream
     torch.cuda.synchronize()
     plan.close()
+
+
+@pytest.mark.parametrize("graph_mode", [False, True])
+def test_step_inside_the_callers_graph_matches_eager_steps(M, graph_mode):
+    """A caller that captures muon_step into a graph of its own (torch.cuda.graph,
+    three NS lanes joined back into the capture stream) gets, on every replay,
+    the same parameters and momenta as eager steps, bitwise; with the library's
+    own graph mode on, the step inside a caller's capture is enqueued as usual."""
+    import torch
+    from gpu_util import device_state
+    shapes, dts, Ws, Gs, Bs = _state()
+    eager = M.MuonPlan(shapes, dts, tune="off", lanes=3)
+    capt = M.MuonPlan(shapes, dts, tune="off", lanes=3)
+    if graph_mode:
+        capt.set_graph(True)
+    Pe, Ge, Be = device_state(Ws, Gs, Bs)
+    Pc, Gc, Bc = device_state(Ws, Gs, Bs)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(11)
+    side = torch.cuda.Stream()
+    # one eager step first: the pointer tables are uploaded outside the capture
+    eager.step(Pe, Ge, Be)
+    with torch.cuda.stream(side):
+        capt.step(Pc, Gc, Bc)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        capt.step(Pc, Gc, Bc)
+    torch.cuda.synchronize()
+    other = torch.randn(1 << 20, device="cuda", generator=gen)
+    for k in range(4):
+        for ge, gc in zip(Ge, Gc):
+            fresh = (torch.randn(ge.shape, device="cuda", generator=gen) * 0.02).to(ge.dtype)
+            ge.copy_(fresh)
+            gc.copy_(fresh)
+        torch.cuda.synchronize()
+        eager.step(Pe, Ge, Be)
+        g.replay()
+        torch.cuda.synchronize()
+        other.mul_(0.5).add_(1.0)
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(Pe + Be, Pc + Bc)):
+            assert torch.equal(a, b), f"replay {k}, tensor {i}"
+        print(f"caller graph (library graph mode {graph_mode}) replay {k}: bitwise equal", flush=True)
+    del g
+    eager.close()
+    capt.close()
