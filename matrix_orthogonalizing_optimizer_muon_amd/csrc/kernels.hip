@@ -752,14 +752,9 @@ hipError_t launch_gemm_cfg(int in_dt, int out_dt, const GemmParams& p, hipStream
 // output in TO, optionally its transpose (bf16) and, for upper-triangle
 // symmetric tiles, the mirrored tile.
 
-__device__ __forceinline__ void st_bf16x4(void* base, int64_t off, const float* v) {
-  *((GLOBAL_AS u32x2_t*)(static_cast<uint16_t*>(base) + off)) =
-      u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-}
-
 // Pipeline of each NT configuration: k-tile (elements) and LDS stages.  One
-// setting serves all four: k-tiles of 32 with three or four stages were
-// measured slower on the 128x128 tile.
+// setting serves all five: k-tiles of 32 with three or four stages were
+// measured slower on the 128x128 and the 256x256 tiles.
 // LDS_CAP: the LDS a block may take without lowering the blocks per CU its
 // registers allow (two 128x128 blocks per CU, one of any other).
 template <int BM, int BN, int WGM, int WGN>
@@ -794,15 +789,6 @@ constexpr int nt_lds() {
   static_assert(stages <= P::LDS_CAP && slab <= P::LDS_CAP && tile16 <= P::LDS_CAP, "LDS budget");
   constexpr int m = stages > slab ? stages : slab;
   return m > tile16 ? m : tile16;
-}
-
-__device__ __forceinline__ void ld8_bf16(const void* base, int64_t off, float* v) {
-  const u32x4_t q = *(GLOBAL_AS const u32x4_t*)(static_cast<const uint16_t*>(base) + off);
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    v[2 * e] = bf16_to_f32(q[e] & 0xffffu);
-    v[2 * e + 1] = bf16_to_f32(q[e] >> 16);
-  }
 }
 
 template <typename TO>

@@ -122,7 +122,10 @@ struct Copier {
 #pragma unroll
     for (int par = 0; par < 2; ++par) {
       const int row = (w * NR + par) * RPI + lane / CPR;   // any copy of this parity
-      const int chunk = (lane % CPR) ^ (T ? swzt(row) : swz<ROWB>(row));
+      int sw;
+      if constexpr (T) sw = swzt(row);
+      else sw = swz<ROWB>(row);
+      const int chunk = (lane % CPR) ^ sw;
       voff[par] = (uint32_t)(lane / CPR) * ld_bytes + (uint32_t)chunk * 16u;
     }
     step = (uint32_t)RPI * ld_bytes;
