@@ -205,8 +205,15 @@ def cpu_baseline(wl, ns_flops_per_step):
         if el >= 10.0 or done >= 3:
             break
     sec = el / done
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), None)
+    except OSError:
+        pass
     return {"value": ns_flops_per_step / sec / 1e12, "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle", "ms_per_step": sec * 1e3,
+            "kind": "oracle", "ms_per_step": sec * 1e3, "host_cpus": os.cpu_count(),
+            "cpu_model": model, "blas_threads": int(threads),
             "sample": f"{done} full step(s) of workload {wl.cfg} ({wl.n_matrices} matrices), "
                       f"fp64 numpy, input generation excluded"}
 
