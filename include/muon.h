@@ -351,9 +351,10 @@ int muon_plan_set_graph(muon_plan* plan, int enable);
  * Ceiling probes (measurement only; not part of a step).  They give the rates
  * this part sustains when nothing else limits them, so a kernel's figure can be
  * read against a measured ceiling beside the published peak (dense bf16 MFMA
- * about 2.5 PFLOP/s, HBM3E 8 TB/s).  Both need a current HIP device, run on a
- * stream of their own (default priority) and return when done: one warm-up
- * launch, then the timed launch(es) between two events.
+ * about 2.5 PFLOP/s, HBM3E 8 TB/s).  Both need a current HIP device, first
+ * wait for all earlier work on it, run on a stream of their own (default
+ * priority) and return when done: one warm-up launch, then the timed
+ * launch(es) between two events.
  *
  * muon_probe_mfma_bf16: 2 blocks of 4 waves per compute unit; every wave runs
  * iters rounds of 4 independent v_mfma_f32_32x32x16_bf16 accumulations on

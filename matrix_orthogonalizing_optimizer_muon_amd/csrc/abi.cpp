@@ -998,6 +998,9 @@ struct ProbeRun {
     if (s) (void)hipStreamDestroy(s);
   }
   int init() {
+    // the probe's stream does not order itself after the caller's streams:
+    // let every earlier piece of device work (e.g. the buffers' fill) finish
+    HIP_TRY(hipDeviceSynchronize());
     HIP_TRY(hipStreamCreateWithFlags(&s, hipStreamNonBlocking));
     HIP_TRY(hipEventCreate(&e0));
     HIP_TRY(hipEventCreate(&e1));
