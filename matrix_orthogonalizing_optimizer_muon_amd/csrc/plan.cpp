@@ -196,11 +196,18 @@ double model_cost_us(const ShapeKey& k, int32_t form, int32_t tile, int count) {
   const double mp = (double)mp64, np = (double)np64;
   double us = 0;
   if (!k.path) {
-    const double st = sym_tiles(mp64, kOld) * c, ft = (mp / kOld) * (np / kOld) * c;
-    const double tf = 2.0 * kOld * kOld;
-    const double g = launch_us(st, tf * np, kOldRateF32, 2);
-    const double sq = launch_us(st, tf * mp, kOldRateF32, 2);
-    const double ap = launch_us(ft, tf * mp, kOldRateF32, 2);
+    // the tile edge the plan takes for a set of c such matrices (64 when their
+    // m x n products have fewer 128-tiles than CUs); a 64-block does a quarter
+    // of the work at half the per-block rate, four blocks per CU
+    const bool small = (mp / kOld) * (np / kOld) * c < kCus;
+    const int e = small ? kOld / 2 : kOld;
+    const double rate = small ? kOldRateF32 / 2 : kOldRateF32;
+    const int per_cu = small ? 4 : 2;
+    const double st = sym_tiles(mp64, e) * c, ft = (mp / e) * (np / e) * c;
+    const double tf = 2.0 * e * e;
+    const double g = launch_us(st, tf * np, rate, per_cu);
+    const double sq = launch_us(st, tf * mp, rate, per_cu);
+    const double ap = launch_us(ft, tf * mp, rate, per_cu);
     us = form == kFormDirect ? T * (g + sq + ap) : g + ap + (4 * T - 3) * sq;
     return us / c;
   }
