@@ -432,6 +432,15 @@ def main():
                     "lanes": info["n_lanes"]}
         if ceil and bf16:
             roofline["frac_of_measured_mfma"] = round(ach / ceil["mfma_bf16_tflops"], 4)
+    # every NS kernel instance against the same peak (profiling pass, per launch)
+    ns_rooflines = []
+    for n, d in sorted(ns_kern.items(), key=lambda kv: -kv[1]["total_ms"]):
+        a_ms = d["total_ms"] / d["launches"]
+        a = d["flops"] / d["launches"] / (a_ms * 1e-3) / 1e12
+        ns_rooflines.append({"kernel": n, "stages": sorted(set(d["stages"])), "achieved": round(a, 2),
+                             "frac": round(a / peak, 4), "avg_launch_us": round(a_ms * 1e3, 2),
+                             "launches_per_step": d["launches"] / args.steps,
+                             "ms_per_step": round(d["total_ms"] / args.steps, 4)})
     ew = {}
     for n, d in ew_kern.items():
         avg_ms = d["total_ms"] / d["launches"]
@@ -459,7 +468,7 @@ def main():
         "ns_kernel_ms_per_step_serial": round(ns_ms, 4) if kt else None,
         "ns_tflops_kernels_serial": round(ns_flops / (ns_ms * 1e-3) / 1e12, 2) if ns_ms else None,
         "step_frac_of_peak": round(value / peak, 4),
-        "elementwise": ew, "roofline": roofline, "ceilings": ceil,
+        "elementwise": ew, "roofline": roofline, "ns_kernel_rooflines": ns_rooflines, "ceilings": ceil,
         "kernels": [{"stage": k["name"], "kernel": k["kernel"],
                      "launches_per_step": k["launches"] / args.steps,
                      "ms_per_step": round(k["total_ms"] / args.steps, 4)} for k in kt],
