@@ -291,7 +291,7 @@ def owner_share(args, wl, MU):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU runs are not "
+        print(json.dumps({"error": "the library runs the per-owner step on one GPU; multi-GPU runs are not "
                                    "supported (matrices would be sharded whole across owners)"}))
         sys.exit(2)
     import workloads as WL
