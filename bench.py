@@ -38,7 +38,7 @@ def parse():
     ap.add_argument("--lanes", type=int, default=None, help="force the NS lane count (1..4)")
     ap.add_argument("--adamw", action="store_true",
                     help="time the fused AdamW step over the non-matrix parameters of the "
-                         "workload-2 model (vocab 32000 embedding and classifier, norms)")
+                         "4-layer d=1024 transformer model (vocab 32000 embedding and classifier, norms)")
     ap.add_argument("--owners", type=int, default=1,
                     help="assign the workload's matrices to this many owners (makespan-balanced) "
                          "and time one owner's share")
@@ -214,7 +214,7 @@ def cpu_baseline(wl, ns_flops_per_step):
     return {"value": ns_flops_per_step / sec / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle", "ms_per_step": sec * 1e3, "host_cpus": os.cpu_count(),
             "cpu_model": model, "blas_threads": int(threads),
-            "sample": f"{done} full step(s) of workload {wl.cfg} ({wl.n_matrices} matrices), "
+            "sample": f"{done} full step(s) of the {wl.name} set ({wl.n_matrices} matrices), "
                       f"fp64 numpy, input generation excluded"}
 
 
@@ -222,7 +222,7 @@ ADAMW_VOCAB, ADAMW_D, ADAMW_LAYERS = 32000, 1024, 4
 
 
 def bench_adamw(args, torch, MU):
-    """The AdamW half of the hybrid on the workload-2 model's non-matrix
+    """The AdamW half of the hybrid on the 4-layer d=1024 transformer model's non-matrix
     parameters (bf16 params and grads, fp32 moments): one fused launch per step."""
     numels = [ADAMW_VOCAB * ADAMW_D, ADAMW_VOCAB * ADAMW_D] + [ADAMW_D] * (2 * ADAMW_LAYERS + 1)
     gen = torch.Generator(device="cuda")

@@ -21,7 +21,7 @@ def _plan(M, shapes, dtype, **kw):
     return M.MuonPlan(shapes, dtype, **kw)
 
 
-def test_c1_single_fp32_matrix(M):
+def test_single_fp32_256x512_matrix(M):
     from gpu_util import run_and_compare
     wl = WL.workload(1)
     Ws = [WL.draw(wl, 0, 0, WL.KIND_W)]
@@ -78,7 +78,7 @@ def test_ns_steps_zero_and_schedule(M):
 
 
 @pytest.mark.parametrize("tune", ["off", "once"])
-def test_c2_three_steps_all_matrices(M, tune, tmp_path):
+def test_transformer_block_set_three_steps_all_matrices(M, tune, tmp_path):
     """The transformer-block workload: 16 bf16 matrices, 3 steps, fresh
     gradients each step, momentum and weights carried over; with the cost
     model's plan and with the plan bench.py times (shapes and the whole set
@@ -88,7 +88,7 @@ def test_c2_three_steps_all_matrices(M, tune, tmp_path):
     from oracle import muon_oracle as O
     wl = WL.workload(2)
     plan = _plan(M, wl.shapes, "bf16", tune=tune, cache_path=str(tmp_path / "tune.txt"))
-    print("c2 plan", tune, plan.info()["n_lanes"], "lanes,",
+    print("transformer block set plan", tune, plan.info()["n_lanes"], "lanes,",
           sorted({(plan.matrix_choice(i)["form"], plan.matrix_choice(i)["tile"]) for i in range(wl.n_matrices)}))
     P = [to_device(WL.draw(wl, i, 0, WL.KIND_W)) for i in range(wl.n_matrices)]
     B = [torch.zeros(s, dtype=torch.float32, device="cuda") for s in wl.shapes]
@@ -115,7 +115,7 @@ def test_c2_three_steps_all_matrices(M, tune, tmp_path):
             floor = np.linalg.norm(ref["W_new_stored"] - ref["W_new"]) / nU
             assert rel(Wn - W_before[i], ref["U"]) <= 2e-2 + 2.5 * floor
     plan.set_update_capture(None)
-    print("c2 worst rel err", worst)
+    print("transformer block set worst rel err", worst)
 
 
 def test_bitwise_determinism(M):
