@@ -290,3 +290,32 @@ def test_fp32_tile_edge_matches_oracle(M, shapes, edge):
     gram = _plan(M, shapes, "f32", form="gram")
     assert f"edge={edge} ".encode() in gram.serialize()
     run_and_compare(gram, Ws, Gs, Bs, WL.F32, ns_steps=5, check=check)
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_seeded_random_shapes_match_oracle(M, case):
+    """Seeded random plans: 3-4 shapes with sides from 1 to 1500 (primes,
+    single rows and columns, both orientations), a random bf16 tile plan,
+    form and NS step count, or the fp32 path; every matrix against the oracle."""
+    from gpu_util import make_state, run_and_compare
+    rng = np.random.default_rng(1000 + case)
+    sides = [1, 2, 7, 31, 64, 127, 128, 129, 257, 383, 512, 641, 1000, 1021, 1500]
+    shapes = []
+    for _ in range(int(rng.integers(3, 5))):
+        a, b = int(rng.choice(sides)), int(rng.choice(sides))
+        if min(a, b) == max(a, b) == 1:
+            b = 64
+        shapes.append((a, b))
+    dtype = WL.F32 if case % 4 == 3 else WL.BF16
+    T = int(rng.integers(1, 7))
+    if dtype == WL.BF16:
+        form = "gram" if case % 5 == 4 else "direct"
+        tiles = [0, 1, 2, 5, 6, 7, 8, 9] if form == "gram" else list(range(10))
+        tile = int(rng.choice(tiles))
+        plan = _plan(M, shapes, "bf16", tile=tile, form=form)
+    else:
+        form, tile = ("gram" if case == 7 else "direct"), None
+        plan = _plan(M, shapes, "f32", form=form)
+    print(f"case {case}: {dtype} shapes {shapes} form {form} tile {tile} T {T}", flush=True)
+    Ws, Gs, Bs = make_state(shapes, dtype, seed=2000 + case, buf_scale=0.01)
+    run_and_compare(plan, Ws, Gs, Bs, dtype, ns_steps=T)
