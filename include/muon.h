@@ -31,6 +31,13 @@
  *     plan was created; "host pointer" means ordinary process memory.
  *   - matrices are dense row-major, rows x cols, leading dimension = cols.
  *   - a stream argument is a hipStream_t passed as void* (NULL = null stream).
+ *   - graphs the caller captures: muon_step, muon_step_schedule,
+ *     muon_orthogonalize and muon_adamw_step keep their per-tensor pointer
+ *     tables in device memory and upload a changed table only outside graphs.
+ *     A call on a stream under capture must pass the pointers of the plan's
+ *     previous call made outside the capture (ESTATE otherwise, nothing
+ *     enqueued); the graph reads the table at every replay, so replay it
+ *     while the plan's latest call outside graphs used those same pointers.
  */
 #ifndef MUON_MI355X_H
 #define MUON_MI355X_H
@@ -178,7 +185,8 @@ int muon_plan_destroy(muon_plan* plan);
  * Nesterov direction.  The plan's workspace is shared by its calls: do not run
  * two steps of one plan concurrently on different streams.
  * Errors: EINVAL (NULL array or entry, ns_steps < 0 or > 64, non-finite scalar),
- * ESTATE (host-only plan), EHIP (launch failure).
+ * ESTATE (host-only plan; changed pointers on a stream under capture), EHIP
+ * (launch failure).
  */
 int muon_step(muon_plan* plan, void* const* params, const void* const* grads,
               float* const* momenta, float lr, float beta, float wd, int ns_steps,
@@ -262,7 +270,8 @@ const char* muon_last_error(void);
  * the plan's workspace, so it must not overlap a muon_step or another call on
  * the same plan.  A non-finite norm sets the flag muon_plan_get_flags reads.
  * EINVAL (NULL array or pointer, ns_steps outside [0, 64], non-finite
- * coefficient), ESTATE (host-only plan), EHIP (launch error).
+ * coefficient), ESTATE (host-only plan; changed pointers on a stream under
+ * capture), EHIP (launch error).
  */
 int muon_orthogonalize(muon_plan* plan, const void* const* inputs, float* const* outputs,
                        int ns_steps, const float* coeffs, void* stream);
@@ -315,7 +324,8 @@ int muon_assign_owners(const double* costs, int n, int n_owners, int64_t node_li
  * muon_adamw_step: host arrays of n caller-owned device pointers (contiguous,
  * numels[i] elements each); params, exp_avg and exp_avg_sq updated in place,
  * grads read only.  One launch on stream, asynchronous.  EINVAL (NULL pointer,
- * step < 1, beta outside [0, 1), eps < 0, non-finite lr, wd or eps), EHIP.
+ * step < 1, beta outside [0, 1), eps < 0, non-finite lr, wd or eps), ESTATE
+ * (changed pointers on a stream under capture), EHIP.
  */
 typedef struct muon_adamw_plan muon_adamw_plan;
 int muon_adamw_plan_create(const int64_t* numels, const int32_t* dtypes, int n,

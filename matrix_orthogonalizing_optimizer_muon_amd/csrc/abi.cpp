@@ -636,11 +636,30 @@ int enqueue_front(muon_plan* p, const ChunkDev& C, int a, int b, float beta, int
 
 bool aligned16(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; }
 
+// Whether stream s is being captured into a graph (the null stream never is).
+int stream_capturing(hipStream_t s, bool* capturing) {
+  *capturing = false;
+  if (!s) return MUON_OK;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  HIP_TRY(hipStreamIsCapturing(s, &cs));
+  *capturing = cs != hipStreamCaptureStatusNone;
+  return MUON_OK;
+}
+
+// Pointer tables are uploaded outside graphs only: a graph captured by the
+// caller reads the table from device memory at every replay, and a copy
+// recorded into it would read the pinned staging buffer that later uploads
+// overwrite.
+const char* kCaptureTableMsg =
+    "stream capture: the plan's device pointer table differs from these pointers; "
+    "run one call with the same pointers outside the capture first";
+
 // Per-matrix pointers of a chunk to the device (skipped when unchanged).
 // momenta NULL: no momentum buffers (orthogonalization alone); use_capture 0:
-// no update capture.
+// no update capture.  capturing: s is being captured (a changed table is
+// then refused).
 int upload_dyn(muon_plan* p, ChunkDev& C, void* const* params, const void* const* grads,
-               float* const* momenta, bool use_capture, hipStream_t s) {
+               float* const* momenta, bool use_capture, bool capturing, hipStream_t s) {
   const size_t nm = C.mats.size();
   std::vector<EwDyn> d(nm);
   for (size_t k = 0; k < nm; ++k) {
@@ -656,6 +675,7 @@ int upload_dyn(muon_plan* p, ChunkDev& C, void* const* params, const void* const
              (!e.upd || aligned16(e.upd))) ? 1 : 0;
   }
   if (C.dyn_valid && std::memcmp(d.data(), C.dyn_last.data(), nm * sizeof(EwDyn)) == 0) return MUON_OK;
+  if (capturing) return fail(MUON_ESTATE, kCaptureTableMsg);
   if (C.upload_pending) HIP_TRY(hipEventSynchronize(C.upload_ev));
   std::memcpy(C.dyn_pinned, d.data(), nm * sizeof(EwDyn));
   HIP_TRY(hipMemcpyAsync(C.dyn, C.dyn_pinned, nm * sizeof(EwDyn), hipMemcpyHostToDevice, s));
@@ -681,10 +701,12 @@ int step_impl(muon_plan* p, void* const* params, const void* const* grads, float
     if (!params[i] || !grads[i] || !momenta[i]) return fail(MUON_EINVAL, "NULL matrix pointer at index " + std::to_string(i));
   hipStream_t s = static_cast<hipStream_t>(stream);
   int rc;
+  bool capturing = false;
+  if ((rc = stream_capturing(s, &capturing))) return rc;
   // every chunk's per-matrix pointers first (uploaded only when they changed;
   // each chunk has its own table), then the kernels
   for (ChunkDev& C : p->chunks)
-    if ((rc = upload_dyn(p, C, params, grads, momenta, true, s))) return rc;
+    if ((rc = upload_dyn(p, C, params, grads, momenta, true, capturing, s))) return rc;
   auto enqueue = [&]() -> int {
     for (ChunkDev& C : p->chunks) {
       const int nm = (int)C.mats.size();
@@ -703,9 +725,7 @@ int step_impl(muon_plan* p, void* const* params, const void* const* grads, float
   };
   if (!p->graph_on || p->profiling) return enqueue();
   if (!s) return fail(MUON_EINVAL, "graph replay needs a stream other than the null stream");
-  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-  HIP_TRY(hipStreamIsCapturing(s, &cs));
-  if (cs != hipStreamCaptureStatusNone) return enqueue();   // the caller captures the step itself
+  if (capturing) return enqueue();   // the caller captures the step itself
   // the step's launches depend on the pointers (through the uploaded tables,
   // which the key pins), the update capture buffers and the scalars
   std::string key;
@@ -765,8 +785,11 @@ int ortho_impl(muon_plan* p, const void* const* inputs, float* const* outputs, i
   hipStream_t s = static_cast<hipStream_t>(stream);
   std::vector<void*> outs(outputs, outputs + n);
   int rc;
+  bool capturing = false;
+  if ((rc = stream_capturing(s, &capturing))) return rc;
+  for (ChunkDev& C : p->chunks)
+    if ((rc = upload_dyn(p, C, outs.data(), inputs, nullptr, false, capturing, s))) return rc;
   for (ChunkDev& C : p->chunks) {
-    if ((rc = upload_dyn(p, C, outs.data(), inputs, nullptr, false, s))) return rc;
     const int nm = (int)C.mats.size();
     // no parameters: the last NS product writes X_T (fp32) to the workspace
     if ((rc = enqueue_chunk(p, C, T, sched, nullptr, 0.f, 0.f, s, [&](int a, int b, hipStream_t ls, hipEvent_t ev) {
@@ -854,7 +877,7 @@ int time_ns(PlanHost&& H, bool with_front, float* best_ms) {
     for (ChunkDev& C : tp.chunks) {
       if (with_front) {
         // the parameters are never touched (no update is applied here)
-        rc = upload_dyn(&tp, C, grads.data(), grads.data(), moms.data(), false, s);
+        rc = upload_dyn(&tp, C, grads.data(), grads.data(), moms.data(), false, false, s);
         if (!rc)
           rc = enqueue_chunk(&tp, C, 5, sched, nullptr, 0.f, 0.f, s, [&](int a, int b, hipStream_t ls, hipEvent_t ev) {
             return enqueue_front(&tp, C, a, b, 0.95f, 0, ls, ev);
@@ -1394,6 +1417,10 @@ int muon_adamw_step(muon_adamw_plan* a, void* const* params, const void* const* 
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (!a->valid || std::memcmp(t.data(), a->last.data(), n * sizeof(AdamTensor)) != 0) {
+    bool capturing = false;
+    int rc;
+    if ((rc = stream_capturing(s, &capturing))) return rc;
+    if (capturing) return fail(MUON_ESTATE, kCaptureTableMsg);
     if (a->pending) HIP_TRY(hipEventSynchronize(a->upload_ev));
     std::memcpy(a->pinned, t.data(), n * sizeof(AdamTensor));
     HIP_TRY(hipMemcpyAsync(a->dev_tensors, a->pinned, n * sizeof(AdamTensor), hipMemcpyHostToDevice, s));

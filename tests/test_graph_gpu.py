@@ -131,3 +131,50 @@ def test_step_inside_the_callers_graph_matches_eager_steps(M, graph_mode):
     del g
     eager.close()
     capt.close()
+
+
+def test_capture_with_pointers_not_yet_uploaded_is_refused(M):
+    """A step, an orthogonalization or an AdamW step on a stream under capture
+    whose pointers differ from the plan's previous call outside the capture is
+    refused (ESTATE) with nothing enqueued: the pointer tables are uploaded
+    outside graphs only.  The plans stay usable: the next eager calls match
+    a fresh plan's bitwise."""
+    import torch
+    from gpu_util import device_state
+    shapes, dts, Ws, Gs, Bs = _state()
+    plan = M.MuonPlan(shapes, dts, tune="off", lanes=3)
+    ref = M.MuonPlan(shapes, dts, tune="off", lanes=3)
+    P, G, B = device_state(Ws, Gs, Bs)
+    Pr, Gr, Br = device_state(Ws, Gs, Bs)
+    outs = [torch.empty(s, device="cuda", dtype=torch.float32) for s in shapes]
+    numels = [16384, 1000]
+    aw = M.AdamWPlan(numels, ["f32", "bf16"])
+    ap = [torch.randn(numels[0], device="cuda"), torch.randn(numels[1], device="cuda").to(torch.bfloat16)]
+    ag = [torch.randn_like(t) for t in ap]
+    am = [torch.zeros(k, device="cuda") for k in numels]
+    av = [torch.zeros(k, device="cuda") for k in numels]
+    torch.cuda.synchronize()
+    calls = [
+        ("muon_step", lambda: plan.step(P, G, B)),
+        ("muon_orthogonalize", lambda: plan.orthogonalize(G, outs)),
+        ("muon_adamw_step", lambda: aw.step(ap, ag, am, av, lr=1e-3)),
+    ]
+    for name, call in calls:
+        g = torch.cuda.CUDAGraph()
+        with pytest.raises(M.MuonError, match="stream capture"):
+            with torch.cuda.graph(g):
+                call()
+        torch.cuda.synchronize()
+        print(f"{name} under capture with new pointers: refused", flush=True)
+        del g
+    plan.step(P, G, B)
+    ref.step(Pr, Gr, Br)
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(zip(P + B, Pr + Br)):
+        assert torch.equal(a, b), f"tensor {i}"
+    aw.step(ap, ag, am, av, lr=1e-3)
+    torch.cuda.synchronize()
+    assert all(torch.isfinite(t.float()).all() for t in ap + am + av)
+    aw.close()
+    plan.close()
+    ref.close()
