@@ -266,3 +266,39 @@ def test_orthogonalize_equals_svd_of_the_normalized_input(shape, T):
 
 def test_orthogonalize_of_zero_is_zero():
     assert np.all(O.orthogonalize_ref(np.zeros((4, 6)), 5) == 0.0)
+
+
+@pytest.mark.parametrize("shape", [(24, 40), (40, 24), (16, 16)])
+@pytest.mark.parametrize("form", ["direct", "gram"])
+def test_whole_step_equals_closed_form_on_shared_singular_vectors(shape, form):
+    """The whole step (momentum, normalization, orientation, NS, RMS scale,
+    decoupled decay, apply) against a closed form: with the gradient and the
+    momentum built on the same singular vectors, g = P diag(gam) Q^T and
+    buf = P diag(mu) Q^T, the Nesterov direction is P diag(delta) Q^T with
+    delta = (1 + beta) gam + beta^2 mu, its Frobenius norm is ||delta||_2, and
+    NS sends each singular value through the scalar odd polynomial, so
+    U = -lr (wd W + s P diag(phi(delta / (||delta||_2 + eps))) Q^T) with
+    s = 0.2 sqrt(max(rows, cols)).  No matrix product of the oracle is reused."""
+    rows, cols = shape
+    k = min(rows, cols)
+    rng = np.random.default_rng(2024 + rows * 100 + cols)
+    P, _ = np.linalg.qr(rng.standard_normal((rows, k)))
+    Q, _ = np.linalg.qr(rng.standard_normal((cols, k)))
+    gam = rng.uniform(0.05, 1.0, k) * 1e-2
+    mu = rng.uniform(-1.0, 1.0, k) * 1e-2
+    g = (P * gam) @ Q.T
+    buf = (P * mu) @ Q.T
+    W = rng.standard_normal(shape) * 0.02
+    lr, beta, wd, eps, T = 0.02, 0.95, 0.01, 1e-7, 5
+    r = O.muon_step_ref(W, g, buf, lr=lr, beta=beta, wd=wd, ns_steps=T, eps=eps, form=form)
+    delta = (1.0 + beta) * gam + beta * beta * mu
+    sig = np.abs(delta) / (np.sqrt(np.sum(delta ** 2)) + eps)
+    phi = _phi_scalar(sig, O.coeff_schedule(O.QUINTIC, T)) * np.sign(delta)
+    X = (P * phi) @ Q.T
+    s = 0.2 * np.sqrt(max(rows, cols))
+    U = -lr * (wd * W + s * X)
+    assert _rel(r["buf_new"], beta * buf + g) < 1e-14
+    assert abs(r["nu"] - np.sqrt(np.sum(delta ** 2))) <= 1e-14 * r["nu"]
+    assert _rel(r["X"], X) < 1e-11
+    assert _rel(r["U"], U) < 1e-11
+    assert _rel(r["W_new"], W + U) < 1e-14
