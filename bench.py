@@ -28,8 +28,10 @@ PEAK_HBM_GBS = 8000.0
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: 400 for workloads 1 and 2, 20 otherwise)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps first (default: 40 for workloads 1 and 2 when timing, 5 otherwise)")
     ap.add_argument("--config", type=int, default=2, help="workload number 1..5")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--tune", default="once", choices=["off", "once", "force"])
@@ -56,7 +58,15 @@ def parse():
                     help="run the steps on a side stream with graph replay (muon_plan_set_graph)")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the measured ceilings (dense bf16 MFMA loop, 1 GiB HBM copy)")
-    return ap.parse_args()
+    args = ap.parse_args()
+    # the sub-millisecond steps of workloads 1 and 2 get enough steps for a
+    # timed region of about half a second; the --pmc probe keeps 5 + 2 steps
+    short = args.config in (1, 2) and not args.adamw and not args.traffic_probe and not args.traffic_from
+    if args.steps is None:
+        args.steps = 400 if short else 20
+    if args.warmup is None:
+        args.warmup = 40 if short else 5
+    return args
 
 
 def source_digest():
