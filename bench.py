@@ -2,10 +2,11 @@
 
 A step is one muon_step over every matrix of the workload (momentum, norm,
 Newton-Schulz, scale / weight decay / apply).  Inputs are synthetic and
-already resident in HBM when timing starts.  Default workload: the 4-layer
-transformer block set (d=1024, ffn=4096; 16 bf16 matrices, fp32 momentum).
+already resident in HBM when timing starts.  Default workload: the
+Llama-style 7B matrix set (32 layers, d=4096, ffn=11008; 160 bf16 matrices,
+fp32 momentum), the largest matrix set that fits one GPU.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 4] [--no-cpu-baseline]
 
 Prints one JSON line.  `value` is the NS throughput of the whole step:
 algorithmic (symmetric-aware) NS flops per step / measured step time.
@@ -32,7 +33,7 @@ def parse():
                     help="timed steps (default: 400 for workloads 1 and 2, 20 otherwise)")
     ap.add_argument("--warmup", type=int, default=None,
                     help="untimed steps first (default: 40 for workloads 1 and 2 when timing, 5 otherwise)")
-    ap.add_argument("--config", type=int, default=2, help="workload number 1..5")
+    ap.add_argument("--config", type=int, default=4, help="workload number 1..5 (default 4, the Llama-7B set)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--tune", default="once", choices=["off", "once", "force"])
     ap.add_argument("--form", default="auto", choices=["auto", "direct", "gram"])
@@ -190,10 +191,88 @@ def make_inputs(wl, torch):
     return P, G, B
 
 
-def cpu_baseline(wl, ns_flops_per_step):
-    """The fp64 oracle on the host cores, on a bounded sample of the same workload."""
+def baseline_sample(wl):
+    """Matrices the oracle leg times and checks, each with the number of
+    matrices of the full set it stands for (the timed sample is scaled by
+    these weights to a full step, labelled extrapolated when any weight > 1):
+    one layer of each repeated block, every matrix of the small sets."""
+    shapes = wl.shapes
+    if wl.cfg == 3:      # backbone layer 0 (x24) and action-expert layer 0 (x12)
+        return [(i, 24) for i in range(4)] + [(96 + i, 12) for i in range(4)]
+    if wl.cfg == 4:      # layer 0: QKV, O, gate, up, down (x32)
+        return [(i, 32) for i in range(5)]
+    if wl.cfg == 5:      # expert 0's gate, up, down (x512 each) and one 512x16384 (x8)
+        return [(0, 512), (1, 512), (2, 512), (len(shapes) - 8, 8)]
+    return [(i, 1) for i in range(len(shapes))]
+
+
+def parity_inputs(wl, sample, P, G, torch):
+    """Writes the host-drawn seeded weights and gradients of the sampled
+    matrices (step 0 of the workload's generator) over their device tensors;
+    returns the stored host values for the oracle."""
     import numpy as np
     import workloads as WL
+    host = {}
+    for i, _w in sample:
+        W, Gs = WL.draw(wl, i, 0, WL.KIND_W), WL.draw(wl, i, 0, WL.KIND_G)
+        host[i] = (W, Gs)
+        for st, t in ((W, P[i]), (Gs, G[i])):
+            raw = np.ascontiguousarray(st.raw)
+            src = torch.from_numpy(raw.view(np.int16)).view(torch.bfloat16) if st.dtype == WL.BF16 \
+                else torch.from_numpy(raw)
+            t.copy_(src.to(t.device))
+    return host
+
+
+def parity_step(plan, wl, sample, P, G, B, torch, h):
+    """One step from zero momenta with the fp32 update of the sampled matrices
+    captured; returns (U, W_new, momentum) per sampled matrix on the host."""
+    cap = [None] * wl.n_matrices
+    for i, _w in sample:
+        cap[i] = torch.empty(wl.shapes[i], dtype=torch.float32, device="cuda")
+    plan.set_update_capture(cap)
+    plan.step(P, G, B, lr=h.lr, beta=h.beta, wd=h.wd, ns_steps=h.ns_steps, coeffs=h.coeffs)
+    torch.cuda.synchronize()
+    plan.set_update_capture(None)
+    out = {}
+    for i, _w in sample:
+        wnew = P[i].view(torch.int16).cpu() if P[i].dtype == torch.bfloat16 else P[i].cpu()
+        out[i] = (cap[i].cpu().numpy(), wnew.numpy(), B[i].cpu().numpy())
+    return out, plan.flags()
+
+
+def line_errors(d, ref):
+    """Largest error of a row and of a column of d against ref: the norm of the
+    line's error over max(the line's own norm, the RMS norm of the lines)."""
+    import numpy as np
+    out = []
+    for ax in (1, 0):
+        err = np.sqrt(np.sum(d * d, axis=ax))
+        nrm = np.sqrt(np.sum(ref * ref, axis=ax))
+        rms = np.sqrt(np.mean(nrm * nrm))
+        out.append(float(np.max(err / np.maximum(nrm, rms))) if rms > 0 else 0.0)
+    return out
+
+
+def ulp_fraction_bf16(w_bits, ref_stored):
+    """Fraction of bf16 weights within one bf16 ulp of the oracle's rounded W_new."""
+    import numpy as np
+    import workloads as WL
+    w = WL.bf16_bits_to_f64(np.asarray(w_bits).view(np.uint16))
+    _m, e = np.frexp(ref_stored)
+    ulp = np.ldexp(1.0, e - 8)             # bf16: 8 significant bits
+    ulp = np.where(ref_stored == 0, np.ldexp(1.0, -133), ulp)
+    return float(np.mean(np.abs(w - ref_stored) <= ulp))
+
+
+def cpu_baseline(wl, ns_flops_per_step, sample, host, gpu, flags):
+    """The fp64 oracle on the host cores over a bounded sample of the same
+    workload (one layer of each repeated block), scaled to the whole step by
+    the sample weights; the same oracle results grade the GPU's parity step on
+    those matrices (relative Frobenius error of the fp32 update, of the stored
+    weight delta and of the momentum; largest row / column error; bf16
+    fraction of weights within one ulp of the oracle's rounded value)."""
+    import numpy as np
     from oracle import muon_oracle as O
     try:
         from threadpoolctl import threadpool_info
@@ -201,31 +280,58 @@ def cpu_baseline(wl, ns_flops_per_step):
     except Exception:
         threads = os.cpu_count()
     h = wl.hyper
-    # sample: whole steps of the workload (every matrix), repeated for >= 10 s (at most 3)
-    mats = [(WL.draw(wl, i, 0, WL.KIND_W).value, WL.draw(wl, i, 0, WL.KIND_G).value)
-            for i in range(wl.n_matrices)]
-    done, t0 = 0, time.perf_counter()
-    while True:
-        for W, g in mats:
-            O.muon_step_ref(W, g, np.zeros_like(W), lr=h.lr, beta=h.beta, wd=h.wd,
-                            ns_steps=h.ns_steps, coeffs=h.coeffs, eps=h.eps,
-                            param_dtype=wl.dtype)
-        done += 1
-        el = time.perf_counter() - t0
-        if el >= 10.0 or done >= 3:
-            break
-    sec = el / done
+
+    def rel(a, b):
+        nb = np.linalg.norm(b)
+        return float(np.linalg.norm(a - b) / nb) if nb > 0 else float(np.linalg.norm(a - b))
+
+    oracle_s, ext_s, parity = 0.0, 0.0, []
+    for i, weight in sample:
+        W, Gs = host[i]
+        t0 = time.perf_counter()
+        ref = O.muon_step_ref(W.value, Gs.value, np.zeros(W.value.shape), lr=h.lr, beta=h.beta,
+                              wd=h.wd, ns_steps=h.ns_steps, coeffs=h.coeffs, eps=h.eps,
+                              param_dtype=wl.dtype)
+        dt = time.perf_counter() - t0
+        oracle_s += dt
+        ext_s += dt * weight
+        U, wnew, buf = gpu[i]
+        U = U.astype(np.float64)
+        if wl.dtype == "bf16":
+            import workloads as WL
+            wn = WL.bf16_bits_to_f64(wnew.view(np.uint16))
+        else:
+            wn = wnew.astype(np.float64)
+        row, col = line_errors(U - ref["U"], ref["U"])
+        rec = {"matrix": i, "shape": list(wl.shapes[i]), "oracle_s": round(dt, 2),
+               "err_update": rel(U, ref["U"]), "err_dW": rel(wn - W.value, ref["U"]),
+               "err_momentum": rel(buf.astype(np.float64), ref["buf_new"]),
+               "max_row_err": row, "max_col_err": col}
+        if wl.dtype == "bf16":
+            rec["bf16_within_1ulp"] = ulp_fraction_bf16(wnew, ref["W_new_stored"])
+        parity.append(rec)
     model = None
     try:
         with open("/proc/cpuinfo") as fh:
             model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), None)
     except OSError:
         pass
-    return {"value": ns_flops_per_step / sec / 1e12, "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle", "ms_per_step": sec * 1e3, "host_cpus": os.cpu_count(),
+    extrapolated = any(w > 1 for _i, w in sample)
+    worst = {k: max(r[k] for r in parity) for k in ("err_update", "err_dW", "err_momentum",
+                                                    "max_row_err", "max_col_err")}
+    if wl.dtype == "bf16":
+        worst["bf16_within_1ulp_min"] = min(r["bf16_within_1ulp"] for r in parity)
+    return {"value": ns_flops_per_step / ext_s / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle", "ms_per_step": ext_s * 1e3, "extrapolated": extrapolated,
+            "oracle_s": round(oracle_s, 2), "host_cpus": os.cpu_count(),
             "cpu_model": model, "blas_threads": int(threads),
-            "sample": f"{done} full step(s) of the {wl.name} set ({wl.n_matrices} matrices), "
-                      f"fp64 numpy, input generation excluded"}
+            "sample": (f"{len(sample)} of the {wl.n_matrices} matrices of the {wl.name} set "
+                       f"({', '.join(f'{wl.shapes[i][0]}x{wl.shapes[i][1]} x{w}' for i, w in sample)}), "
+                       f"one step each, fp64 numpy, input generation excluded"
+                       + ("; the full step is extrapolated from the sample by the weights" if extrapolated else "")),
+            "parity": {"flags": flags, "worst": worst, "matrices": parity,
+                       "how": "GPU step from zero momenta on the sampled matrices' seeded host inputs, "
+                              "fp32 update captured, against the fp64 oracle on the same stored inputs"}}
 
 
 ADAMW_VOCAB, ADAMW_D, ADAMW_LAYERS = 32000, 1024, 4
@@ -331,6 +437,15 @@ def main():
         choices.setdefault(f"{min(r, c)}x{max(r, c)}", f"{ch['form']}/tile{ch['tile']}")
     P, G, B = make_inputs(wl, torch)
     h = wl.hyper
+    # parity step of the oracle leg: seeded host inputs on a sample of the
+    # matrices, one step from zero momenta, before any other step
+    parity = None
+    if not args.no_cpu_baseline and not args.traffic_probe and not args.graph:
+        sample = baseline_sample(wl)
+        host = parity_inputs(wl, sample, P, G, torch)
+        gpu, flags = parity_step(plan, wl, sample, P, G, B, torch, h)
+        parity = (sample, host, gpu, flags)
+        print(f"# parity step done on {len(sample)} sampled matrices", file=sys.stderr, flush=True)
     if args.graph:
         # graph capture needs a stream other than the null stream; the inputs
         # were made on the default stream, so let that work finish first
@@ -489,9 +604,9 @@ def main():
         "wall_s_timed": round(wall, 3),
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
-        print("# cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(wl, ns_flops)
+    if parity is not None:
+        print("# cpu baseline (fp64 oracle on the sampled matrices)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(wl, ns_flops, *parity)
     plan.close()
     print(json.dumps(out), flush=True)
 

@@ -40,3 +40,47 @@ def best_makespan(costs, n_owners):
         if best is None or m < best:
             best, arg = m, list(owner)
     return best, arg
+
+
+def best_makespan_by_counts(costs, n_owners, max_states=200000):
+    """Minimum makespan by dynamic programming over how many items of each
+    distinct cost every owner takes: with d distinct costs c_j held n_j times,
+    f(owners, r) = min over a take t <= r of max(sum_j t_j c_j, f(owners - 1, r - t))
+    and f(1, r) = sum_j r_j c_j.  Exact; practical when the items come in few
+    distinct costs (the workloads' matrix sets).  Returns None when the count
+    vectors exceed max_states."""
+    from functools import lru_cache
+
+    groups = {}
+    for c in costs:
+        groups[c] = groups.get(c, 0) + 1
+    vals = sorted(groups)
+    counts = tuple(groups[v] for v in vals)
+    states = 1
+    for n in counts:
+        states *= n + 1
+    if states > max_states:
+        return None
+    if not costs:
+        return 0.0
+    takes = list(itertools.product(*(range(n + 1) for n in counts)))
+
+    def load(t):
+        return sum(k * v for k, v in zip(t, vals))
+
+    @lru_cache(maxsize=None)
+    def f(owners, rem):
+        if owners == 1:
+            return load(rem)
+        best = load(rem)          # this owner takes everything left
+        for t in takes:
+            if any(a > b for a, b in zip(t, rem)):
+                continue
+            lt = load(t)
+            if lt >= best:
+                continue
+            rest = f(owners - 1, tuple(b - a for a, b in zip(t, rem)))
+            best = min(best, max(lt, rest))
+        return best
+
+    return f(n_owners, counts)

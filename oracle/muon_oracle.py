@@ -23,7 +23,8 @@ bf16 values.  The functions follow the method as the pages describe it:
   the parameter update rule, so every execution form must give this result.
 
 Where the pages are silent the readings are:
-  momentum   SGD-Nesterov: buf <- beta*buf + g, d <- g + beta*buf.
+  momentum   SGD-Nesterov: buf <- beta*buf + g, d <- g + beta*buf (with
+             nesterov=False the plain buffer: d <- buf, the library's option).
   normalize  X0 = d / (||d||_F + eps), eps = 1e-7.
   polynomial odd quintic X <- a X + b (X X^T) X + c (X X^T)^2 X, the same
              (a, b, c) each step unless a per-step schedule is given.
@@ -34,7 +35,8 @@ Where the pages are silent the readings are:
 Pins (tests/test_oracle_pins.py) tie every function here to something other
 than itself: the SVD closed form of the matrix polynomial, convergence of the
 cubic iteration to scipy's polar factor, Gram == direct, orientation and
-orthogonal equivariance, the momentum closed form, RMS = 0.2 for an exact
+orthogonal equivariance, the momentum closed forms (Nesterov and plain), the
+whole step on shared singular vectors (both momentum forms), RMS = 0.2 for an exact
 polar factor, and the zero-gradient / lr = 0 / ns_steps = 0 special cases.
 No function here is parity-unpinned.
 """
@@ -71,6 +73,15 @@ def nesterov_momentum(buf: np.ndarray, g: np.ndarray, beta: float):
     buf_new = beta * buf + g
     d = g + beta * buf_new
     return buf_new, d
+
+
+def plain_momentum(buf: np.ndarray, g: np.ndarray, beta: float):
+    """Plain (heavy-ball) momentum, the library's option with Nesterov off:
+    buf_new = beta*buf + g;  d = buf_new.  Returns (buf_new, d)."""
+    buf = np.asarray(buf, dtype=np.float64)
+    g = np.asarray(g, dtype=np.float64)
+    buf_new = beta * buf + g
+    return buf_new, buf_new.copy()
 
 
 def frobenius_normalize(d: np.ndarray, eps: float = 1e-7):
@@ -169,14 +180,18 @@ def round_to_f32(x: np.ndarray) -> np.ndarray:
 
 def muon_step_ref(W, g, buf, *, lr: float = 0.02, beta: float = 0.95, wd: float = 0.01,
                   ns_steps: int = 5, coeffs=QUINTIC, eps: float = 1e-7,
-                  rms_base: float = 0.2, form: str = "direct", param_dtype: str = "f32"):
+                  rms_base: float = 0.2, form: str = "direct", param_dtype: str = "f32",
+                  nesterov: bool = True):
     """One Muon update of one matrix, every step in fp64.
+
+    nesterov=False orthogonalizes the plain momentum buffer instead of the
+    Nesterov direction (the library's option of the same name).
 
     Returns a dict: U (the update), buf_new, W_new (fp64), W_new_stored (rounded to
     the parameter dtype), X (the NS output), nu (the Frobenius norm of d)."""
     W = np.asarray(W, dtype=np.float64)
     rows, cols = W.shape
-    buf_new, d = nesterov_momentum(buf, g, beta)
+    buf_new, d = (nesterov_momentum if nesterov else plain_momentum)(buf, g, beta)
     X0, nu = frobenius_normalize(d, eps)
     if form == "direct":
         X = ns_direct(X0, ns_steps, coeffs)

@@ -7,6 +7,37 @@ import workloads as WL
 from oracle import muon_oracle as O
 
 REL_TOL = {WL.F32: 1e-4, WL.BF16: 2e-2}
+# A row or column of U may carry at most this multiple of the Frobenius
+# tolerance, measured as the norm of the line's error over max(the line's own
+# norm, the RMS norm of all lines).  Rounding spreads the error evenly over a
+# line of >= 256 elements (its relative spread is ~1/sqrt(2 L) < 5%), while a
+# wrong row, column or strip has a line error near 1.
+LINE_FACTOR = 2.5
+LINE_MIN_LEN = 256
+
+
+def line_errors(d, ref):
+    """(largest row error, largest column error) of d = U - U_ref against ref,
+    each line's error norm over max(its own norm, the RMS norm of the lines)."""
+    out = []
+    for ax in (1, 0):
+        err = np.sqrt(np.sum(d * d, axis=ax))
+        nrm = np.sqrt(np.sum(ref * ref, axis=ax))
+        rms = np.sqrt(np.mean(nrm * nrm))
+        out.append(float(np.max(err / np.maximum(nrm, rms))) if rms > 0 else float(np.max(err)))
+    return out
+
+
+def check_lines(U, ref, tol, what):
+    """Asserts the per-row and per-column bound on lines of >= LINE_MIN_LEN
+    elements (rows when there are that many columns, and vice versa)."""
+    row, col = line_errors(U - ref, ref)
+    rows, cols = ref.shape
+    if cols >= LINE_MIN_LEN:
+        assert row <= LINE_FACTOR * tol, f"{what}: worst row error {row:.3e} > {LINE_FACTOR * tol:.1e}"
+    if rows >= LINE_MIN_LEN:
+        assert col <= LINE_FACTOR * tol, f"{what}: worst column error {col:.3e} > {LINE_FACTOR * tol:.1e}"
+    return row, col
 
 
 def to_device(stored):
@@ -48,7 +79,7 @@ def device_state(Ws, Gs, Bs):
 
 
 def run_and_compare(plan, Ws, Gs, Bs, dtype, *, lr=0.02, beta=0.95, wd=0.01, ns_steps=5,
-                    coeffs=None, check=None, tol=None):
+                    coeffs=None, check=None, tol=None, nesterov=True):
     """One GPU step through the C ABI vs the oracle on the same stored inputs.
 
     check: indices of matrices to compare (default all).  Returns per-matrix errors."""
@@ -66,7 +97,7 @@ def run_and_compare(plan, Ws, Gs, Bs, dtype, *, lr=0.02, beta=0.95, wd=0.01, ns_
     errs = []
     for i in idx:
         ref = O.muon_step_ref(Ws[i].value, Gs[i].value, Bs[i].value, lr=lr, beta=beta, wd=wd,
-                              ns_steps=ns_steps, coeffs=co, param_dtype=dtype)
+                              ns_steps=ns_steps, coeffs=co, param_dtype=dtype, nesterov=nesterov)
         U = cap[i].cpu().numpy().astype(np.float64)
         e_u = rel(U, ref["U"])
         e_buf = rel(to_f64(M[i]), ref["buf_new"])
@@ -75,6 +106,7 @@ def run_and_compare(plan, Ws, Gs, Bs, dtype, *, lr=0.02, beta=0.95, wd=0.01, ns_
         errs.append({"i": i, "err_U": e_u, "err_buf": e_buf, "err_dW": e_dw})
         assert np.all(np.isfinite(U)), f"matrix {i}: non-finite update"
         assert e_u <= tol, f"matrix {i} {Ws[i].value.shape}: rel err of U {e_u:.3e} > {tol}"
+        check_lines(U, ref["U"], tol, f"matrix {i} {Ws[i].value.shape}")
         assert e_buf <= 1e-6, f"matrix {i}: momentum rel err {e_buf:.3e}"
         # the stored weights are W + U rounded to the parameter dtype: allow the error of U
         # plus twice the rounding floor that the oracle's own rounding of W + U shows

@@ -60,6 +60,18 @@ def test_solver_beats_greedy_on_the_classic_case():
     assert optimal and span == 6.0
 
 
+def test_count_dp_equals_brute_force():
+    # the exact check used on the large sets, pinned to brute force on tiny
+    # instances with repeated costs
+    rng = random.Random(5)
+    for trial in range(80):
+        k = rng.randint(1, 3)
+        pool = [rng.choice([1.0, 2.5, 3.0, 4.25, 7.0]) for _ in range(3)]
+        costs = [rng.choice(pool) for _ in range(rng.randint(0, 8))]
+        want, _ = A.best_makespan(costs, k)
+        assert A.best_makespan_by_counts(costs, k) == pytest.approx(want, rel=1e-12, abs=0)
+
+
 def test_budget_exhausted_keeps_the_greedy_guarantee():
     # with a one-node budget the result is the LPT schedule improved by local moves:
     # never worse than LPT's bound (4/3 - 1/(3k)) * optimum
@@ -85,10 +97,14 @@ def test_large_matrix_sets_are_balanced():
         _check_valid(costs, owner, 8, span)
         lower = max(max(costs), sum(costs) / 8)
         assert span >= lower * (1 - 1e-12)
-        # many similar items: within 5% of the lower bound, unless the schedule is
-        # proven optimal (the 16 transformer-block matrices come in 3-4 costs over
-        # 8 owners: two per owner, and the bound itself may be out of reach)
-        assert span <= 1.05 * lower or optimal, (cfg, span, lower)
+        # many similar items: within 5% of the lower bound; where the bound is out
+        # of reach (the 16 transformer-block matrices come in 3-4 costs over 8
+        # owners), equal to the exact optimum of the dynamic program over counts
+        # of equal-cost matrices (independent of the solver's own optimality flag)
+        if span > 1.05 * lower:
+            exact = A.best_makespan_by_counts(costs, 8)
+            assert exact is not None, (cfg, "too many distinct costs for the exact check")
+            assert abs(span - exact) <= 1e-9 * exact, (cfg, span, exact)
         # deterministic
         assert M.assign_owners(costs, 8) == (owner, span, optimal)
 

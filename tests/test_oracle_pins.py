@@ -161,6 +161,19 @@ def test_momentum_closed_form():
         assert np.max(np.abs(d - (gs[k] + beta * closed))) < 1e-13
 
 
+def test_plain_momentum_closed_form():
+    """Plain momentum from zero: buf_k = d_k = sum_j beta^(k-j) g_j (no Nesterov look-ahead)."""
+    rng = np.random.default_rng(42)
+    beta = 0.9
+    gs = [rng.standard_normal((5, 7)) for _ in range(4)]
+    buf = np.zeros((5, 7))
+    for k, g in enumerate(gs):
+        buf, d = O.plain_momentum(buf, g, beta)
+        closed = sum(beta ** (k - j) * gs[j] for j in range(k + 1))
+        assert np.allclose(buf, closed, rtol=1e-14, atol=1e-14)
+        assert np.array_equal(d, buf)
+
+
 def test_nesterov_ema_variant_gives_same_update():
     """Reading of 'momentum-based update': the EMA form differs only by (1-beta),
     which the Frobenius normalization removes (up to eps)."""
@@ -302,3 +315,12 @@ def test_whole_step_equals_closed_form_on_shared_singular_vectors(shape, form):
     assert _rel(r["X"], X) < 1e-11
     assert _rel(r["U"], U) < 1e-11
     assert _rel(r["W_new"], W + U) < 1e-14
+    # plain momentum: the direction is the new buffer itself, P diag(gam + beta mu) Q^T
+    rp = O.muon_step_ref(W, g, buf, lr=lr, beta=beta, wd=wd, ns_steps=T, eps=eps, form=form,
+                         nesterov=False)
+    dp = gam + beta * mu
+    sp = np.abs(dp) / (np.sqrt(np.sum(dp ** 2)) + eps)
+    Xp = (P * (_phi_scalar(sp, O.coeff_schedule(O.QUINTIC, T)) * np.sign(dp))) @ Q.T
+    assert abs(rp["nu"] - np.sqrt(np.sum(dp ** 2))) <= 1e-14 * rp["nu"]
+    assert _rel(rp["U"], -lr * (wd * W + s * Xp)) < 1e-11
+    assert _rel(rp["buf_new"], beta * buf + g) < 1e-14

@@ -55,6 +55,20 @@ def test_ragged_mixed_shapes_one_plan(M, dtype):
     run_and_compare(plan, Ws, Gs, Bs, dtype)
 
 
+@pytest.mark.parametrize("form", ["direct", "gram"])
+@pytest.mark.parametrize("dtype", [WL.F32, WL.BF16])
+def test_plain_momentum_option(M, dtype, form):
+    """nesterov=False orthogonalizes the momentum buffer itself (nonzero
+    incoming buffers), with NS and with ns_steps = 0 (X_T = X0)."""
+    from gpu_util import make_state, run_and_compare
+    shapes = [(100, 300), (300, 100), (129, 257), (513, 77), (256, 640)]
+    Ws, Gs, Bs = make_state(shapes, dtype, seed=21, buf_scale=0.01)
+    plan = _plan(M, shapes, dtype, nesterov=False, form=form)
+    run_and_compare(plan, Ws, Gs, Bs, dtype, nesterov=False)
+    Ws2, Gs2, _ = make_state(shapes, dtype, seed=22)
+    run_and_compare(plan, Ws2, Gs2, Bs, dtype, nesterov=False, ns_steps=0)
+
+
 @pytest.mark.parametrize("dtype", [WL.F32, WL.BF16])
 def test_gram_form_matches_oracle(M, dtype):
     from gpu_util import make_state, run_and_compare
