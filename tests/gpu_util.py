@@ -9,10 +9,13 @@ from oracle import muon_oracle as O
 REL_TOL = {WL.F32: 1e-4, WL.BF16: 2e-2}
 # A row or column of U may carry at most this multiple of the Frobenius
 # tolerance, measured as the norm of the line's error over max(the line's own
-# norm, the RMS norm of all lines).  Rounding spreads the error evenly over a
-# line of >= 256 elements (its relative spread is ~1/sqrt(2 L) < 5%), while a
-# wrong row, column or strip has a line error near 1.
-LINE_FACTOR = 2.5
+# norm, the RMS norm of all lines).  With Gaussian inputs bf16 rounding gives
+# worst lines within about 2x the Frobenius error; heavy-tailed (Student-t)
+# gradients concentrate it on the lines that carry the outliers, up to about
+# 5x (0.05 on a 512 x 512 matrix, which a numpy model of the bf16 operand
+# rounding reproduces: tests/test_line_check_cpu.py).  A wrong row, column or
+# strip has a line error near 1, ten times the bound.
+LINE_FACTOR = 5.0
 LINE_MIN_LEN = 256
 
 
