@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define MUON_ABI_VERSION 10
+#define MUON_ABI_VERSION 11
 
 typedef enum muon_status {
   MUON_OK = 0,
@@ -386,6 +386,41 @@ int muon_plan_set_graph(muon_plan* plan, int enable);
  */
 int muon_probe_mfma_bf16(int iters, double* tflops, double* flops);
 int muon_probe_hbm_copy(void* dst, const void* src, uint64_t bytes, int reps, double* gbs);
+
+/*
+ * One Muon step of ONE matrix that allocates no device memory, for callers
+ * that cannot call hipMalloc (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  The same update as muon_step on
+ * that matrix, with a fixed configuration instead of a plan: direct NS form,
+ * 128 x 128 tiles for every product (on the bf16 path the m x n product reads
+ * X k-major, as tile plan 5 does), no timing, no lanes.  The workspace, the
+ * norm partials, the scale, the matrix descriptor and the work-item lists live
+ * in one static device array of 64 MiB per device that the library holds
+ * until the process ends; a call enqueues kernels only (a set-up kernel writes
+ * the tables into that array), so it can be captured into a graph.
+ *   desc      host; rows, cols >= 1, dtype MUON_F32 or MUON_BF16, reserved 0
+ *   opts      host, nullable (defaults); nesterov, eps and rms_scale are used;
+ *             form GRAM or precision other than AUTO: EUNSUPPORTED; the other
+ *             fields are ignored
+ *   param     device, rows x cols row-major in desc.dtype, updated in place
+ *   grad      device, same shape and dtype, read only
+ *   momentum  device, rows x cols fp32, updated in place
+ *   coeffs    host, (a, b, c) used at every NS step; NULL: the quintic
+ * Size limit: with m = min(rows, cols) and n = max(rows, cols) each rounded up
+ * to 128, the workspace 4 (m n + m m) bytes (bf16) or 12 m n + 8 m m bytes
+ * (fp32), plus under 0.3 MiB of tables, must fit 64 MiB (e.g. bf16 2048 x
+ * 4096 or 1024 x 8192; fp32 1024 x 4096); larger: ENOMEM, nothing enqueued.
+ * Every call on a device uses that device's one array and leaves its contents
+ * there: calls that overlap on one device (different streams, unordered
+ * threads) race; calls in order on one stream are safe.  No non-finite flag is
+ * reported.  Errors: EINVAL (NULL pointer, ns_steps outside [0, 64],
+ * non-finite scalar or coefficient, opts.struct_size), EUNSUPPORTED (dtype,
+ * zero or over-large size, no gfx950 device, form / precision), ENOMEM (over
+ * the array), EHIP (symbol lookup or launch error).
+ */
+int muon_step_noalloc(const muon_matrix_desc* desc, const muon_plan_opts* opts, void* param,
+                      const void* grad, float* momentum, float lr, float beta, float wd,
+                      int ns_steps, const float* coeffs, void* stream);
 
 /* MUON_ABI_VERSION of the library. */
 int muon_abi_version(void);

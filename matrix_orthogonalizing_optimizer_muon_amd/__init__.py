@@ -15,7 +15,7 @@ from . import _lib as L
 from ._lib import MuonError  # noqa: F401
 
 __all__ = ["MuonPlan", "AdamWPlan", "MuonError", "library_path", "assign_owners",
-           "probe_mfma_bf16", "probe_hbm_copy"]
+           "probe_mfma_bf16", "probe_hbm_copy", "step_noalloc"]
 
 
 def library_path():
@@ -249,6 +249,41 @@ class MuonPlan:
                  "launches": arr[k].launches,
                  "total_ms": arr[k].total_ms, "flops": arr[k].flops, "bytes": arr[k].bytes}
                 for k in range(n.value)]
+
+
+def step_noalloc(param, grad, momentum, *, lr=0.02, beta=0.95, wd=0.01, ns_steps=5, coeffs=None,
+                 nesterov=True, eps=1e-7, rms_scale=0.2, stream=None):
+    """One Muon step of one matrix through muon_step_noalloc: no plan and no
+    device allocation (the library's fixed per-device scratch array holds the
+    workspace).  param / grad: 2-D contiguous fp32 or bf16 tensors of one
+    dtype on the GPU; momentum: fp32 of the same shape."""
+    import torch
+    if param.dim() != 2 or grad.shape != param.shape or momentum.shape != param.shape:
+        raise ValueError("param, grad and momentum must be 2-D tensors of one shape")
+    if param.dtype not in (torch.float32, torch.bfloat16) or grad.dtype != param.dtype:
+        raise ValueError("param and grad must share dtype float32 or bfloat16")
+    if momentum.dtype != torch.float32:
+        raise ValueError("momentum must be float32")
+    for name, t in (("param", param), ("grad", grad), ("momentum", momentum)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+        if t.device != param.device:
+            raise ValueError(f"{name} is on {t.device}, param on {param.device}")
+    desc = L.MatrixDesc(int(param.shape[0]), int(param.shape[1]),
+                        L.MUON_F32 if param.dtype == torch.float32 else L.MUON_BF16, 0)
+    opts = L.PlanOpts()
+    L.check(L.lib().muon_plan_opts_default(ctypes.byref(opts)))
+    opts.nesterov = 1 if nesterov else 0
+    opts.eps = eps
+    opts.rms_scale = rms_scale
+    co = None
+    if coeffs is not None:
+        co = (ctypes.c_float * 3)(*[float(x) for x in coeffs])
+    L.check(L.lib().muon_step_noalloc(ctypes.byref(desc), ctypes.byref(opts),
+                                      ctypes.c_void_p(param.data_ptr()), ctypes.c_void_p(grad.data_ptr()),
+                                      ctypes.c_void_p(momentum.data_ptr()), float(lr), float(beta),
+                                      float(wd), int(ns_steps), co,
+                                      MuonPlan._stream(stream, param.device)))
 
 
 def assign_owners(costs, n_owners, node_limit=0):

@@ -103,6 +103,10 @@ PROTOTYPES = {
                                            ctypes.c_int, ctypes.POINTER(ctypes.c_double)]),
     "muon_plan_matrix_cost": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int,
                                              ctypes.POINTER(ctypes.c_double)]),
+    "muon_step_noalloc": (ctypes.c_int, [ctypes.POINTER(MatrixDesc), ctypes.POINTER(PlanOpts),
+                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_int,
+                                         _FP, ctypes.c_void_p]),
     "muon_assign_owners": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double), ctypes.c_int, ctypes.c_int,
                                           ctypes.c_int64, ctypes.POINTER(ctypes.c_int32),
                                           ctypes.POINTER(ctypes.c_double),

@@ -43,7 +43,7 @@ def build(verbose: bool = False) -> str:
     hipcc = _hipcc()
     with tempfile.TemporaryDirectory(prefix="muon_build_") as tmp:
         objs = []
-        for src, kind in (("kernels.hip", "hip"), ("probe.hip", "hip"), ("abi.cpp", "hip"),
+        for src, kind in (("kernels.hip", "hip"), ("probe.hip", "hip"), ("noalloc.hip", "hip"), ("abi.cpp", "hip"),
                           ("plan.cpp", "host"), ("assign.cpp", "host")):
             obj = os.path.join(tmp, src + ".o")
             path = os.path.join(CSRC, src)

@@ -11,6 +11,7 @@
 #include <vector>
 
 #include "muon.h"
+#include "errors.hpp"
 #include "kernels.hpp"
 #include "probe.hpp"
 #include "assign.hpp"
@@ -26,6 +27,12 @@ int fail(int code, const std::string& msg) {
   g_err = msg;
   return code;
 }
+
+}  // namespace
+
+int muon::report_error(int code, const std::string& msg) { return fail(code, msg); }
+
+namespace {
 
 #define HIP_TRY(x)                                                                        \
   do {                                                                                    \
