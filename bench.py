@@ -71,11 +71,13 @@ def parse():
 
 
 def source_digest():
-    """sha256 of the kernel sources: a recorded traffic figure is only valid for them."""
+    """sha256 of the kernel sources and of the planner (whose work-item order
+    sets how much a launch re-reads): a recorded traffic figure is only valid
+    for them."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "matrix_orthogonalizing_optimizer_muon_amd", "csrc")
-    for f in ("kernels.hip", "mfma_nt.hpp", "kernels.hpp"):
+    for f in ("kernels.hip", "mfma_nt.hpp", "kernels.hpp", "plan.cpp"):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
