@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--adamw", action="store_true",
                     help="time the fused AdamW step over the non-matrix parameters of the "
                          "4-layer d=1024 transformer model (vocab 32000 embedding and classifier, norms)")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="time torch.matmul (hipBLASLt) on the workload's NS product shapes with random "
+                         "bf16 operands, batched per shape as the library batches them")
     ap.add_argument("--owners", type=int, default=1,
                     help="assign the workload's matrices to this many owners (makespan-balanced) "
                          "and time one owner's share")
@@ -383,6 +386,47 @@ def bench_adamw(args, torch, MU):
     plan.close()
 
 
+def bench_vendor_gemm(args, wl, torch):
+    """Reference rates of the vendor GEMM (torch.matmul on ROCm, hipBLASLt) for
+    the products of one NS step of the workload, per canonical shape: X X^T
+    (m x n times n x m; the full product, the library computes the upper
+    triangle), A A (m x m times m x m) and B X (m x m times m x n), batched
+    over the matrices of that shape, random N(0, 1) bf16 operands, both operands
+    contiguous.  Flops counted as issued by the vendor product (2 m n k)."""
+    shapes = {}
+    for r, c in wl.shapes:
+        shapes.setdefault((min(r, c), max(r, c)), 0)
+        shapes[(min(r, c), max(r, c))] += 1
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(7)
+    out = []
+    for (m, n), count in sorted(shapes.items()):
+        batch = min(count, 32)
+        X = torch.randn(batch, m, n, device="cuda", generator=gen).to(torch.bfloat16)
+        Xt = X.transpose(1, 2).contiguous()
+        A = torch.randn(batch, m, m, device="cuda", generator=gen).to(torch.bfloat16)
+        prods = (("X X^T", X, Xt, 2.0 * m * m * n), ("A A", A, A, 2.0 * m * m * m), ("B X", A, X, 2.0 * m * m * n))
+        for name, p, q, fl in prods:
+            for _ in range(3):
+                torch.matmul(p, q)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = 10
+            e0.record()
+            for _ in range(reps):
+                torch.matmul(p, q)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            out.append({"shape": f"{m}x{n}", "product": name, "batch": batch, "ms": round(ms, 4),
+                        "tflops": round(batch * fl / (ms * 1e-3) / 1e12, 1)})
+        del X, Xt, A
+        torch.cuda.empty_cache()
+    print(json.dumps({"metric": "vendor GEMM reference (torch.matmul / hipBLASLt), TFLOP/s",
+                      "workload": wl.name, "operands": "random N(0,1) bf16, contiguous",
+                      "products": out}))
+
+
 def owner_share(args, wl, MU):
     """The matrices one owner gets when the workload is balanced over
     args.owners owners by estimated step time (plan costs, muon_assign_owners)."""
@@ -423,6 +467,9 @@ def main():
     torch.cuda.init()
     if args.adamw:
         bench_adamw(args, torch, MU)
+        return
+    if args.vendor_gemm:
+        bench_vendor_gemm(args, wl, torch)
         return
     os.makedirs(os.path.dirname(args.cache), exist_ok=True)
     owner_info = None
@@ -513,15 +560,19 @@ def main():
     if not args.no_ceilings:
         mfma_tf, _ = MU.probe_mfma_bf16(iters=100000)              # about 17 ms
         mfma_sus, _ = MU.probe_mfma_bf16(iters=1000000)            # about 170 ms
+        mfma_rnd, _ = MU.probe_mfma_bf16(iters=1000000, random_operands=True)
         a = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
         b = torch.empty_like(a)
         copy_gbs = MU.probe_hbm_copy(b, a, reps=10)
         del a, b
         ceil = {"mfma_bf16_tflops": round(mfma_tf, 1), "mfma_bf16_tflops_sustained": round(mfma_sus, 1),
+                "mfma_bf16_tflops_random_operands": round(mfma_rnd, 1),
                 "hbm_copy_gbs": round(copy_gbs, 1),
                 "how": "muon_probe_mfma_bf16 (2 blocks of 4 waves per CU, 4 independent "
                        "32x32x16 bf16 MFMA chains per wave, no memory traffic; 1e5 and 1e6 "
-                       "rounds) and muon_probe_hbm_copy (1 GiB copy, read + written bytes, "
+                       "rounds; and 1e6 rounds with eight random operand pairs per wave, "
+                       "muon_probe_mfma_bf16_random, the switching activity of real data "
+                       "under the part's power limit) and muon_probe_hbm_copy (1 GiB copy, read + written bytes, "
                        "best of 8 launch variants)"}
     ns_flops = info["ns_flops_min"]
     bf16 = wl.dtype == "bf16"
@@ -559,6 +610,8 @@ def main():
                     "lanes": info["n_lanes"]}
         if ceil and bf16:
             roofline["frac_of_measured_mfma"] = round(ach / ceil["mfma_bf16_tflops"], 4)
+            roofline["frac_of_measured_mfma_random_operands"] = round(
+                ach / ceil["mfma_bf16_tflops_random_operands"], 4)
     # every NS kernel instance against the same peak (profiling pass, per launch)
     ns_rooflines = []
     for n, d in sorted(ns_kern.items(), key=lambda kv: -kv[1]["total_ms"]):

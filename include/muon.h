@@ -385,6 +385,12 @@ int muon_plan_set_graph(muon_plan* plan, int enable);
  * EHIP: launch error.
  */
 int muon_probe_mfma_bf16(int iters, double* tflops, double* flops);
+/* As muon_probe_mfma_bf16, but each MFMA of a round of eight takes another of
+ * eight pairs of random bf16 register operands (random signs and mantissas):
+ * the switching activity of real data.  The part is power-limited under dense
+ * MFMA load, so this rate, not the fixed-operand one, is the ceiling a
+ * contraction on random data is read against. */
+int muon_probe_mfma_bf16_random(int iters, double* tflops, double* flops);
 int muon_probe_hbm_copy(void* dst, const void* src, uint64_t bytes, int reps, double* gbs);
 
 /*

@@ -300,13 +300,15 @@ def assign_owners(costs, n_owners, node_limit=0):
     return [out[i] for i in range(n)], span.value, bool(opt.value)
 
 
-def probe_mfma_bf16(iters=20000):
-    """Measured dense bf16 MFMA rate of the current device (muon_probe_mfma_bf16).
+def probe_mfma_bf16(iters=20000, random_operands=False):
+    """Measured dense bf16 MFMA rate of the current device (muon_probe_mfma_bf16,
+    or muon_probe_mfma_bf16_random with random register operands).
 
     Returns (TFLOP/s, flop count of the timed launch)."""
     tf = ctypes.c_double()
     fl = ctypes.c_double()
-    L.check(L.lib().muon_probe_mfma_bf16(int(iters), ctypes.byref(tf), ctypes.byref(fl)))
+    fn = L.lib().muon_probe_mfma_bf16_random if random_operands else L.lib().muon_probe_mfma_bf16
+    L.check(fn(int(iters), ctypes.byref(tf), ctypes.byref(fl)))
     return tf.value, fl.value
 
 

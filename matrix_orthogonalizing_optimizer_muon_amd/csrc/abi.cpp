@@ -1055,7 +1055,7 @@ int device_cus(int* cus) {
 
 }  // namespace
 
-int muon_probe_mfma_bf16(int iters, double* tflops, double* flops) {
+static int probe_mfma(int iters, bool random_operands, double* tflops, double* flops) {
   if (iters < 1 || iters > (1 << 24) || !tflops) return fail(MUON_EINVAL, "iters out of [1, 2^24] or NULL tflops");
   int cus = 0, rc;
   if ((rc = device_cus(&cus))) return rc;
@@ -1063,9 +1063,9 @@ int muon_probe_mfma_bf16(int iters, double* tflops, double* flops) {
   ProbeRun r;
   if ((rc = r.init())) return rc;
   HIP_TRY(hipMalloc(&r.out, (size_t)blocks * 256 * sizeof(float)));
-  HIP_TRY(launch_probe_mfma(blocks, iters, r.out, r.s));   // warm-up: clocks settle
+  HIP_TRY(launch_probe_mfma(blocks, iters, random_operands, r.out, r.s));   // warm-up: clocks settle
   HIP_TRY(hipEventRecord(r.e0, r.s));
-  HIP_TRY(launch_probe_mfma(blocks, iters, r.out, r.s));
+  HIP_TRY(launch_probe_mfma(blocks, iters, random_operands, r.out, r.s));
   HIP_TRY(hipEventRecord(r.e1, r.s));
   double ms = 0;
   if ((rc = r.elapsed(&ms))) return rc;
@@ -1073,6 +1073,14 @@ int muon_probe_mfma_bf16(int iters, double* tflops, double* flops) {
   if (flops) *flops = fl;
   *tflops = ms > 0 ? fl / (ms * 1e-3) / 1e12 : 0.0;
   return MUON_OK;
+}
+
+int muon_probe_mfma_bf16(int iters, double* tflops, double* flops) {
+  return probe_mfma(iters, false, tflops, flops);
+}
+
+int muon_probe_mfma_bf16_random(int iters, double* tflops, double* flops) {
+  return probe_mfma(iters, true, tflops, flops);
 }
 
 int muon_probe_hbm_copy(void* dst, const void* src, uint64_t bytes, int reps, double* gbs) {

@@ -14,23 +14,60 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 namespace {
 
+// One bf16 operand value from a hash of (thread, index): random sign and
+// 7-bit mantissa, magnitude in [2^-7, 2^-5), so every multiplier input bit
+// toggles between consecutive MFMAs as it does on real data.
+__device__ __forceinline__ __bf16 probe_rand_bf16(uint32_t key) {
+  key ^= key >> 16;
+  key *= 0x7feb352du;
+  key ^= key >> 15;
+  key *= 0x846ca68bu;
+  key ^= key >> 16;
+  const uint16_t bits = (uint16_t)((key & 0x8000u) | ((120u + ((key >> 8) & 1u)) << 7) | (key & 0x7fu));
+  return __builtin_bit_cast(__bf16, bits);
+}
+
+// RAND = false: every MFMA of a wave takes the same register operands.
+// RAND = true: eight operand pairs of random values, a different pair for
+// each MFMA of a round of eight (the register file still feeds them, no
+// memory traffic), which is the switching activity of random data.
+template <bool RAND>
 __global__ __launch_bounds__(256) void k_probe_mfma(int iters, float* __restrict__ out) {
   const int lane = threadIdx.x & 63;
-  bf16x8_t a, b;
+  constexpr int NOP = RAND ? 8 : 1;
+  bf16x8_t a[NOP], b[NOP];
+  const uint32_t tid = blockIdx.x * blockDim.x + threadIdx.x;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    a[e] = (__bf16)(0.001f * (float)(lane + e));
-    b[e] = (__bf16)(0.002f * (float)(lane - e));
-  }
+  for (int k = 0; k < NOP; ++k)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if constexpr (RAND) {
+        a[k][e] = probe_rand_bf16(tid * 131u + (uint32_t)(k * 8 + e) * 2u);
+        b[k][e] = probe_rand_bf16(tid * 131u + (uint32_t)(k * 8 + e) * 2u + 1u);
+      } else {
+        a[k][e] = (__bf16)(0.001f * (float)(lane + e));
+        b[k][e] = (__bf16)(0.002f * (float)(lane - e));
+      }
+    }
   f32x16_t acc[kProbeChains];
 #pragma unroll
   for (int c = 0; c < kProbeChains; ++c)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[c][r] = 0.f;
-  for (int i = 0; i < iters; ++i) {
+  int i = 0;
+  if constexpr (RAND) {
+    for (; i + 8 <= iters; i += 8) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int c = 0; c < kProbeChains; ++c)
+          acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[(j + c) % 8], b[(j + 3 * c + 1) % 8], acc[c], 0, 0, 0);
+    }
+  }
+  for (; i < iters; ++i) {
 #pragma unroll
     for (int c = 0; c < kProbeChains; ++c)
-      acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
+      acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], b[0], acc[c], 0, 0, 0);
   }
   float sum = 0.f;
 #pragma unroll
@@ -86,8 +123,11 @@ __global__ __launch_bounds__(256) void k_probe_copy_runs(const u32x4_t* __restri
 
 }  // namespace
 
-hipError_t launch_probe_mfma(int blocks, int iters, float* out, hipStream_t s) {
-  hipLaunchKernelGGL(k_probe_mfma, dim3((unsigned)blocks), dim3(256), 0, s, iters, out);
+hipError_t launch_probe_mfma(int blocks, int iters, bool random_operands, float* out, hipStream_t s) {
+  if (random_operands)
+    hipLaunchKernelGGL(k_probe_mfma<true>, dim3((unsigned)blocks), dim3(256), 0, s, iters, out);
+  else
+    hipLaunchKernelGGL(k_probe_mfma<false>, dim3((unsigned)blocks), dim3(256), 0, s, iters, out);
   return hipGetLastError();
 }
 

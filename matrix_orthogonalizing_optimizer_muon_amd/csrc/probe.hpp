@@ -9,8 +9,10 @@ namespace muon {
 // k_probe_mfma: `blocks` blocks of 4 waves; every wave runs `iters` rounds of
 // kProbeChains independent v_mfma_f32_32x32x16_bf16 accumulations with no
 // memory traffic, then stores one float per thread into out (blocks * 256).
+// random_operands: each MFMA takes another of eight random register operand
+// pairs (real data's switching activity) instead of the same pair.
 constexpr int kProbeChains = 4;
-hipError_t launch_probe_mfma(int blocks, int iters, float* out, hipStream_t s);
+hipError_t launch_probe_mfma(int blocks, int iters, bool random_operands, float* out, hipStream_t s);
 // k_probe_copy: dst[i] = src[i] for n16 16-byte words (grid-stride, `blocks`
 // blocks of 256 threads, 4 words in flight per thread), plain or nontemporal
 // loads and stores; blocks <= 0: one block per contiguous 1024-word run.

@@ -24,6 +24,18 @@ def test_mfma_probe_rate_is_physical(M):
     assert 0.2 * PEAK_BF16_TFLOPS < tflops <= 1.02 * PEAK_BF16_TFLOPS
 
 
+def test_mfma_probe_with_random_operands(M):
+    # the same flop count; random operands switch more bits, so under the
+    # part's power limit the rate is no higher than with fixed operands
+    fixed, _ = M.probe_mfma_bf16(iters=40000)
+    rnd, flops = M.probe_mfma_bf16(iters=40000, random_operands=True)
+    print(f"mfma probe: fixed operands {fixed:.1f}, random operands {rnd:.1f} TFLOP/s", flush=True)
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert flops == 2 * cus * 4 * 40000 * 4 * 32768
+    assert 0.2 * PEAK_BF16_TFLOPS < rnd <= 1.05 * fixed
+
+
 def test_hbm_copy_probe_copies_and_rate_is_physical(M):
     import torch
     n = (1 << 30) // 4 + 4   # 1 GiB + 16 bytes: the grid-stride tail runs too
