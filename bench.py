@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--form", default="auto", choices=["auto", "direct", "gram"])
     ap.add_argument("--tile", type=int, default=None, help="force a tile plan (0..9)")
     ap.add_argument("--lanes", type=int, default=None, help="force the NS lane count (1..4)")
+    ap.add_argument("--workspace-cap-gib", type=float, default=0,
+                    help="plan workspace cap in GiB (0: the library default)")
     ap.add_argument("--adamw", action="store_true",
                     help="time the fused AdamW step over the non-matrix parameters of the "
                          "4-layer d=1024 transformer model (vocab 32000 embedding and classifier, norms)")
@@ -477,7 +479,7 @@ def main():
         wl, owner_info = owner_share(args, wl, MU)
     t0 = time.perf_counter()
     plan = MU.MuonPlan(wl.shapes, wl.dtype, tune=args.tune, cache_path=args.cache, form=args.form,
-                       tile=args.tile, lanes=args.lanes)
+                       tile=args.tile, lanes=args.lanes, workspace_cap=int(args.workspace_cap_gib * (1 << 30)))
     plan_s = time.perf_counter() - t0
     info = plan.info()
     choices = {}

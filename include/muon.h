@@ -112,7 +112,7 @@ typedef struct muon_plan_opts {
                                    to their own streams (forked from and joined back into the
                                    caller's stream).  0 (default): 1, or the count the
                                    whole-set timing picks when tuning; 1..4: forced */
-  uint64_t workspace_cap_bytes; /* 0: default (48 GiB).  Matrices are processed in chunks
+  uint64_t workspace_cap_bytes; /* 0: default (96 GiB).  Matrices are processed in chunks
                                    whose workspace fits the cap; one matrix over it: ENOMEM */
   const char* cache_path;       /* tune cache file; NULL: $MUON_TUNE_CACHE, else no cache */
 } muon_plan_opts;

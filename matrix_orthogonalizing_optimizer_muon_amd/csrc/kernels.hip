@@ -79,6 +79,16 @@ __device__ __forceinline__ void store1(void* base, int dt, int64_t off, float v)
   else static_cast<float*>(base)[off] = v;
 }
 
+// Workgroup barrier for LDS traffic only: this wave's LDS accesses complete
+// (lgkmcnt(0)), then s_barrier.  __syncthreads() would also wait for every
+// outstanding global access of the wave (vmcnt(0)), draining the global
+// stores just issued at each barrier; no wave of these kernels reads global
+// memory that another wave of its block writes.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(nt::kWaitLgkm0);
+  nt::block_barrier();
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
@@ -219,7 +229,7 @@ __global__ __launch_bounds__(256) void k_ew_momentum(
       for (int k = 0; k < 4; ++k)
 #pragma unroll
         for (int e = 0; e < 4; ++e) tT[cq + e][rq + 16 * k] = dv[k][e];
-      __syncthreads();
+      lds_barrier();
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         float o[4];
@@ -230,9 +240,9 @@ __global__ __launch_bounds__(256) void k_ew_momentum(
     }
     ss = wave_sum(ss);
     if ((tid & 63) == 0) red[tid >> 6] = ss;
-    __syncthreads();
+    lds_barrier();
     if (tid == 0) partials[t] = (red[0] + red[1]) + (red[2] + red[3]);
-    __syncthreads();
+    lds_barrier();   // red and tT are reused by the next tile
   }
 }
 
@@ -391,12 +401,12 @@ __global__ __launch_bounds__(256) void k_ew_apply(
 #pragma unroll
         for (int e = 0; e < 4; ++e) tT[rq + 16 * k][cq + e] = o[e];
       }
-      __syncthreads();
+      lds_barrier();
 #pragma unroll
       for (int k = 0; k < 4; ++k)
 #pragma unroll
         for (int e = 0; e < 4; ++e) x[k][e] = tT[cq + e][rq + 16 * k];
-      __syncthreads();
+      lds_barrier();
       sr0 = j0;
       sc0 = i0;
     }
@@ -941,7 +951,7 @@ __device__ __forceinline__ void nt_epilogue(const nt::f32x16_t (&acc)[BM / 32 / 
       constexpr int PB = bf16_pitch<BN>();
       constexpr int TPR = BN / 8, RPP = NT / TPR;
       MUON_LDS uint16_t* Cb = reinterpret_cast<MUON_LDS uint16_t*>(C);
-      __syncthreads();   // every wave is done with the main loop's LDS
+      lds_barrier();   // every wave is done with the main loop's LDS
 #pragma unroll
       for (int a = 0; a < G::MT; ++a) {
         const int r = wy * G::WM + a * 32 + (lane & 31), i = m0 + r;
@@ -963,7 +973,7 @@ __device__ __forceinline__ void nt_epilogue(const nt::f32x16_t (&acc)[BM / 32 / 
             *(MUON_LDS u32x2_t*)(Cb + r * PB + c) = u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
           }
       }
-      __syncthreads();
+      lds_barrier();
       const int cc = (tid % TPR) * 8;
 #pragma unroll 4
       for (int r = tid / TPR; r < BM; r += RPP)
@@ -972,7 +982,7 @@ __device__ __forceinline__ void nt_epilogue(const nt::f32x16_t (&acc)[BM / 32 / 
       return;
     }
   }
-  __syncthreads();   // every wave is done with the main loop's LDS
+  lds_barrier();   // every wave is done with the main loop's LDS
 #pragma unroll 1
   for (int s0 = 0; s0 < BM; s0 += SH) {
     // lane l holds row l % 32 of each MFMA tile, 4 consecutive columns per
@@ -992,7 +1002,7 @@ __device__ __forceinline__ void nt_epilogue(const nt::f32x16_t (&acc)[BM / 32 / 
               nt::f32x4_t{acc[a][b][4 * g], acc[a][b][4 * g + 1], acc[a][b][4 * g + 2], acc[a][b][4 * g + 3]};
         }
     }
-    __syncthreads();
+    lds_barrier();
     // row pass: this thread's SH / RPP rows, 8 columns each; Cin for all of
     // them (or, for an update applied here, the bf16 W rows) is requested
     // before any is used
@@ -1049,7 +1059,7 @@ __device__ __forceinline__ void nt_epilogue(const nt::f32x16_t (&acc)[BM / 32 / 
       }
     }
     if (colpass) {
-      __syncthreads();
+      lds_barrier();
       // every thread takes CI (column, 8-row group) items
       constexpr int CI = BN * (SH / 8) / NT;
       static_assert(BN * (SH / 8) % NT == 0 && CI % 2 == 0, "column items per thread");
@@ -1091,7 +1101,7 @@ __device__ __forceinline__ void nt_epilogue(const nt::f32x16_t (&acc)[BM / 32 / 
         for (int ci = 0; ci < CI; ++ci) item(ci, false, u32x4_t{0, 0, 0, 0});
       }
     }
-    __syncthreads();   // the slab buffer is reused
+    lds_barrier();   // the slab buffer is reused
   }
 }
 

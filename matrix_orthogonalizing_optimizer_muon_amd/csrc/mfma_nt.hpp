@@ -48,6 +48,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 constexpr int waitcnt_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | 0x70 | 0xF00; }
 static_assert(waitcnt_vm(0) == 0xF70, "encoding");
 constexpr int kWaitVmLgkm0 = 0x0070;   // vmcnt(0) lgkmcnt(0)
+constexpr int kWaitLgkm0 = 0xC07F;     // lgkmcnt(0) only (vmcnt 63, expcnt 7 leave them be)
+static_assert((waitcnt_vm(63) & ~0x0F00) == kWaitLgkm0, "encoding");
 
 // BM x BN output tile, BK bf16 per k-tile (32 or 64), S LDS stages, a WGM x WGN
 // grid of waves (each owns a (BM/WGM) x (BN/WGN) tile).

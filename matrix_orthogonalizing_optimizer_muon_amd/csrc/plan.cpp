@@ -13,7 +13,7 @@ namespace muon {
 namespace {
 
 constexpr uint64_t kAlign = 256;
-constexpr uint64_t kDefaultCap = 48ull << 30;
+constexpr uint64_t kDefaultCap = 96ull << 30;   // a third of a 288 GB part
 constexpr int kEw = 64;           // elementwise tile edge
 constexpr int kOld = 128;         // tile edge of the fp32 (register-staged) kernel
 constexpr int kXcds = 8;          // MI355X: 8 XCDs, workgroups dealt round-robin
