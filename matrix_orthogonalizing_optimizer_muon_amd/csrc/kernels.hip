@@ -902,7 +902,9 @@ __device__ __forceinline__ void apply_update8(const UpdCtx& c, int64_t row, int6
 //     out = (s alpha) acc + (s beta) Cin + gamma [i == j] (0 outside the real
 //     extents) and stores 16-byte runs of the output (Cin read the same way);
 //  3. column pass (transposed copy or mirrored tile only): every thread takes 8
-//     consecutive rows of one column and stores them as a 16-byte run.
+//     consecutive rows of one column and stores them as a 16-byte run; the
+//     lanes of a wave cover 4 columns x 16 row groups, so each store
+//     instruction writes four 256-byte runs of the transposed output.
 template <int BM, int BN, int WGM, int WGN, typename TO>
 __device__ __forceinline__ void nt_epilogue(const nt::f32x16_t (&acc)[BM / 32 / WGM][BN / 32 / WGN],
                                             MUON_LDS float* C, const GemmParams& p,
@@ -983,6 +985,21 @@ __device__ __forceinline__ void nt_epilogue(const nt::f32x16_t (&acc)[BM / 32 / 
     }
   }
   lds_barrier();   // every wave is done with the main loop's LDS
+  // With the whole tile in one slab (SW), slab element (r, col) sits at
+  // r * PITCH + (col ^ 4 ((r >> 3) & 7)).  The XOR keeps 4-aligned column
+  // quads whole (the 16-byte accesses of the accumulator writes and the row
+  // pass keep their shape) and puts the eight 8-row groups of a column on
+  // distinct bank quads, so the column pass can hand consecutive lanes
+  // consecutive 8-row groups of one column: its 16-byte stores then form
+  // 256-byte runs of the transposed rows, and its LDS reads stay
+  // conflict-free.  (A tile staged in two slabs keeps half its accumulators
+  // live through the first; there the extra addressing spilled registers and
+  // cost more than the coalescing gained, so it keeps the plain layout.)
+  constexpr bool SW = SH == BM;
+  auto slab = [&](int r, int col) {
+    if constexpr (SW) return C + r * PITCH + (col ^ (4 * ((r >> 3) & 7)));
+    else return C + r * PITCH + col;
+  };
 #pragma unroll 1
   for (int s0 = 0; s0 < BM; s0 += SH) {
     // lane l holds row l % 32 of each MFMA tile, 4 consecutive columns per
@@ -998,28 +1015,32 @@ __device__ __forceinline__ void nt_epilogue(const nt::f32x16_t (&acc)[BM / 32 / 
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int c = wx * G::WN + b * 32 + g * 8 + (lane >> 5) * 4;
-          *(MUON_LDS nt::f32x4_t*)(C + r * PITCH + c) =
+          *(MUON_LDS nt::f32x4_t*)slab(r, c) =
               nt::f32x4_t{acc[a][b][4 * g], acc[a][b][4 * g + 1], acc[a][b][4 * g + 2], acc[a][b][4 * g + 3]};
         }
     }
     lds_barrier();
-    // row pass: this thread's SH / RPP rows, 8 columns each; Cin for all of
-    // them (or, for an update applied here, the bf16 W rows) is requested
-    // before any is used
+    // row pass: this thread's RPT consecutive rows of the slab, 8 columns
+    // each (consecutive rows share the slab swizzle); Cin for all of them (or,
+    // for an update applied here, the bf16 W rows) is requested before any is
+    // used
     constexpr int RPT = SH / RPP;
     static_assert(SH % RPP == 0, "rows per thread");
-    const int c = (tid % TPR) * 8, r_first = tid / TPR;
+    // rows of this thread: RPT consecutive ones (one swizzle) or, in the plain
+    // layout, every RPP-th
+    const int c = (tid % TPR) * 8, r_first = SW ? (tid / TPR) * RPT : tid / TPR;
+    constexpr int RS = SW ? 1 : RPP;   // row step
     const int j = n0 + c;
     u32x4_t craw[RPT];
     if (Cin) {
 #pragma unroll
       for (int t = 0; t < RPT; ++t)
         craw[t] = *(GLOBAL_AS const u32x4_t*)(static_cast<const uint16_t*>(Cin) +
-                                              (int64_t)(m0 + s0 + r_first + t * RPP) * ldo + j);
+                                              (int64_t)(m0 + s0 + r_first + t * RS) * ldo + j);
     } else if (wrow) {
 #pragma unroll
       for (int t = 0; t < RPT; ++t) {
-        const int i = m0 + s0 + r_first + t * RPP;
+        const int i = m0 + s0 + r_first + t * RS;
         if (i < Mr && j + 8 <= Nr)
           craw[t] = *(GLOBAL_AS const u32x4_t*)(static_cast<const uint16_t*>(uc.w) +
                                                 (int64_t)i * uc.cols + j);
@@ -1027,12 +1048,18 @@ __device__ __forceinline__ void nt_epilogue(const nt::f32x16_t (&acc)[BM / 32 / 
     }
 #pragma unroll
     for (int t = 0; t < RPT; ++t) {
-      const int r = r_first + t * RPP;
+      const int r = r_first + t * RS;
       const int i = m0 + s0 + r;
       float v[8];
-      MUON_LDS float* src = C + r * PITCH + c;
+      {
+        const nt::f32x4_t a4 = *(const MUON_LDS nt::f32x4_t*)slab(r, c);
+        const nt::f32x4_t b4 = *(const MUON_LDS nt::f32x4_t*)slab(r, c + 4);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = src[e];
+        for (int e = 0; e < 4; ++e) {
+          v[e] = a4[e];
+          v[4 + e] = b4[e];
+        }
+      }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         float x = as * v[e];
@@ -1054,21 +1081,31 @@ __device__ __forceinline__ void nt_epilogue(const nt::f32x16_t (&acc)[BM / 32 / 
         else apply_update8(uc, i, j, nv < 8 ? nv : 8, v);
       }
       if (colpass) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) src[e] = v[e];
+        *(MUON_LDS nt::f32x4_t*)slab(r, c) = nt::f32x4_t{v[0], v[1], v[2], v[3]};
+        *(MUON_LDS nt::f32x4_t*)slab(r, c + 4) = nt::f32x4_t{v[4], v[5], v[6], v[7]};
       }
     }
     if (colpass) {
       lds_barrier();
-      // every thread takes CI (column, 8-row group) items
-      constexpr int CI = BN * (SH / 8) / NT;
-      static_assert(BN * (SH / 8) % NT == 0 && CI % 2 == 0, "column items per thread");
+      // every thread takes CI (column, 8-row group) items.  Swizzled layout:
+      // item wi = tid + ci NT is column 4 (wi / (4 GR)) + wi % 4 and row group
+      // (wi / 4) % GR, so the 4 lanes of a quad take 4 columns and the next
+      // quads the next row groups (with NT a multiple of 4 GR a thread keeps
+      // its row group and steps its column by NT / GR per item).  Plain
+      // layout: column wi % BN, row group wi / BN.
+      constexpr int GR = SH / 8;
+      constexpr int CI = BN * GR / NT;
+      static_assert(BN * GR % NT == 0 && CI % 2 == 0 && (SW ? NT % (4 * GR) == 0 : NT % BN == 0),
+                    "column items per thread");
+      const int jc0 = SW ? 4 * (tid / (4 * GR)) + tid % 4 : tid % BN;
+      const int rg0 = SW ? ((tid / 4) % GR) * 8 : (tid / BN) * 8;
+      auto col_of = [&](int ci) { return SW ? jc0 + ci * (NT / GR) : jc0; };
+      auto grp_of = [&](int ci) { return SW ? rg0 : rg0 + ci * (NT / BN) * 8; };
       auto item = [&](int ci, bool have_w, u32x4_t wq) {
-        const int wi = tid + ci * NT;
-        const int jc = wi % BN, r0 = (wi / BN) * 8;
+        const int jc = col_of(ci), r0 = grp_of(ci);
         float v[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = C[(r0 + e) * PITCH + jc];
+        for (int e = 0; e < 8; ++e) v[e] = *slab(r0 + e, jc);
         const int j = n0 + jc, i0 = m0 + s0 + r0;
         if (OutT) st8<uint16_t>(OutT, (int64_t)j * m_pad + i0, v);
         if (mirror) st8<TO>(Out, (int64_t)j * ldo + i0, v);
@@ -1082,8 +1119,7 @@ __device__ __forceinline__ void nt_epilogue(const nt::f32x16_t (&acc)[BM / 32 / 
         // the update of a tall matrix: items in pairs, both bf16 W runs
         // requested before either is used
         auto wrun = [&](int ci) {
-          const int wi = tid + ci * NT;
-          const int j = n0 + wi % BN, i0 = m0 + s0 + (wi / BN) * 8;
+          const int j = n0 + col_of(ci), i0 = m0 + s0 + grp_of(ci);
           u32x4_t q = {0, 0, 0, 0};
           if (j < Nr && i0 + 8 <= Mr)
             q = *(GLOBAL_AS const u32x4_t*)(static_cast<const uint16_t*>(uc.w) +
