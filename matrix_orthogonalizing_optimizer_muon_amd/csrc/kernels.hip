@@ -893,10 +893,11 @@ __device__ __forceinline__ void apply_update8(const UpdCtx& c, int64_t row, int6
   }
 }
 
-// Epilogue of the NT kernel.  With only a bf16 row-major output to write (no
-// Cin, transposed copy, mirrored tile or update) the values are finished in
-// registers and the whole tile goes through LDS once, as bf16.  Otherwise it
-// goes through LDS in fp32 slabs of SH rows:
+// Epilogue of the NT kernel.  With only bf16 outputs to write (no Cin or
+// update: the row-major output and possibly its transposed copy or mirrored
+// tile) the values are finished in registers and the whole tile goes through
+// LDS once, as bf16, for a row pass and a column pass.  Otherwise it goes
+// through LDS in fp32 slabs of SH rows:
 //  1. each wave writes its accumulators of the slab's rows into an fp32 tile;
 //  2. row pass: every thread takes 8 consecutive columns of a row, applies
 //     out = (s alpha) acc + (s beta) Cin + gamma [i == j] (0 outside the real
@@ -946,13 +947,22 @@ __device__ __forceinline__ void nt_epilogue(const nt::f32x16_t (&acc)[BM / 32 / 
   const bool wvec = fuse && uc.pdtype == kBF16 && uc.vec;
   const bool wrow = wvec && !ftrans, wcol = wvec && ftrans;
   if constexpr (sizeof(TO) == 2) {
-    if (!colpass && !fuse && !Cin) {
-      // only the bf16 row-major output: each lane finishes its values in
-      // registers (4 consecutive columns of a row per register group) and
-      // stages them as bf16 for the whole tile; then 16-byte row runs out
+    if (!fuse && !Cin) {
+      // bf16 outputs only (the row-major output, with or without a transposed
+      // copy or mirrored tile): each lane finishes its values in registers (4
+      // consecutive columns of a row per register group) and the whole tile is
+      // staged once in LDS as bf16, element (r, col) at r PB + (col ^ 8 ((r >>
+      // 3) & 7)).  The XOR keeps 8-element (16-byte) groups whole and puts the
+      // eight 8-row groups of a column on distinct bank quads.  A row pass
+      // stores 16-byte row runs; for the transposed copy or mirror a column
+      // pass follows in which the 4 lanes of a quad take 4 columns and
+      // consecutive quads consecutive 8-row groups, so every store instruction
+      // writes four 256-byte runs of transposed rows and the 2-byte LDS reads
+      // stay conflict-free.
       constexpr int PB = bf16_pitch<BN>();
       constexpr int TPR = BN / 8, RPP = NT / TPR;
       MUON_LDS uint16_t* Cb = reinterpret_cast<MUON_LDS uint16_t*>(C);
+      auto at = [&](int r, int col) { return Cb + r * PB + (col ^ (8 * ((r >> 3) & 7))); };
       lds_barrier();   // every wave is done with the main loop's LDS
 #pragma unroll
       for (int a = 0; a < G::MT; ++a) {
@@ -972,7 +982,7 @@ __device__ __forceinline__ void nt_epilogue(const nt::f32x16_t (&acc)[BM / 32 / 
                 if (i >= Mr || j + q >= Nr) v[q] = 0.f;
               }
             }
-            *(MUON_LDS u32x2_t*)(Cb + r * PB + c) = u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+            *(MUON_LDS u32x2_t*)at(r, c) = u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
           }
       }
       lds_barrier();
@@ -980,7 +990,27 @@ __device__ __forceinline__ void nt_epilogue(const nt::f32x16_t (&acc)[BM / 32 / 
 #pragma unroll 4
       for (int r = tid / TPR; r < BM; r += RPP)
         *(GLOBAL_AS u32x4_t*)(static_cast<uint16_t*>(Out) + (int64_t)(m0 + r) * ldo + n0 + cc) =
-            *(const MUON_LDS u32x4_t*)(Cb + r * PB + cc);
+            *(const MUON_LDS u32x4_t*)at(r, cc);
+      if (colpass) {
+        // items (column jc, 8-row group r0): item wi is column 4 (wi / (4 GR))
+        // + wi % 4 and row group (wi / 4) % GR; with NT a multiple of 4 GR a
+        // thread keeps its row group and steps its column by NT / GR
+        constexpr int GR = BM / 8;
+        static_assert(BN * GR % NT == 0 && NT % (4 * GR) == 0, "column items per thread");
+        const int jc0 = 4 * (tid / (4 * GR)) + tid % 4, r0 = ((tid / 4) % GR) * 8;
+        const int i0 = m0 + r0;
+#pragma unroll 2
+        for (int ci = 0; ci < BN * GR / NT; ++ci) {
+          const int jc = jc0 + ci * (NT / GR), j = n0 + jc;
+          uint32_t w[4];
+#pragma unroll
+          for (int h = 0; h < 4; ++h)
+            w[h] = (uint32_t)*at(r0 + 2 * h, jc) | ((uint32_t)*at(r0 + 2 * h + 1, jc) << 16);
+          const u32x4_t q = u32x4_t{w[0], w[1], w[2], w[3]};
+          if (OutT) *(GLOBAL_AS u32x4_t*)(static_cast<uint16_t*>(OutT) + (int64_t)j * m_pad + i0) = q;
+          if (mirror) *(GLOBAL_AS u32x4_t*)(static_cast<uint16_t*>(Out) + (int64_t)j * ldo + i0) = q;
+        }
+      }
       return;
     }
   }
