@@ -947,9 +947,10 @@ __device__ __forceinline__ void nt_epilogue(const nt::f32x16_t (&acc)[BM / 32 / 
   const bool wvec = fuse && uc.pdtype == kBF16 && uc.vec;
   const bool wrow = wvec && !ftrans, wcol = wvec && ftrans;
   if constexpr (sizeof(TO) == 2) {
-    if (!fuse && !Cin) {
-      // bf16 outputs only (the row-major output, with or without a transposed
-      // copy or mirrored tile): each lane finishes its values in registers (4
+    {
+      // bf16 outputs (the row-major output, with or without a transposed copy
+      // or mirrored tile; the launcher refuses an update fused into a bf16
+      // launch): each lane finishes its values in registers (4
       // consecutive columns of a row per register group) and the whole tile is
       // staged once in LDS as bf16, element (r, col) at r PB + (col ^ 8 ((r >>
       // 3) & 7)).  The XOR keeps 8-element (16-byte) groups whole and puts the
@@ -958,12 +959,32 @@ __device__ __forceinline__ void nt_epilogue(const nt::f32x16_t (&acc)[BM / 32 / 
       // pass follows in which the 4 lanes of a quad take 4 columns and
       // consecutive quads consecutive 8-row groups, so every store instruction
       // writes four 256-byte runs of transposed rows and the 2-byte LDS reads
-      // stay conflict-free.
+      // stay conflict-free.  With Cin, its tile is first copied into the same
+      // staging layout (16-byte row runs), and each lane combines the values
+      // at its own positions in fp32 before they are rounded once to bf16.
       constexpr int PB = bf16_pitch<BN>();
       constexpr int TPR = BN / 8, RPP = NT / TPR;
       MUON_LDS uint16_t* Cb = reinterpret_cast<MUON_LDS uint16_t*>(C);
       auto at = [&](int r, int col) { return Cb + r * PB + (col ^ (8 * ((r >> 3) & 7))); };
-      lds_barrier();   // every wave is done with the main loop's LDS
+      const int cc = (tid % TPR) * 8;
+      if (Cin) {
+        // rows of this thread in batches of CB 16-byte loads (all of a batch
+        // in flight at once, within the registers the accumulators leave)
+        constexpr int CR = BM / RPP, CB = CR < 8 ? CR : 8;
+        static_assert(BM % RPP == 0 && CR % CB == 0, "Cin rows per thread");
+#pragma unroll
+        for (int t0 = 0; t0 < CR; t0 += CB) {
+          u32x4_t cr[CB];
+#pragma unroll
+          for (int t = 0; t < CB; ++t)
+            cr[t] = *(GLOBAL_AS const u32x4_t*)(static_cast<const uint16_t*>(Cin) +
+                                                (int64_t)(m0 + tid / TPR + (t0 + t) * RPP) * ldo + n0 + cc);
+          if (t0 == 0) lds_barrier();   // every wave is done with the main loop's LDS
+#pragma unroll
+          for (int t = 0; t < CB; ++t) *(MUON_LDS u32x4_t*)at(tid / TPR + (t0 + t) * RPP, cc) = cr[t];
+        }
+      }
+      lds_barrier();   // the main loop's LDS is free; Cin (if any) is staged
 #pragma unroll
       for (int a = 0; a < G::MT; ++a) {
         const int r = wy * G::WM + a * 32 + (lane & 31), i = m0 + r;
@@ -975,6 +996,13 @@ __device__ __forceinline__ void nt_epilogue(const nt::f32x16_t (&acc)[BM / 32 / 
             float v[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) v[q] = as * acc[a][b][4 * g + q];
+            if (Cin) {
+              const u32x2_t c2 = *(const MUON_LDS u32x2_t*)at(r, c);
+              v[0] = fmaf(bs, bf16_to_f32(c2[0] & 0xffffu), v[0]);
+              v[1] = fmaf(bs, bf16_to_f32(c2[0] >> 16), v[1]);
+              v[2] = fmaf(bs, bf16_to_f32(c2[1] & 0xffffu), v[2]);
+              v[3] = fmaf(bs, bf16_to_f32(c2[1] >> 16), v[3]);
+            }
             if (edge) {
 #pragma unroll
               for (int q = 0; q < 4; ++q) {
@@ -986,7 +1014,6 @@ __device__ __forceinline__ void nt_epilogue(const nt::f32x16_t (&acc)[BM / 32 / 
           }
       }
       lds_barrier();
-      const int cc = (tid % TPR) * 8;
 #pragma unroll 4
       for (int r = tid / TPR; r < BM; r += RPP)
         *(GLOBAL_AS u32x4_t*)(static_cast<uint16_t*>(Out) + (int64_t)(m0 + r) * ldo + n0 + cc) =
@@ -1225,6 +1252,7 @@ hipError_t launch_nt_t(const GemmParams& p, hipStream_t s) {
 
 template <int BM, int BN, int WGM, int WGN>
 hipError_t launch_nt_cfg(int out_dt, const GemmParams& p, hipStream_t s) {
+  if (p.fuse && out_dt != kF32) return hipErrorInvalidValue;   // the update is applied from fp32 tiles
   if (p.qt) {
     if (p.shape != kShapeApplyT) return hipErrorInvalidValue;
     if constexpr (BN >= 128) {   // k-major Q tiles need rows of >= 256 bytes
