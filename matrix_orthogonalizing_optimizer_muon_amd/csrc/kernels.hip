@@ -366,6 +366,12 @@ __global__ __launch_bounds__(256) void k_adamw(const AdamTensor* __restrict__ ts
 
 // ------------------------------------------------------------ elementwise: apply
 
+// The update of one element: U = -lr (wd W + s x), one fused multiply-add
+// written out so that every kernel that applies it rounds the same way.
+__device__ __forceinline__ float update_u(float w, float x, float lr, float wd, float s) {
+  return -lr * fmaf(wd, w, s * x);
+}
+
 // Same thread layout as k_ew_momentum (rows rq + 16 k, columns cq .. cq + 3).
 __global__ __launch_bounds__(256) void k_ew_apply(
     const EwMat* __restrict__ mats, const EwDyn* __restrict__ dyn,
@@ -435,7 +441,7 @@ __global__ __launch_bounds__(256) void k_ew_apply(
         load4_vec(D.w, M.pdtype, off, w);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          u[e] = -lr * (wd * w[e] + s * (sx * x[k][e]));
+          u[e] = update_u(w[e], sx * x[k][e], lr, wd, s);
           w[e] = w[e] + u[e];
         }
         store4_vec(D.w, M.pdtype, off, w);
@@ -446,7 +452,7 @@ __global__ __launch_bounds__(256) void k_ew_apply(
           if (sr < M.rows && sc + e < M.cols) {
             const int64_t off = sr * M.cols + sc + e;
             const float w = load1(D.w, M.pdtype, off);
-            const float u = -lr * (wd * w + s * (sx * x[k][e]));
+            const float u = update_u(w, sx * x[k][e], lr, wd, s);
             store1(D.w, M.pdtype, off, w + u);
             if (D.upd) D.upd[off] = u;
           }
@@ -840,7 +846,7 @@ __device__ __forceinline__ void apply_update8_bf16(const UpdCtx& c, int64_t off,
   }
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    u[e] = -c.lr * (c.wd * w[e] + c.s * x[e]);
+    u[e] = update_u(w[e], x[e], c.lr, c.wd, c.s);
     w[e] = w[e] + u[e];
   }
   *(GLOBAL_AS u32x4_t*)(static_cast<uint16_t*>(c.w) + off) =
@@ -873,7 +879,7 @@ __device__ __forceinline__ void apply_update8(const UpdCtx& c, int64_t row, int6
     float w[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]}, u[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      u[e] = -lr * (wd * w[e] + sc * x[e]);
+      u[e] = update_u(w[e], x[e], lr, wd, sc);
       w[e] = w[e] + u[e];
     }
     src[0] = f32x4_t{w[0], w[1], w[2], w[3]};
@@ -887,7 +893,7 @@ __device__ __forceinline__ void apply_update8(const UpdCtx& c, int64_t row, int6
   }
   for (int e = 0; e < nvalid; ++e) {
     const float w = load1(c.w, dt, off + e);
-    const float u = -lr * (wd * w + sc * x[e]);
+    const float u = update_u(w, x[e], lr, wd, sc);
     store1(c.w, dt, off + e, w + u);
     if (c.upd) c.upd[off + e] = u;
   }
@@ -1036,6 +1042,108 @@ __device__ __forceinline__ void nt_epilogue(const nt::f32x16_t (&acc)[BM / 32 / 
           const u32x4_t q = u32x4_t{w[0], w[1], w[2], w[3]};
           if (OutT) *(GLOBAL_AS u32x4_t*)(static_cast<uint16_t*>(OutT) + (int64_t)j * m_pad + i0) = q;
           if (mirror) *(GLOBAL_AS u32x4_t*)(static_cast<uint16_t*>(Out) + (int64_t)j * ldo + i0) = q;
+        }
+      }
+      return;
+    }
+  }
+  if constexpr (sizeof(TO) == 4) {
+    if (wvec && !edge) {
+      // The update applied to an interior tile of bf16 parameters: W's tile
+      // is staged in LDS as bf16 in the layout of the bf16 epilogue above (W's
+      // row runs, or for a transposed matrix its column runs, scattered 2 bytes
+      // at a time the way the column pass gathers them), each lane updates the
+      // elements at its own accumulator positions in fp32 and rounds each once,
+      // and the tile goes back to W in 16-byte runs (the row pass, or for a
+      // transposed matrix the column pass).  The capture of U, when set, is
+      // written from the lanes' registers.
+      constexpr int PB = bf16_pitch<BN>();
+      constexpr int TPR = BN / 8, RPP = NT / TPR, GR = BM / 8, CI = BN * GR / NT;
+      static_assert(BM % RPP == 0 && BN * GR % NT == 0 && NT % (4 * GR) == 0, "staged update items");
+      MUON_LDS uint16_t* Cb = reinterpret_cast<MUON_LDS uint16_t*>(C);
+      auto at = [&](int r, int col) { return Cb + r * PB + (col ^ (8 * ((r >> 3) & 7))); };
+      uint16_t* W = static_cast<uint16_t*>(uc.w);
+      const int64_t ldw = uc.cols;
+      const int cc = (tid % TPR) * 8;
+      const int jc0 = 4 * (tid / (4 * GR)) + tid % 4, r0 = ((tid / 4) % GR) * 8;
+      if (!ftrans) {
+        constexpr int CR = BM / RPP, CB = CR < 8 ? CR : 8;
+        static_assert(CR % CB == 0, "W rows per thread");
+#pragma unroll
+        for (int t0 = 0; t0 < CR; t0 += CB) {
+          u32x4_t q[CB];
+#pragma unroll
+          for (int t = 0; t < CB; ++t)
+            q[t] = *(GLOBAL_AS const u32x4_t*)(W + (int64_t)(m0 + tid / TPR + (t0 + t) * RPP) * ldw + n0 + cc);
+          if (t0 == 0) lds_barrier();   // every wave is done with the main loop's LDS
+#pragma unroll
+          for (int t = 0; t < CB; ++t) *(MUON_LDS u32x4_t*)at(tid / TPR + (t0 + t) * RPP, cc) = q[t];
+        }
+      } else {
+        constexpr int CB = CI < 8 ? CI : 8;
+        static_assert(CI % CB == 0, "W column runs per thread");
+#pragma unroll
+        for (int t0 = 0; t0 < CI; t0 += CB) {
+          u32x4_t q[CB];
+#pragma unroll
+          for (int t = 0; t < CB; ++t)
+            q[t] = *(GLOBAL_AS const u32x4_t*)(W + (int64_t)(n0 + jc0 + (t0 + t) * (NT / GR)) * ldw + m0 + r0);
+          if (t0 == 0) lds_barrier();   // every wave is done with the main loop's LDS
+#pragma unroll
+          for (int t = 0; t < CB; ++t) {
+            const int jc = jc0 + (t0 + t) * (NT / GR);
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+              *at(r0 + 2 * h, jc) = (uint16_t)(q[t][h] & 0xffffu);
+              *at(r0 + 2 * h + 1, jc) = (uint16_t)(q[t][h] >> 16);
+            }
+          }
+        }
+      }
+      lds_barrier();
+#pragma unroll
+      for (int a = 0; a < G::MT; ++a) {
+        const int r = wy * G::WM + a * 32 + (lane & 31);
+#pragma unroll
+        for (int b = 0; b < G::NT; ++b)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int c = wx * G::WN + b * 32 + g * 8 + (lane >> 5) * 4;
+            const u32x2_t w2 = *(const MUON_LDS u32x2_t*)at(r, c);
+            float w[4] = {bf16_to_f32(w2[0] & 0xffffu), bf16_to_f32(w2[0] >> 16), bf16_to_f32(w2[1] & 0xffffu),
+                          bf16_to_f32(w2[1] >> 16)};
+            float u[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              u[q] = update_u(w[q], as * acc[a][b][4 * g + q], uc.lr, uc.wd, uc.s);
+              w[q] = w[q] + u[q];
+            }
+            if (uc.upd) {
+              const int64_t i = m0 + r, j = n0 + c;
+              if (!ftrans) {
+                *(GLOBAL_AS nt::f32x4_t*)(uc.upd + i * ldw + j) = nt::f32x4_t{u[0], u[1], u[2], u[3]};
+              } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) uc.upd[(j + q) * ldw + i] = u[q];
+              }
+            }
+            *(MUON_LDS u32x2_t*)at(r, c) = u32x2_t{pack_bf16x2(w[0], w[1]), pack_bf16x2(w[2], w[3])};
+          }
+      }
+      lds_barrier();
+      if (!ftrans) {
+#pragma unroll 4
+        for (int r = tid / TPR; r < BM; r += RPP)
+          *(GLOBAL_AS u32x4_t*)(W + (int64_t)(m0 + r) * ldw + n0 + cc) = *(const MUON_LDS u32x4_t*)at(r, cc);
+      } else {
+#pragma unroll 2
+        for (int ci = 0; ci < CI; ++ci) {
+          const int jc = jc0 + ci * (NT / GR);
+          uint32_t w[4];
+#pragma unroll
+          for (int h = 0; h < 4; ++h)
+            w[h] = (uint32_t)*at(r0 + 2 * h, jc) | ((uint32_t)*at(r0 + 2 * h + 1, jc) << 16);
+          *(GLOBAL_AS u32x4_t*)(W + (int64_t)(n0 + jc) * ldw + m0 + r0) = u32x4_t{w[0], w[1], w[2], w[3]};
         }
       }
       return;
