@@ -112,6 +112,7 @@ def traffic_for(kernel, workload, launches_per_step):
 
 
 COPY_BYTES = 1 << 30   # bytes read and written by the calibration copy
+NT_CORE_DIM = 8192          # m = n = k of the NT core probe's product
 
 
 def demangled(label):
@@ -563,18 +564,27 @@ def main():
         mfma_tf, _ = MU.probe_mfma_bf16(iters=100000)              # about 17 ms
         mfma_sus, _ = MU.probe_mfma_bf16(iters=1000000)            # about 170 ms
         mfma_rnd, _ = MU.probe_mfma_bf16(iters=1000000, random_operands=True)
+        # the NT contraction core alone (no epilogue) on a random 8192^3 product
+        gen = torch.Generator(device="cuda").manual_seed(11)
+        pa = (torch.randn(NT_CORE_DIM, NT_CORE_DIM, device="cuda", generator=gen) * 0.02).to(torch.bfloat16)
+        qa = (torch.randn(NT_CORE_DIM, NT_CORE_DIM, device="cuda", generator=gen) * 0.02).to(torch.bfloat16)
+        nt_core, _ = MU.probe_nt_bf16(pa, qa, reps=5)
+        del pa, qa
         a = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
         b = torch.empty_like(a)
         copy_gbs = MU.probe_hbm_copy(b, a, reps=10)
         del a, b
         ceil = {"mfma_bf16_tflops": round(mfma_tf, 1), "mfma_bf16_tflops_sustained": round(mfma_sus, 1),
                 "mfma_bf16_tflops_random_operands": round(mfma_rnd, 1),
+                "nt_core_bf16_tflops": round(nt_core, 1),
                 "hbm_copy_gbs": round(copy_gbs, 1),
                 "how": "muon_probe_mfma_bf16 (2 blocks of 4 waves per CU, 4 independent "
                        "32x32x16 bf16 MFMA chains per wave, no memory traffic; 1e5 and 1e6 "
                        "rounds; and 1e6 rounds with eight random operand pairs per wave, "
                        "muon_probe_mfma_bf16_random, the switching activity of real data "
-                       "under the part's power limit) and muon_probe_hbm_copy (1 GiB copy, read + written bytes, "
+                       "under the part's power limit), muon_probe_nt_bf16 (the 256x256 NT "
+                       "contraction core without an epilogue on a random 8192^3 bf16 product, "
+                       "5 launches) and muon_probe_hbm_copy (1 GiB copy, read + written bytes, "
                        "best of 8 launch variants)"}
     ns_flops = info["ns_flops_min"]
     bf16 = wl.dtype == "bf16"
@@ -614,6 +624,7 @@ def main():
             roofline["frac_of_measured_mfma"] = round(ach / ceil["mfma_bf16_tflops"], 4)
             roofline["frac_of_measured_mfma_random_operands"] = round(
                 ach / ceil["mfma_bf16_tflops_random_operands"], 4)
+            roofline["frac_of_nt_core"] = round(ach / ceil["nt_core_bf16_tflops"], 4)
     # every NS kernel instance against the same peak (profiling pass, per launch)
     ns_rooflines = []
     for n, d in sorted(ns_kern.items(), key=lambda kv: -kv[1]["total_ms"]):

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define MUON_ABI_VERSION 11
+#define MUON_ABI_VERSION 12
 
 typedef enum muon_status {
   MUON_OK = 0,
@@ -392,6 +392,21 @@ int muon_probe_mfma_bf16(int iters, double* tflops, double* flops);
  * contraction on random data is read against. */
 int muon_probe_mfma_bf16_random(int iters, double* tflops, double* flops);
 int muon_probe_hbm_copy(void* dst, const void* src, uint64_t bytes, int reps, double* gbs);
+/* The NT contraction core of the large NS products (256x256 tiles of 8
+ * waves, k-tiles of 64 copied global -> LDS, two stages) alone, without an
+ * epilogue: one launch computes every 256x256 tile of P Q^T (P: m x k, Q:
+ * n x k, bf16 row-major, caller-owned device buffers, 16-byte aligned; m and
+ * n positive multiples of 256, k a positive multiple of 64, m k and n k below
+ * 2^31) and keeps only each thread's sum of its accumulators.  One warm-up
+ * launch, then reps timed launches; tflops receives 2 m n k reps / time /
+ * 1e12; checksum (nullable) the sum over all tiles of their accumulator sums,
+ * i.e. the sum of all entries of P Q^T as the kernel accumulated it.  Read a
+ * kernel against this rate to see what its epilogue, tile order and operand
+ * traffic cost beyond the core.  Allocates and frees a small output buffer.
+ * EINVAL: NULL pointer, sizes, alignment, reps outside [1, 100].  EHIP:
+ * device or launch error. */
+int muon_probe_nt_bf16(const void* P, const void* Q, int m, int n, int k, int reps, double* tflops,
+                       double* checksum);
 
 /*
  * One Muon step of ONE matrix that allocates no device memory, for callers

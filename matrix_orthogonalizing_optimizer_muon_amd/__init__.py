@@ -15,7 +15,7 @@ from . import _lib as L
 from ._lib import MuonError  # noqa: F401
 
 __all__ = ["MuonPlan", "AdamWPlan", "MuonError", "library_path", "assign_owners",
-           "probe_mfma_bf16", "probe_hbm_copy", "step_noalloc"]
+           "probe_mfma_bf16", "probe_nt_bf16", "probe_hbm_copy", "step_noalloc"]
 
 
 def library_path():
@@ -310,6 +310,26 @@ def probe_mfma_bf16(iters=20000, random_operands=False):
     fn = L.lib().muon_probe_mfma_bf16_random if random_operands else L.lib().muon_probe_mfma_bf16
     L.check(fn(int(iters), ctypes.byref(tf), ctypes.byref(fl)))
     return tf.value, fl.value
+
+
+def probe_nt_bf16(P, Q, reps=5):
+    """Measured rate of the NT contraction core alone (muon_probe_nt_bf16) on
+    P Q^T: P (m x k) and Q (n x k) contiguous bf16 device tensors, m and n
+    multiples of 256, k a multiple of 64.
+
+    Returns (TFLOP/s, sum of all entries of P Q^T as the core accumulated it)."""
+    import torch
+    for t in (P, Q):
+        if not (t.is_cuda and t.is_contiguous() and t.dtype == torch.bfloat16 and t.dim() == 2):
+            raise ValueError("P and Q must be contiguous 2-D bf16 device tensors")
+    if P.shape[1] != Q.shape[1]:
+        raise ValueError("P and Q must have the same number of columns")
+    tf = ctypes.c_double()
+    cs = ctypes.c_double()
+    L.check(L.lib().muon_probe_nt_bf16(ctypes.c_void_p(P.data_ptr()), ctypes.c_void_p(Q.data_ptr()),
+                                       int(P.shape[0]), int(Q.shape[0]), int(P.shape[1]), int(reps),
+                                       ctypes.byref(tf), ctypes.byref(cs)))
+    return tf.value, cs.value
 
 
 def probe_hbm_copy(dst, src, reps=10):

@@ -1083,6 +1083,38 @@ int muon_probe_mfma_bf16_random(int iters, double* tflops, double* flops) {
   return probe_mfma(iters, true, tflops, flops);
 }
 
+int muon_probe_nt_bf16(const void* P, const void* Q, int m, int n, int k, int reps, double* tflops,
+                       double* checksum) {
+  if (!P || !Q || !tflops) return fail(MUON_EINVAL, "NULL pointer");
+  if (m <= 0 || n <= 0 || k <= 0 || m % kProbeNtTile || n % kProbeNtTile || k % 64)
+    return fail(MUON_EINVAL, "m and n must be positive multiples of 256, k a positive multiple of 64");
+  if ((int64_t)m * k >= (1ll << 31) || (int64_t)n * k >= (1ll << 31))
+    return fail(MUON_EINVAL, "m k and n k must stay below 2^31");
+  if (!aligned16(P) || !aligned16(Q)) return fail(MUON_EINVAL, "P and Q must be 16-byte aligned");
+  if (reps < 1 || reps > 100) return fail(MUON_EINVAL, "reps out of [1, 100]");
+  const int64_t outn = (int64_t)(m / kProbeNtTile) * (n / kProbeNtTile) * kProbeNtThreads;
+  int rc;
+  ProbeRun r;
+  if ((rc = r.init())) return rc;
+  HIP_TRY(hipMalloc(&r.out, (size_t)outn * sizeof(float)));
+  HIP_TRY(launch_probe_nt(P, Q, m, n, k, r.out, r.s));   // warm-up
+  HIP_TRY(hipEventRecord(r.e0, r.s));
+  for (int i = 0; i < reps; ++i) HIP_TRY(launch_probe_nt(P, Q, m, n, k, r.out, r.s));
+  HIP_TRY(hipEventRecord(r.e1, r.s));
+  double ms = 0;
+  if ((rc = r.elapsed(&ms))) return rc;
+  const double fl = 2.0 * m * (double)n * k * reps;
+  *tflops = ms > 0 ? fl / (ms * 1e-3) / 1e12 : 0.0;
+  if (checksum) {
+    std::vector<float> h((size_t)outn);
+    HIP_TRY(hipMemcpy(h.data(), r.out, h.size() * sizeof(float), hipMemcpyDeviceToHost));
+    double t = 0.0;
+    for (float v : h) t += v;
+    *checksum = t;
+  }
+  return MUON_OK;
+}
+
 int muon_probe_hbm_copy(void* dst, const void* src, uint64_t bytes, int reps, double* gbs) {
   if (!dst || !src || !gbs) return fail(MUON_EINVAL, "NULL pointer");
   if (bytes == 0 || bytes % 16 || !aligned16(dst) || !aligned16(src))

@@ -1,9 +1,10 @@
 // Ceiling probes (declared in probe.hpp): the rates this part sustains for
-// dense bf16 MFMA work and for streaming HBM copies when nothing else limits
-// them.
+// dense bf16 MFMA work, for the NT contraction core and for streaming HBM
+// copies when nothing else limits them.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "mfma_nt.hpp"
 #include "probe.hpp"
 
 namespace muon {
@@ -77,6 +78,32 @@ __global__ __launch_bounds__(256) void k_probe_mfma(int iters, float* __restrict
   out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = sum;
 }
 
+using ProbeNtGeom = nt::Geom<kProbeNtTile, kProbeNtTile, 64, 2, 2, 4>;
+static_assert(ProbeNtGeom::THREADS == kProbeNtThreads, "probe block");
+
+__global__ __launch_bounds__(kProbeNtThreads) void k_probe_nt(const uint16_t* __restrict__ P,
+                                                              const uint16_t* __restrict__ Q, int m,
+                                                              int n, int k, float* __restrict__ out) {
+  extern __shared__ __attribute__((aligned(1024))) char probe_smem[];
+  using G = ProbeNtGeom;
+  const int tn_count = n / kProbeNtTile;
+  const int tm = blockIdx.x / tn_count, tn = blockIdx.x % tn_count;
+  const __amdgpu_buffer_rsrc_t Pr = nt::make_rsrc(P, (uint32_t)((size_t)m * k * 2));
+  const __amdgpu_buffer_rsrc_t Qr = nt::make_rsrc(Q, (uint32_t)((size_t)n * k * 2));
+  nt::f32x16_t acc[G::MT][G::NT];
+  nt::mainloop<kProbeNtTile, kProbeNtTile, 64, 2, 2, 4, false>(
+      acc, (MUON_LDS char*)probe_smem, Pr, Qr, (uint32_t)k, (uint32_t)k, (uint32_t)(tm * kProbeNtTile),
+      (uint32_t)(tn * kProbeNtTile), k);
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < G::MT; ++i)
+#pragma unroll
+    for (int j = 0; j < G::NT; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sum += acc[i][j][r];
+  out[(int64_t)blockIdx.x * kProbeNtThreads + threadIdx.x] = sum;
+}
+
 template <bool NTMP>
 __device__ __forceinline__ u32x4_t probe_ld(const u32x4_t* p) {
   if constexpr (NTMP) return __builtin_nontemporal_load(p);
@@ -128,6 +155,23 @@ hipError_t launch_probe_mfma(int blocks, int iters, bool random_operands, float*
     hipLaunchKernelGGL(k_probe_mfma<true>, dim3((unsigned)blocks), dim3(256), 0, s, iters, out);
   else
     hipLaunchKernelGGL(k_probe_mfma<false>, dim3((unsigned)blocks), dim3(256), 0, s, iters, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_probe_nt(const void* P, const void* Q, int m, int n, int k, float* out, hipStream_t s) {
+  if (m <= 0 || n <= 0 || k <= 0 || m % kProbeNtTile || n % kProbeNtTile || k % 64 ||
+      (int64_t)m * k >= (1ll << 31) || (int64_t)n * k >= (1ll << 31))
+    return hipErrorInvalidValue;
+  static bool attr_done = false;
+  if (!attr_done) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_probe_nt),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, ProbeNtGeom::LDS);
+    if (e != hipSuccess) return e;
+    attr_done = true;
+  }
+  const int tiles = (m / kProbeNtTile) * (n / kProbeNtTile);
+  hipLaunchKernelGGL(k_probe_nt, dim3((unsigned)tiles), dim3(kProbeNtThreads), ProbeNtGeom::LDS, s,
+                     static_cast<const uint16_t*>(P), static_cast<const uint16_t*>(Q), m, n, k, out);
   return hipGetLastError();
 }
 

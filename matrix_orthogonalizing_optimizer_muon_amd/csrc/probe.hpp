@@ -1,5 +1,6 @@
 // Ceiling probes of the gfx950 device (measurement only, never part of a
-// step): a dense bf16 MFMA loop without memory traffic and an HBM copy.
+// step): a dense bf16 MFMA loop without memory traffic, the NT contraction
+// core alone and an HBM copy.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -13,6 +14,14 @@ namespace muon {
 // pairs (real data's switching activity) instead of the same pair.
 constexpr int kProbeChains = 4;
 hipError_t launch_probe_mfma(int blocks, int iters, bool random_operands, float* out, hipStream_t s);
+// k_probe_nt: the NT contraction core (mfma_nt.hpp, 256x256 tiles of 8
+// waves, the configuration of the large NS products) without an epilogue:
+// block t computes tile (t / (n / 256), t % (n / 256)) of P Q^T over k (P m x
+// k, Q n x k, bf16 row-major) and stores the sum of its accumulators, one
+// float per thread, into out ((m / 256) * (n / 256) * 512 floats).  m, n
+// multiples of 256, k a multiple of 64, m k and n k below 2^31.
+constexpr int kProbeNtTile = 256, kProbeNtThreads = 512;
+hipError_t launch_probe_nt(const void* P, const void* Q, int m, int n, int k, float* out, hipStream_t s);
 // k_probe_copy: dst[i] = src[i] for n16 16-byte words (grid-stride, `blocks`
 // blocks of 256 threads, 4 words in flight per thread), plain or nontemporal
 // loads and stores; blocks <= 0: one block per contiguous 1024-word run.

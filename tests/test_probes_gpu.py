@@ -1,6 +1,7 @@
-"""Ceiling probes through the C ABI: the dense bf16 MFMA loop and the HBM copy
-give rates inside what the part can physically reach (published dense bf16
-peak about 2.5 PFLOP/s, HBM3E 8 TB/s), and the copy probe copies."""
+"""Ceiling probes through the C ABI: the dense bf16 MFMA loop, the NT
+contraction core and the HBM copy give rates inside what the part can
+physically reach (published dense bf16 peak about 2.5 PFLOP/s, HBM3E 8 TB/s),
+the core computes the product it times, and the copy probe copies."""
 import pytest
 
 pytestmark = pytest.mark.gpu
@@ -50,3 +51,23 @@ def test_hbm_copy_probe_copies_and_rate_is_physical(M):
         M.probe_hbm_copy(dst[:-4], src)
     with pytest.raises(M.MuonError):
         M.probe_hbm_copy(dst[4:], dst[:-4])   # overlapping buffers
+
+
+def test_nt_core_probe_checksum_and_rate(M):
+    """The NT core probe computes every 256x256 tile of P Q^T: its checksum is
+    the sum of all entries of the product, which equals the dot product of the
+    column sums of P and Q (positive operands: no cancellation)."""
+    import torch
+    g = torch.Generator().manual_seed(5)
+    m, n, k = 512, 768, 1024
+    P = torch.rand(m, k, generator=g).to(torch.bfloat16)
+    Q = torch.rand(n, k, generator=g).to(torch.bfloat16)
+    want = float((P.double().sum(0) * Q.double().sum(0)).sum())
+    tf, cs = M.probe_nt_bf16(P.cuda(), Q.cuda(), reps=2)
+    print(f"nt core probe: {tf:.1f} TFLOP/s, checksum {cs:.6e} against {want:.6e}", flush=True)
+    assert 0 < tf <= 1.02 * PEAK_BF16_TFLOPS
+    assert abs(cs - want) <= 1e-4 * abs(want), (cs, want)
+    with pytest.raises(M.MuonError):   # k not a multiple of 64
+        M.probe_nt_bf16(P[:, :1000].contiguous().cuda(), Q[:, :1000].contiguous().cuda())
+    with pytest.raises(M.MuonError):   # m not a multiple of 256
+        M.probe_nt_bf16(P[:500].contiguous().cuda(), Q.cuda())
