@@ -620,6 +620,13 @@ def main():
                     "launches_per_step": dom["launches"] / args.steps,
                     "share_of_step": round(dom["total_ms"] / args.steps / ms, 4),
                     "lanes": info["n_lanes"]}
+        # the same launches credited with GEMM-equivalent flops (the symmetric
+        # products X X^T and A A counted as whole products, 2 m^2 n and 2 m^3)
+        geq = sum(k["flops"] * (2.0 if k["name"] in ("ns_syrk", "ns_comb") else 1.0)
+                  for k in kt if k["kernel"] == name)
+        a_geq = geq / dom["launches"] / (avg_ms * 1e-3) / 1e12
+        roofline["achieved_gemm_equivalent"] = round(a_geq, 2)
+        roofline["frac_gemm_equivalent"] = round(a_geq / peak, 4)
         if ceil and bf16:
             roofline["frac_of_measured_mfma"] = round(ach / ceil["mfma_bf16_tflops"], 4)
             roofline["frac_of_measured_mfma_random_operands"] = round(
@@ -644,6 +651,12 @@ def main():
         if ceil:
             ew[n]["frac_of_measured_copy"] = round(gbs / ceil["hbm_copy_gbs"], 4)
     value = ns_flops / (ms * 1e-3) / 1e12
+    # direct-form GEMM-equivalent NS flops, T (4 m^2 n + 2 m^3) per matrix (m the
+    # smaller side): every product counted whole, whatever form or symmetry
+    # the plan uses
+    geq_flops = float(sum(h.ns_steps * (4.0 * min(r, c) ** 2 * max(r, c) + 2.0 * min(r, c) ** 3)
+                          for r, c in wl.shapes))
+    geq_value = geq_flops / (ms * 1e-3) / 1e12
     out = {
         "metric": "Muon optimizer-step ms + NS TFLOP/s (% of MI355X bf16 MFMA peak)",
         "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -661,6 +674,9 @@ def main():
         "ns_kernel_ms_per_step_serial": round(ns_ms, 4) if kt else None,
         "ns_tflops_kernels_serial": round(ns_flops / (ns_ms * 1e-3) / 1e12, 2) if ns_ms else None,
         "step_frac_of_peak": round(value / peak, 4),
+        "ns_flops_gemm_equivalent_per_step": geq_flops,
+        "step_tflops_gemm_equivalent": round(geq_value, 2),
+        "step_frac_of_peak_gemm_equivalent": round(geq_value / peak, 4),
         "elementwise": ew, "roofline": roofline, "ns_kernel_rooflines": ns_rooflines, "ceilings": ceil,
         "kernels": [{"stage": k["name"], "kernel": k["kernel"],
                      "launches_per_step": k["launches"] / args.steps,
