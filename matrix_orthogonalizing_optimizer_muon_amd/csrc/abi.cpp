@@ -580,13 +580,13 @@ int enqueue_ns(muon_plan* p, const SetDev& S, int T, const float* sched, const E
 
 // A chunk's front and NS stages.  front(a, b, stream, ev) enqueues the front
 // (momentum or input load, then k_norm) of the chunk's matrices [a, b) and,
-// when ev is set, records it once the HBM-heavy part is done.  With one lane
-// (or T = 0) everything goes to s.  With more, lane l runs on its own stream
-// (lane 0 on s): its front starts when lane l-1's momentum is done, then its
-// NS launch sets follow, so each lane's HBM-bound front runs beside the
-// MFMA-bound NS of the lanes before it.  Lanes 1.. are joined back into s.
-// While profiling, the same launches run lane after lane on s, so each
-// recorded dispatch time is the kernel's own, not shared with another lane.
+// when ev is set, records it once the HBM-heavy part is done.  The whole
+// chunk's front runs on s as one launch pair; then, with more than one lane
+// (and T > 0), lane l's NS launch sets run on a stream of their own (lane 0
+// on s), all lanes starting when the front is done, and lanes 1.. are
+// joined back into s.  While profiling, the same launches run lane after lane
+// on s, so each recorded dispatch time is the kernel's own, not shared with
+// another lane.
 template <class Front>
 int enqueue_chunk(muon_plan* p, const ChunkDev& C, int T, const float* sched, const EwDyn* dyn,
                   float lr, float wd, hipStream_t s, Front&& front) {
@@ -600,12 +600,11 @@ int enqueue_chunk(muon_plan* p, const ChunkDev& C, int T, const float* sched, co
     return MUON_OK;
   }
   const bool serial = p->profiling;
+  if ((rc = front(0, (int)C.mats.size(), s, nullptr))) return rc;
+  if (!serial) HIP_TRY(hipEventRecord(p->lane_front[0], s));
   for (int l = 0; l < L; ++l) {
     hipStream_t ls = (l == 0 || serial) ? s : p->lane_streams[l - 1];
-    if (l > 0 && !serial) HIP_TRY(hipStreamWaitEvent(ls, p->lane_front[l - 1], 0));
-    if ((rc = front(C.lane_first[l], C.lane_first[l + 1], ls,
-                    (l + 1 < L && !serial) ? p->lane_front[l] : nullptr)))
-      return rc;
+    if (l > 0 && !serial) HIP_TRY(hipStreamWaitEvent(ls, p->lane_front[0], 0));
     for (const SetDev& S : C.sets)
       if (S.lane == l && (rc = enqueue_ns(p, S, T, sched, dyn, lr, wd, ls))) return rc;
   }
@@ -814,10 +813,9 @@ const float kQuintic[3] = {3.4445f, -4.7750f, 2.0315f};
 
 // Times the NS stages (T = 5) of a host plan on bounded synthetic operands:
 // every workspace byte 0x3C (bf16 and fp32 ~0.0115), X0 scaled to unit
-// Frobenius norm.  with_front: each chunk's fronts run too, lane-staggered as
-// in a step (the momentum kernel on synthetic gradients and momenta, also
-// 0x3C bytes, then k_norm), so the timing sees fronts overlapping NS.  4 runs
-// over all chunks, best of the last 3, in ms.
+// Frobenius norm.  with_front: each chunk's front runs too, as in a step (the
+// momentum kernel on synthetic gradients and momenta, also 0x3C bytes, then
+// k_norm).  best_ms: the time per step of the best of 3 timed repetitions.
 int time_ns(PlanHost&& H, bool with_front, float* best_ms) {
   muon_plan tp;
   tp.host = std::move(H);
@@ -878,9 +876,14 @@ int time_ns(PlanHost&& H, bool with_front, float* best_ms) {
   }
   float sched[15];
   for (int i = 0; i < 5; ++i) std::memcpy(sched + 3 * i, kQuintic, sizeof kQuintic);
+  // one untimed step, then 3 timed repetitions of `steps` consecutive steps
+  // (enough for about 4 ms, so that short steps are not timed one by one);
+  // the best repetition's time per step
   float best = 1e30f;
+  int steps = 1;
   for (int rep = 0; rep < 4; ++rep) {
     (void)hipEventRecord(e0, s);
+    for (int st = 0; st < steps; ++st)
     for (ChunkDev& C : tp.chunks) {
       if (with_front) {
         // the parameters are never touched (no update is applied here)
@@ -905,7 +908,8 @@ int time_ns(PlanHost&& H, bool with_front, float* best_ms) {
     if (hipEventSynchronize(e1) != hipSuccess) { cleanup(); return fail(MUON_EHIP, "tuning sync failed"); }
     float ms = 0;
     (void)hipEventElapsedTime(&ms, e0, e1);
-    if (rep > 0) best = std::min(best, ms);
+    if (rep == 0) steps = std::max(1, std::min(64, (int)std::ceil(4.0f / std::max(ms, 1e-3f))));
+    else best = std::min(best, ms / steps);
   }
   cleanup();
   *best_ms = best;

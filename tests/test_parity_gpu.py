@@ -96,7 +96,7 @@ def test_transformer_block_set_three_steps_all_matrices(M, tune, tmp_path):
     """The transformer-block workload: 16 bf16 matrices, 3 steps, fresh
     gradients each step, momentum and weights carried over; with the cost
     model's plan and with the plan bench.py times (shapes and the whole set
-    timed once into a fresh cache: tile plan, NS lanes, staggered fronts)."""
+    timed once into a fresh cache: tile plan and NS lanes)."""
     import torch
     from gpu_util import to_device, to_f64, rel
     from oracle import muon_oracle as O
