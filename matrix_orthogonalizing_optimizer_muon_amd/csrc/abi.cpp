@@ -812,10 +812,12 @@ int ortho_impl(muon_plan* p, const void* const* inputs, float* const* outputs, i
 const float kQuintic[3] = {3.4445f, -4.7750f, 2.0315f};
 
 // Times the NS stages (T = 5) of a host plan on bounded synthetic operands:
-// every workspace byte 0x3C (bf16 and fp32 ~0.0115), X0 scaled to unit
-// Frobenius norm.  with_front: each chunk's front runs too, as in a step (the
-// momentum kernel on synthetic gradients and momenta, also 0x3C bytes, then
-// k_norm).  best_ms: the time per step of the best of 3 timed repetitions.
+// the workspace filled with random bf16 values of magnitude [2^-7, 2^-6)
+// (read as fp32, values of the same size), X0 scaled to about unit Frobenius
+// norm, so the MFMAs see real data's switching activity.  with_front: each
+// chunk's front runs too, as in a step (the momentum kernel on gradients and
+// momenta filled the same way, then k_norm).  best_ms: the time per step of
+// the best of 3 timed repetitions.
 int time_ns(PlanHost&& H, bool with_front, float* best_ms) {
   muon_plan tp;
   tp.host = std::move(H);
@@ -844,7 +846,7 @@ int time_ns(PlanHost&& H, bool with_front, float* best_ms) {
     }
     char* fm = nullptr;
     if ((rc = dev_alloc(&tp, &fm, most))) { free_plan_memory(&tp); return rc; }
-    if (hipMemset(fm, 0x3C, most) != hipSuccess) {
+    if (launch_fill_random_bf16(fm, most, 2, nullptr) != hipSuccess) {
       free_plan_memory(&tp);
       return fail(MUON_EHIP, "tuning setup failed");
     }
@@ -856,8 +858,7 @@ int time_ns(PlanHost&& H, bool with_front, float* best_ms) {
   std::vector<float> r(n);
   for (size_t i = 0; i < n; ++i) {
     const MatPlan& M = tp.host.mats[i];
-    const double v = M.path ? 0.011474609375 : 0.011483338475227356;
-    r[i] = (float)(1.0 / (v * std::sqrt((double)M.m_pad * M.n_pad)));
+    r[i] = (float)(1.0 / (kTuneFillRms * std::sqrt((double)M.m_pad * M.n_pad)));
   }
   hipStream_t s = nullptr;
   hipEvent_t e0 = nullptr, e1 = nullptr;
@@ -867,7 +868,8 @@ int time_ns(PlanHost&& H, bool with_front, float* best_ms) {
     if (s) (void)hipStreamDestroy(s);
     free_plan_memory(&tp);
   };
-  if (hipMemset(tp.ws, 0x3C, tp.host.ws_bytes) != hipSuccess ||
+  if (launch_fill_random_bf16(tp.ws, tp.host.ws_bytes, 1, nullptr) != hipSuccess ||
+      hipDeviceSynchronize() != hipSuccess ||
       hipMemcpy(tp.rscale, r.data(), n * sizeof(float), hipMemcpyHostToDevice) != hipSuccess ||
       hipStreamCreate(&s) != hipSuccess || hipEventCreate(&e0) != hipSuccess ||
       hipEventCreate(&e1) != hipSuccess) {

@@ -773,6 +773,28 @@ hipError_t launch_gemm_cfg(int in_dt, int out_dt, const GemmParams& p, hipStream
 // measured slower on the 128x128 and the 256x256 tiles.
 // LDS_CAP: the LDS a block may take without lowering the blocks per CU its
 // registers allow (two 128x128 blocks per CU, one of any other).
+// One random bf16 (sign, fixed exponent 2^-7, 7 random mantissa bits) from a
+// 32-bit hash of its key.
+__device__ __forceinline__ uint32_t tune_bf16(uint32_t key) {
+  key ^= key >> 16;
+  key *= 0x7feb352du;
+  key ^= key >> 15;
+  key *= 0x846ca68bu;
+  key ^= key >> 16;
+  return (key & 0x8000u) | (120u << 7) | (key & 0x7fu);
+}
+
+__global__ __launch_bounds__(256) void k_fill_random_bf16(u32x4_t* __restrict__ p, int64_t n16, uint32_t seed) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) {
+    const uint32_t b = (uint32_t)(i * 8) ^ (seed * 0x9e3779b9u) ^ (uint32_t)(i >> 29);
+    u32x4_t v;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) v[w] = tune_bf16(b + 2 * w) | (tune_bf16(b + 2 * w + 1) << 16);
+    p[i] = v;
+  }
+}
+
 template <int BM, int BN, int WGM, int WGN>
 struct NtPipe {
   static constexpr int BK = 64, S = 2;
@@ -1422,6 +1444,16 @@ hipError_t launch_gemm(int tile_cfg, int in_dtype, int out_dtype, const GemmPara
     case 1: return launch_gemm_cfg<64, 64>(in_dtype, out_dtype, p, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_fill_random_bf16(void* p, uint64_t bytes, uint32_t seed, hipStream_t s) {
+  if (bytes % 16 || (bytes && !p)) return hipErrorInvalidValue;
+  const int64_t n16 = (int64_t)(bytes / 16);
+  if (n16 == 0) return hipSuccess;
+  const int64_t want = (n16 + 255) / 256;
+  const unsigned blocks = (unsigned)(want < 65536 ? want : 65536);
+  hipLaunchKernelGGL(k_fill_random_bf16, dim3(blocks), dim3(256), 0, s, static_cast<u32x4_t*>(p), n16, seed);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm_nt(int nt_cfg, int out_dtype, const GemmParams& p, hipStream_t s) {

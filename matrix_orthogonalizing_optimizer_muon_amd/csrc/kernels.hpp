@@ -176,6 +176,14 @@ hipError_t launch_gemm(int tile_cfg, int in_dtype, int out_dtype, const GemmPara
 // out_dtype: kF32 or kBF16; Cin (c_id) and out^T (ot_id) are bf16.
 hipError_t launch_gemm_nt(int nt_cfg, int out_dtype, const GemmParams& p, hipStream_t s);
 
+// Tuning operands: fills `bytes` (a multiple of 16) at p with random bf16
+// values of random sign and magnitude in [2^-7, 2^-6) (root mean square
+// 0.01193), from a hash of (seed, position).  Read as fp32, each pair of them
+// is a value of the same magnitude.  Random operands make the timed kernels
+// draw the power real data does (constant operands run the MFMAs faster).
+constexpr double kTuneFillRms = 0.011934;
+hipError_t launch_fill_random_bf16(void* p, uint64_t bytes, uint32_t seed, hipStream_t s);
+
 // Profiling: the next kernel launched by any launcher above on this thread
 // records its dispatch start and end in these events (hipExtLaunchKernel), the
 // times a kernel-trace profiler reports even when streams overlap.  launched()
