@@ -137,8 +137,10 @@ __device__ __forceinline__ void store4_vec(void* base, int dt, int64_t off, cons
 // 64-element row segment, 4 consecutive columns each, so every wave-wide
 // access covers four whole row segments (128 contiguous bytes of bf16, 256 of
 // fp32).  Thread tid holds rows rq + 16 k (rq = tid / 16, k = 0..3) at
-// columns cq .. cq + 3 (cq = 4 (tid % 16)).  The same layout makes the LDS
-// transpose below free of bank conflicts (row pitch 65 floats).
+// columns cq .. cq + 3 (cq = 4 (tid % 16)).  The LDS transpose below (row
+// pitch 65 floats) has two-way bank conflicts (lanes 8 apart in a row group
+// share a bank; 41% of its LDS cycles on the Llama-7B set, measured), which
+// this HBM-bound kernel's time does not show.
 __global__ __launch_bounds__(256) void k_ew_momentum(
     const EwMat* __restrict__ mats, const EwDyn* __restrict__ dyn,
     const int64_t* __restrict__ prefix, int nmats, int64_t t_begin, int64_t t_end,
@@ -987,7 +989,7 @@ __device__ __forceinline__ void nt_epilogue(const nt::f32x16_t (&acc)[BM / 32 / 
       // pass follows in which the 4 lanes of a quad take 4 columns and
       // consecutive quads consecutive 8-row groups, so every store instruction
       // writes four 256-byte runs of transposed rows and the 2-byte LDS reads
-      // stay conflict-free.  With Cin, its tile is first copied into the same
+      // of a column spread over the banks.  With Cin, its tile is first copied into the same
       // staging layout (16-byte row runs), and each lane combines the values
       // at its own positions in fp32 before they are rounded once to bf16.
       constexpr int PB = bf16_pitch<BN>();
