@@ -56,6 +56,12 @@ def parse():
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc output dirs (FETCH_SIZE, WRITE_SIZE passes over "
                          "--traffic-probe) into profiles/traffic.json for the workload's dominant kernel")
+    ap.add_argument("--core-sweep", action="store_true",
+                    help="time the NT core probe at its settled clock on random 8192 x 8192 x K bf16 "
+                         "products for K = 8192, 4096, 2048, 1024 (per-tile start-up cost)")
+    ap.add_argument("--clock-from", metavar="PMC_DIR", default=None,
+                    help="per-kernel engine clock and MFMA busy fraction from a rocprofv3 --pmc "
+                         "pass with GRBM_GUI_ACTIVE and SQ_VALU_MFMA_BUSY_CYCLES")
     ap.add_argument("--kernel", default=None, help="kernel instance for --traffic-from, e.g. k_nt<128,128,bf16>")
     ap.add_argument("--cache", default=os.path.join(os.path.expanduser("~"), ".cache", "muon_mi355x",
                                                     "tune.txt"))
@@ -176,6 +182,78 @@ def write_traffic(args, wl):
     with open(path, "w") as fh:
         json.dump(rec, fh, indent=1, sort_keys=True)
     print(json.dumps(entry))
+
+
+def core_sweep(torch, MU):
+    """The NT core probe (the 256x256 main loop without an epilogue) on random
+    N(0, 0.02^2) bf16 products 8192 x 8192 x K, K from 8192 down to 1024: a
+    tile's start-up cost (block launch, the first k-tiles' copies) shows as
+    the rate lost at short K.  About 0.2 s of untimed launches come first,
+    then each K twice (about 60 ms each), in alternation."""
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    n = NT_CORE_DIM
+    p = (torch.randn(n, n, device="cuda", generator=gen) * 0.02).to(torch.bfloat16)
+    q = (torch.randn(n, n, device="cuda", generator=gen) * 0.02).to(torch.bfloat16)
+    views = {k: (p[:, :k].contiguous(), q[:, :k].contiguous()) for k in (8192, 4096, 2048, 1024)}
+    MU.probe_nt_bf16(*views[8192], reps=100)
+    MU.probe_nt_bf16(*views[8192], reps=100)
+    rates = {k: [] for k in views}
+    for _ in range(2):
+        for k, (a, b) in views.items():
+            reps = max(1, min(100, int(60e-3 / (2.0 * n * n * k / 1.3e15))))
+            tf, _ = MU.probe_nt_bf16(a, b, reps=reps)
+            rates[k].append(round(tf, 1))
+    print(json.dumps({"metric": "NT core probe, TFLOP/s (settled clock)", "m": n, "n": n,
+                      "operands": "random N(0, 0.02^2) bf16",
+                      "k": {str(k): v for k, v in rates.items()}}))
+
+
+def clock_report(dirpath):
+    """Engine clock and MFMA busy fraction per kernel from one rocprofv3 --pmc
+    pass with GRBM_GUI_ACTIVE and SQ_VALU_MFMA_BUSY_CYCLES.  GRBM_GUI_ACTIVE
+    sums the busy engine-clock cycles of all XCDs over a dispatch, so divided
+    by the XCD count and the dispatch's duration it is the mean clock; the
+    MFMA busy cycles are summed over all SIMDs.  At a clock f and busy fraction
+    u the bf16 MFMA pipes issue PEAK * (f / 2.4 GHz) * u.  Dispatches shorter
+    than 200 us are left out: the counters' window exceeds their timestamps."""
+    import csv
+    import glob
+    import statistics
+    xcc, simds = None, None
+    disp = {}
+    for path in glob.glob(os.path.join(dirpath, "**", "*agent_info.csv"), recursive=True):
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                if r.get("Name", "").startswith("gfx"):
+                    xcc, simds = int(r["Num_Xcc"]), int(r["Simd_Count"])
+    for path in glob.glob(os.path.join(dirpath, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                d = disp.setdefault((path, r["Dispatch_Id"]), {"name": r["Kernel_Name"]})
+                d[r["Counter_Name"]] = float(r["Counter_Value"])
+                d["ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    if not xcc or not disp:
+        raise SystemExit(f"no agent info or counter rows in {dirpath}")
+    groups = {}
+    for d in disp.values():
+        if "GRBM_GUI_ACTIVE" not in d or "SQ_VALU_MFMA_BUSY_CYCLES" not in d or d["ns"] < 200_000:
+            continue
+        name = d["name"].replace("void ", "").replace("muon::(anonymous namespace)::", "")
+        m = re.match(r"[\w:]+(<[^()]*>)?", name)
+        key = m.group(0) if m else name[:60]
+        clk = d["GRBM_GUI_ACTIVE"] / xcc / d["ns"]               # GHz
+        busy = d["SQ_VALU_MFMA_BUSY_CYCLES"] / (d["GRBM_GUI_ACTIVE"] / xcc * simds)
+        groups.setdefault(key, []).append((d["ns"] * 1e-3, clk, busy))
+    out = []
+    for key, v in sorted(groups.items(), key=lambda kv: -sum(x[0] for x in kv[1])):
+        clk = [x[1] for x in v]
+        busy = [x[2] for x in v]
+        out.append({"kernel": key, "dispatches": len(v), "avg_us": round(statistics.mean(x[0] for x in v), 1),
+                    "clock_ghz": round(statistics.mean(clk), 3), "clock_range": [round(min(clk), 3), round(max(clk), 3)],
+                    "mfma_busy": round(statistics.mean(busy), 3), "busy_range": [round(min(busy), 3), round(max(busy), 3)],
+                    "bf16_mfma_tflops_issued": round(PEAK_BF16_TFLOPS * statistics.mean(clk) / 2.4
+                                                     * statistics.mean(busy), 1)})
+    print(json.dumps({"source": dirpath, "xcds": xcc, "simds": simds, "kernels": out}))
 
 
 def make_inputs(wl, torch):
@@ -395,7 +473,8 @@ def bench_vendor_gemm(args, wl, torch):
     (m x n times n x m; the full product, the library computes the upper
     triangle), A A (m x m times m x m) and B X (m x m times m x n), batched
     over the matrices of that shape, random N(0, 1) bf16 operands, both operands
-    contiguous.  Flops counted as issued by the vendor product (2 m n k)."""
+    contiguous, timed at the settled clock.  Flops counted as issued by the
+    vendor product (2 m n k)."""
     shapes = {}
     for r, c in wl.shapes:
         shapes.setdefault((min(r, c), max(r, c)), 0)
@@ -412,9 +491,17 @@ def bench_vendor_gemm(args, wl, torch):
         for name, p, q, fl in prods:
             for _ in range(3):
                 torch.matmul(p, q)
-            torch.cuda.synchronize()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            reps = 10
+            e0.record()
+            torch.matmul(p, q)
+            e1.record()
+            torch.cuda.synchronize()
+            one = max(e0.elapsed_time(e1), 1e-3)
+            # sustained MFMA work settles the part's clock within a few ms: about
+            # 0.1 s of untimed calls, then at least 20 ms (and 10 calls) timed
+            for _ in range(min(20000, int(100.0 / one))):
+                torch.matmul(p, q)
+            reps = max(10, min(20000, int(20.0 / one)))
             e0.record()
             for _ in range(reps):
                 torch.matmul(p, q)
@@ -464,6 +551,9 @@ def main():
     if args.traffic_from:
         write_traffic(args, wl)
         return
+    if args.clock_from:
+        clock_report(args.clock_from)
+        return
     import torch
     import matrix_orthogonalizing_optimizer_muon_amd as MU
 
@@ -473,6 +563,9 @@ def main():
         return
     if args.vendor_gemm:
         bench_vendor_gemm(args, wl, torch)
+        return
+    if args.core_sweep:
+        core_sweep(torch, MU)
         return
     os.makedirs(os.path.dirname(args.cache), exist_ok=True)
     owner_info = None
@@ -568,7 +661,10 @@ def main():
         gen = torch.Generator(device="cuda").manual_seed(11)
         pa = (torch.randn(NT_CORE_DIM, NT_CORE_DIM, device="cuda", generator=gen) * 0.02).to(torch.bfloat16)
         qa = (torch.randn(NT_CORE_DIM, NT_CORE_DIM, device="cuda", generator=gen) * 0.02).to(torch.bfloat16)
-        nt_core, _ = MU.probe_nt_bf16(pa, qa, reps=5)
+        # sustained MFMA work lowers the part's clock within a few ms (its power
+        # limit), so 100 untimed launches (about 0.1 s) come before the 100 timed
+        MU.probe_nt_bf16(pa, qa, reps=100)
+        nt_core, _ = MU.probe_nt_bf16(pa, qa, reps=100)
         del pa, qa
         a = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
         b = torch.empty_like(a)
@@ -584,7 +680,7 @@ def main():
                        "muon_probe_mfma_bf16_random, the switching activity of real data "
                        "under the part's power limit), muon_probe_nt_bf16 (the 256x256 NT "
                        "contraction core without an epilogue on a random 8192^3 bf16 product, "
-                       "5 launches) and muon_probe_hbm_copy (1 GiB copy, read + written bytes, "
+                       "100 launches after 100 untimed ones) and muon_probe_hbm_copy (1 GiB copy, read + written bytes, "
                        "best of 8 launch variants)"}
     ns_flops = info["ns_flops_min"]
     bf16 = wl.dtype == "bf16"
