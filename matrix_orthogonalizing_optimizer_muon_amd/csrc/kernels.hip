@@ -845,6 +845,22 @@ __device__ __forceinline__ void st8(void* base, int64_t off, const float* v) {
   }
 }
 
+// A 16-byte output store of the staged epilogues (element offset off of a
+// bf16 buffer), nontemporal when the launch streams its outputs
+// (GemmParams::stream_out).  The nontemporal form is a buffer store whose
+// cache policy is an immediate, so the compiler cannot fold the two forms
+// into one store and drop the hint; its descriptor spans 4 GiB from base,
+// and every output buffer is smaller than 2 GiB.
+constexpr int kCpolNt = 2;   // cache-policy operand: the nt bit
+__device__ __forceinline__ void st_out16(void* base, int64_t off, u32x4_t v, bool stream) {
+  if (stream) {
+    const __amdgpu_buffer_rsrc_t r = nt::make_rsrc(base, 0xFFFFFFFFu);
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, (uint32_t)(off * 2), 0, kCpolNt);
+  } else {
+    *(GLOBAL_AS u32x4_t*)(static_cast<uint16_t*>(base) + off) = v;
+  }
+}
+
 // What the weight update applied in an epilogue needs, read once per block
 // (the output stores may alias the descriptor tables, so nothing is re-read).
 struct UpdCtx {
@@ -966,6 +982,7 @@ __device__ __forceinline__ void nt_epilogue(const nt::f32x16_t (&acc)[BM / 32 / 
   const WorkItem it = p.items[blockIdx.x];
   const bool mirror = p.sym && it.tm != it.tn;
   const bool fuse = p.fuse != 0, ftrans = fuse && nmp->trans;
+  const bool stream = p.stream_out != 0;
   const bool colpass = mirror || OutT != nullptr || ftrans;
   const int m_pad = nmp->m_pad;
   UpdCtx uc = {nullptr, nullptr, 0, 0.f, 0.f, 0.f, 0, 0};
@@ -1046,8 +1063,7 @@ __device__ __forceinline__ void nt_epilogue(const nt::f32x16_t (&acc)[BM / 32 / 
       lds_barrier();
 #pragma unroll 4
       for (int r = tid / TPR; r < BM; r += RPP)
-        *(GLOBAL_AS u32x4_t*)(static_cast<uint16_t*>(Out) + (int64_t)(m0 + r) * ldo + n0 + cc) =
-            *(const MUON_LDS u32x4_t*)at(r, cc);
+        st_out16(Out, (int64_t)(m0 + r) * ldo + n0 + cc, *(const MUON_LDS u32x4_t*)at(r, cc), stream);
       if (colpass) {
         // items (column jc, 8-row group r0): item wi is column 4 (wi / (4 GR))
         // + wi % 4 and row group (wi / 4) % GR; with NT a multiple of 4 GR a
@@ -1064,8 +1080,8 @@ __device__ __forceinline__ void nt_epilogue(const nt::f32x16_t (&acc)[BM / 32 / 
           for (int h = 0; h < 4; ++h)
             w[h] = (uint32_t)*at(r0 + 2 * h, jc) | ((uint32_t)*at(r0 + 2 * h + 1, jc) << 16);
           const u32x4_t q = u32x4_t{w[0], w[1], w[2], w[3]};
-          if (OutT) *(GLOBAL_AS u32x4_t*)(static_cast<uint16_t*>(OutT) + (int64_t)j * m_pad + i0) = q;
-          if (mirror) *(GLOBAL_AS u32x4_t*)(static_cast<uint16_t*>(Out) + (int64_t)j * ldo + i0) = q;
+          if (OutT) st_out16(OutT, (int64_t)j * m_pad + i0, q, stream);
+          if (mirror) st_out16(Out, (int64_t)j * ldo + i0, q, stream);
         }
       }
       return;
@@ -1158,7 +1174,7 @@ __device__ __forceinline__ void nt_epilogue(const nt::f32x16_t (&acc)[BM / 32 / 
       if (!ftrans) {
 #pragma unroll 4
         for (int r = tid / TPR; r < BM; r += RPP)
-          *(GLOBAL_AS u32x4_t*)(W + (int64_t)(m0 + r) * ldw + n0 + cc) = *(const MUON_LDS u32x4_t*)at(r, cc);
+          st_out16(W, (int64_t)(m0 + r) * ldw + n0 + cc, *(const MUON_LDS u32x4_t*)at(r, cc), stream);
       } else {
 #pragma unroll 2
         for (int ci = 0; ci < CI; ++ci) {
@@ -1167,7 +1183,7 @@ __device__ __forceinline__ void nt_epilogue(const nt::f32x16_t (&acc)[BM / 32 / 
 #pragma unroll
           for (int h = 0; h < 4; ++h)
             w[h] = (uint32_t)*at(r0 + 2 * h, jc) | ((uint32_t)*at(r0 + 2 * h + 1, jc) << 16);
-          *(GLOBAL_AS u32x4_t*)(W + (int64_t)(n0 + jc) * ldw + m0 + r0) = u32x4_t{w[0], w[1], w[2], w[3]};
+          st_out16(W, (int64_t)(n0 + jc) * ldw + m0 + r0, u32x4_t{w[0], w[1], w[2], w[3]}, stream);
         }
       }
       return;

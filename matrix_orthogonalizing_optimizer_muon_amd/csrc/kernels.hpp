@@ -139,6 +139,10 @@ struct GemmParams {
   // NT kernel, kShapeApplyT: 1 = Q is X itself (m_pad x n_pad, read k-major
   // with LDS transpose reads) instead of X^T
   int32_t qt;
+  // NT kernel: 1 = the staged bf16 tiles go out with nontemporal stores (set
+  // when the launch writes more than the last-level cache holds, so that its
+  // outputs would not stay cached for the next launch anyway)
+  int32_t stream_out;
 };
 
 // Kernel configurations (the planner's tile choices).
