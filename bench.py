@@ -59,6 +59,10 @@ def parse():
     ap.add_argument("--core-sweep", action="store_true",
                     help="time the NT core probe at its settled clock on random 8192 x 8192 x K bf16 "
                          "products for K = 8192, 4096, 2048, 1024 (per-tile start-up cost)")
+    ap.add_argument("--epilogue-probe", action="store_true",
+                    help="time the NT core probe on random 8192 x 8192 x 4096 bf16 products without an "
+                         "output, with a bf16 row pass, with row and column passes, and with those "
+                         "stores nontemporal (what writing a 256x256 tile costs)")
     ap.add_argument("--clock-from", metavar="PMC_DIR", default=None,
                     help="per-kernel engine clock and MFMA busy fraction from a rocprofv3 --pmc "
                          "pass with GRBM_GUI_ACTIVE and SQ_VALU_MFMA_BUSY_CYCLES")
@@ -206,6 +210,43 @@ def core_sweep(torch, MU):
     print(json.dumps({"metric": "NT core probe, TFLOP/s (settled clock)", "m": n, "n": n,
                       "operands": "random N(0, 0.02^2) bf16",
                       "k": {str(k): v for k, v in rates.items()}}))
+
+
+def epilogue_probe(torch, MU):
+    """The NT core probe (256x256 tiles, K = 4096 as in the Llama-7B set's A A
+    and B X launches) with the outputs the NS products write: none (the sum
+    of each thread's accumulators), a bf16 row pass (128 KB per tile), row and
+    column passes (256 KB, a transposed copy or a mirrored tile), and the same
+    with nontemporal stores.  About 0.2 s of untimed launches first; each
+    variant twice in alternation, 100 timed launches after 20 untimed."""
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    n, k = NT_CORE_DIM, 4096
+    p = (torch.randn(n, k, device="cuda", generator=gen) * 0.02).to(torch.bfloat16)
+    q = (torch.randn(n, k, device="cuda", generator=gen) * 0.02).to(torch.bfloat16)
+    c = torch.empty(n, n, device="cuda", dtype=torch.bfloat16)
+    ct = torch.empty(n, n, device="cuda", dtype=torch.bfloat16)
+    MU.probe_nt_bf16(p, q, reps=100)
+    MU.probe_nt_bf16(p, q, reps=100)
+    names = {0: "no output", 1: "row pass", 2: "row and column passes", 3: "row and column passes, nontemporal"}
+    rates = {m: [] for m in names}
+    for _ in range(2):
+        for mode in names:
+            if mode == 0:
+                MU.probe_nt_bf16(p, q, reps=20)
+                tf, _ = MU.probe_nt_bf16(p, q, reps=100)
+            else:
+                MU.probe_nt_out_bf16(p, q, c, ct, mode=mode, reps=20)
+                tf = MU.probe_nt_out_bf16(p, q, c, ct, mode=mode, reps=100)
+            rates[mode].append(tf)
+    waves = (n // 256) ** 2 / 256            # 256x256 tiles per CU per launch
+    fl = 2.0 * n * n * k
+    out = []
+    for mode, name in names.items():
+        best = max(rates[mode])
+        out.append({"mode": mode, "epilogue": name, "tflops": [round(t, 1) for t in rates[mode]],
+                    "us_per_tile": round(fl / (best * 1e12) / waves * 1e6, 2)})
+    print(json.dumps({"metric": "NT core probe with output epilogues, TFLOP/s (settled clock)",
+                      "m": n, "n": n, "k": k, "operands": "random N(0, 0.02^2) bf16", "variants": out}))
 
 
 def clock_report(dirpath):
@@ -566,6 +607,9 @@ def main():
         return
     if args.core_sweep:
         core_sweep(torch, MU)
+        return
+    if args.epilogue_probe:
+        epilogue_probe(torch, MU)
         return
     os.makedirs(os.path.dirname(args.cache), exist_ok=True)
     owner_info = None

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define MUON_ABI_VERSION 12
+#define MUON_ABI_VERSION 13
 
 typedef enum muon_status {
   MUON_OK = 0,
@@ -407,6 +407,19 @@ int muon_probe_hbm_copy(void* dst, const void* src, uint64_t bytes, int reps, do
  * device or launch error. */
 int muon_probe_nt_bf16(const void* P, const void* Q, int m, int n, int k, int reps, double* tflops,
                        double* checksum);
+/* The same core with an epilogue shaped as the NS products' bf16 one, to
+ * read what writing the product costs: every 256x256 tile of P Q^T is
+ * rounded to bf16 (nearest even), staged once in LDS and stored by a row
+ * pass into C (m x n row-major); mode 2 adds a column pass storing the tile
+ * transposed into CT (n x m row-major, the shape of a transposed copy or a
+ * mirrored tile); mode 3 is mode 2 with nontemporal stores.  P, Q, C, CT:
+ * caller-owned device buffers, 16-byte aligned (CT unused and nullable in
+ * mode 1); sizes as muon_probe_nt_bf16, m n below 2^30.  One warm-up launch,
+ * then reps timed launches; tflops receives 2 m n k reps / time / 1e12.
+ * EINVAL: NULL pointer, mode, sizes, alignment, reps outside [1, 100].
+ * EHIP: device or launch error. */
+int muon_probe_nt_out_bf16(const void* P, const void* Q, void* C, void* CT, int m, int n, int k, int mode,
+                           int reps, double* tflops);
 
 /*
  * One Muon step of ONE matrix that allocates no device memory, for callers

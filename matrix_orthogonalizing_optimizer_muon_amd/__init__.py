@@ -15,7 +15,7 @@ from . import _lib as L
 from ._lib import MuonError  # noqa: F401
 
 __all__ = ["MuonPlan", "AdamWPlan", "MuonError", "library_path", "assign_owners",
-           "probe_mfma_bf16", "probe_nt_bf16", "probe_hbm_copy", "step_noalloc"]
+           "probe_mfma_bf16", "probe_nt_bf16", "probe_nt_out_bf16", "probe_hbm_copy", "step_noalloc"]
 
 
 def library_path():
@@ -330,6 +330,29 @@ def probe_nt_bf16(P, Q, reps=5):
                                        int(P.shape[0]), int(Q.shape[0]), int(P.shape[1]), int(reps),
                                        ctypes.byref(tf), ctypes.byref(cs)))
     return tf.value, cs.value
+
+
+def probe_nt_out_bf16(P, Q, C, CT=None, mode=1, reps=5):
+    """Measured rate of the NT contraction core with a bf16 output epilogue
+    (muon_probe_nt_out_bf16): C (m x n) receives P Q^T rounded to bf16; modes
+    2 and 3 also store its transpose into CT (n x m), mode 3 with nontemporal
+    stores.  All contiguous bf16 device tensors; m and n multiples of 256, k a
+    multiple of 64.  Returns TFLOP/s."""
+    import torch
+    m, k = P.shape
+    n = Q.shape[0]
+    want = [(P, (m, k)), (Q, (n, k)), (C, (m, n))] + ([(CT, (n, m))] if mode >= 2 else [])
+    for t, shape in want:
+        if not (t is not None and t.is_cuda and t.is_contiguous() and t.dtype == torch.bfloat16
+                and tuple(t.shape) == shape):
+            raise ValueError(f"P, Q, C and CT must be contiguous bf16 device tensors of shapes "
+                             f"(m, k), (n, k), (m, n) and (n, m)")
+    tf = ctypes.c_double()
+    ct = ctypes.c_void_p(CT.data_ptr()) if CT is not None else ctypes.c_void_p(None)
+    L.check(L.lib().muon_probe_nt_out_bf16(ctypes.c_void_p(P.data_ptr()), ctypes.c_void_p(Q.data_ptr()),
+                                           ctypes.c_void_p(C.data_ptr()), ct, int(m), int(n), int(k),
+                                           int(mode), int(reps), ctypes.byref(tf)))
+    return tf.value
 
 
 def probe_hbm_copy(dst, src, reps=10):

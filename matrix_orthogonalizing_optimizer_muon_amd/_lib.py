@@ -104,6 +104,9 @@ PROTOTYPES = {
     "muon_probe_nt_bf16": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
                                           ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_double),
                                           ctypes.POINTER(ctypes.c_double)]),
+    "muon_probe_nt_out_bf16": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                              ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                              ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_double)]),
     "muon_probe_hbm_copy": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64,
                                            ctypes.c_int, ctypes.POINTER(ctypes.c_double)]),
     "muon_plan_matrix_cost": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int,

@@ -1137,6 +1137,30 @@ int muon_probe_nt_bf16(const void* P, const void* Q, int m, int n, int k, int re
   return MUON_OK;
 }
 
+int muon_probe_nt_out_bf16(const void* P, const void* Q, void* C, void* CT, int m, int n, int k, int mode,
+                           int reps, double* tflops) {
+  if (!P || !Q || !C || !tflops || (mode >= 2 && !CT)) return fail(MUON_EINVAL, "NULL pointer");
+  if (mode < 1 || mode > 3) return fail(MUON_EINVAL, "mode must be 1, 2 or 3");
+  if (m <= 0 || n <= 0 || k <= 0 || m % kProbeNtTile || n % kProbeNtTile || k % 64)
+    return fail(MUON_EINVAL, "m and n must be positive multiples of 256, k a positive multiple of 64");
+  if ((int64_t)m * k >= (1ll << 31) || (int64_t)n * k >= (1ll << 31) || (int64_t)m * n >= (1ll << 30))
+    return fail(MUON_EINVAL, "m k and n k must stay below 2^31, m n below 2^30");
+  if (!aligned16(P) || !aligned16(Q) || !aligned16(C) || (mode >= 2 && !aligned16(CT)))
+    return fail(MUON_EINVAL, "P, Q, C and CT must be 16-byte aligned");
+  if (reps < 1 || reps > 100) return fail(MUON_EINVAL, "reps out of [1, 100]");
+  int rc;
+  ProbeRun r;
+  if ((rc = r.init())) return rc;
+  HIP_TRY(launch_probe_nt_out(P, Q, C, CT, m, n, k, mode, r.s));   // warm-up
+  HIP_TRY(hipEventRecord(r.e0, r.s));
+  for (int i = 0; i < reps; ++i) HIP_TRY(launch_probe_nt_out(P, Q, C, CT, m, n, k, mode, r.s));
+  HIP_TRY(hipEventRecord(r.e1, r.s));
+  double ms = 0;
+  if ((rc = r.elapsed(&ms))) return rc;
+  *tflops = ms > 0 ? 2.0 * m * (double)n * k * reps / (ms * 1e-3) / 1e12 : 0.0;
+  return MUON_OK;
+}
+
 int muon_probe_hbm_copy(void* dst, const void* src, uint64_t bytes, int reps, double* gbs) {
   if (!dst || !src || !gbs) return fail(MUON_EINVAL, "NULL pointer");
   if (bytes == 0 || bytes % 16 || !aligned16(dst) || !aligned16(src))

@@ -22,6 +22,13 @@ hipError_t launch_probe_mfma(int blocks, int iters, bool random_operands, float*
 // multiples of 256, k a multiple of 64, m k and n k below 2^31.
 constexpr int kProbeNtTile = 256, kProbeNtThreads = 512;
 hipError_t launch_probe_nt(const void* P, const void* Q, int m, int n, int k, float* out, hipStream_t s);
+// k_probe_nt_out: the same core with an epilogue that writes the product:
+// each 256x256 tile is rounded to bf16 (RNE), staged once in LDS and stored
+// by a row pass into C (m x n row-major); mode 2 adds a column pass storing
+// the transposed tile into CT (n x m row-major); mode 3 is mode 2 with
+// nontemporal stores.  m n below 2^30.
+hipError_t launch_probe_nt_out(const void* P, const void* Q, void* C, void* CT, int m, int n, int k, int mode,
+                               hipStream_t s);
 // k_probe_copy: dst[i] = src[i] for n16 16-byte words (grid-stride, `blocks`
 // blocks of 256 threads, 4 words in flight per thread), plain or nontemporal
 // loads and stores; blocks <= 0: one block per contiguous 1024-word run.

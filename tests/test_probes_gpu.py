@@ -1,7 +1,8 @@
 """Ceiling probes through the C ABI: the dense bf16 MFMA loop, the NT
-contraction core and the HBM copy give rates inside what the part can
-physically reach (published dense bf16 peak about 2.5 PFLOP/s, HBM3E 8 TB/s),
-the core computes the product it times, and the copy probe copies."""
+contraction core (alone and with an output epilogue) and the HBM copy give
+rates inside what the part can physically reach (published dense bf16 peak
+about 2.5 PFLOP/s, HBM3E 8 TB/s), the core computes the product it times, and
+the copy probe copies."""
 import pytest
 
 pytestmark = pytest.mark.gpu
@@ -51,6 +52,40 @@ def test_hbm_copy_probe_copies_and_rate_is_physical(M):
         M.probe_hbm_copy(dst[:-4], src)
     with pytest.raises(M.MuonError):
         M.probe_hbm_copy(dst[4:], dst[:-4])   # overlapping buffers
+
+
+def test_nt_core_probe_with_output_writes_the_product(M):
+    """The output epilogue of the core probe stores P Q^T rounded to bf16 once
+    from its fp32 accumulators: against the fp64 product rounded to bf16, every
+    element within one bf16 ulp and nearly all equal (positive operands, so
+    only values on a rounding boundary can differ); the column pass stores
+    exactly the transpose, with plain and with nontemporal stores."""
+    import torch
+    g = torch.Generator().manual_seed(6)
+    m, n, k = 512, 768, 1024
+    P = torch.rand(m, k, generator=g).to(torch.bfloat16)
+    Q = torch.rand(n, k, generator=g).to(torch.bfloat16)
+    ref = (P.double() @ Q.double().t()).to(torch.bfloat16).float()
+    Pd, Qd = P.cuda(), Q.cuda()
+    for mode in (1, 2, 3):
+        C = torch.full((m, n), float("nan"), device="cuda", dtype=torch.bfloat16)
+        CT = torch.full((n, m), float("nan"), device="cuda", dtype=torch.bfloat16) if mode >= 2 else None
+        tf = M.probe_nt_out_bf16(Pd, Qd, C, CT, mode=mode, reps=2)
+        got = C.float().cpu()
+        ulp = torch.abs(ref) * 2.0 ** -7
+        exact = float((got == ref).double().mean())
+        print(f"nt core probe, output mode {mode}: {tf:.1f} TFLOP/s, {exact:.4%} equal to the rounded "
+              f"fp64 product", flush=True)
+        assert 0 < tf <= 1.02 * PEAK_BF16_TFLOPS
+        assert bool(torch.all(torch.abs(got - ref) <= ulp)), "an element is more than one ulp off"
+        assert exact >= 0.99
+        if CT is not None:
+            assert torch.equal(CT.cpu().view(torch.int16), C.cpu().t().contiguous().view(torch.int16))
+    C = torch.empty((m, n), device="cuda", dtype=torch.bfloat16)
+    with pytest.raises(M.MuonError):   # no such mode
+        M.probe_nt_out_bf16(Pd, Qd, C, None, mode=0)
+    with pytest.raises(ValueError):    # the transposed copy needs CT
+        M.probe_nt_out_bf16(Pd, Qd, C, None, mode=2)
 
 
 def test_nt_core_probe_checksum_and_rate(M):
