@@ -150,7 +150,7 @@ def counter_rows(dirpath, counter):
     return out
 
 
-def write_traffic(args, wl):
+def write_traffic(args, wl, path=None):
     """Per-launch HBM bytes of one kernel from FETCH_SIZE / WRITE_SIZE (KiB per
     dispatch), each scaled so that the calibration copy reads as COPY_BYTES.
     The passes ran --traffic-probe with the same --warmup (warmup + 2 steps, the
@@ -175,7 +175,7 @@ def write_traffic(args, wl):
                          f"do not fit {args.warmup} + 2 steps")
     entry["launches_per_step"] = entry["fetch_dispatches"] / (args.warmup + 2)
     entry["copy_factor"] = [entry["fetch_copy_factor"], entry["write_copy_factor"]]
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+    path = path or os.path.join(ROOT, "profiles", "traffic.json")
     rec = {"entries": []}
     if os.path.exists(path):
         with open(path) as fh:

@@ -2,12 +2,15 @@
 
 `--clock-from` turns one rocprofv3 --pmc pass (GRBM_GUI_ACTIVE and
 SQ_VALU_MFMA_BUSY_CYCLES per dispatch) into a per-kernel clock and MFMA busy
-fraction; the files here are written by hand with known values.
+fraction; `--traffic-from` turns a FETCH_SIZE and a WRITE_SIZE pass into
+bytes per launch, scaled by the calibration copy.  The files here are written
+by hand with known values.
 """
 import csv
 import importlib.util
 import json
 import os
+import types
 
 import pytest
 
@@ -67,3 +70,58 @@ def test_clock_report_recovers_clock_and_busy(tmp_path, capsys):
 def test_clock_report_without_counters_fails(tmp_path):
     with pytest.raises(SystemExit):
         _bench().clock_report(str(tmp_path))
+
+
+NT256 = "void muon::(anonymous namespace)::k_nt<256, 256, 2, 4, unsigned short, false>(muon::GemmParams)"
+NT256QT = "void muon::(anonymous namespace)::k_nt<256, 256, 2, 4, unsigned short, true>(muon::GemmParams)"
+NT128F = "void muon::(anonymous namespace)::k_nt<128, 128, 2, 2, float, false>(muon::GemmParams)"
+COPY = "void at::native::vectorized_elementwise_kernel<4, at::native::FillFunctor<float>>(int)"
+
+
+def test_kernel_labels_match_profiler_names():
+    b = _bench()
+    assert b.demangled("k_nt<256,256,bf16>").search(NT256)
+    assert not b.demangled("k_nt<256,256,bf16>").search(NT256QT)
+    assert b.demangled("k_nt<256,256,bf16,qt>").search(NT256QT)
+    assert b.demangled("k_nt<128,128,f32>").search(NT128F)
+    assert not b.demangled("k_nt<128,128,bf16>").search(NT128F)
+    assert b.demangled("k_ew_momentum").search("muon::(anonymous namespace)::k_ew_momentum(muon::EwMat const*)")
+
+
+def _pmc(dirpath, counter, rows):
+    dirpath.mkdir()
+    with open(dirpath / "x_counter_collection.csv", "w", newline="") as fh:
+        w = csv.writer(fh)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        for i, (name, kib) in enumerate(rows):
+            w.writerow([i, name, counter, kib])
+
+
+def test_traffic_record_scales_by_the_calibration_copy(tmp_path, capsys):
+    b = _bench()
+    gib_kib = (1 << 30) / 1024
+    # warmup 1 + 2 steps, 2 launches per step; the copy reads twice its size
+    # (the fetch counter's factor is then 1/2) and writes exactly its size
+    fetch = [(NT256, 1000.0), (NT256, 3000.0)] * 3 + [(NT256QT, 9e9), (COPY, 2 * gib_kib)]
+    write = [(NT256, 500.0)] * 6 + [(COPY, gib_kib)]
+    _pmc(tmp_path / "f", "FETCH_SIZE", fetch)
+    _pmc(tmp_path / "w", "WRITE_SIZE", write)
+    args = types.SimpleNamespace(kernel="k_nt<256,256,bf16>", warmup=1,
+                                 traffic_from=[str(tmp_path / "f"), str(tmp_path / "w")])
+    wl = types.SimpleNamespace(name="synthetic set")
+    out = tmp_path / "traffic.json"
+    b.write_traffic(args, wl, path=str(out))
+    rec = json.loads(out.read_text())["entries"]
+    assert len(rec) == 1
+    e = rec[0]
+    assert e["launches_per_step"] == 2
+    assert e["fetch_bytes_per_launch"] == pytest.approx(2000.0 * 1024 * 0.5)
+    assert e["write_bytes_per_launch"] == pytest.approx(500.0 * 1024)
+    assert e["source"] == b.source_digest() and e["workload"] == "synthetic set"
+    # a second record for the same kernel and workload replaces the first
+    b.write_traffic(args, wl, path=str(out))
+    assert len(json.loads(out.read_text())["entries"]) == 1
+    # dispatch counts that do not fit warmup + 2 steps are refused
+    args.warmup = 2
+    with pytest.raises(SystemExit):
+        b.write_traffic(args, wl, path=str(out))
